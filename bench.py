@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""QSA layer-path throughput on one MI355X.
+
+A step is one pass of the whole per-layer path -- append + pool the rows'
+index keys, score every visible pooled block, select the top 512 blocks,
+gathered attention with the split-K LSE merge -- over all 12 QSA layers of
+one synthetic batch, captured once as a HIP graph and replayed.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload verify_262k]
+
+The metric is query-rows/s per layer (rows x layers x steps / time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="verify_262k",
+                    choices=["verify_262k", "decode_262k", "decode_32k", "prefill", "batched"])
+    ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-m1", action="store_true", help="skip the M=1 companion measurement")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- set-up
+
+class SeqLayer:
+    """One layer of one sequence, resident on the device."""
+
+    def __init__(self, Q, wl, layer, dev):
+        import torch
+        import datagen
+
+        n = wl.n_ctx
+        self.cap = -(-(n + 4) // 256) * 256
+        bf = torch.bfloat16
+        self.idx_cache = torch.zeros((1, self.cap, 128), dtype=bf, device=dev)
+        self.pooled = torch.zeros((1, self.cap // 4, 128), dtype=torch.float32, device=dev)
+        self.k = torch.zeros((wl.hkv, self.cap, wl.head_dim), dtype=bf, device=dev)
+        self.v = torch.zeros_like(self.k)
+        m = wl.m
+        self.idx_q = torch.empty((m, 4, 128), dtype=bf, device=dev)
+        self.q = torch.empty((m, wl.hq, wl.head_dim), dtype=bf, device=dev)
+        idx32 = torch.empty((n, 128), dtype=torch.float32, device=dev)
+        datagen.fill_layer_device(wl, layer, idx32, self.idx_q, self.q, self.k, self.v)
+        idx = idx32.to(bf)
+        del idx32
+        Q.qsa_append_pool(idx, torch.arange(n, dtype=torch.int64, device=dev), self.idx_cache, self.pooled)
+        self.rows = torch.tensor(wl.rows, dtype=torch.int64, device=dev)
+        self.new_idx = idx[self.rows].contiguous()   # the rows' own keys, re-appended each step
+        self.new_pos = self.rows.clone()
+        self.kv = Q.KvSegments.single(self.k, self.v, n)
+        self.row_seq = None
+
+
+def build_single(Q, wl, layers, dev):
+    import torch
+
+    L = [SeqLayer(Q, wl, i, dev) for i in range(layers)]
+    nb_max = (max(wl.rows) + 1) // 4
+    m = wl.m
+    k = wl.k_blocks
+    shared = dict(
+        scores=torch.empty((m, -(-nb_max // 4) * 4), dtype=torch.float32, device=dev),
+        sel=torch.empty((m, k), dtype=torch.int32, device=dev),
+        n_sel=torch.empty((m,), dtype=torch.int32, device=dev),
+        out=torch.empty((m, wl.hq, wl.head_dim), dtype=torch.bfloat16, device=dev),
+        lse=torch.empty((m, wl.hq), dtype=torch.float32, device=dev),
+        ws=torch.empty(max(1, Q.qsa_attn_workspace_bytes(m, wl.hq, wl.head_dim, k)), dtype=torch.uint8, device=dev),
+        ws_sel=None,
+    )
+    wsb = Q.qsa_select_workspace_bytes(m, nb_max, k)
+    if wsb:
+        shared["ws_sel"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    return L, shared, nb_max
+
+
+def step_fn(Q, L, sh, nb_max, wl, only=None):
+    """Enqueue one step (all layers).  ``only`` restricts to one kernel family."""
+    def run():
+        for ly in L:
+            if only in (None, "append"):
+                Q.qsa_append_pool(ly.new_idx, ly.new_pos, ly.idx_cache, ly.pooled, seq=getattr(ly, "seq", None))
+            if only in (None, "score"):
+                Q.qsa_score_blocks(ly.idx_q, ly.rows, ly.pooled, sh["scores"], nb_max, row_seq=ly.row_seq)
+            if only in (None, "select"):
+                Q.qsa_select_topk(sh["scores"], ly.rows, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"], sh["ws_sel"])
+            if only in (None, "attn"):
+                Q.qsa_gathered_attn(ly.q, ly.rows, ly.kv, sh["sel"], sh["n_sel"], sh["out"], sh["lse"], wl.hkv,
+                                    row_seq=ly.row_seq, workspace=sh["ws"])
+    return run
+
+
+def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
+    """Average device time of one launch of ``kind`` (HIP events on the
+    launch stream).  A spin kernel runs first so that every event/launch pair
+    is queued before the device reaches it (no host gaps in the interval)."""
+    import torch
+
+    evs = []
+    torch.cuda.synchronize()
+    try:
+        torch.cuda._sleep(int(2e8))
+    except Exception:  # pragma: no cover - spin kernel unavailable: host gaps may inflate the figure
+        pass
+    for _ in range(reps):
+        for ly in L:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            step_fn(Q, [ly], sh, nb_max, wl, only=kind)()
+            b.record()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return sum(ts) / len(ts), min(ts), max(ts)
+
+
+# ----------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl_name: str, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on the host: same per-layer work for the
+    same rows (pool the blocks the new tokens complete, score, select, attend)."""
+    import numpy as np
+
+    import datagen
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    d = datagen.gen_layer(wl_name)
+    wl = d["workload"]
+    pooled = O.pool_index_keys(d["idx"])
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    rows = [int(r) for r in d["rows"]]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        for i, p in enumerate(rows):
+            lo = (p // 4) * 4
+            if p % 4 == 3:
+                pooled[p // 4] = O.pool_index_keys(d["idx"][lo:lo + 4])[0]
+            s = O.score_blocks(d["idx_q"][i], pooled, p + 1)
+            sel = O.select_blocks(s, wl.k_blocks)
+            tok = O.attended_tokens(sel, p + 1)
+            O.attend(d["q"][i], d["k"], d["v"], tok, scale)
+            done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": done / el, "unit": "query-rows/s per layer", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} rows of one {wl_name} layer (n_ctx {wl.n_ctx}) in {el:.1f} s, numpy fp64"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import datagen
+    import long_context_sparse_qsa_amd as Q
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    Q.qsa_device_check()
+    wl = datagen.WORKLOADS[args.workload]
+    layers = args.layers
+    t_setup = time.time()
+    L, sh, nb_max = build_single(Q, wl, layers, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] set-up {wl.name}: {layers} layers, n_ctx {wl.n_ctx}, M {wl.m} in "
+          f"{time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
+
+    run = step_fn(Q, L, sh, nb_max, wl)
+    run()
+    torch.cuda.synchronize()
+    if args.eager:
+        replay = run
+    else:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            run()
+        replay = g.replay
+    for _ in range(args.warmup):
+        replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_step = ms / args.steps
+    rows_per_s = wl.m * layers * args.steps / (ms / 1e3)
+
+    # per-kernel device time (dominant kernel: scoring, HBM-bound)
+    kt = {kind: per_launch_us(Q, L, sh, nb_max, wl, kind) for kind in ("score", "select", "attn", "append")}
+    score_us = kt["score"][0]
+    score_bytes = nb_max * 128 * 4 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
+    achieved = score_bytes / (score_us * 1e-6) / 1e9
+    # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries
+    tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
+    path_bytes = nb_max * 512 + tok * wl.hkv * 2 * wl.head_dim * 2 + wl.m * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2)
+    layer_us = ms_step * 1e3 / layers
+    res = {
+        "metric": "QSA query-rows/s per layer at 262K ctx (M=1,4) + achieved HBM GB/s / MFMA %",
+        "value": rows_per_s,
+        "unit": "query-rows/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_ctx": wl.n_ctx, "rows": wl.m, "row_pos": [wl.rows[0], wl.rows[-1]],
+                   "layers": layers, "budget_tokens": wl.k_blocks * 4, "hq": wl.hq, "hkv": wl.hkv,
+                   "head_dim": wl.head_dim, "graph": not args.eager},
+        "roofline": {"bound": "hbm", "kernel": "score_fewrow_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": score_bytes, "launch_us": score_us},
+        "path": {"layer_us": layer_us, "bytes_per_layer_step": path_bytes,
+                 "achieved_GBs": path_bytes / (layer_us * 1e-6) / 1e9,
+                 "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                 "kernel_us": {k_: round(v[0], 2) for k_, v in kt.items()}},
+    }
+    if not args.no_m1 and wl.name == "verify_262k":
+        wl1 = datagen.WORKLOADS["decode_262k"]
+        for ly in L:
+            ly.rows = ly.rows[-1:].contiguous()
+            ly.new_idx = ly.new_idx[-1:].contiguous()
+            ly.new_pos = ly.new_pos[-1:].contiguous()
+            ly.idx_q = ly.idx_q[-1:].contiguous()
+            ly.q = ly.q[-1:].contiguous()
+        sh1 = dict(sh)
+        sh1["out"] = sh["out"][-1:].contiguous()
+        sh1["lse"] = sh["lse"][-1:].contiguous()
+        run1 = step_fn(Q, L, sh1, nb_max, wl1)
+        run1()
+        torch.cuda.synchronize()
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            run1()
+        for _ in range(args.warmup):
+            g1.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            g1.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms1 = start.elapsed_time(end)
+        res["m1"] = {"workload": "decode_262k", "value": layers * args.steps / (ms1 / 1e3),
+                     "ms_per_step": ms1 / args.steps, "layer_us": ms1 * 1e3 / args.steps / layers}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * qsa.h -- C ABI of the QSA (Qwen Sparse Attention) per-layer path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (hipfire page "QSA sparse attention and the VMM KV backend",
+ * section 02 "How QSA chooses what to read"): every token of a QSA layer
+ * writes one 128-wide index key beside its K/V; each run of 4 consecutive
+ * index keys is averaged into one pooled block key; for each query row, 4
+ * index-query heads score every causally visible pooled block as the sum of
+ * their ReLU'd dot products times 1/sqrt(128); the best-scoring blocks inside
+ * a 2,048-token budget (512 blocks) are kept together with the incomplete
+ * block at the end; grouped-query attention then reads only those rows.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises; all work is enqueued on
+ *    `stream` (NULL = the null stream) and is safe to capture in a HIP graph.
+ *  - Sizes and shapes are host scalars.  Host-side validation runs before any
+ *    enqueue: a failed check returns a negative qsa_status, launches nothing
+ *    and records a reason readable through qsa_last_error().
+ *  - Values that live in device memory (positions, selections, segment
+ *    tables) are the caller's contract.  Kernels clamp every index they
+ *    derive from them, so a broken contract gives unspecified results but
+ *    never an out-of-bounds access.
+ *  - A query row at absolute position p sees tokens 0..p (inclusive).  It has
+ *    nb(p) = (p+1)/4 complete blocks and a tail of (p+1)%4 tokens.
+ *  - Layouts are dense row-major; "[a][b]" means b is contiguous.
+ *  - bf16 is IEEE bfloat16 (upper half of a float32), round-to-nearest-even
+ *    wherever the library rounds.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type (hipStream_t) without pulling in HIP headers. */
+typedef struct ihipStream_t* qsa_stream_t;
+
+#define QSA_INDEX_DIM 128       /* width of an index key and of an index-query head */
+#define QSA_INDEX_HEADS 4       /* index-query heads per query row */
+#define QSA_BLOCK_TOKENS 4      /* tokens per pooled block */
+#define QSA_MAX_K_BLOCKS 1024   /* largest supported budget, in blocks */
+#define QSA_MAX_SEGMENTS 16     /* K/V segments per sequence */
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_ARG = -1,          /* bad pointer, size or shape */
+  QSA_ERR_UNSUPPORTED = -2,  /* valid request this build does not serve */
+  QSA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  QSA_ERR_LAUNCH = -4,       /* the HIP runtime refused a launch */
+  QSA_ERR_DEVICE = -5        /* current device is not gfx950 */
+} qsa_status;
+
+typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+/*
+ * qsa_append_pool -- write index keys in place and pool completed blocks.
+ *
+ * Page: hipfire "QSA sparse attention ...", section 02 (one index key per
+ * token; every 4 consecutive keys averaged into a pooled block key).  The
+ * write is in place and never reallocates (MTPLX PR #482, section 3,
+ * optimization 1: the verify's KV write goes in place).
+ *
+ *  new_idx   [n_new][128] dtype          index keys of the new tokens
+ *  dtype     QSA_F32 or QSA_BF16         dtype of new_idx and idx_cache
+ *  n_new     >= 0                        tokens appended (0: no-op)
+ *  pos       int64 [n_new]               absolute position of each new token
+ *  seq       int32 [n_new] or NULL       sequence of each token (NULL: all 0)
+ *  idx_cache [n_seq][capacity][128] dtype  per-token index keys (written)
+ *  pooled    float32 [n_seq][capacity/4][128]  pooled block keys (written)
+ *  n_seq     >= 1; capacity > 0, multiple of 4
+ *
+ * Every new token's key is copied to idx_cache[seq][pos].  Every block b
+ * whose last token 4b+3 is among the new tokens gets
+ *   pooled[seq][b] = (((x0 + x1) + x2) + x3) * 0.25
+ * in float32 (round-to-nearest-even, no fused multiply-add), x_i being the
+ * keys of tokens 4b+i, taken from this call when present, else from
+ * idx_cache.  Contract: within one call, the tokens of one sequence are
+ * consecutive in new_idx and in ascending position order.  Tokens whose
+ * pos or seq is out of range are skipped.
+ */
+int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
+                    const int64_t* pos, const int32_t* seq,
+                    void* idx_cache, float* pooled,
+                    int32_t n_seq, int64_t capacity, qsa_stream_t stream);
+
+/*
+ * qsa_score_blocks -- score every causally visible pooled block.
+ *
+ * Page: hipfire "QSA sparse attention ...", section 02 (four index-query
+ * heads, sum of ReLU'd dot products, scaled by 1/sqrt(128)) and section 03
+ * (a few-row variant for <= 8 rows and a 16-row variant for prefill).
+ *
+ *  idx_q    [M][4][128] dtype           index queries of the rows
+ *  M        >= 0 rows (0: no-op)
+ *  row_pos  int64 [M]                    absolute position of each row
+ *  row_seq  int32 [M] or NULL            sequence of each row (NULL: all 0;
+ *                                        rows then share one read of pooled)
+ *  pooled   float32 [n_seq][capacity/4][128]
+ *  nb_max   >= 0, <= capacity/4          host bound on nb(row_pos[m])
+ *  scores   float32 [M][ld], ld >= nb_max  (written)
+ *
+ * scores[m][b] = (sum_h max(0, idx_q[m][h] . pooled[seq][b])) / sqrt(128)
+ * for b < min(nb(row_pos[m]), nb_max), accumulated in float32.  Entries past
+ * a row's block count are left untouched.
+ */
+int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
+                     const int64_t* row_pos, const int32_t* row_seq,
+                     const float* pooled, int32_t n_seq, int64_t capacity,
+                     int64_t nb_max, float* scores, int64_t ld, qsa_stream_t stream);
+
+/*
+ * qsa_select_topk -- keep the best blocks of each row within the budget.
+ *
+ * Page: hipfire "QSA sparse attention ...", section 02 (top-scoring blocks
+ * within a 2,048-token budget, 512 blocks; the incomplete tail block is kept
+ * in addition) and section 03 (a radix select follows the scoring).
+ *
+ *  scores    float32 [M][ld]            as written by qsa_score_blocks
+ *  row_pos   int64 [M]; nb_max as for qsa_score_blocks
+ *  k_blocks  1..QSA_MAX_K_BLOCKS        budget in blocks (512 = 2,048 tokens)
+ *  sel       int32 [M][k_blocks]        kept block ids, ascending; unused
+ *                                       entries are set to -1 (written)
+ *  n_sel     int32 [M]                  min(k_blocks, nb) (written)
+ *  workspace / workspace_bytes          >= qsa_select_workspace_bytes(...)
+ *
+ * When nb <= k_blocks every block is kept.  Otherwise the k_blocks largest
+ * scores are kept; equal scores go to the lower block index.  The tail
+ * tokens 4*nb..p are not listed; every attention call adds them.  Scores are
+ * compared as float32 with -0 equal to +0.
+ */
+int qsa_select_topk(const float* scores, int64_t ld, int32_t M,
+                    const int64_t* row_pos, int64_t nb_max, int32_t k_blocks,
+                    int32_t* sel, int32_t* n_sel,
+                    void* workspace, size_t workspace_bytes, qsa_stream_t stream);
+
+/* K/V of a batch of sequences, each held as 1..QSA_MAX_SEGMENTS segments.
+ * Segments follow MTPLX PR #610 ("How it works": one immutable segment per
+ * finished turn plus a growing tail; attention reads all segments in one
+ * launch).  Every array below is DEVICE memory owned by the caller; the
+ * struct itself is read on the host during the call only. */
+typedef struct qsa_kv_segments {
+  int32_t n_seq;                /* sequences described (>= 1) */
+  int32_t n_seg_total;          /* segments over all sequences (>= n_seq) */
+  int32_t max_seg_per_seq;      /* host bound, 1..QSA_MAX_SEGMENTS */
+  int32_t reserved;
+  const int32_t* seq_seg_begin; /* int32 [n_seq+1]: sequence s owns segments
+                                   seq_seg_begin[s] .. seq_seg_begin[s+1]-1 */
+  const int64_t* seg_start;     /* int64 [n_seg_total]: first logical token held */
+  const int64_t* seg_len;       /* int64 [n_seg_total]: tokens held */
+  const int64_t* seg_cap;       /* int64 [n_seg_total]: token stride between KV heads */
+  const void* const* k_seg;     /* [n_seg_total] -> K [hkv][seg_cap][head_dim] dtype */
+  const void* const* v_seg;     /* [n_seg_total] -> V [hkv][seg_cap][head_dim] dtype */
+} qsa_kv_segments;
+
+/*
+ * qsa_gathered_attn -- grouped-query attention over the kept rows only.
+ *
+ * Pages: hipfire "QSA sparse attention ...", section 02 (full attention over
+ * the selected rows plus the tail, at most 2,048 + 3 tokens per query) and
+ * section 03 (one workgroup per KV group of query heads reads each selected
+ * K/V row once for the whole group; gathered prefill tiles on matrix
+ * cores); MTPLX PR #610 ("What changes": partials merged by log-sum-exp in
+ * float32, rounded once; rows with no visible key give zeros, not NaN).
+ *
+ *  q          [M][hq][head_dim] dtype   query rows
+ *  M >= 0; hq, hkv with hq % hkv == 0 and hq/hkv == 12; head_dim 128 or 256
+ *  scale      softmax scale (finite), usually 1/sqrt(head_dim)
+ *  row_pos    int64 [M]; row_seq int32 [M] or NULL (all sequence 0)
+ *  kv         K/V segment table of the sequences
+ *  sel/n_sel  as written by qsa_select_topk; k_blocks its budget
+ *  out        [M][hq][head_dim] dtype   (written)
+ *  lse        float32 [M][hq]           natural-log sum of exp of the
+ *                                       scaled logits; -inf for a row with no
+ *                                       visible token (written)
+ *  workspace / workspace_bytes          >= qsa_attn_workspace_bytes(...)
+ *
+ * Row m reads tokens 4b..4b+3 of every kept block b plus its tail tokens
+ * 4*nb..p; query head h uses KV head h / (hq/hkv).  Logits, softmax and
+ * partial outputs are float32; the output is rounded once to dtype.
+ */
+int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
+                      int32_t head_dim, float scale,
+                      const int64_t* row_pos, const int32_t* row_seq,
+                      const qsa_kv_segments* kv,
+                      const int32_t* sel, const int32_t* n_sel, int32_t k_blocks,
+                      void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, qsa_stream_t stream);
+
+/* Workspace bytes qsa_select_topk needs for up to max_M rows of up to
+ * nb_max blocks (0 means no workspace is needed). */
+size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks);
+
+/* Workspace bytes qsa_gathered_attn needs for up to max_M rows (split-K
+ * partials).  Reserve it once at load; it never grows (hipfire page,
+ * section 03: scratch reserved at load never grows under a captured graph). */
+size_t qsa_attn_workspace_bytes(int32_t max_M, int32_t hq, int32_t head_dim, int32_t k_blocks);
+
+/* Checks that the current HIP device is gfx950 and that the kernels load.
+ * QSA_OK, or QSA_ERR_DEVICE with a reason. */
+int qsa_device_check(void);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* qsa_last_error(void);
+
+/* Library version string. */
+const char* qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

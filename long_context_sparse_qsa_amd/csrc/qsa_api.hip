@@ -1,0 +1,161 @@
+// C ABI of the QSA layer path: host-side validation, reason strings and
+// dispatch to the kernels.  Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return QSA_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool dtype_ok(int32_t dt) { return dt == QSA_F32 || dt == QSA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new, const int64_t* pos,
+                    const int32_t* seq, void* idx_cache, float* pooled, int32_t n_seq,
+                    int64_t capacity, qsa_stream_t stream) {
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_append_pool: dtype %d is not QSA_F32 or QSA_BF16", dtype);
+  if (n_new < 0) return fail(QSA_ERR_ARG, "qsa_append_pool: n_new = %d < 0", n_new);
+  if (n_seq < 1) return fail(QSA_ERR_ARG, "qsa_append_pool: n_seq = %d < 1", n_seq);
+  if (capacity <= 0 || capacity % QSA_BLOCK_TOKENS != 0)
+    return fail(QSA_ERR_ARG, "qsa_append_pool: capacity %lld must be a positive multiple of 4",
+                (long long)capacity);
+  if (n_new == 0) return ok();
+  if (!new_idx || !pos || !idx_cache || !pooled)
+    return fail(QSA_ERR_ARG, "qsa_append_pool: null pointer (new_idx, pos, idx_cache or pooled)");
+  return launch_status(qsa::launch_append_pool(new_idx, dtype, n_new, pos, seq, idx_cache, pooled,
+                                               n_seq, capacity, (hipStream_t)stream),
+                       "qsa_append_pool");
+}
+
+int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t* row_pos,
+                     const int32_t* row_seq, const float* pooled, int32_t n_seq, int64_t capacity,
+                     int64_t nb_max, float* scores, int64_t ld, qsa_stream_t stream) {
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_score_blocks: dtype %d is not QSA_F32 or QSA_BF16", dtype);
+  if (M < 0) return fail(QSA_ERR_ARG, "qsa_score_blocks: M = %d < 0", M);
+  if (n_seq < 1) return fail(QSA_ERR_ARG, "qsa_score_blocks: n_seq = %d < 1", n_seq);
+  if (capacity <= 0 || capacity % QSA_BLOCK_TOKENS != 0)
+    return fail(QSA_ERR_ARG, "qsa_score_blocks: capacity %lld must be a positive multiple of 4",
+                (long long)capacity);
+  if (nb_max < 0 || nb_max > capacity / QSA_BLOCK_TOKENS)
+    return fail(QSA_ERR_ARG, "qsa_score_blocks: nb_max %lld outside [0, capacity/4 = %lld]",
+                (long long)nb_max, (long long)(capacity / QSA_BLOCK_TOKENS));
+  if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_score_blocks: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  if (M == 0 || nb_max == 0) return ok();
+  if (!idx_q || !row_pos || !pooled || !scores)
+    return fail(QSA_ERR_ARG, "qsa_score_blocks: null pointer (idx_q, row_pos, pooled or scores)");
+  return launch_status(qsa::launch_score_blocks(idx_q, dtype, M, row_pos, row_seq, pooled, n_seq,
+                                                capacity, nb_max, scores, ld, (hipStream_t)stream),
+                       "qsa_score_blocks");
+}
+
+size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks) {
+  if (max_M <= 0 || nb_max < 0 || k_blocks <= 0) return 0;
+  return qsa::select_workspace_bytes(max_M, nb_max, k_blocks);
+}
+
+int qsa_select_topk(const float* scores, int64_t ld, int32_t M, const int64_t* row_pos,
+                    int64_t nb_max, int32_t k_blocks, int32_t* sel, int32_t* n_sel,
+                    void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
+  if (M < 0) return fail(QSA_ERR_ARG, "qsa_select_topk: M = %d < 0", M);
+  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
+    return fail(QSA_ERR_ARG, "qsa_select_topk: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
+  if (nb_max < 0) return fail(QSA_ERR_ARG, "qsa_select_topk: nb_max %lld < 0", (long long)nb_max);
+  if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_select_topk: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  const size_t need = qsa::select_workspace_bytes(M, nb_max, k_blocks);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(QSA_ERR_WORKSPACE, "qsa_select_topk: workspace %zu B < %zu B needed", workspace_bytes, need);
+  if (M == 0) return ok();
+  if (!row_pos || !sel || !n_sel || (nb_max > 0 && !scores))
+    return fail(QSA_ERR_ARG, "qsa_select_topk: null pointer (scores, row_pos, sel or n_sel)");
+  return launch_status(qsa::launch_select_topk(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel,
+                                               workspace, workspace_bytes, (hipStream_t)stream),
+                       "qsa_select_topk");
+}
+
+size_t qsa_attn_workspace_bytes(int32_t max_M, int32_t hq, int32_t head_dim, int32_t k_blocks) {
+  if (max_M <= 0 || hq <= 0 || head_dim <= 0 || k_blocks <= 0 || k_blocks > QSA_MAX_K_BLOCKS) return 0;
+  return qsa::attn_workspace_bytes(max_M, hq, head_dim, k_blocks);
+}
+
+int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
+                      int32_t head_dim, float scale, const int64_t* row_pos,
+                      const int32_t* row_seq, const qsa_kv_segments* kv, const int32_t* sel,
+                      const int32_t* n_sel, int32_t k_blocks, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_gathered_attn: dtype %d is not QSA_F32 or QSA_BF16", dtype);
+  if (M < 0) return fail(QSA_ERR_ARG, "qsa_gathered_attn: M = %d < 0", M);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: hq %d must be a positive multiple of hkv %d", hq, hkv);
+  if (hq / hkv != 12)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: %d query heads per KV head; this build serves 12", hq / hkv);
+  if (head_dim != 128 && head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: head_dim %d; this build serves 128 and 256", head_dim);
+  if (dtype == QSA_F32 && head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: float32 K/V is served at head_dim 128 only");
+  if (!(scale == scale) || isinf(scale)) return fail(QSA_ERR_ARG, "qsa_gathered_attn: scale is not finite");
+  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
+  if (!kv) return fail(QSA_ERR_ARG, "qsa_gathered_attn: kv is NULL");
+  if (kv->n_seq < 1 || kv->n_seg_total < kv->n_seq)
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: kv n_seq %d / n_seg_total %d invalid", kv->n_seq, kv->n_seg_total);
+  if (kv->max_seg_per_seq < 1 || kv->max_seg_per_seq > QSA_MAX_SEGMENTS)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: max_seg_per_seq %d outside [1, %d]",
+                kv->max_seg_per_seq, QSA_MAX_SEGMENTS);
+  if (!kv->seq_seg_begin || !kv->seg_start || !kv->seg_len || !kv->seg_cap || !kv->k_seg || !kv->v_seg)
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: null pointer in the kv segment table");
+  const size_t need = qsa::attn_workspace_bytes(M, hq, head_dim, k_blocks);
+  if (M > 0 && (workspace_bytes < need || (need && !workspace)))
+    return fail(QSA_ERR_WORKSPACE, "qsa_gathered_attn: workspace %zu B < %zu B needed", workspace_bytes, need);
+  if (M == 0) return ok();
+  if (!q || !row_pos || !sel || !n_sel || !out || !lse)
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: null pointer (q, row_pos, sel, n_sel, out or lse)");
+  return launch_status(qsa::launch_gathered_attn(q, dtype, M, hq, hkv, head_dim, scale, row_pos,
+                                                 row_seq, kv, sel, n_sel, k_blocks, out, lse,
+                                                 workspace, workspace_bytes, (hipStream_t)stream),
+                       "qsa_gathered_attn");
+}
+
+int qsa_device_check(void) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QSA_ERR_DEVICE, "qsa_device_check: no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess)
+    return fail(QSA_ERR_DEVICE, "qsa_device_check: hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(QSA_ERR_DEVICE, "qsa_device_check: device %d is %s; this library is built for gfx950",
+                dev, prop.gcnArchName);
+  return ok();
+}
+
+const char* qsa_last_error(void) { return g_err; }
+
+const char* qsa_version(void) { return "qsa-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

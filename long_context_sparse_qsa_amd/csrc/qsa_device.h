@@ -1,0 +1,76 @@
+// Device helpers shared by the QSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kIndexDim = 128;
+constexpr int kIndexHeads = 4;
+constexpr int kBlockTokens = 4;
+constexpr int kWave = 64;
+constexpr int kMaxSegments = 16;
+
+// Element types.  bf16 values are carried as raw 16-bit patterns.
+struct F32 {
+  using T = float;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float to_f(T x) { return x; }
+  __device__ static __forceinline__ T from_f(float x) { return x; }
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round-to-nearest-even float32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float to_f(T x) { return bf16_bits_to_f32(x); }
+  __device__ static __forceinline__ T from_f(float x) { return f32_to_bf16_bits(x); }
+};
+
+// Wave-wide reductions over 64 lanes (result in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Make a value known to be wave-uniform visible as such to the compiler, so
+// that loads addressed by it become scalar loads.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int64_t clamp_nb(int64_t pos, int64_t nb_max) {
+  int64_t nb = (pos + 1) / kBlockTokens;
+  if (nb < 0) nb = 0;
+  return nb < nb_max ? nb : nb_max;
+}
+
+}  // namespace qsa

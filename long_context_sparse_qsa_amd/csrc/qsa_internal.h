@@ -1,0 +1,43 @@
+// Host-side launchers of the QSA kernels (internal; the public ABI is qsa.h).
+// Each launcher assumes its arguments were validated by qsa_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qsa.h"
+
+namespace qsa {
+
+hipError_t launch_append_pool(const void* new_idx, int dtype, int n_new, const int64_t* pos,
+                              const int32_t* seq, void* idx_cache, float* pooled, int n_seq,
+                              int64_t capacity, hipStream_t stream);
+
+hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_t* row_pos,
+                               const int32_t* row_seq, const float* pooled, int n_seq,
+                               int64_t capacity, int64_t nb_max, float* scores, int64_t ld,
+                               hipStream_t stream);
+
+size_t select_workspace_bytes(int max_M, int64_t nb_max, int k_blocks);
+hipError_t launch_select_topk(const float* scores, int64_t ld, int M, const int64_t* row_pos,
+                              int64_t nb_max, int k_blocks, int32_t* sel, int32_t* n_sel,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Split plan of the gathered attention for M rows (same on every call with
+// the same arguments, so results are reproducible bit for bit).
+struct AttnPlan {
+  int tile_tokens;     // tokens per inner tile
+  int splits;          // split-K parts per (row, KV head)
+  int tiles_per_split; // tiles walked by one workgroup
+};
+AttnPlan attn_plan(int M, int hkv, int k_blocks);
+size_t attn_workspace_bytes(int max_M, int hq, int head_dim, int k_blocks);
+
+hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv, int head_dim,
+                                float scale, const int64_t* row_pos, const int32_t* row_seq,
+                                const qsa_kv_segments* kv, const int32_t* sel,
+                                const int32_t* n_sel, int k_blocks, void* out, float* lse,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace qsa

@@ -1,0 +1,136 @@
+"""The C ABI on the CPU: the library loads, exports every symbol qsa.h
+declares, and refuses bad arguments with its status codes before anything
+is enqueued (no GPU work is started by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+Q = pytest.importorskip("long_context_sparse_qsa_amd", reason="libqsa.so not built")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(qsa_[a-z_0-9]+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn"):
+        assert n in names
+    assert set(names) == set(Q.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(Q.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in Q.version()
+
+
+L = Q.lib()
+ERR_ARG, ERR_UNS, ERR_WS = Q.QSA_ERR_ARG, Q.QSA_ERR_UNSUPPORTED, Q.QSA_ERR_WORKSPACE
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _err():
+    return L.qsa_last_error().decode()
+
+
+@pytest.mark.parametrize("args,code,word", [
+    ((FAKE, 7, 1, FAKE, None, FAKE, FAKE, 1, 16, None), ERR_ARG, "dtype"),
+    ((FAKE, 1, -1, FAKE, None, FAKE, FAKE, 1, 16, None), ERR_ARG, "n_new"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, FAKE, 0, 16, None), ERR_ARG, "n_seq"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, FAKE, 1, 18, None), ERR_ARG, "capacity"),
+    ((FAKE, 1, 1, None, None, FAKE, FAKE, 1, 16, None), ERR_ARG, "null"),
+    ((None, 1, 0, None, None, None, None, 1, 16, None), Q.QSA_OK, ""),
+])
+def test_append_pool_validation(args, code, word):
+    assert L.qsa_append_pool(*args) == code
+    assert word in _err()
+
+
+@pytest.mark.parametrize("args,code,word", [
+    ((FAKE, 3, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None), ERR_ARG, "dtype"),
+    ((FAKE, 1, -2, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None), ERR_ARG, "M ="),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 17, FAKE, 17, None), ERR_ARG, "nb_max"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 8, None), ERR_ARG, "ld"),
+    ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None), ERR_ARG, "null"),
+    ((None, 1, 0, None, None, None, 1, 64, 16, None, 16, None), Q.QSA_OK, ""),
+])
+def test_score_validation(args, code, word):
+    assert L.qsa_score_blocks(*args) == code
+    assert word in _err()
+
+
+@pytest.mark.parametrize("args,code,word", [
+    ((FAKE, 16, 1, FAKE, 16, 0, FAKE, FAKE, None, 0, None), ERR_ARG, "k_blocks"),
+    ((FAKE, 16, 1, FAKE, 16, 2000, FAKE, FAKE, None, 0, None), ERR_ARG, "k_blocks"),
+    ((FAKE, 8, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, None), ERR_ARG, "ld"),
+    ((FAKE, 16, 1, FAKE, 16, 4, None, FAKE, None, 0, None), ERR_ARG, "null"),
+    ((None, 16, 0, None, 16, 4, None, None, None, 0, None), Q.QSA_OK, ""),
+])
+def test_select_validation(args, code, word):
+    assert L.qsa_select_topk(*args) == code
+    assert word in _err()
+
+
+def _kv(n_seq=1, n_seg=1, max_seg=1, null=False):
+    return Q.QsaKvSegments(n_seq, n_seg, max_seg, 0, None if null else FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FAKE, wsb=1 << 30,
+          out=FAKE):
+    kv = kv or _kv()
+    return L.qsa_gathered_attn(FAKE, dtype, M, hq, hkv, d, scale, FAKE, None, ctypes.byref(kv), FAKE,
+                               FAKE, k, out, FAKE, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(dtype=5), ERR_ARG, "dtype"),
+    (dict(M=-1), ERR_ARG, "M ="),
+    (dict(hq=25), ERR_ARG, "multiple"),
+    (dict(hq=16, hkv=2), ERR_UNS, "12"),
+    (dict(d=64), ERR_UNS, "head_dim"),
+    (dict(dtype=0, d=256), ERR_UNS, "float32"),
+    (dict(scale=float("nan")), ERR_ARG, "scale"),
+    (dict(scale=float("inf")), ERR_ARG, "scale"),
+    (dict(k=0), ERR_ARG, "k_blocks"),
+    (dict(kv=_kv(n_seq=0)), ERR_ARG, "n_seq"),
+    (dict(kv=_kv(max_seg=17)), ERR_UNS, "max_seg"),
+    (dict(kv=_kv(null=True)), ERR_ARG, "null"),
+    (dict(ws=None, wsb=0), ERR_WS, "workspace"),
+    (dict(wsb=100), ERR_WS, "workspace"),
+    (dict(out=None), ERR_ARG, "null"),
+    (dict(M=0, ws=None, wsb=0), Q.QSA_OK, ""),
+])
+def test_attn_validation(kw, code, word):
+    assert _attn(**kw) == code
+    assert word in _err()
+
+
+def test_attn_null_kv():
+    r = L.qsa_gathered_attn(FAKE, 1, 1, 24, 2, 256, 0.1, FAKE, None, None, FAKE, FAKE, 512, FAKE,
+                            FAKE, FAKE, 1 << 30, None)
+    assert r == ERR_ARG and "kv" in _err()
+
+
+def test_workspace_sizes():
+    # one row, 2 KV heads, budget 512 blocks: 33 tiles of 64 tokens -> 33 splits
+    assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 33 * 257 * 4
+    # sizing is monotone in max_M (a call with fewer rows always fits)
+    prev = 0
+    for m in (1, 2, 3, 4, 8, 16, 64, 256, 2048):
+        cur = Q.qsa_attn_workspace_bytes(m, 24, 256, 512)
+        assert cur >= prev
+        prev = cur
+    assert Q.qsa_attn_workspace_bytes(0, 24, 256, 512) == 0
+    assert Q.qsa_select_workspace_bytes(4, 65280, 512) >= 0

@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: index keys and pooled keys bit-exact; selection bit-exact against the
+oracle's own selection rule applied to the GPU's float32 scores, and equal
+to the oracle's fp64 selection outside the near-cutoff band; attention
+within max-abs 2e-2 (bf16 K/V) / 1e-4 (fp32), recomputed in fp64 over the
+GPU's selection plus the tail.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import (DEV, Layer, check_attention, check_selection, to_dev,  # noqa: E402
+                         to_host_f32)
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import long_context_sparse_qsa_amd as Q
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    Q.qsa_device_check()
+    return Q
+
+
+def _check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
+    wl = d["workload"]
+    k = k or wl.k_blocks
+    n = d["idx"].shape[0]
+    # index keys copied bit for bit; pooled keys bit-exact
+    cache = layer.idx_cache[0, :n].float().cpu().numpy()
+    assert np.array_equal(cache, d["idx"])
+    pooled_gpu = layer.pooled[0, : n // 4].cpu().numpy()
+    pooled_ref = O.pool_index_keys(d["idx"])
+    assert np.array_equal(pooled_gpu.view(np.uint32), pooled_ref.view(np.uint32))
+    sc = res["scores"].cpu().numpy()
+    sel = res["sel"].cpu().numpy()
+    n_sel = res["n_sel"].cpu().numpy()
+    out = to_host_f32(res["out"])
+    lse = res["lse"].cpu().numpy()
+    rows = range(len(d["rows"])) if rows is None else rows
+    attn_rows = rows if attn_rows is None else attn_rows
+    stats = []
+    for i in rows:
+        p = int(d["rows"][i])
+        s64 = O.score_blocks(d["idx_q"][i], pooled_ref, p + 1)
+        nb = len(s64)
+        g32 = sc[i, :nb].astype(np.float64)
+        # scores: float32 accumulation against fp64
+        assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), float(np.max(np.abs(g32 - s64)))
+        # the select kernel is exact on its own input
+        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), "select != exact top-k of GPU scores"
+        st = check_selection(sel[i], int(n_sel[i]), s64, k)
+        if i in attn_rows:
+            err, lerr = check_attention(out[i], lse[i], d, i, sel[i, : n_sel[i]], wl.dtype)
+            st.update(err=err, lse_err=lerr)
+        stats.append(st)
+    return stats
+
+
+def test_tiny_fp32(Q):
+    say("tiny fp32 N=1023")
+    d = datagen.gen_layer("tiny")
+    layer = Layer(d)
+    res = layer.run()
+    st = _check_layer(d, res, layer)
+    say(st)
+    # the planted blocks are found
+    assert len(set(d["planted"].tolist()) & set(res["sel"][0].cpu().tolist())) >= 6
+
+
+def test_tiny_budget_covers_context_is_dense(Q):
+    say("tiny with budget >= context")
+    d = datagen.gen_layer("tiny")
+    layer = Layer(d)
+    res = layer.run(k_blocks=256)
+    assert int(res["n_sel"][0]) == 255
+    st = _check_layer(d, res, layer, k=256)
+    say(st)
+
+
+def test_decode_32k(Q):
+    say("decode M=1 at 32768 bf16")
+    d = datagen.gen_layer("decode_32k")
+    layer = Layer(d)
+    res = layer.run()
+    say(_check_layer(d, res, layer))
+
+
+def test_decode_32k_layers_differ(Q):
+    say("decode 32k, layer 5")
+    d = datagen.gen_layer("decode_32k", layer=5)
+    layer = Layer(d)
+    say(_check_layer(d, layer.run(), layer))
+
+
+def test_verify_262k_full_size(Q):
+    say("verify M=4 at 261122 bf16 (full size)")
+    d = datagen.gen_layer("verify_262k")
+    layer = Layer(d)
+    res = layer.run()
+    say(_check_layer(d, res, layer))
+
+
+def test_decode_262k_full_size(Q):
+    say("decode M=1 at 261122 bf16 (full size)")
+    d = datagen.gen_layer("decode_262k")
+    layer = Layer(d)
+    say(_check_layer(d, layer.run(), layer))
+
+
+def test_prefill_full_size_sampled(Q):
+    say("prefill 2048 rows at 200000 bf16 (full size, sampled rows)")
+    d = datagen.gen_layer("prefill")
+    layer = Layer(d, prefix_split=200000)
+    res = layer.run()
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 2, 3, 15, 16, 1023, 2046, 2047] + rng.choice(2048, 16, replace=False).tolist()))
+    say(_check_layer(d, res, layer, rows=rows))
+
+
+@pytest.mark.parametrize("rows", [(0,), (1,), (2,), (3,), (4,), (5, 6, 7), (30, 100, 255),
+                                  (1019, 1020, 1021, 1022)])
+def test_short_and_ragged_rows(Q, rows):
+    """Rows with nb <= k (every block kept), empty block sets (tail only) and
+    ragged tails inside one call."""
+    say("ragged rows", rows)
+    base = datagen.gen_layer("tiny")
+    d = dict(base)
+    d["rows"] = np.asarray(rows, dtype=np.int64)
+    rng = np.random.default_rng(sum(rows))
+    d["idx_q"] = rng.standard_normal((len(rows), 4, 128)).astype(np.float32)
+    d["q"] = rng.standard_normal((len(rows), 24, 128)).astype(np.float32)
+    layer = Layer(d, prefix_split=1023)
+    res = layer.run(k_blocks=16)
+    say(_check_layer(d, res, layer, k=16))
+
+
+def test_row_without_visible_token_gives_zeros(Q):
+    say("row at position -1")
+    d = dict(datagen.gen_layer("tiny"))
+    d["rows"] = np.asarray([-1, 1022], dtype=np.int64)
+    d["q"] = np.concatenate([d["q"], d["q"]])
+    d["idx_q"] = np.concatenate([d["idx_q"], d["idx_q"]])
+    layer = Layer(d, prefix_split=1023)
+    res = layer.run()
+    assert int(res["n_sel"][0]) == 0
+    out = res["out"].cpu().numpy()
+    lse = res["lse"].cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_zero_queries_tie_rule(Q):
+    """All index queries zero: every score is 0 and the lowest k blocks win."""
+    say("zero index queries")
+    d = dict(datagen.gen_layer("decode_32k"))
+    d["idx_q"] = np.zeros_like(d["idx_q"])
+    layer = Layer(d)
+    res = layer.run()
+    assert np.all(res["scores"][0, : 8192].cpu().numpy() == 0)
+    assert res["sel"][0].cpu().tolist() == list(range(512))
+
+
+def test_deterministic_bitwise(Q):
+    say("determinism")
+    d = datagen.gen_layer("decode_32k")
+    layer = Layer(d)
+    a = layer.run()
+    b = layer.run()
+    for key in ("scores", "sel", "n_sel", "lse"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+
+
+def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
+    """Sequences with K/V in several segments (some empty, some cutting a
+    4-token block), one row per sequence, scored and attended in one call."""
+    rng = np.random.default_rng(seed)
+    wl = datagen.WORKLOADS["decode_32k"]
+    n_seq = len(n_ctx_list)
+    cap_max = max(-(-(n + 4) // 256) * 256 for n in n_ctx_list)
+    idx_cache = torch.zeros((n_seq, cap_max, 128), dtype=torch.bfloat16, device=DEV)
+    pooled = torch.zeros((n_seq, cap_max // 4, 128), dtype=torch.float32, device=DEV)
+    seqs, segs_dev, host = [], [], []
+    for s, (n, nseg) in enumerate(zip(n_ctx_list, nseg_list)):
+        idx = datagen.round_bf16(rng.standard_normal((n, 128)).astype(np.float32))
+        iq = datagen.round_bf16(rng.standard_normal((1, 4, 128)).astype(np.float32))
+        q = datagen.round_bf16(rng.standard_normal((1, 24, 256)).astype(np.float32))
+        k_ = datagen.round_bf16(rng.standard_normal((2, n, 256)).astype(np.float32))
+        v_ = datagen.round_bf16(rng.standard_normal((2, n, 256)).astype(np.float32))
+        cuts = sorted(rng.choice(np.arange(0, n + 1), size=nseg - 1, replace=True).tolist()) if nseg > 1 else []
+        bounds = [0] + cuts + [n]
+        segs = []
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            cap = max(hi - lo, 1) + int(rng.integers(0, 9))
+            kt = torch.zeros((2, cap, 256), dtype=torch.bfloat16, device=DEV)
+            vt = torch.zeros_like(kt)
+            if hi > lo:
+                kt[:, : hi - lo] = to_dev(np.ascontiguousarray(k_[:, lo:hi]), "bf16")
+                vt[:, : hi - lo] = to_dev(np.ascontiguousarray(v_[:, lo:hi]), "bf16")
+            segs.append((lo, hi - lo, kt, vt))
+        segs_dev.append(segs)
+        Q.qsa_append_pool(to_dev(idx, "bf16"), torch.arange(n, dtype=torch.int64, device=DEV),
+                          idx_cache[s : s + 1], pooled[s : s + 1])
+        host.append(dict(idx=idx, idx_q=iq, q=q, k=k_, v=v_, n=n))
+    kv = Q.KvSegments(segs_dev)
+    m = n_seq
+    rows = torch.tensor([h["n"] - 1 for h in host], dtype=torch.int64, device=DEV)
+    row_seq = torch.arange(m, dtype=torch.int32, device=DEV)
+    idx_q = to_dev(np.concatenate([h["idx_q"] for h in host]), "bf16")
+    q = to_dev(np.concatenate([h["q"] for h in host]), "bf16")
+    nb_max = max(h["n"] for h in host) // 4
+    scores = torch.zeros((m, nb_max + 4), dtype=torch.float32, device=DEV)
+    Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
+    sel = torch.empty((m, k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((m,), dtype=torch.int32, device=DEV)
+    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel)
+    out = torch.empty_like(q)
+    lse = torch.empty((m, 24), dtype=torch.float32, device=DEV)
+    ws = torch.empty(Q.qsa_attn_workspace_bytes(m, 24, 256, k), dtype=torch.uint8, device=DEV)
+    Q.qsa_gathered_attn(q, rows, kv, sel, n_sel, out, lse, 2, row_seq=row_seq, workspace=ws)
+    torch.cuda.synchronize()
+    out = to_host_f32(out)
+    lse = lse.cpu().numpy()
+    sc = scores.cpu().numpy()
+    sel = sel.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    for i, h in enumerate(host):
+        pr = O.pool_index_keys(h["idx"])
+        assert np.array_equal(pooled[i, : h["n"] // 4].cpu().numpy().view(np.uint32), pr.view(np.uint32))
+        s64 = O.score_blocks(h["idx_q"][0], pr, h["n"])
+        g32 = sc[i, : len(s64)].astype(np.float64)
+        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k))
+        check_selection(sel[i], int(n_sel[i]), s64, k)
+        dd = {"workload": wl, "rows": np.asarray([h["n"] - 1]), "q": h["q"], "k": h["k"], "v": h["v"]}
+        check_attention(out[i], lse[i], dd, 0, sel[i, : n_sel[i]], "bf16")
+
+
+@pytest.mark.parametrize("seed,nseg", [(1, [1, 2, 3]), (2, [13, 5, 1]), (3, [4, 12, 7, 9]), (4, [16])])
+def test_segments_small(Q, seed, nseg):
+    say("segments", seed, nseg)
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
+    _segmented_case(Q, ctx, nseg, seed)
+
+
+def test_batched_segmented_full_size(Q):
+    """16 sequences, contexts 4,096..131,072, 1..5 segments each (seeded)."""
+    say("batched segmented decode, 16 sequences (full size)")
+    specs = datagen.batched_specs()
+    data = datagen.gen_batched_layer(specs)
+    n_seq = len(specs)
+    cap_max = max(-(-(sp.n_ctx + 4) // 256) * 256 for sp in specs)
+    idx_cache = torch.zeros((n_seq, cap_max, 128), dtype=torch.bfloat16, device=DEV)
+    pooled = torch.zeros((n_seq, cap_max // 4, 128), dtype=torch.float32, device=DEV)
+    segs_dev = []
+    for s, (sp, h) in enumerate(zip(specs, data)):
+        Q.qsa_append_pool(to_dev(h["idx"], "bf16"), torch.arange(sp.n_ctx, dtype=torch.int64, device=DEV),
+                          idx_cache[s : s + 1], pooled[s : s + 1])
+        segs = []
+        for st, ln, cap in zip(sp.seg_start, sp.seg_len, sp.seg_cap):
+            kt = torch.zeros((2, cap, 256), dtype=torch.bfloat16, device=DEV)
+            vt = torch.zeros_like(kt)
+            kt[:, :ln] = to_dev(np.ascontiguousarray(h["k"][:, st : st + ln]), "bf16")
+            vt[:, :ln] = to_dev(np.ascontiguousarray(h["v"][:, st : st + ln]), "bf16")
+            segs.append((st, ln, kt, vt))
+        segs_dev.append(segs)
+    kv = Q.KvSegments(segs_dev)
+    rows = torch.tensor([sp.row for sp in specs], dtype=torch.int64, device=DEV)
+    row_seq = torch.arange(n_seq, dtype=torch.int32, device=DEV)
+    idx_q = to_dev(np.concatenate([h["idx_q"] for h in data]), "bf16")
+    q = to_dev(np.concatenate([h["q"] for h in data]), "bf16")
+    nb_max = max(sp.n_ctx for sp in specs) // 4
+    k = 512
+    scores = torch.zeros((n_seq, nb_max), dtype=torch.float32, device=DEV)
+    Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
+    sel = torch.empty((n_seq, k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((n_seq,), dtype=torch.int32, device=DEV)
+    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel)
+    out = torch.empty_like(q)
+    lse = torch.empty((n_seq, 24), dtype=torch.float32, device=DEV)
+    ws = torch.empty(Q.qsa_attn_workspace_bytes(n_seq, 24, 256, k), dtype=torch.uint8, device=DEV)
+    Q.qsa_gathered_attn(q, rows, kv, sel, n_sel, out, lse, 2, row_seq=row_seq, workspace=ws)
+    torch.cuda.synchronize()
+    out, lse = to_host_f32(out), lse.cpu().numpy()
+    sc, sel, n_sel = scores.cpu().numpy(), sel.cpu().numpy(), n_sel.cpu().numpy()
+    wl = datagen.WORKLOADS["decode_32k"]
+    for i, (sp, h) in enumerate(zip(specs, data)):
+        pr = O.pool_index_keys(h["idx"])
+        assert np.array_equal(pooled[i, : sp.n_ctx // 4].cpu().numpy().view(np.uint32), pr.view(np.uint32))
+        s64 = O.score_blocks(h["idx_q"][0], pr, sp.n_ctx)
+        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(sc[i, : len(s64)].astype(np.float64), k))
+        check_selection(sel[i], int(n_sel[i]), s64, k)
+        dd = {"workload": wl, "rows": np.asarray([sp.row]), "q": h["q"], "k": h["k"], "v": h["v"]}
+        check_attention(out[i], lse[i], dd, 0, sel[i, : n_sel[i]], "bf16")
