@@ -89,7 +89,7 @@ def build_single(Q, wl, layers, dev):
     )
     wsb = Q.qsa_select_workspace_bytes(m, nb_max, k)
     if wsb:
-        shared["ws_sel"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        shared["ws_sel"] = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     return L, shared, nb_max
 
 
@@ -100,9 +100,11 @@ def step_fn(Q, L, sh, nb_max, wl, only=None):
             if only in (None, "append"):
                 Q.qsa_append_pool(ly.new_idx, ly.new_pos, ly.idx_cache, ly.pooled, seq=getattr(ly, "seq", None))
             if only in (None, "score"):
-                Q.qsa_score_blocks(ly.idx_q, ly.rows, ly.pooled, sh["scores"], nb_max, row_seq=ly.row_seq)
+                Q.qsa_score_blocks(ly.idx_q, ly.rows, ly.pooled, sh["scores"], nb_max, row_seq=ly.row_seq,
+                                   sel_workspace=sh["ws_sel"])
             if only in (None, "select"):
-                Q.qsa_select_topk(sh["scores"], ly.rows, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"], sh["ws_sel"])
+                Q.qsa_select_topk(sh["scores"], ly.rows, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"], sh["ws_sel"],
+                                  prepared=True)
             if only in (None, "attn"):
                 Q.qsa_gathered_attn(ly.q, ly.rows, ly.kv, sh["sel"], sh["n_sel"], sh["out"], sh["lse"], wl.hkv,
                                     row_seq=ly.row_seq, workspace=sh["ws"])
@@ -112,9 +114,13 @@ def step_fn(Q, L, sh, nb_max, wl, only=None):
 def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
     """Average device time of one launch of ``kind`` (HIP events on the
     launch stream).  A spin kernel runs first so that every event/launch pair
-    is queued before the device reaches it (no host gaps in the interval)."""
+    is queued before the device reaches it (no host gaps in the interval).
+    The scoring pass builds the selection's histograms, so "score" is timed
+    with its selection run after the interval and "select" after a scoring
+    run before it: the workspace stays consistent."""
     import torch
 
+    partner = {"score": (None, "select"), "select": ("score", None)}.get(kind, (None, None))
     evs = []
     torch.cuda.synchronize()
     try:
@@ -125,9 +131,13 @@ def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
         for ly in L:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            if partner[0]:
+                step_fn(Q, [ly], sh, nb_max, wl, only=partner[0])()
             a.record()
             step_fn(Q, [ly], sh, nb_max, wl, only=kind)()
             b.record()
+            if partner[1]:
+                step_fn(Q, [ly], sh, nb_max, wl, only=partner[1])()
             evs.append((a, b))
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) * 1e3 for a, b in evs]

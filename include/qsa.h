@@ -109,11 +109,17 @@ int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
  * scores[m][b] = (sum_h max(0, idx_q[m][h] . pooled[seq][b])) / sqrt(128)
  * for b < min(nb(row_pos[m]), nb_max), accumulated in float32.  Entries past
  * a row's block count are left untouched.
+ *
+ *  sel_workspace  NULL, or a qsa_select_topk workspace: the scoring pass then
+ *                 also stores the score sample the selection starts from, and
+ *                 the following qsa_select_topk on these scores may be called
+ *                 with prepared = 1 (it skips its own sampling pass).
  */
 int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
                      const int64_t* row_pos, const int32_t* row_seq,
                      const float* pooled, int32_t n_seq, int64_t capacity,
-                     int64_t nb_max, float* scores, int64_t ld, qsa_stream_t stream);
+                     int64_t nb_max, float* scores, int64_t ld,
+                     void* sel_workspace, size_t sel_workspace_bytes, qsa_stream_t stream);
 
 /*
  * qsa_select_topk -- keep the best blocks of each row within the budget.
@@ -128,7 +134,12 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
  *  sel       int32 [M][k_blocks]        kept block ids, ascending; unused
  *                                       entries are set to -1 (written)
  *  n_sel     int32 [M]                  min(k_blocks, nb) (written)
- *  workspace / workspace_bytes          >= qsa_select_workspace_bytes(...)
+ *  workspace / workspace_bytes          >= qsa_select_workspace_bytes(...);
+ *                                       needs no initialisation.  Calls
+ *                                       sharing a workspace must not overlap
+ *                                       in time.
+ *  prepared  0, or 1 when qsa_score_blocks stored the sample of these
+ *            scores into this workspace (same M, row_pos and nb_max)
  *
  * When nb <= k_blocks every block is kept.  Otherwise the k_blocks largest
  * scores are kept; equal scores go to the lower block index.  The tail
@@ -138,7 +149,8 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
 int qsa_select_topk(const float* scores, int64_t ld, int32_t M,
                     const int64_t* row_pos, int64_t nb_max, int32_t k_blocks,
                     int32_t* sel, int32_t* n_sel,
-                    void* workspace, size_t workspace_bytes, qsa_stream_t stream);
+                    void* workspace, size_t workspace_bytes, int32_t prepared,
+                    qsa_stream_t stream);
 
 /* K/V of a batch of sequences, each held as 1..QSA_MAX_SEGMENTS segments.
  * Segments follow MTPLX PR #610 ("How it works": one immutable segment per

@@ -61,8 +61,8 @@ class QsaKvSegments(ctypes.Structure):
 
 
 _lib.qsa_append_pool.argtypes = [_P, _I32, _I32, _P, _P, _P, _P, _I32, _I64, _P]
-_lib.qsa_score_blocks.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, _P, _I64, _P]
-_lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
+_lib.qsa_score_blocks.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, _P, _I64, _P, _SZ, _P]
+_lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ, _I32, _P]
 _lib.qsa_gathered_attn.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P, _SZ, _P]
 _lib.qsa_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
@@ -94,6 +94,10 @@ def _check(status: int) -> None:
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream) -> int | None:
@@ -151,8 +155,9 @@ def qsa_append_pool(new_idx: torch.Tensor, pos: torch.Tensor, idx_cache: torch.T
 
 def qsa_score_blocks(idx_q: torch.Tensor, row_pos: torch.Tensor, pooled: torch.Tensor,
                      scores: torch.Tensor, nb_max: int, row_seq: torch.Tensor | None = None,
-                     stream=None) -> None:
-    """``scores`` [M, ld] float32 <- block scores of the rows ``idx_q`` [M,4,128]."""
+                     sel_workspace: torch.Tensor | None = None, stream=None) -> None:
+    """``scores`` [M, ld] float32 <- block scores of the rows ``idx_q`` [M,4,128].
+    With ``sel_workspace`` the pass also prepares ``qsa_select_topk(prepared=True)``."""
     pl = pooled if pooled.dim() == 3 else pooled.unsqueeze(0)
     _need(idx_q.is_contiguous() and pl.is_contiguous() and scores.is_contiguous(), "tensors must be contiguous")
     _need(row_pos.dtype == torch.int64 and (row_seq is None or row_seq.dtype == torch.int32), "row_pos int64, row_seq int32")
@@ -161,20 +166,23 @@ def qsa_score_blocks(idx_q: torch.Tensor, row_pos: torch.Tensor, pooled: torch.T
     _need(scores.dim() == 2 and scores.shape[0] >= m and scores.dtype == torch.float32, "scores [M, ld] float32")
     _check(_lib.qsa_score_blocks(_ptr(idx_q), _dtype_code(idx_q), m, _ptr(row_pos), _ptr(row_seq),
                                  _ptr(pl), pl.shape[0], pl.shape[1] * BLOCK_TOKENS, int(nb_max),
-                                 _ptr(scores), scores.shape[1], _stream(stream)))
+                                 _ptr(scores), scores.shape[1], _ptr(sel_workspace), _nbytes(sel_workspace),
+                                 _stream(stream)))
 
 
 def qsa_select_topk(scores: torch.Tensor, row_pos: torch.Tensor, nb_max: int, k_blocks: int,
                     sel: torch.Tensor, n_sel: torch.Tensor, workspace: torch.Tensor | None = None,
-                    stream=None) -> None:
-    """``sel`` [M,k] int32 (ascending, -1 padded), ``n_sel`` [M] int32."""
+                    prepared: bool = False, stream=None) -> None:
+    """``sel`` [M,k] int32 (ascending, -1 padded), ``n_sel`` [M] int32.
+    ``workspace``: zero-filled once; ``prepared``: the scoring call built its
+    histograms (``qsa_score_blocks(..., sel_workspace=workspace)``)."""
     m = row_pos.numel()
     _need(sel.dtype == torch.int32 and n_sel.dtype == torch.int32 and sel.is_contiguous(), "sel/n_sel int32")
     _need(sel.shape[0] >= m and sel.shape[1] == k_blocks, "sel must be [M, k_blocks]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.qsa_select_topk(_ptr(scores), scores.shape[1], m, _ptr(row_pos), int(nb_max),
                                 int(k_blocks), _ptr(sel), _ptr(n_sel), _ptr(workspace), ws_bytes,
-                                _stream(stream)))
+                                1 if prepared else 0, _stream(stream)))
 
 
 class KvSegments:

@@ -7,16 +7,21 @@
 //
 // Decode / verify kernel: one workgroup (4 waves) per (row, KV head, split).
 // A split walks 64-token tiles of the row's token list (kept blocks in
-// ascending order, then the tail).  Per tile:
-//   1. 64 lanes resolve their token to a K/V row through the sequence's
-//      segment table (segments may cut a 4-token block anywhere);
-//   2. the K and V rows (512 B each at head_dim 256, bf16) are staged into
-//      LDS with 16-byte loads, once for all 12 query heads;
-//   3. QK: wave w handles heads 3w..3w+2, lane = token; the query row is
+// ascending order, then the tail).  Memory round trips are what bound this
+// kernel at decode sizes, so every independent load (row position, kept
+// count, the kept block ids of this split, the segment table) is issued at
+// once, and each lane resolves its own staging rows.  Per tile:
+//   1. each lane resolves 8 of the tile's tokens to K/V rows through the
+//      segment table (segments may cut a 4-token block anywhere) and stages
+//      one 16-byte chunk of each into LDS, once for all 12 query heads: K
+//      row-major with padded rows, V (bf16) interleaved by token pairs;
+//   2. QK: wave w handles heads 3w..3w+2, lane = token; the query row is
 //      wave-uniform (scalar registers) and bf16 pairs go through the packed
 //      dot2 instruction with float32 accumulation;
-//   4. online softmax (base-2 exponentials of logits pre-scaled by log2 e);
-//   5. PV: lane = (dim group, 6 heads), probabilities broadcast from LDS.
+//   3. online softmax with base-2 exponentials of logits pre-scaled by log2 e;
+//      bf16 probabilities are packed in token pairs;
+//   4. PV: lane = (dims, 6 heads); for bf16 one dot2 consumes a token pair
+//      of V and of P, float32 accumulation.
 // Split partials (normalised output + lse) go to the workspace and a second
 // kernel merges them; with a single split the output is written directly.
 #include "qsa_device.h"
@@ -53,16 +58,37 @@ struct KvArgs {
   int n_seg_total;
 };
 
-// Element-type specific pieces of the tile loop.
+struct SegDesc {
+  int64_t lo, hi, cap;
+  const unsigned char* k;
+  const unsigned char* v;
+};
+
+// Element-type specific constants of the tile loop.
 template <class E, int D>
 struct Tile {
-  using T = typename E::T;
   static constexpr int kRowBytes = D * E::kBytes;
-  static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row
-  static constexpr int kKStride = kRowBytes + 16;      // padded K row in LDS
+  static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+  static constexpr int kKStride = kRowBytes + 16;       // padded K row in LDS
   static constexpr int kElemsPerChunk = 16 / E::kBytes;
   static constexpr int kDimsPerThread = D / (kThreads / kHeadHalves);  // PV dims per lane
+  static constexpr int kItems = (kTileTok / 2) * kChunks;  // (token pair, chunk) staging items
+  static constexpr int kItemsPerThread = kItems / kThreads;
 };
+
+// bf16 words (x of token t, y of token t+1) -> interleaved pairs per dim.
+__device__ __forceinline__ void interleave(uint4 a, uint4 b, uint4& lo, uint4& hi) {
+  // out word 2e   = (a.e low,  b.e low)  : dims 2e of the chunk
+  // out word 2e+1 = (a.e high, b.e high) : dims 2e+1
+  lo.x = __builtin_amdgcn_perm(b.x, a.x, 0x05040100u);
+  lo.y = __builtin_amdgcn_perm(b.x, a.x, 0x07060302u);
+  lo.z = __builtin_amdgcn_perm(b.y, a.y, 0x05040100u);
+  lo.w = __builtin_amdgcn_perm(b.y, a.y, 0x07060302u);
+  hi.x = __builtin_amdgcn_perm(b.z, a.z, 0x05040100u);
+  hi.y = __builtin_amdgcn_perm(b.z, a.z, 0x07060302u);
+  hi.z = __builtin_amdgcn_perm(b.w, a.w, 0x05040100u);
+  hi.w = __builtin_amdgcn_perm(b.w, a.w, 0x07060302u);
+}
 
 template <class E, int D>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -74,16 +100,15 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
                    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   using TT = Tile<E, D>;
   using T = typename E::T;
+  constexpr bool kBf = (E::kBytes == 2);
   __shared__ __align__(16) unsigned char k_lds[kTileTok * TT::kKStride];
   __shared__ __align__(16) unsigned char v_lds[kTileTok * TT::kRowBytes];
-  __shared__ __align__(16) float p_lds[kTileTok][kGroup];
+  __shared__ __align__(16) uint32_t p_lds[kTileTok * kGroup];  // bf16: [32 pairs][12]; fp32: [64][12]
   __shared__ float alpha_lds[kGroup];
   __shared__ float m_lds[kGroup], l_lds[kGroup];
-  __shared__ const unsigned char* krow[kTileTok];
-  __shared__ const unsigned char* vrow[kTileTok];
-  __shared__ int64_t seg_lo[kMaxSegments], seg_hi[kMaxSegments], seg_cap[kMaxSegments];
-  __shared__ const unsigned char* seg_k[kMaxSegments];
-  __shared__ const unsigned char* seg_v[kMaxSegments];
+  __shared__ SegDesc segs[kMaxSegments];
+  __shared__ uint32_t valid_lds[kTileTok];
+  __shared__ int nseg_sh;
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -91,35 +116,63 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = uniform(tid / kWave);
+  const int tok_begin = split * tiles_per_split * kTileTok;
+  const int32_t* __restrict__ srow = sel + (int64_t)m * k_blocks;
+
+  // ---- independent loads, issued together
+  const int64_t p = row_pos[m];
+  const int ns_raw = n_sel[m];
+  const int sq_raw = row_seq ? row_seq[m] : 0;
+  // kept block ids this lane's staging rows may need (speculative: every id
+  // read lies inside the row's k_blocks entries)
+  int32_t bid[TT::kItemsPerThread * 2];
+#pragma unroll
+  for (int it = 0; it < TT::kItemsPerThread; ++it) {
+    const int pair = (tid + it * kThreads) / TT::kChunks;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = tok_begin + 2 * pair + u;
+      bid[it * 2 + u] = (j >> 2) < k_blocks ? srow[j >> 2] : -1;
+    }
+  }
+  if (kv.n_seq == 1) {
+    // one sequence: its segments are entries 0 .. n_seg_total-1
+    if (tid < kMaxSegments && tid < kv.n_seg_total) {
+      const int64_t st = kv.seg_start[tid];
+      segs[tid].lo = st;
+      segs[tid].hi = st + kv.seg_len[tid];
+      segs[tid].cap = kv.seg_cap[tid];
+      segs[tid].k = static_cast<const unsigned char*>(kv.k_seg[tid]);
+      segs[tid].v = static_cast<const unsigned char*>(kv.v_seg[tid]);
+    }
+    if (tid == 0) nseg_sh = kv.n_seg_total < kMaxSegments ? kv.n_seg_total : kMaxSegments;
+  } else {
+    const bool seq_ok = sq_raw >= 0 && sq_raw < kv.n_seq;
+    const int sq = seq_ok ? sq_raw : 0;
+    int s_begin = kv.seq_seg_begin[sq], s_end = kv.seq_seg_begin[sq + 1];
+    s_begin = s_begin < 0 ? 0 : s_begin;
+    s_end = s_end > kv.n_seg_total ? kv.n_seg_total : s_end;
+    const int nseg = (seq_ok && s_end > s_begin) ? min(s_end - s_begin, kMaxSegments) : 0;
+    if (tid < nseg) {
+      const int si = s_begin + tid;
+      const int64_t st = kv.seg_start[si];
+      segs[tid].lo = st;
+      segs[tid].hi = st + kv.seg_len[si];
+      segs[tid].cap = kv.seg_cap[si];
+      segs[tid].k = static_cast<const unsigned char*>(kv.k_seg[si]);
+      segs[tid].v = static_cast<const unsigned char*>(kv.v_seg[si]);
+    }
+    if (tid == 0) nseg_sh = nseg;
+  }
 
   // Row geometry.
-  const int64_t p = row_pos[m];
   const int64_t n_vis = p + 1 > 0 ? p + 1 : 0;
   const int64_t nb = n_vis / kBlockTokens;
   const int tail = (int)(n_vis - nb * kBlockTokens);
-  int ns = n_sel[m];
-  ns = ns < 0 ? 0 : ns;
+  int ns = ns_raw < 0 ? 0 : ns_raw;
   ns = ns > k_blocks ? k_blocks : ns;
   ns = (int64_t)ns > nb ? (int)nb : ns;
   const int total = ns * kBlockTokens + tail;
-
-  // Segment table of this row's sequence.
-  int sq = row_seq ? row_seq[m] : 0;
-  const bool seq_ok = sq >= 0 && sq < kv.n_seq;
-  sq = seq_ok ? sq : 0;
-  int s_begin = kv.seq_seg_begin[sq], s_end = kv.seq_seg_begin[sq + 1];
-  s_begin = s_begin < 0 ? 0 : s_begin;
-  s_end = s_end > kv.n_seg_total ? kv.n_seg_total : s_end;
-  const int nseg = (seq_ok && s_end > s_begin) ? min(s_end - s_begin, kMaxSegments) : 0;
-  if (tid < nseg) {
-    const int si = s_begin + tid;
-    const int64_t st = kv.seg_start[si];
-    seg_lo[tid] = st;
-    seg_hi[tid] = st + kv.seg_len[si];
-    seg_cap[tid] = kv.seg_cap[si];
-    seg_k[tid] = static_cast<const unsigned char*>(kv.k_seg[si]);
-    seg_v[tid] = static_cast<const unsigned char*>(kv.v_seg[si]);
-  }
 
   // Running softmax state of this wave's QK heads (identical in all lanes).
   float m_run[kHeadsPerWaveQK], l_run[kHeadsPerWaveQK];
@@ -128,7 +181,6 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.f;
   }
-  // PV accumulators: lane owns dims [dg*DPT, dg*DPT+DPT) of heads half*6..half*6+5.
   constexpr int DPT = TT::kDimsPerThread;
   const int dg = tid % (kThreads / kHeadHalves);
   const int half = tid / (kThreads / kHeadHalves);
@@ -139,60 +191,66 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
     for (int d = 0; d < DPT; ++d) acc[h][d] = 0.f;
 
   const T* __restrict__ qrow = q + ((int64_t)m * hq + (int64_t)g * kGroup) * D;
-  const int32_t* __restrict__ srow = sel + (int64_t)m * k_blocks;
   __syncthreads();
+  const int nseg = nseg_sh;
 
-  const int tok_begin = split * tiles_per_split * kTileTok;
   for (int t = 0; t < tiles_per_split; ++t) {
     const int j0 = tok_begin + t * kTileTok;
     if (j0 >= total) break;
 
-    // 1. resolve tokens
-    if (tid < kTileTok) {
-      const int j = j0 + tid;
-      const unsigned char* kr = nullptr;
-      const unsigned char* vr = nullptr;
-      if (j < total) {
+    // 1. resolve this lane's staging rows and stage them
+#pragma unroll
+    for (int it = 0; it < TT::kItemsPerThread; ++it) {
+      const int item = tid + it * kThreads;
+      const int pair = item / TT::kChunks;
+      const int c = item % TT::kChunks;
+      uint4 kk[2], vv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 2 * pair + u;
+        const int j = j0 + r;
         int64_t tok = -1;
-        if (j < ns * kBlockTokens) {
-          const int64_t b = srow[j >> 2];
-          if (b >= 0 && b < nb) tok = b * kBlockTokens + (j & 3);
-        } else {
-          tok = nb * kBlockTokens + (j - ns * kBlockTokens);
+        if (j < total) {
+          if (j < ns * kBlockTokens) {
+            const int64_t b = (t == 0) ? (int64_t)bid[it * 2 + u] : (int64_t)srow[j >> 2];
+            if (b >= 0 && b < nb) tok = b * kBlockTokens + (j & 3);
+          } else {
+            tok = nb * kBlockTokens + (j - ns * kBlockTokens);
+          }
         }
+        const unsigned char* kr = nullptr;
+        const unsigned char* vr = nullptr;
         if (tok >= 0) {
           for (int si = 0; si < nseg; ++si) {
-            if (tok >= seg_lo[si] && tok < seg_hi[si] && tok - seg_lo[si] < seg_cap[si]) {
-              const int64_t off = ((int64_t)g * seg_cap[si] + (tok - seg_lo[si])) * TT::kRowBytes;
-              kr = seg_k[si] + off;
-              vr = seg_v[si] + off;
+            const SegDesc& sd = segs[si];
+            if (tok >= sd.lo && tok < sd.hi && tok - sd.lo < sd.cap) {
+              const int64_t off = ((int64_t)g * sd.cap + (tok - sd.lo)) * TT::kRowBytes + c * 16;
+              kr = sd.k + off;
+              vr = sd.v + off;
               break;
             }
           }
         }
+        kk[u] = kr ? *reinterpret_cast<const uint4*>(kr) : make_uint4(0, 0, 0, 0);
+        vv[u] = kr ? *reinterpret_cast<const uint4*>(vr) : make_uint4(0, 0, 0, 0);
+        if (c == 0) valid_lds[r] = kr ? 1u : 0u;
+        *reinterpret_cast<uint4*>(k_lds + r * TT::kKStride + c * 16) = kk[u];
       }
-      krow[tid] = kr;
-      vrow[tid] = vr;
+      if constexpr (kBf) {
+        // pair-interleaved V: word (pair, dim) = (V[2 pair][dim], V[2 pair + 1][dim])
+        uint4 lo, hi;
+        interleave(vv[0], vv[1], lo, hi);
+        uint4* dst = reinterpret_cast<uint4*>(v_lds + (pair * D + c * TT::kElemsPerChunk) * 4);
+        dst[0] = lo;
+        dst[1] = hi;
+      } else {
+        *reinterpret_cast<uint4*>(v_lds + (2 * pair) * TT::kRowBytes + c * 16) = vv[0];
+        *reinterpret_cast<uint4*>(v_lds + (2 * pair + 1) * TT::kRowBytes + c * 16) = vv[1];
+      }
     }
     __syncthreads();
 
-    // 2. stage K and V rows (zeros for missing rows)
-    for (int idx = tid; idx < kTileTok * TT::kChunks; idx += kThreads) {
-      const int r = idx / TT::kChunks;
-      const int c = idx % TT::kChunks;
-      const unsigned char* kr = krow[r];
-      const unsigned char* vr = vrow[r];
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (kr) {
-        kv4 = *reinterpret_cast<const uint4*>(kr + c * 16);
-        vv4 = *reinterpret_cast<const uint4*>(vr + c * 16);
-      }
-      *reinterpret_cast<uint4*>(k_lds + r * TT::kKStride + c * 16) = kv4;
-      *reinterpret_cast<uint4*>(v_lds + r * TT::kRowBytes + c * 16) = vv4;
-    }
-    __syncthreads();
-
-    // 3. QK for heads 3w..3w+2, lane = token
+    // 2. QK for heads 3w..3w+2, lane = token
     float sc[kHeadsPerWaveQK];
 #pragma unroll
     for (int hh = 0; hh < kHeadsPerWaveQK; ++hh) sc[hh] = 0.f;
@@ -200,47 +258,55 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
     const T* __restrict__ qw = qrow + (wave * kHeadsPerWaveQK) * D;
 #pragma unroll 4
     for (int c = 0; c < TT::kChunks; ++c) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(kl + c * 16);
+      const uint4 kv4 = *reinterpret_cast<const uint4*>(kl + c * 16);
 #pragma unroll
       for (int hh = 0; hh < kHeadsPerWaveQK; ++hh) {
         const T* qc = qw + hh * D + c * TT::kElemsPerChunk;
-        if constexpr (E::kBytes == 2) {
+        if constexpr (kBf) {
           const uint32_t* q32 = reinterpret_cast<const uint32_t*>(qc);
           float a = sc[hh];
-          a = dot2_bf16(q32[0], kk.x, a);
-          a = dot2_bf16(q32[1], kk.y, a);
-          a = dot2_bf16(q32[2], kk.z, a);
-          a = dot2_bf16(q32[3], kk.w, a);
+          a = dot2_bf16(q32[0], kv4.x, a);
+          a = dot2_bf16(q32[1], kv4.y, a);
+          a = dot2_bf16(q32[2], kv4.z, a);
+          a = dot2_bf16(q32[3], kv4.w, a);
           sc[hh] = a;
         } else {
           float a = sc[hh];
-          a = fmaf(qc[0], __uint_as_float(kk.x), a);
-          a = fmaf(qc[1], __uint_as_float(kk.y), a);
-          a = fmaf(qc[2], __uint_as_float(kk.z), a);
-          a = fmaf(qc[3], __uint_as_float(kk.w), a);
+          a = fmaf(qc[0], __uint_as_float(kv4.x), a);
+          a = fmaf(qc[1], __uint_as_float(kv4.y), a);
+          a = fmaf(qc[2], __uint_as_float(kv4.z), a);
+          a = fmaf(qc[3], __uint_as_float(kv4.w), a);
           sc[hh] = a;
         }
       }
     }
-    const bool valid = krow[lane] != nullptr;
+    const bool valid = valid_lds[lane] != 0u;
 
-    // 4. online softmax
+    // 3. online softmax
 #pragma unroll
     for (int hh = 0; hh < kHeadsPerWaveQK; ++hh) {
       const float s2 = valid ? sc[hh] * scale_log2 : -INFINITY;
       const float tmax = wave_max(s2);
       const float m_new = fmaxf(m_run[hh], tmax);
       const float alpha = (m_run[hh] == m_new) ? 1.f : exp2f(m_run[hh] - m_new);
-      const float pv = (s2 == -INFINITY) ? 0.f : exp2f(s2 - m_new);
+      float pv = (s2 == -INFINITY) ? 0.f : exp2f(s2 - m_new);
+      const int h = wave * kHeadsPerWaveQK + hh;
+      if constexpr (kBf) {
+        // the PV dot2 consumes bf16 probabilities: normalise by the same values
+        const uint32_t pb = f32_to_bf16_bits(pv);
+        pv = __uint_as_float(pb << 16);
+        const uint32_t nb16 = __shfl_xor(pb, 1, kWave);
+        if ((lane & 1) == 0) p_lds[(lane >> 1) * kGroup + h] = pb | (nb16 << 16);
+      } else {
+        p_lds[lane * kGroup + h] = __float_as_uint(pv);
+      }
       l_run[hh] = l_run[hh] * alpha + wave_sum(pv);
       m_run[hh] = m_new;
-      const int h = wave * kHeadsPerWaveQK + hh;
-      p_lds[lane][h] = pv;
       if (lane == 0) alpha_lds[h] = alpha;
     }
     __syncthreads();
 
-    // 5. PV
+    // 4. PV
 #pragma unroll
     for (int h = 0; h < kHeadsPV; ++h) {
       const float a = alpha_lds[half * kHeadsPV + h];
@@ -248,27 +314,38 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
       for (int d = 0; d < DPT; ++d) acc[h][d] *= a;
     }
     const int rows = min(kTileTok, total - j0);
-    for (int r = 0; r < rows; ++r) {
-      float vv[DPT];
-      const unsigned char* vp = v_lds + r * TT::kRowBytes + dg * DPT * E::kBytes;
-      if constexpr (E::kBytes == 2) {
+    if constexpr (kBf) {
+      const int pairs = (rows + 1) >> 1;
+      for (int pr = 0; pr < pairs; ++pr) {
+        uint32_t w[DPT];
         if constexpr (DPT == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
-          vv[0] = __uint_as_float(w << 16);
-          vv[1] = __uint_as_float(w & 0xffff0000u);
+          const uint2 x = *reinterpret_cast<const uint2*>(v_lds + (pr * D + dg * 2) * 4);
+          w[0] = x.x;
+          w[1] = x.y;
         } else {
-          vv[0] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(vp));
+          w[0] = *reinterpret_cast<const uint32_t*>(v_lds + (pr * D + dg) * 4);
         }
-      } else {
+        const uint32_t* pp = &p_lds[pr * kGroup + half * kHeadsPV];
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) vv[d] = reinterpret_cast<const float*>(vp)[d];
+        for (int h = 0; h < kHeadsPV; ++h) {
+          const uint32_t pw = pp[h];
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) acc[h][d] = dot2_bf16(pw, w[d], acc[h][d]);
+        }
       }
-      const float* pr = &p_lds[r][half * kHeadsPV];
+    } else {
+      for (int r = 0; r < rows; ++r) {
+        float vv[DPT];
+        const float* vp = reinterpret_cast<const float*>(v_lds + r * TT::kRowBytes) + dg * DPT;
 #pragma unroll
-      for (int h = 0; h < kHeadsPV; ++h) {
-        const float w = pr[h];
+        for (int d = 0; d < DPT; ++d) vv[d] = vp[d];
+        const float* pr = reinterpret_cast<const float*>(&p_lds[r * kGroup + half * kHeadsPV]);
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) acc[h][d] = fmaf(w, vv[d], acc[h][d]);
+        for (int h = 0; h < kHeadsPV; ++h) {
+          const float w = pr[h];
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) acc[h][d] = fmaf(w, vv[d], acc[h][d]);
+        }
       }
     }
     __syncthreads();
@@ -283,6 +360,7 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
     }
   }
   __syncthreads();
+  // bf16 PV dims: lane dg owns dims 2dg, 2dg+1 (DPT 2) or dg (DPT 1)
 #pragma unroll
   for (int h6 = 0; h6 < kHeadsPV; ++h6) {
     const int h = half * kHeadsPV + h6;
@@ -349,12 +427,12 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   }
   __syncthreads();
   tot = tot_sh;
+  // every partial is finite (an empty split stores zeros), so the loads are
+  // unconditional and independent
   float o = 0.f;
   const float* O = ws_o + head * splits * D + tid;
-  for (int i = 0; i < splits; ++i) {
-    const float w = w_lds[i];
-    if (w != 0.f) o = fmaf(w, O[(int64_t)i * D], o);
-  }
+#pragma unroll 8
+  for (int i = 0; i < splits; ++i) o = fmaf(w_lds[i], O[(int64_t)i * D], o);
   o = (empty || tot == 0.f) ? 0.f : o / tot;
   out[head * D + tid] = E::from_f(o);
   if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot);
@@ -429,8 +507,7 @@ hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv
       return launch_typed<BF16, 256>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
     return launch_typed<BF16, 128>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
   }
-  if (head_dim == 256)
-    return launch_typed<F32, 256>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+  // float32 K/V is served at head_dim 128 (validated by the caller)
   return launch_typed<F32, 128>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
 }
 

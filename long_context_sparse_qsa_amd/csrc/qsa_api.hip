@@ -54,7 +54,8 @@ int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new, const int
 
 int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t* row_pos,
                      const int32_t* row_seq, const float* pooled, int32_t n_seq, int64_t capacity,
-                     int64_t nb_max, float* scores, int64_t ld, qsa_stream_t stream) {
+                     int64_t nb_max, float* scores, int64_t ld, void* sel_workspace,
+                     size_t sel_workspace_bytes, qsa_stream_t stream) {
   if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_score_blocks: dtype %d is not QSA_F32 or QSA_BF16", dtype);
   if (M < 0) return fail(QSA_ERR_ARG, "qsa_score_blocks: M = %d < 0", M);
   if (n_seq < 1) return fail(QSA_ERR_ARG, "qsa_score_blocks: n_seq = %d < 1", n_seq);
@@ -65,11 +66,15 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t*
     return fail(QSA_ERR_ARG, "qsa_score_blocks: nb_max %lld outside [0, capacity/4 = %lld]",
                 (long long)nb_max, (long long)(capacity / QSA_BLOCK_TOKENS));
   if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_score_blocks: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  if (sel_workspace && sel_workspace_bytes < qsa::select_workspace_bytes(M, nb_max, 1))
+    return fail(QSA_ERR_WORKSPACE, "qsa_score_blocks: selection workspace %zu B < %zu B needed",
+                sel_workspace_bytes, qsa::select_workspace_bytes(M, nb_max, 1));
   if (M == 0 || nb_max == 0) return ok();
   if (!idx_q || !row_pos || !pooled || !scores)
     return fail(QSA_ERR_ARG, "qsa_score_blocks: null pointer (idx_q, row_pos, pooled or scores)");
   return launch_status(qsa::launch_score_blocks(idx_q, dtype, M, row_pos, row_seq, pooled, n_seq,
-                                                capacity, nb_max, scores, ld, (hipStream_t)stream),
+                                                capacity, nb_max, scores, ld,
+                                                static_cast<uint32_t*>(sel_workspace), (hipStream_t)stream),
                        "qsa_score_blocks");
 }
 
@@ -80,7 +85,7 @@ size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_block
 
 int qsa_select_topk(const float* scores, int64_t ld, int32_t M, const int64_t* row_pos,
                     int64_t nb_max, int32_t k_blocks, int32_t* sel, int32_t* n_sel,
-                    void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
+                    void* workspace, size_t workspace_bytes, int32_t prepared, qsa_stream_t stream) {
   if (M < 0) return fail(QSA_ERR_ARG, "qsa_select_topk: M = %d < 0", M);
   if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
     return fail(QSA_ERR_ARG, "qsa_select_topk: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
@@ -92,6 +97,11 @@ int qsa_select_topk(const float* scores, int64_t ld, int32_t M, const int64_t* r
   if (M == 0) return ok();
   if (!row_pos || !sel || !n_sel || (nb_max > 0 && !scores))
     return fail(QSA_ERR_ARG, "qsa_select_topk: null pointer (scores, row_pos, sel or n_sel)");
+  if (prepared != 0 && prepared != 1) return fail(QSA_ERR_ARG, "qsa_select_topk: prepared = %d is not 0 or 1", prepared);
+  if (prepared)
+    return launch_status(qsa::launch_select_after_hist(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel,
+                                                       workspace, (hipStream_t)stream),
+                         "qsa_select_topk");
   return launch_status(qsa::launch_select_topk(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel,
                                                workspace, workspace_bytes, (hipStream_t)stream),
                        "qsa_select_topk");

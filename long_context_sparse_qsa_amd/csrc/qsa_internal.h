@@ -14,15 +14,22 @@ hipError_t launch_append_pool(const void* new_idx, int dtype, int n_new, const i
                               const int32_t* seq, void* idx_cache, float* pooled, int n_seq,
                               int64_t capacity, hipStream_t stream);
 
+// With sel_ws non-null the scoring epilogue also builds the per-row key
+// histograms the selection consumes (see select.hip).
 hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_t* row_pos,
                                const int32_t* row_seq, const float* pooled, int n_seq,
                                int64_t capacity, int64_t nb_max, float* scores, int64_t ld,
-                               hipStream_t stream);
+                               uint32_t* sel_ws, hipStream_t stream);
 
 size_t select_workspace_bytes(int max_M, int64_t nb_max, int k_blocks);
+// Standalone selection: histogram, collect and finalize passes.
 hipError_t launch_select_topk(const float* scores, int64_t ld, int M, const int64_t* row_pos,
                               int64_t nb_max, int k_blocks, int32_t* sel, int32_t* n_sel,
                               void* ws, size_t ws_bytes, hipStream_t stream);
+// Selection after a histogram-building scoring pass: collect and finalize.
+hipError_t launch_select_after_hist(const float* scores, int64_t ld, int M, const int64_t* row_pos,
+                                   int64_t nb_max, int k_blocks, int32_t* sel, int32_t* n_sel,
+                                   void* ws, hipStream_t stream);
 
 // Split plan of the gathered attention for M rows (same on every call with
 // the same arguments, so results are reproducible bit for bit).

@@ -3,167 +3,199 @@
 // products times 1/sqrt(128); section 03: a few-row variant for decode and
 // verify and a 16-row variant for prefill).
 //
-// Few-row variant (this file): the pass streams the float32 pooled keys
-// (512 B per block) once for a group of up to 8 rows that share one
-// sequence, so it is bound by HBM bandwidth.  One wave owns 64 consecutive
-// blocks.  The tile is read from HBM in four 32-dimension slabs with fully
-// coalesced 16-byte loads (each slab row is one 128-byte line), transposed
-// through LDS so that each lane holds one block, and the next slab's loads
-// are issued before the current slab is consumed.  The index queries are
-// wave-uniform, so they live in scalar registers and every multiply-add is a
-// single VALU op with a scalar operand.  Accumulation is float32.
+// Few-row variant (this file).  The pass streams the float32 pooled keys
+// (512 B per block) once for a group of up to 8 rows of one sequence, so HBM
+// bandwidth bounds it.  The contraction itself -- (rows x 4 heads) x 128
+// dims against 16 blocks at a time -- runs on the float32 matrix cores
+// (v_mfma_f32_16x16x4_f32): A = 16 blocks x 4 dims of pooled keys, B = 4
+// dims x 16 (row, head) columns of index queries, float32 accumulation.  On
+// the vector ALU the same work at 4 rows would need ~3.4 us of pure FMA
+// issue for 4.2 us of HBM time at peak; on the matrix cores it needs half
+// that and leaves the VALU free, so the pass stays memory bound.
+//
+// Data flow per wave: groups of 16 consecutive blocks.  Lane l reads 16
+// bytes of block (l % 16) at dimension 16c + 4(l / 16), for c = 0..7: each
+// load instruction covers 64 contiguous bytes of 16 blocks, and every pooled
+// byte is read once.  The dimension order inside the MFMA k-axis is a
+// permutation (dims 16c + 4(l/16) + t for the t-th of 4 MFMAs of chunk c);
+// the index-query operand is loaded with the same permutation, so the sum
+// is unchanged.  All of a wave's loads are issued before the first MFMA.
+// Output D[i][j] (i = block, j = row*4 + head) is ReLU'd and summed over the
+// 4 heads with two lane shuffles inside each group of 4 lanes.
+//
+// With HIST, the epilogue also feeds the top-k selection: the score of one
+// block per 16-block group (at a hashed offset) is stored in the row's sample
+// slots in the selection workspace (plain stores, no atomics).
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "select_common.h"
 
 namespace qsa {
 
 namespace {
 
-constexpr int kTile = 64;          // blocks per wave
-constexpr int kSlab = 32;          // dimensions per slab
-constexpr int kSlabs = kIndexDim / kSlab;
-constexpr int kPad = 4;            // LDS row padding (floats): conflict-free 16 B reads
-constexpr int kRow = kSlab + kPad;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroupBlocks = 16;   // blocks per MFMA row group
+constexpr int kChunks = kIndexDim / 16;  // 8 chunks of 16 dims
+constexpr int kGroupsPerWave = 2;
+constexpr int kWavesPerWG = 4;
+constexpr int kBlocksPerWave = kGroupBlocks * kGroupsPerWave;
+constexpr int kBlocksPerWG = kBlocksPerWave * kWavesPerWG;
 constexpr float kScoreScale = 0.08838834764831845f;  // 1/sqrt(128)
 
-// Four consecutive index-query values (wave-uniform address: scalar loads).
 template <class EQ>
-__device__ __forceinline__ void load_q4(const typename EQ::T* __restrict__ q, float* v);
+__device__ __forceinline__ float4 load_q4(const typename EQ::T* __restrict__ q);
 template <>
-__device__ __forceinline__ void load_q4<F32>(const float* __restrict__ q, float* v) {
-  const float4 x = *reinterpret_cast<const float4*>(q);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+__device__ __forceinline__ float4 load_q4<F32>(const float* __restrict__ q) {
+  return *reinterpret_cast<const float4*>(q);
 }
 template <>
-__device__ __forceinline__ void load_q4<BF16>(const uint16_t* __restrict__ q, float* v) {
+__device__ __forceinline__ float4 load_q4<BF16>(const uint16_t* __restrict__ q) {
   const uint2 x = *reinterpret_cast<const uint2*>(q);
-  v[0] = __uint_as_float(x.x << 16);
-  v[1] = __uint_as_float(x.x & 0xffff0000u);
-  v[2] = __uint_as_float(x.y << 16);
-  v[3] = __uint_as_float(x.y & 0xffff0000u);
+  return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                     __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
 }
 
-template <class EQ, int MR>
-__global__ void __launch_bounds__(kWave)
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// NSET column sets of 16 (row, head) columns (4 rows per set); RPG rows per
+// group (RPG = 1 when every row has its own sequence).
+template <class EQ, int NSET, int RPG, bool HIST>
+__global__ void __launch_bounds__(kWave * kWavesPerWG)
 score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
                     const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                     const float* __restrict__ pooled, int n_seq, int64_t capacity,
-                    int64_t nb_max, float* __restrict__ scores, int64_t ld) {
-  __shared__ float4 lds4[2][kTile * kRow / 4];
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.y * MR;
-  const int rows = min(MR, M - m0);
+                    int64_t nb_max, float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ ws) {
+  static_assert(RPG <= 4 * NSET, "rows per group exceed the column sets");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * RPG;
+  const int rows = min(RPG, M - m0);
 
-  int64_t nb_r[MR];
   int64_t nb_hi = 0;
-#pragma unroll
-  for (int r = 0; r < MR; ++r) {
-    nb_r[r] = r < rows ? clamp_nb(row_pos[m0 + r], nb_max) : 0;
-    nb_hi = nb_r[r] > nb_hi ? nb_r[r] : nb_hi;
+  for (int r = 0; r < rows; ++r) {
+    const int64_t nb = clamp_nb(row_pos[m0 + r], nb_max);
+    nb_hi = nb > nb_hi ? nb : nb_hi;
   }
-  const int64_t b0 = (int64_t)blockIdx.x * kTile;
-  if (b0 >= nb_hi) return;
+  const int64_t wave_b0 = (int64_t)blockIdx.x * kBlocksPerWG + wave * kBlocksPerWave;
   const int s = row_seq ? row_seq[m0] : 0;
-  if (s < 0 || s >= n_seq) return;
-  const float* __restrict__ P = pooled + (int64_t)s * (capacity / kBlockTokens) * kIndexDim;
-  const typename EQ::T* __restrict__ Q = idx_q + (int64_t)m0 * kIndexHeads * kIndexDim;
+  const bool active = wave_b0 < nb_hi && s >= 0 && s < n_seq;
+  const int64_t rw = sel::row_words(nb_max);
+  if constexpr (HIST) {
+    // the candidate counter of each row starts from zero for the collect pass
+    if (blockIdx.x == 0 && (int)threadIdx.x < rows) ws[(size_t)(m0 + threadIdx.x) * rw + sel::RowWs::kCount] = 0u;
+  }
+  if (!active) return;
+  const float* __restrict__ P = pooled + (int64_t)(active ? s : 0) * (capacity / kBlockTokens) * kIndexDim;
 
-  // Slab loads: float4 number f = j*64 + lane covers row f/8, column (f%8)*4.
-  float4 pre[8];
-  auto load_slab = [&](int c) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = j * kWave + lane;
-      const int r = f >> 3;
-      const int64_t b = b0 + r;
-      if (b < nb_hi) {
-        pre[j] = *reinterpret_cast<const float4*>(P + b * kIndexDim + c * kSlab + (f & 7) * 4);
-      } else {
-        pre[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-  };
-  auto store_slab = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = j * kWave + lane;
-      lds4[buf][(f >> 3) * (kRow / 4) + (f & 7)] = pre[j];
-    }
-  };
+  const int i16 = lane & 15;   // A row (block in group) / B column
+  const int kq = lane >> 4;    // k slot 0..3
 
-  float acc[MR][kIndexHeads];
+  // Pooled loads: all groups, all chunks, issued up front.
+  float4 a[kGroupsPerWave][kChunks];
 #pragma unroll
-  for (int r = 0; r < MR; ++r)
+  for (int g = 0; g < kGroupsPerWave; ++g) {
+    const int64_t b = wave_b0 + g * kGroupBlocks + i16;
+    const float* src = P + b * kIndexDim + 4 * kq;
 #pragma unroll
-    for (int h = 0; h < kIndexHeads; ++h) acc[r][h] = 0.f;
+    for (int c = 0; c < kChunks; ++c)
+      a[g][c] = (active && b < nb_hi) ? *reinterpret_cast<const float4*>(src + 16 * c) : zero4();
+  }
 
-  load_slab(0);
-#pragma unroll 1
-  for (int c = 0; c < kSlabs; ++c) {
-    const int buf = c & 1;
-    store_slab(buf);
-    __syncthreads();
-    if (c + 1 < kSlabs) load_slab(c + 1);
-#pragma unroll 1
-    for (int d4 = 0; d4 < kSlab / 4; ++d4) {
-      const float4 p = lds4[buf][lane * (kRow / 4) + d4];
-      const int dim0 = c * kSlab + d4 * 4;
+  // Index-query operand: column j = row*4 + head of set st, dims 16c + 4*kq + t.
+  float4 bq[NSET][kChunks];
 #pragma unroll
-      for (int r = 0; r < MR; ++r) {
-        const int rr = r < rows ? r : 0;  // rows past the group end reuse row 0 (not stored)
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    const int h = i16 & 3;
+    const bool live = r < rows;
+    const typename EQ::T* qsrc = idx_q + ((int64_t)(m0 + (live ? r : 0)) * kIndexHeads + h) * kIndexDim + 4 * kq;
 #pragma unroll
-        for (int h = 0; h < kIndexHeads; ++h) {
-          float qv[4];
-          load_q4<EQ>(Q + (rr * kIndexHeads + h) * kIndexDim + dim0, qv);
-          float a = acc[r][h];
-          a = fmaf(p.x, qv[0], a);
-          a = fmaf(p.y, qv[1], a);
-          a = fmaf(p.z, qv[2], a);
-          a = fmaf(p.w, qv[3], a);
-          acc[r][h] = a;
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? load_q4<EQ>(qsrc + 16 * c) : zero4();
+  }
+
+  int64_t nb_row[NSET];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    nb_row[st] = r < rows ? clamp_nb(row_pos[m0 + r], nb_max) : 0;
+  }
+
+  float sv[kGroupsPerWave][NSET][4];
+#pragma unroll
+  for (int g = 0; g < kGroupsPerWave; ++g) {
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].x, bq[st][c].x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].y, bq[st][c].y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].z, bq[st][c].z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].w, bq[st][c].w, acc, 0, 0, 0);
         }
       }
+      // acc[v] = D[4*kq + v][i16]: block wave_b0 + 16g + 4kq + v, column i16.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = fmaxf(acc[v], 0.f);
+        x += __shfl_xor(x, 1, kWave);
+        x += __shfl_xor(x, 2, kWave);
+        sv[g][st][v] = x * kScoreScale;
+      }
+      const int r = st * 4 + (i16 >> 2);
+      if (active && (i16 & 3) == 0 && r < rows) {
+        float* dst = scores + (int64_t)(m0 + r) * ld;
+        const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (bb + v < nb_row[st]) dst[bb + v] = sv[g][st][v];
+      }
     }
   }
 
-  const int64_t b = b0 + lane;
+  if constexpr (HIST) {
+    // one sampled block per 16-block group: its score goes to the group's slot
 #pragma unroll
-  for (int r = 0; r < MR; ++r) {
-    if (r < rows && b < nb_r[r]) {
-      float sum = fmaxf(acc[r][0], 0.f);
+    for (int g = 0; g < kGroupsPerWave; ++g) {
 #pragma unroll
-      for (int h = 1; h < kIndexHeads; ++h) sum += fmaxf(acc[r][h], 0.f);
-      scores[(int64_t)(m0 + r) * ld + b] = sum * kScoreScale;
+      for (int st = 0; st < NSET; ++st) {
+        const int r = st * 4 + (i16 >> 2);
+        const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if ((i16 & 3) == 0 && r < rows && bb + v < nb_row[st] && sel::sampled((uint32_t)(bb + v)))
+            reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + sel::RowWs::kSamples + ((bb + v) >> 4)] =
+                sv[g][st][v];
+      }
     }
   }
 }
 
-template <class EQ, int MR>
+template <class EQ, int NSET, int RPG, bool HIST>
 hipError_t launch_fewrow(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
                          const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
-                         float* scores, int64_t ld, hipStream_t stream) {
-  const int64_t tiles = (nb_max + kTile - 1) / kTile;
-  if (tiles == 0) return hipSuccess;
-  dim3 grid((unsigned)tiles, (unsigned)((M + MR - 1) / MR)), block(kWave);
-  hipLaunchKernelGGL((score_fewrow_kernel<EQ, MR>), grid, block, 0, stream,
+                         float* scores, int64_t ld, uint32_t* ws, hipStream_t stream) {
+  const int64_t wgs = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
+  if (wgs == 0) return hipSuccess;
+  dim3 grid((unsigned)wgs, (unsigned)((M + RPG - 1) / RPG));
+  hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST>), grid, dim3(kWave * kWavesPerWG), 0, stream,
                      static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled,
-                     n_seq, capacity, nb_max, scores, ld);
+                     n_seq, capacity, nb_max, scores, ld, ws);
   return hipGetLastError();
 }
 
-template <class EQ>
+template <class EQ, bool HIST>
 hipError_t dispatch_rows(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
                          const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
-                         float* scores, int64_t ld, hipStream_t stream) {
-  // Rows of different sequences read different pooled keys: score them one
-  // by one.  Rows of one sequence share each pooled read in groups of <= 8.
-  const int mr = row_seq ? 1 : (M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8);
-  switch (mr) {
-    case 1: return launch_fewrow<EQ, 1>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
-    case 2: return launch_fewrow<EQ, 2>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
-    case 4: return launch_fewrow<EQ, 4>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
-    default: return launch_fewrow<EQ, 8>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
-  }
+                         float* scores, int64_t ld, uint32_t* ws, hipStream_t stream) {
+  // Rows of different sequences read different pooled keys: one row per
+  // group.  Rows of one sequence share each pooled read, 4 or 8 at a time.
+  if (row_seq) return launch_fewrow<EQ, 1, 1, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
+  if (M <= 4) return launch_fewrow<EQ, 1, 4, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
+  return launch_fewrow<EQ, 2, 8, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
 }
 
 }  // namespace
@@ -171,11 +203,16 @@ hipError_t dispatch_rows(const void* idx_q, int M, const int64_t* row_pos, const
 hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_t* row_pos,
                                const int32_t* row_seq, const float* pooled, int n_seq,
                                int64_t capacity, int64_t nb_max, float* scores, int64_t ld,
-                               hipStream_t stream) {
+                               uint32_t* sel_ws, hipStream_t stream) {
   if (M == 0 || nb_max == 0) return hipSuccess;
+  if (sel_ws) {
+    if (dtype == QSA_BF16)
+      return dispatch_rows<BF16, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, stream);
+    return dispatch_rows<F32, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, stream);
+  }
   if (dtype == QSA_BF16)
-    return dispatch_rows<BF16>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
-  return dispatch_rows<F32>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, stream);
+    return dispatch_rows<BF16, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, stream);
+  return dispatch_rows<F32, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, stream);
 }
 
 }  // namespace qsa

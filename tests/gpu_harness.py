@@ -76,8 +76,20 @@ class Layer:
         sel = torch.empty((m, k), dtype=torch.int32, device=DEV)
         n_sel = torch.empty((m,), dtype=torch.int32, device=DEV)
         wsb = Q.qsa_select_workspace_bytes(m, self.nb_max, k)
-        ws_sel = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV) if wsb else None
+        # the workspace needs no initialisation: start from garbage
+        ws_sel = torch.randint(0, 255, (max(wsb, 1),), dtype=torch.uint8, device=DEV)
         Q.qsa_select_topk(scores, self.rows, self.nb_max, k, sel, n_sel, ws_sel)
+        # the prepared path (sample stored while scoring) must give the same
+        # scores and selection, call after call
+        for _ in range(2):
+            scores_f = torch.full_like(scores, -7.0)
+            sel_f = torch.full_like(sel, -5)
+            n_sel_f = torch.full_like(n_sel, -5)
+            Q.qsa_score_blocks(self.idx_q, self.rows, self.pooled, scores_f, self.nb_max, sel_workspace=ws_sel)
+            Q.qsa_select_topk(scores_f, self.rows, self.nb_max, k, sel_f, n_sel_f, ws_sel, prepared=True)
+            torch.cuda.synchronize()
+            assert torch.equal(scores_f, scores), "prepared-path scores differ"
+            assert torch.equal(sel_f, sel) and torch.equal(n_sel_f, n_sel), "prepared-path selection differs"
         out = torch.empty_like(self.q)
         lse = torch.empty((m, wl.hq), dtype=torch.float32, device=DEV)
         wsa = Q.qsa_attn_workspace_bytes(m, wl.hq, wl.head_dim, k)

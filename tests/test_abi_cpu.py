@@ -59,12 +59,13 @@ def test_append_pool_validation(args, code, word):
 
 
 @pytest.mark.parametrize("args,code,word", [
-    ((FAKE, 3, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None), ERR_ARG, "dtype"),
-    ((FAKE, 1, -2, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None), ERR_ARG, "M ="),
-    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 17, FAKE, 17, None), ERR_ARG, "nb_max"),
-    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 8, None), ERR_ARG, "ld"),
-    ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None), ERR_ARG, "null"),
-    ((None, 1, 0, None, None, None, 1, 64, 16, None, 16, None), Q.QSA_OK, ""),
+    ((FAKE, 3, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "dtype"),
+    ((FAKE, 1, -2, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "M ="),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 17, FAKE, 17, None, 0, None), ERR_ARG, "nb_max"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 8, None, 0, None), ERR_ARG, "ld"),
+    ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "null"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, FAKE, 100, None), ERR_WS, "workspace"),
+    ((None, 1, 0, None, None, None, 1, 64, 16, None, 16, None, 0, None), Q.QSA_OK, ""),
 ])
 def test_score_validation(args, code, word):
     assert L.qsa_score_blocks(*args) == code
@@ -72,11 +73,14 @@ def test_score_validation(args, code, word):
 
 
 @pytest.mark.parametrize("args,code,word", [
-    ((FAKE, 16, 1, FAKE, 16, 0, FAKE, FAKE, None, 0, None), ERR_ARG, "k_blocks"),
-    ((FAKE, 16, 1, FAKE, 16, 2000, FAKE, FAKE, None, 0, None), ERR_ARG, "k_blocks"),
-    ((FAKE, 8, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, None), ERR_ARG, "ld"),
-    ((FAKE, 16, 1, FAKE, 16, 4, None, FAKE, None, 0, None), ERR_ARG, "null"),
-    ((None, 16, 0, None, 16, 4, None, None, None, 0, None), Q.QSA_OK, ""),
+    ((FAKE, 16, 1, FAKE, 16, 0, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "k_blocks"),
+    ((FAKE, 16, 1, FAKE, 16, 2000, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "k_blocks"),
+    ((FAKE, 8, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "ld"),
+    ((FAKE, 16, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_WS, "workspace"),
+    ((FAKE, 16, 1, FAKE, 16, 4, FAKE, FAKE, FAKE, 100, 0, None), ERR_WS, "workspace"),
+    ((FAKE, 16, 1, FAKE, 16, 4, None, FAKE, FAKE, 1 << 30, 0, None), ERR_ARG, "null"),
+    ((FAKE, 16, 1, FAKE, 16, 4, FAKE, FAKE, FAKE, 1 << 30, 2, None), ERR_ARG, "prepared"),
+    ((None, 16, 0, None, 16, 4, None, None, None, 0, 0, None), Q.QSA_OK, ""),
 ])
 def test_select_validation(args, code, word):
     assert L.qsa_select_topk(*args) == code
@@ -133,4 +137,6 @@ def test_workspace_sizes():
         assert cur >= prev
         prev = cur
     assert Q.qsa_attn_workspace_bytes(0, 24, 256, 512) == 0
-    assert Q.qsa_select_workspace_bytes(4, 65280, 512) >= 0
+    # select: one fixed-size record per row (histogram, candidate list)
+    per_row = Q.qsa_select_workspace_bytes(1, 65280, 512)
+    assert per_row > 0 and Q.qsa_select_workspace_bytes(4, 65280, 512) == 4 * per_row

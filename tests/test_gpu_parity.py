@@ -227,7 +227,8 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
     sel = torch.empty((m, k), dtype=torch.int32, device=DEV)
     n_sel = torch.empty((m,), dtype=torch.int32, device=DEV)
-    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel)
+    ws_sel = torch.zeros(Q.qsa_select_workspace_bytes(m, nb_max, k), dtype=torch.uint8, device=DEV)
+    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel, ws_sel)
     out = torch.empty_like(q)
     lse = torch.empty((m, 24), dtype=torch.float32, device=DEV)
     ws = torch.empty(Q.qsa_attn_workspace_bytes(m, 24, 256, k), dtype=torch.uint8, device=DEV)
@@ -289,7 +290,8 @@ def test_batched_segmented_full_size(Q):
     Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
     sel = torch.empty((n_seq, k), dtype=torch.int32, device=DEV)
     n_sel = torch.empty((n_seq,), dtype=torch.int32, device=DEV)
-    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel)
+    ws_sel = torch.zeros(Q.qsa_select_workspace_bytes(n_seq, nb_max, k), dtype=torch.uint8, device=DEV)
+    Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel, ws_sel)
     out = torch.empty_like(q)
     lse = torch.empty((n_seq, 24), dtype=torch.float32, device=DEV)
     ws = torch.empty(Q.qsa_attn_workspace_bytes(n_seq, 24, 256, k), dtype=torch.uint8, device=DEV)
