@@ -14,6 +14,7 @@ The metric is query-rows/s per layer (rows x layers x steps / time).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -24,6 +25,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+CSRC = os.path.join(ROOT, "long_context_sparse_qsa_amd", "csrc")
+# sources of the scoring kernel (the dominant kernel): PMC figures taken on
+# another build of them are not reported
+SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h")
+PMC_FILE = os.path.join(ROOT, "profiles", "score_fewrow_kernel.verify_262k.pmc.txt")
+COPY_BYTES = 256 << 20  # plain copy of known size used to scale the PMC byte counters
 
 
 def parse():
@@ -37,7 +44,33 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 companion measurement")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy first (scales FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
+
+
+def score_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic() -> int | None:
+    """HBM bytes per launch of the scoring kernel from the committed PMC
+    summary, if it was taken on the current kernel sources."""
+    try:
+        kv = {}
+        for line in open(PMC_FILE):
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("source_hash") != score_source_hash():
+            return None
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 # ----------------------------------------------------------------- set-up
@@ -112,36 +145,34 @@ def step_fn(Q, L, sh, nb_max, wl, only=None):
 
 
 def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
-    """Average device time of one launch of ``kind`` (HIP events on the
-    launch stream).  A spin kernel runs first so that every event/launch pair
-    is queued before the device reaches it (no host gaps in the interval).
-    The scoring pass builds the selection's histograms, so "score" is timed
-    with its selection run after the interval and "select" after a scoring
-    run before it: the workspace stays consistent."""
+    """Average device time of one launch of ``kind``, from HIP events on the
+    launch stream around ``reps`` x layers launches queued back to back.  A
+    spin kernel runs first so that the whole sequence is queued before the
+    device reaches it (no host gaps inside the interval).  The prepared
+    selection consumes what the scoring pass left in the workspace, so
+    "select" is timed as score+select pairs minus the scoring time."""
     import torch
 
-    partner = {"score": (None, "select"), "select": ("score", None)}.get(kind, (None, None))
-    evs = []
-    torch.cuda.synchronize()
-    try:
-        torch.cuda._sleep(int(2e8))
-    except Exception:  # pragma: no cover - spin kernel unavailable: host gaps may inflate the figure
-        pass
-    for _ in range(reps):
-        for ly in L:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            if partner[0]:
-                step_fn(Q, [ly], sh, nb_max, wl, only=partner[0])()
-            a.record()
-            step_fn(Q, [ly], sh, nb_max, wl, only=kind)()
-            b.record()
-            if partner[1]:
-                step_fn(Q, [ly], sh, nb_max, wl, only=partner[1])()
-            evs.append((a, b))
-    torch.cuda.synchronize()
-    ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    return sum(ts) / len(ts), min(ts), max(ts)
+    def timed(kinds):
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2e8))
+        except Exception:  # pragma: no cover - spin kernel unavailable: host gaps may inflate the figure
+            pass
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for ly in L:
+                for k_ in kinds:
+                    step_fn(Q, [ly], sh, nb_max, wl, only=k_)()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * len(L))
+
+    if kind == "select":
+        return timed(("score", "select")) - timed(("score",))
+    return timed((kind,))
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -207,6 +238,13 @@ def main():
     print(f"[bench] set-up {wl.name}: {layers} layers, n_ctx {wl.n_ctx}, M {wl.m} in "
           f"{time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
+    if args.pmc_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     run = step_fn(Q, L, sh, nb_max, wl)
     run()
     torch.cuda.synchronize()
@@ -239,7 +277,7 @@ def main():
 
     # per-kernel device time (dominant kernel: scoring, HBM-bound)
     kt = {kind: per_launch_us(Q, L, sh, nb_max, wl, kind) for kind in ("score", "select", "attn", "append")}
-    score_us = kt["score"][0]
+    score_us = kt["score"]
     score_bytes = nb_max * 128 * 4 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
     achieved = score_bytes / (score_us * 1e-6) / 1e9
     # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries
@@ -263,12 +301,12 @@ def main():
                    "layers": layers, "budget_tokens": wl.k_blocks * 4, "hq": wl.hq, "hkv": wl.hkv,
                    "head_dim": wl.head_dim, "graph": not args.eager},
         "roofline": {"bound": "hbm", "kernel": "score_fewrow_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
                      "bytes_per_launch": score_bytes, "launch_us": score_us},
         "path": {"layer_us": layer_us, "bytes_per_layer_step": path_bytes,
                  "achieved_GBs": path_bytes / (layer_us * 1e-6) / 1e9,
                  "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                 "kernel_us": {k_: round(v[0], 2) for k_, v in kt.items()}},
+                 "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}},
     }
     if not args.no_m1 and wl.name == "verify_262k":
         wl1 = datagen.WORKLOADS["decode_262k"]
