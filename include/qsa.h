@@ -104,7 +104,8 @@ int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
  *                                        rows then share one read of pooled)
  *  pooled   float32 [n_seq][capacity/4][128]
  *  nb_max   >= 0, <= capacity/4          host bound on nb(row_pos[m])
- *  scores   float32 [M][ld], ld >= nb_max  (written)
+ *  scores   float32 [M][ld], ld >= nb_max, ld a multiple of 4, 16-byte
+ *           aligned (written)
  *
  * scores[m][b] = (sum_h max(0, idx_q[m][h] . pooled[seq][b])) / sqrt(128)
  * for b < min(nb(row_pos[m]), nb_max), accumulated in float32.  Entries past
@@ -128,7 +129,8 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
  * within a 2,048-token budget, 512 blocks; the incomplete tail block is kept
  * in addition) and section 03 (a radix select follows the scoring).
  *
- *  scores    float32 [M][ld]            as written by qsa_score_blocks
+ *  scores    float32 [M][ld]            as written by qsa_score_blocks (same
+ *                                       ld and alignment rules)
  *  row_pos   int64 [M]; nb_max as for qsa_score_blocks
  *  k_blocks  1..QSA_MAX_K_BLOCKS        budget in blocks (512 = 2,048 tokens)
  *  sel       int32 [M][k_blocks]        kept block ids, ascending; unused

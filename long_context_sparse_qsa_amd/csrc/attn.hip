@@ -47,6 +47,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// 16-byte load through a global (not generic) pointer: generic loads may
+// alias LDS, which would keep them ordered behind the staging writes.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(const unsigned char* p) {
+  typedef __attribute__((address_space(1))) const u32x4_t GU4;
+  const u32x4_t v = *(GU4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 struct KvArgs {
   const int32_t* seq_seg_begin;
   const int64_t* seg_start;
@@ -104,6 +113,7 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
   __shared__ __align__(16) unsigned char k_lds[kTileTok * TT::kKStride];
   __shared__ __align__(16) unsigned char v_lds[kTileTok * TT::kRowBytes];
   __shared__ __align__(16) uint32_t p_lds[kTileTok * kGroup];  // bf16: [32 pairs][12]; fp32: [64][12]
+  __shared__ __align__(16) unsigned char q_lds[kGroup * TT::kRowBytes];  // the group's 12 query rows
   __shared__ float alpha_lds[kGroup];
   __shared__ float m_lds[kGroup], l_lds[kGroup];
   __shared__ SegDesc segs[kMaxSegments];
@@ -125,7 +135,8 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
   const int sq_raw = row_seq ? row_seq[m] : 0;
   // kept block ids this lane's staging rows may need (speculative: every id
   // read lies inside the row's k_blocks entries)
-  int32_t bid[TT::kItemsPerThread * 2];
+  constexpr int kRows = TT::kItemsPerThread * 2;  // staging rows per lane per tile
+  int32_t bid[kRows];
 #pragma unroll
   for (int it = 0; it < TT::kItemsPerThread; ++it) {
     const int pair = (tid + it * kThreads) / TT::kChunks;
@@ -135,35 +146,47 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
       bid[it * 2 + u] = (j >> 2) < k_blocks ? srow[j >> 2] : -1;
     }
   }
+  // the group's query rows, staged once (loads issued before the LDS writes)
+  const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(q + ((int64_t)m * hq + (int64_t)g * kGroup) * D);
+  constexpr int kQChunks = kGroup * TT::kChunks;
+  constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
+  uint4 qv[kQPer];
+#pragma unroll
+  for (int e = 0; e < kQPer; ++e) {
+    const int i = tid + e * kThreads;
+    qv[e] = ldg16(qbytes + (i < kQChunks ? i : 0) * 16);
+  }
+  // this sequence's segment descriptors (loads before any LDS write)
+  int si_lo = 0, nseg_all = 0;
   if (kv.n_seq == 1) {
     // one sequence: its segments are entries 0 .. n_seg_total-1
-    if (tid < kMaxSegments && tid < kv.n_seg_total) {
-      const int64_t st = kv.seg_start[tid];
-      segs[tid].lo = st;
-      segs[tid].hi = st + kv.seg_len[tid];
-      segs[tid].cap = kv.seg_cap[tid];
-      segs[tid].k = static_cast<const unsigned char*>(kv.k_seg[tid]);
-      segs[tid].v = static_cast<const unsigned char*>(kv.v_seg[tid]);
-    }
-    if (tid == 0) nseg_sh = kv.n_seg_total < kMaxSegments ? kv.n_seg_total : kMaxSegments;
+    nseg_all = kv.n_seg_total < kMaxSegments ? kv.n_seg_total : kMaxSegments;
   } else {
     const bool seq_ok = sq_raw >= 0 && sq_raw < kv.n_seq;
     const int sq = seq_ok ? sq_raw : 0;
     int s_begin = kv.seq_seg_begin[sq], s_end = kv.seq_seg_begin[sq + 1];
     s_begin = s_begin < 0 ? 0 : s_begin;
     s_end = s_end > kv.n_seg_total ? kv.n_seg_total : s_end;
-    const int nseg = (seq_ok && s_end > s_begin) ? min(s_end - s_begin, kMaxSegments) : 0;
-    if (tid < nseg) {
-      const int si = s_begin + tid;
-      const int64_t st = kv.seg_start[si];
-      segs[tid].lo = st;
-      segs[tid].hi = st + kv.seg_len[si];
-      segs[tid].cap = kv.seg_cap[si];
-      segs[tid].k = static_cast<const unsigned char*>(kv.k_seg[si]);
-      segs[tid].v = static_cast<const unsigned char*>(kv.v_seg[si]);
-    }
-    if (tid == 0) nseg_sh = nseg;
+    si_lo = s_begin;
+    nseg_all = (seq_ok && s_end > s_begin) ? min(s_end - s_begin, kMaxSegments) : 0;
   }
+  SegDesc mine{};
+  if (tid < nseg_all) {
+    const int si = si_lo + tid;
+    const int64_t st = kv.seg_start[si];
+    mine.lo = st;
+    mine.hi = st + kv.seg_len[si];
+    mine.cap = kv.seg_cap[si];
+    mine.k = static_cast<const unsigned char*>(kv.k_seg[si]);
+    mine.v = static_cast<const unsigned char*>(kv.v_seg[si]);
+  }
+#pragma unroll
+  for (int e = 0; e < kQPer; ++e) {
+    const int i = tid + e * kThreads;
+    if (i < kQChunks) *reinterpret_cast<uint4*>(q_lds + i * 16) = qv[e];
+  }
+  if (tid < nseg_all) segs[tid] = mine;
+  if (tid == 0) nseg_sh = nseg_all;
 
   // Row geometry.
   const int64_t n_vis = p + 1 > 0 ? p + 1 : 0;
@@ -190,7 +213,6 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 #pragma unroll
     for (int d = 0; d < DPT; ++d) acc[h][d] = 0.f;
 
-  const T* __restrict__ qrow = q + ((int64_t)m * hq + (int64_t)g * kGroup) * D;
   __syncthreads();
   const int nseg = nseg_sh;
 
@@ -198,54 +220,93 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
     const int j0 = tok_begin + t * kTileTok;
     if (j0 >= total) break;
 
-    // 1. resolve this lane's staging rows and stage them
+    // 1. resolve this lane's staging rows, then issue all their loads at once
+    int64_t tokv[kRows];
 #pragma unroll
     for (int it = 0; it < TT::kItemsPerThread; ++it) {
-      const int item = tid + it * kThreads;
-      const int pair = item / TT::kChunks;
-      const int c = item % TT::kChunks;
-      uint4 kk[2], vv[2];
+      const int pair = (tid + it * kThreads) / TT::kChunks;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int r = 2 * pair + u;
-        const int j = j0 + r;
+        const int i = it * 2 + u;
+        const int j = j0 + 2 * pair + u;
         int64_t tok = -1;
         if (j < total) {
           if (j < ns * kBlockTokens) {
-            const int64_t b = (t == 0) ? (int64_t)bid[it * 2 + u] : (int64_t)srow[j >> 2];
+            const int64_t b = bid[i];
             if (b >= 0 && b < nb) tok = b * kBlockTokens + (j & 3);
           } else {
             tok = nb * kBlockTokens + (j - ns * kBlockTokens);
           }
         }
-        const unsigned char* kr = nullptr;
-        const unsigned char* vr = nullptr;
-        if (tok >= 0) {
-          for (int si = 0; si < nseg; ++si) {
-            const SegDesc& sd = segs[si];
-            if (tok >= sd.lo && tok < sd.hi && tok - sd.lo < sd.cap) {
-              const int64_t off = ((int64_t)g * sd.cap + (tok - sd.lo)) * TT::kRowBytes + c * 16;
-              kr = sd.k + off;
-              vr = sd.v + off;
-              break;
-            }
-          }
+        tokv[i] = tok;
+      }
+    }
+    const unsigned char* kp[kRows];
+    const unsigned char* vp[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      kp[i] = qbytes;  // any readable address; masked below
+      vp[i] = qbytes;
+    }
+    uint32_t okm = 0u;
+    static_assert(kThreads % TT::kChunks == 0, "a lane keeps one chunk column");
+    const int c_lane = tid % TT::kChunks;  // every item of a lane has the same chunk
+    for (int si = 0; si < nseg; ++si) {  // uniform loop, one LDS broadcast per segment
+      const SegDesc sd = segs[si];
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        const int64_t rel = tokv[i] - sd.lo;
+        const bool hit = tokv[i] >= 0 && rel >= 0 && tokv[i] < sd.hi && rel < sd.cap && !((okm >> i) & 1u);
+        const int64_t off = ((int64_t)g * sd.cap + rel) * TT::kRowBytes + c_lane * 16;
+        kp[i] = hit ? sd.k + off : kp[i];
+        vp[i] = hit ? sd.v + off : vp[i];
+        okm |= hit ? (1u << i) : 0u;
+      }
+    }
+    uint4 kk[kRows], vv[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      kk[i] = ldg16(kp[i]);
+      vv[i] = ldg16(vp[i]);
+    }
+    // next tile's block ids, in flight during this tile's compute
+    if (t + 1 < tiles_per_split) {
+#pragma unroll
+      for (int it = 0; it < TT::kItemsPerThread; ++it) {
+        const int pair = (tid + it * kThreads) / TT::kChunks;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + kTileTok + 2 * pair + u;
+          bid[it * 2 + u] = (j >> 2) < k_blocks ? srow[j >> 2] : -1;
         }
-        kk[u] = kr ? *reinterpret_cast<const uint4*>(kr) : make_uint4(0, 0, 0, 0);
-        vv[u] = kr ? *reinterpret_cast<const uint4*>(vr) : make_uint4(0, 0, 0, 0);
-        if (c == 0) valid_lds[r] = kr ? 1u : 0u;
-        *reinterpret_cast<uint4*>(k_lds + r * TT::kKStride + c * 16) = kk[u];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TT::kItemsPerThread; ++it) {
+      const int item = tid + it * kThreads;
+      const int pair = item / TT::kChunks;
+      const int c = item % TT::kChunks;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = it * 2 + u;
+        const bool ok = (okm >> i) & 1u;
+        if (!ok) {
+          kk[i] = make_uint4(0, 0, 0, 0);
+          vv[i] = make_uint4(0, 0, 0, 0);
+        }
+        if (c == 0) valid_lds[2 * pair + u] = ok ? 1u : 0u;
+        *reinterpret_cast<uint4*>(k_lds + (2 * pair + u) * TT::kKStride + c * 16) = kk[i];
       }
       if constexpr (kBf) {
         // pair-interleaved V: word (pair, dim) = (V[2 pair][dim], V[2 pair + 1][dim])
         uint4 lo, hi;
-        interleave(vv[0], vv[1], lo, hi);
+        interleave(vv[it * 2], vv[it * 2 + 1], lo, hi);
         uint4* dst = reinterpret_cast<uint4*>(v_lds + (pair * D + c * TT::kElemsPerChunk) * 4);
         dst[0] = lo;
         dst[1] = hi;
       } else {
-        *reinterpret_cast<uint4*>(v_lds + (2 * pair) * TT::kRowBytes + c * 16) = vv[0];
-        *reinterpret_cast<uint4*>(v_lds + (2 * pair + 1) * TT::kRowBytes + c * 16) = vv[1];
+        *reinterpret_cast<uint4*>(v_lds + (2 * pair) * TT::kRowBytes + c * 16) = vv[it * 2];
+        *reinterpret_cast<uint4*>(v_lds + (2 * pair + 1) * TT::kRowBytes + c * 16) = vv[it * 2 + 1];
       }
     }
     __syncthreads();
@@ -255,29 +316,26 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 #pragma unroll
     for (int hh = 0; hh < kHeadsPerWaveQK; ++hh) sc[hh] = 0.f;
     const unsigned char* kl = k_lds + lane * TT::kKStride;
-    const T* __restrict__ qw = qrow + (wave * kHeadsPerWaveQK) * D;
+    const unsigned char* qw = q_lds + (wave * kHeadsPerWaveQK) * TT::kRowBytes;
 #pragma unroll 4
     for (int c = 0; c < TT::kChunks; ++c) {
       const uint4 kv4 = *reinterpret_cast<const uint4*>(kl + c * 16);
 #pragma unroll
       for (int hh = 0; hh < kHeadsPerWaveQK; ++hh) {
-        const T* qc = qw + hh * D + c * TT::kElemsPerChunk;
+        const uint4 q4 = *reinterpret_cast<const uint4*>(qw + hh * TT::kRowBytes + c * 16);  // broadcast
+        float a = sc[hh];
         if constexpr (kBf) {
-          const uint32_t* q32 = reinterpret_cast<const uint32_t*>(qc);
-          float a = sc[hh];
-          a = dot2_bf16(q32[0], kv4.x, a);
-          a = dot2_bf16(q32[1], kv4.y, a);
-          a = dot2_bf16(q32[2], kv4.z, a);
-          a = dot2_bf16(q32[3], kv4.w, a);
-          sc[hh] = a;
+          a = dot2_bf16(q4.x, kv4.x, a);
+          a = dot2_bf16(q4.y, kv4.y, a);
+          a = dot2_bf16(q4.z, kv4.z, a);
+          a = dot2_bf16(q4.w, kv4.w, a);
         } else {
-          float a = sc[hh];
-          a = fmaf(qc[0], __uint_as_float(kv4.x), a);
-          a = fmaf(qc[1], __uint_as_float(kv4.y), a);
-          a = fmaf(qc[2], __uint_as_float(kv4.z), a);
-          a = fmaf(qc[3], __uint_as_float(kv4.w), a);
-          sc[hh] = a;
+          a = fmaf(__uint_as_float(q4.x), __uint_as_float(kv4.x), a);
+          a = fmaf(__uint_as_float(q4.y), __uint_as_float(kv4.y), a);
+          a = fmaf(__uint_as_float(q4.z), __uint_as_float(kv4.z), a);
+          a = fmaf(__uint_as_float(q4.w), __uint_as_float(kv4.w), a);
         }
+        sc[hh] = a;
       }
     }
     const bool valid = valid_lds[lane] != 0u;

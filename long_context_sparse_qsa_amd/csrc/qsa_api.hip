@@ -66,6 +66,9 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t*
     return fail(QSA_ERR_ARG, "qsa_score_blocks: nb_max %lld outside [0, capacity/4 = %lld]",
                 (long long)nb_max, (long long)(capacity / QSA_BLOCK_TOKENS));
   if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_score_blocks: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
+    return fail(QSA_ERR_ARG, "qsa_score_blocks: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
+                (long long)ld);
   if (sel_workspace && sel_workspace_bytes < qsa::select_workspace_bytes(M, nb_max, 1))
     return fail(QSA_ERR_WORKSPACE, "qsa_score_blocks: selection workspace %zu B < %zu B needed",
                 sel_workspace_bytes, qsa::select_workspace_bytes(M, nb_max, 1));
@@ -91,6 +94,9 @@ int qsa_select_topk(const float* scores, int64_t ld, int32_t M, const int64_t* r
     return fail(QSA_ERR_ARG, "qsa_select_topk: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
   if (nb_max < 0) return fail(QSA_ERR_ARG, "qsa_select_topk: nb_max %lld < 0", (long long)nb_max);
   if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_select_topk: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
+    return fail(QSA_ERR_ARG, "qsa_select_topk: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
+                (long long)ld);
   const size_t need = qsa::select_workspace_bytes(M, nb_max, k_blocks);
   if (workspace_bytes < need || (need && !workspace))
     return fail(QSA_ERR_WORKSPACE, "qsa_select_topk: workspace %zu B < %zu B needed", workspace_bytes, need);

@@ -73,21 +73,15 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   const int m0 = blockIdx.y * RPG;
   const int rows = min(RPG, M - m0);
 
-  int64_t nb_hi = 0;
-  for (int r = 0; r < rows; ++r) {
-    const int64_t nb = clamp_nb(row_pos[m0 + r], nb_max);
-    nb_hi = nb > nb_hi ? nb : nb_hi;
-  }
+  // The pooled loads depend only on nb_max (the host bound): they are issued
+  // before the row positions arrive.
   const int64_t wave_b0 = (int64_t)blockIdx.x * kBlocksPerWG + wave * kBlocksPerWave;
+  if (wave_b0 >= nb_max) return;
   const int s = row_seq ? row_seq[m0] : 0;
-  const bool active = wave_b0 < nb_hi && s >= 0 && s < n_seq;
+  const bool seq_ok = s >= 0 && s < n_seq;
   const int64_t rw = sel::row_words(nb_max);
-  if constexpr (HIST) {
-    // the candidate counter of each row starts from zero for the collect pass
-    if (blockIdx.x == 0 && (int)threadIdx.x < rows) ws[(size_t)(m0 + threadIdx.x) * rw + sel::RowWs::kCount] = 0u;
-  }
-  if (!active) return;
-  const float* __restrict__ P = pooled + (int64_t)(active ? s : 0) * (capacity / kBlockTokens) * kIndexDim;
+  const int64_t smp_off = sel::sample_off(nb_max);
+  const float* __restrict__ P = pooled + (int64_t)(seq_ok ? s : 0) * (capacity / kBlockTokens) * kIndexDim;
 
   const int i16 = lane & 15;   // A row (block in group) / B column
   const int kq = lane >> 4;    // k slot 0..3
@@ -100,9 +94,8 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     const float* src = P + b * kIndexDim + 4 * kq;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
-      a[g][c] = (active && b < nb_hi) ? *reinterpret_cast<const float4*>(src + 16 * c) : zero4();
+      a[g][c] = b < nb_max ? *reinterpret_cast<const float4*>(src + 16 * c) : zero4();
   }
-
   // Index-query operand: column j = row*4 + head of set st, dims 16c + 4*kq + t.
   float4 bq[NSET][kChunks];
 #pragma unroll
@@ -114,6 +107,14 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? load_q4<EQ>(qsrc + 16 * c) : zero4();
   }
+
+  int64_t nb_hi = 0;
+  for (int r = 0; r < rows; ++r) {
+    const int64_t nb = clamp_nb(row_pos[m0 + r], nb_max);
+    nb_hi = nb > nb_hi ? nb : nb_hi;
+  }
+  const bool active = wave_b0 < nb_hi && seq_ok;
+  if (!active) return;
 
   int64_t nb_row[NSET];
 #pragma unroll
@@ -167,7 +168,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if ((i16 & 3) == 0 && r < rows && bb + v < nb_row[st] && sel::sampled((uint32_t)(bb + v)))
-            reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + sel::RowWs::kSamples + ((bb + v) >> 4)] =
+            reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + smp_off + ((bb + v) >> 4)] =
                 sv[g][st][v];
       }
     }

@@ -4,31 +4,34 @@
 // selector's on-chip memory).  Equal scores go to the lower block index.
 //
 // Scores map to order-preserving 32-bit keys (-0 folded into +0); the top 12
-// key bits are a histogram digit (8 bins per octave of positive scores).  The work is spread over many compute units, with kernel
-// boundaries (not fences) ordering the passes:
+// key bits are a histogram digit (8 bins per octave of positive scores).  The
+// work is spread over many compute units, with kernel boundaries (not fences)
+// ordering the passes:
 //
 //  sample   (standalone selection only; the scoring kernel does the same in
 //           its epilogue) one block of every 16-block group, at a hashed
 //           offset, has its score copied to the group's slot in the row's
 //           workspace record.
-//  collect  many workgroups per row histogram the row's samples in LDS and
-//           walk the histogram from the top to the digit B where the sample
-//           count reaches (1.25 k + 256) / 16: a conservative threshold, about
-//           1.25 k + 256 blocks are expected at or above it.  Every (key, id)
-//           with digit >= B goes to the row's candidate list (one atomic per
-//           wave).
-//  finalize one workgroup per row: an exact radix select over the candidate
-//           keys gives the k-th key T and how many keys equal to T to keep;
-//           those go to the lowest ids (a radix select on complemented ids).
-//           Kept ids are set in an LDS bitmap that a prefix popcount writes
-//           out in ascending order.  A candidate list shorter than k (the
-//           sample misled the threshold), one that overflows (massive ties)
-//           or a row beyond the bitmap takes an exact radix select over the
-//           whole row in the same workgroup, so the result is exact in every
-//           case.
+//  collect  one workgroup per 4,096-block chunk of a row histograms the row's
+//           samples in LDS and walks the histogram from the top to the digit
+//           B where the sample count reaches (1.25 k + 256) / 16: a
+//           conservative threshold, about 1.25 k + 256 blocks are expected at
+//           or above it.  The chunk's (key, id) pairs with digit >= B go to
+//           the chunk's own slots in ascending block order (a block scan
+//           places them; no atomics).
+//  finalize one workgroup per row gathers the chunks' candidates (ascending
+//           block order) and finds the k-th largest candidate key TK with
+//           three histogram levels (12, 10 and 10 key bits; each level counts
+//           only the candidates sharing the bits found so far).  Keys above TK
+//           are kept, and of the keys equal to TK the first ones in block
+//           order; a block scan writes the kept ids in ascending order.  A
+//           candidate list shorter than k (the sample misled the threshold),
+//           one longer than the on-chip list (massive ties) or a row of more
+//           than 64 chunks takes an exact radix select over the whole row in
+//           the same workgroup, so the result is exact in every case.
 //
-// The workspace holds one record per row (sel::RowWs); no part of it needs
-// initialising.
+// The workspace holds one record per row (sel::row_words); no part of it
+// needs initialising.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
@@ -38,18 +41,20 @@ namespace qsa {
 namespace {
 
 using sel::kCandMax;
+using sel::kChunk;
 using sel::kDigits;
 using sel::kDigitShift;
+using sel::kMaxChunks;
 using sel::order_key;
-using sel::RowWs;
 
 constexpr int kBins = 256;
 constexpr int kCopies = 16;
 constexpr int kChunkThreads = 256;
-constexpr int kChunkPer = 16;
-constexpr int kChunk = kChunkThreads * kChunkPer;  // 4,096 scores per workgroup
+constexpr int kChunkPer = kChunk / kChunkThreads;  // 16 consecutive scores per lane
 constexpr int kFinThreads = 512;
-constexpr int kBitmapWords = 8192;                 // 262,144 blocks
+constexpr int kFinPer = kCandMax / kFinThreads;    // 8 candidates per thread
+constexpr int kLowBins = 1024;                     // 10-bit digits below the 12-bit one
+static_assert(kChunkPer % 4 == 0, "float4 score loads");
 
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
@@ -104,72 +109,17 @@ __device__ void find_digit_desc(const uint32_t* cnt, int nbins, uint32_t want, u
 }
 
 struct FinSmem {
-  uint32_t hist16[kBins * kCopies];
+  uint32_t hist16[kBins * kCopies];  // exact-path radix passes; also the 12-bit digit histogram
   uint32_t tot[kBins];
-  uint32_t ck[kCandMax];
-  uint32_t ci[kCandMax];
-  uint32_t bm[kBitmapWords];
+  uint32_t h2[kLowBins];             // bits 19..10 of the cut-digit keys
+  uint32_t h3[kLowBins];             // bits 9..0 of the cut keys
+  uint32_t ck[kCandMax];             // candidate keys, ascending block order
+  uint32_t ci[kCandMax];             // their block ids
+  uint32_t coff[kMaxChunks + 1];     // chunk offsets into the candidate list
   uint32_t scan_sh[2 * (kFinThreads / kWave)];
   uint32_t out3[3];
-  uint32_t n_eq;
 };
-
-// Radix select over LDS keys[0..n): the want-th largest key among all n,
-// 8 bits per pass from bit 32 down.  out3 = {key T, keys == T to keep}.
-__device__ void lds_radix_select(const uint32_t* keys, int n, uint32_t want, FinSmem& sm) {
-  constexpr int NT = kFinThreads;
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t prefix = 0u, mask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < kBins * kCopies; i += NT) sm.hist16[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t u = keys[i];
-      if ((u & mask) == prefix) atomicAdd(&sm.hist16[((u >> shift) & 0xffu) * kCopies + (lane & (kCopies - 1))], 1u);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBins; i += NT) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int c = 0; c < kCopies; ++c) t += sm.hist16[i * kCopies + c];
-      sm.tot[i] = t;
-    }
-    __syncthreads();
-    find_digit_desc<NT>(sm.tot, kBins, want, sm.scan_sh, sm.out3);
-    prefix |= sm.out3[0] << shift;
-    mask |= 0xffu << shift;
-    want = sm.out3[1];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    sm.out3[0] = prefix;
-    sm.out3[1] = want;
-  }
-  __syncthreads();
-}
-
-// Kept ids, ascending, from the LDS bitmap.
-__device__ void write_from_bitmap(const uint32_t* bm, int nwords, int32_t* out, int k, uint32_t* scan_sh) {
-  constexpr int NT = kFinThreads;
-  const int per = (nwords + NT - 1) / NT;
-  const int w0 = threadIdx.x * per;
-  uint32_t cnt = 0;
-  for (int j = 0; j < per; ++j)
-    if (w0 + j < nwords) cnt += __popc(bm[w0 + j]);
-  uint32_t tot;
-  uint32_t pos = block_excl_scan<NT>(cnt, scan_sh, tot);
-  for (int j = 0; j < per; ++j) {
-    const int w = w0 + j;
-    if (w >= nwords) break;
-    uint32_t bits = bm[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      if (pos < (uint32_t)k) out[pos] = w * 32 + b;
-      ++pos;
-    }
-  }
-}
+static_assert(kDigits == kBins * kCopies, "the digit histogram reuses the radix histogram");
 
 // Exact path over the whole row: four 8-bit radix passes over all keys,
 // then an order-preserving compaction in index order.
@@ -234,7 +184,7 @@ __device__ void exact_row_select(const float* __restrict__ s, int64_t nb, int k,
 // ---------------------------------------------------------------- kernels
 
 // Standalone selection: write each row's sampled scores (one per 16-block
-// group) into the workspace and zero the candidate counter.
+// group) into the workspace.
 __global__ void __launch_bounds__(kChunkThreads)
 select_sample_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
                      int64_t nb_max, uint32_t* __restrict__ ws) {
@@ -242,9 +192,8 @@ select_sample_kernel(const float* __restrict__ scores, int64_t ld, const int64_t
   const int64_t grp = (int64_t)blockIdx.x * kChunkThreads + threadIdx.x;
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
   uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
-  if (blockIdx.x == 0 && threadIdx.x == 0) W[RowWs::kCount] = 0u;
   const int64_t b = grp * 16 + sel::sample_offset((uint32_t)grp);
-  if (b < nb) reinterpret_cast<float*>(W)[RowWs::kSamples + grp] = scores[(int64_t)m * ld + b];
+  if (b < nb) reinterpret_cast<float*>(W)[sel::sample_off(nb_max) + grp] = scores[(int64_t)m * ld + b];
 }
 
 __global__ void __launch_bounds__(kChunkThreads)
@@ -254,38 +203,56 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   __shared__ uint32_t scan_sh[2 * (kChunkThreads / kWave)];
   __shared__ uint32_t out3[3];
   const int m = blockIdx.y;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)c * kChunk;
   const float* __restrict__ s = scores + (int64_t)m * ld;
   uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
-  const float* __restrict__ smp = reinterpret_cast<const float*>(W + RowWs::kSamples);
-  // everything this pass reads is independent: issue it together
-  const int64_t lim = nb_max - base;
-  uint32_t key[kChunkPer];
-#pragma unroll
-  for (int e = 0; e < kChunkPer; ++e) {
-    const int64_t j = (int64_t)e * kChunkThreads + threadIdx.x;
-    key[e] = j < lim ? order_key(s[base + j]) : 0u;
-  }
+  const float* __restrict__ smp = reinterpret_cast<const float*>(W + sel::sample_off(nb_max));
   const int64_t n_grp = sel::sample_groups(nb_max);
-  constexpr int kSampPer = 16;  // samples per lane per round
-  for (int i = threadIdx.x; i < kDigits; i += kChunkThreads) h[i] = 0u;
+
+  // every load this pass needs is independent: issue them together
+  const int64_t i0 = base + (int64_t)tid * kChunkPer;  // this lane's 16 consecutive blocks
+  float4 sv[kChunkPer / 4];
+#pragma unroll
+  for (int q = 0; q < kChunkPer / 4; ++q) {
+    const int64_t j = i0 + 4 * q;  // rows are padded to a multiple of 4 floats
+    sv[q] = j < nb_max ? *reinterpret_cast<const float4*>(s + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  constexpr int kSampPer = kChunk / kChunkThreads;  // samples per lane per round
+  float smpv[kSampPer];
+#pragma unroll
+  for (int e = 0; e < kSampPer; ++e) {
+    const int64_t gi = (int64_t)e * kChunkThreads + tid;
+    smpv[e] = gi < n_grp ? smp[gi] : 0.f;
+  }
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
-  if (nb <= k || base >= nb) return;
+  for (int i = tid; i < kDigits; i += kChunkThreads) h[i] = 0u;
+  if (nb <= k) return;  // the finalize pass keeps every block
+  if (base >= nb) {
+    if (tid == 0) W[c] = 0u;
+    return;
+  }
   __syncthreads();
   // histogram of the row's samples (blocks < nb only)
-  for (int64_t g0 = 0; g0 < n_grp; g0 += (int64_t)kChunkThreads * kSampPer) {
-    float sv[kSampPer];
+#pragma unroll
+  for (int e = 0; e < kSampPer; ++e) {
+    const int64_t gi = (int64_t)e * kChunkThreads + tid;
+    if (gi < n_grp && gi * 16 + sel::sample_offset((uint32_t)gi) < nb)
+      atomicAdd(&h[order_key(smpv[e]) >> kDigitShift], 1u);
+  }
+  for (int64_t g0 = kChunk; g0 < n_grp; g0 += kChunk) {  // rows of more than 65,536 blocks
+    float v[kSampPer];
 #pragma unroll
     for (int e = 0; e < kSampPer; ++e) {
-      const int64_t gi = g0 + (int64_t)e * kChunkThreads + threadIdx.x;
-      sv[e] = gi < n_grp ? smp[gi] : 0.f;
+      const int64_t gi = g0 + (int64_t)e * kChunkThreads + tid;
+      v[e] = gi < n_grp ? smp[gi] : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < kSampPer; ++e) {
-      const int64_t gi = g0 + (int64_t)e * kChunkThreads + threadIdx.x;
+      const int64_t gi = g0 + (int64_t)e * kChunkThreads + tid;
       if (gi < n_grp && gi * 16 + sel::sample_offset((uint32_t)gi) < nb)
-        atomicAdd(&h[order_key(sv[e]) >> kDigitShift], 1u);
+        atomicAdd(&h[order_key(v[e]) >> kDigitShift], 1u);
     }
   }
   __syncthreads();
@@ -293,29 +260,32 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   find_digit_desc<kChunkThreads>(h, kDigits, sel::sample_target((uint32_t)k), scan_sh, out3);
   const uint32_t B = out3[2] ? 0u : out3[0];
 
-  uint32_t mine = 0;
+  uint32_t key[kChunkPer];
+  uint32_t flags = 0u;
 #pragma unroll
-  for (int e = 0; e < kChunkPer; ++e) {
-    const int64_t i = base + (int64_t)e * kChunkThreads + threadIdx.x;
-    mine += (i < nb && (key[e] >> kDigitShift) >= B) ? 1u : 0u;
+  for (int q = 0; q < kChunkPer / 4; ++q) {
+    key[4 * q + 0] = order_key(sv[q].x);
+    key[4 * q + 1] = order_key(sv[q].y);
+    key[4 * q + 2] = order_key(sv[q].z);
+    key[4 * q + 3] = order_key(sv[q].w);
   }
-  // one atomic per wave reserves its slots
-  const uint32_t incl = wave_incl_scan(mine, lane);
-  uint32_t wbase = 0;
-  if (lane == kWave - 1 && incl) wbase = atomicAdd(&W[RowWs::kCount], incl);
-  wbase = __shfl(wbase, kWave - 1, kWave);
-  uint32_t p = wbase + incl - mine;
+#pragma unroll
+  for (int e = 0; e < kChunkPer; ++e)
+    if (i0 + e < nb && (key[e] >> kDigitShift) >= B) flags |= 1u << e;
+  // the chunk's candidates in ascending block order, in the chunk's own slots
+  uint32_t total;
+  uint32_t pos = block_excl_scan<kChunkThreads>((uint32_t)__popc(flags), scan_sh, total);
+  uint32_t* K = W + sel::key_off(nb_max) + base;
+  uint32_t* I = W + sel::id_off(nb_max) + base;
 #pragma unroll
   for (int e = 0; e < kChunkPer; ++e) {
-    const int64_t i = base + (int64_t)e * kChunkThreads + threadIdx.x;
-    if (i < nb && (key[e] >> kDigitShift) >= B) {
-      if (p < (uint32_t)kCandMax) {
-        W[RowWs::kKeys + p] = key[e];
-        W[RowWs::kIds + p] = (uint32_t)i;
-      }
-      ++p;
+    if ((flags >> e) & 1u) {
+      K[pos] = key[e];
+      I[pos] = (uint32_t)(i0 + e);
+      ++pos;
     }
   }
+  if (tid == 0) W[c] = total;
 }
 
 __global__ void __launch_bounds__(kFinThreads)
@@ -324,63 +294,123 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
                        uint32_t* __restrict__ ws) {
   __shared__ FinSmem sm;
   const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const float* __restrict__ s = scores + (int64_t)m * ld;
   int32_t* __restrict__ out = sel + (int64_t)m * k;
-  uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
-  const uint32_t n_cand = W[RowWs::kCount];
+  const uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
+  // every chunk count of the row is written by the collect pass whenever the
+  // candidate path runs: load them before the row position arrives
+  const int64_t nch_max = sel::n_chunks(nb_max);
+  const uint32_t cnt_raw = (tid < kWave && tid < kMaxChunks && tid < nch_max) ? W[tid] : 0u;
   if (nb <= k) {
-    for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < nb ? i : -1;
-    if (threadIdx.x == 0) n_sel[m] = (int32_t)nb;
+    for (int i = tid; i < k; i += kFinThreads) out[i] = i < nb ? i : -1;
+    if (tid == 0) n_sel[m] = (int32_t)nb;
     return;
   }
-  if (threadIdx.x == 0) n_sel[m] = k;
-  const int nwords = (int)((nb + 31) / 32);
-  if (n_cand < (uint32_t)k || n_cand > (uint32_t)kCandMax || nwords > kBitmapWords) {
+  if (tid == 0) n_sel[m] = k;
+  const int nch = (int)((nb + kChunk - 1) / kChunk);
+  if (nch > kMaxChunks) {
     exact_row_select(s, nb, k, out, sm);
     return;
   }
-  for (uint32_t i = threadIdx.x; i < n_cand; i += kFinThreads) {
-    sm.ck[i] = W[RowWs::kKeys + i];
-    sm.ci[i] = W[RowWs::kIds + i];
+  for (int i = tid; i < kDigits; i += kFinThreads) sm.hist16[i] = 0u;
+  for (int i = tid; i < kLowBins; i += kFinThreads) {
+    sm.h2[i] = 0u;
+    sm.h3[i] = 0u;
   }
-  for (int i = threadIdx.x; i < nwords; i += kFinThreads) sm.bm[i] = 0u;
-  if (threadIdx.x == 0) sm.n_eq = 0u;
+  if (tid < kWave) {  // chunk offsets (nch <= 64: one wave)
+    const uint32_t incl = wave_incl_scan(tid < nch ? cnt_raw : 0u, lane);
+    sm.coff[lane + 1] = incl;
+    if (lane == 0) sm.coff[0] = 0u;
+  }
   __syncthreads();
+  const uint32_t n_cand = sm.coff[nch];
+  if (n_cand < (uint32_t)k || n_cand > (uint32_t)kCandMax) {
+    exact_row_select(s, nb, k, out, sm);
+    return;
+  }
 
-  lds_radix_select(sm.ck, (int)n_cand, (uint32_t)k, sm);
-  const uint32_t T = sm.out3[0];
-  const uint32_t need_t = sm.out3[1];
-  uint32_t* eqk = sm.hist16;  // free after the radix passes
-  for (uint32_t i = threadIdx.x; i < n_cand; i += kFinThreads) {
-    const uint32_t kk = sm.ck[i];
-    const uint32_t id = sm.ci[i];
-    if ((int64_t)id >= nb) continue;  // never past the row (list written by this call's collect)
-    if (kk > T) atomicOr(&sm.bm[id >> 5], 1u << (id & 31));
-    else if (kk == T) eqk[atomicAdd(&sm.n_eq, 1u)] = ~id;
-  }
-  __syncthreads();
-  const uint32_t n_eq = sm.n_eq;
-  if (n_eq <= need_t) {
-    for (uint32_t i = threadIdx.x; i < n_eq; i += kFinThreads) {
-      const uint32_t id = ~eqk[i];
-      atomicOr(&sm.bm[id >> 5], 1u << (id & 31));
+  // gather the candidates (chunk order = ascending block order)
+  const uint32_t* K = W + sel::key_off(nb_max);
+  const uint32_t* I = W + sel::id_off(nb_max);
+  uint32_t kk[kFinPer], ii[kFinPer];
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+    // chunk of candidate i: the last c with coff[c] <= i
+    int lo = 0, hi = nch;  // coff[lo] <= i < coff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.coff[mid] <= i) lo = mid; else hi = mid;
     }
-  } else {
-    // the need_t lowest ids among equal keys = the largest complemented ids
-    for (uint32_t i = threadIdx.x; i < n_eq; i += kFinThreads) sm.ck[i] = eqk[i];
-    __syncthreads();
-    lds_radix_select(sm.ck, (int)n_eq, need_t, sm);
-    const uint32_t t_id = sm.out3[0];
-    for (uint32_t i = threadIdx.x; i < n_eq; i += kFinThreads) {
-      if (sm.ck[i] >= t_id) {
-        const uint32_t id = ~sm.ck[i];
-        atomicOr(&sm.bm[id >> 5], 1u << (id & 31));
-      }
+    const bool live = i < n_cand;
+    const int64_t slot = live ? (int64_t)lo * kChunk + (i - sm.coff[lo]) : 0;
+    kk[e] = live ? K[slot] : 0u;
+    ii[e] = live ? I[slot] : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+    if (i < n_cand) {
+      sm.ck[i] = kk[e];
+      sm.ci[i] = ii[e];
+      atomicAdd(&sm.hist16[kk[e] >> kDigitShift], 1u);
     }
   }
   __syncthreads();
-  write_from_bitmap(sm.bm, nwords, out, k, sm.scan_sh);
+  // The k-th largest candidate key TK, 12 + 10 + 10 bits at a time; each
+  // level histograms only the candidates that share the bits found so far.
+  find_digit_desc<kFinThreads>(sm.hist16, kDigits, (uint32_t)k, sm.scan_sh, sm.out3);
+  const uint32_t t1 = sm.out3[0];
+  uint32_t need = sm.out3[1];
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+    if (i < n_cand && (kk[e] >> kDigitShift) == t1) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
+  }
+  __syncthreads();
+  find_digit_desc<kFinThreads>(sm.h2, kLowBins, need, sm.scan_sh, sm.out3);
+  const uint32_t t12 = (t1 << 10) | sm.out3[0];
+  need = sm.out3[1];
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+    if (i < n_cand && (kk[e] >> 10) == t12) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
+  }
+  __syncthreads();
+  find_digit_desc<kFinThreads>(sm.h3, kLowBins, need, sm.scan_sh, sm.out3);
+  const uint32_t TK = (t12 << 10) | sm.out3[0];
+  need = sm.out3[1];  // keys equal to TK kept: the first `need` in block order
+
+  // keep flags over contiguous ranges of the (ascending) candidate list
+  const uint32_t r0 = (uint32_t)tid * kFinPer;
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) n_eq += (r0 + e < n_cand && sm.ck[r0 + e] == TK) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t eq_rank = block_excl_scan<kFinThreads>(n_eq, sm.scan_sh, tot);
+  uint32_t keep = 0u, n_keep = 0u;
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = r0 + e;
+    if (i >= n_cand) break;
+    const uint32_t key = sm.ck[i];
+    bool kp = key > TK;
+    if (key == TK) kp = eq_rank++ < need;
+    keep |= kp ? (1u << e) : 0u;
+    n_keep += kp ? 1u : 0u;
+  }
+  // kept candidates are already in ascending block order: compact them
+  uint32_t pos = block_excl_scan<kFinThreads>(n_keep, sm.scan_sh, tot);
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    if ((keep >> e) & 1u) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)sm.ci[r0 + e];
+      ++pos;
+    }
+  }
 }
 
 hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_t* row_pos, int64_t nb_max,

@@ -63,6 +63,8 @@ def test_append_pool_validation(args, code, word):
     ((FAKE, 1, -2, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "M ="),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 17, FAKE, 17, None, 0, None), ERR_ARG, "nb_max"),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 8, None, 0, None), ERR_ARG, "ld"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 18, None, 0, None), ERR_ARG, "aligned"),
+    ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE + 4, 16, None, 0, None), ERR_ARG, "aligned"),
     ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "null"),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, FAKE, 100, None), ERR_WS, "workspace"),
     ((None, 1, 0, None, None, None, 1, 64, 16, None, 16, None, 0, None), Q.QSA_OK, ""),
@@ -76,6 +78,8 @@ def test_score_validation(args, code, word):
     ((FAKE, 16, 1, FAKE, 16, 0, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "k_blocks"),
     ((FAKE, 16, 1, FAKE, 16, 2000, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "k_blocks"),
     ((FAKE, 8, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "ld"),
+    ((FAKE, 18, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "aligned"),
+    ((FAKE + 4, 16, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_ARG, "aligned"),
     ((FAKE, 16, 1, FAKE, 16, 4, FAKE, FAKE, None, 0, 0, None), ERR_WS, "workspace"),
     ((FAKE, 16, 1, FAKE, 16, 4, FAKE, FAKE, FAKE, 100, 0, None), ERR_WS, "workspace"),
     ((FAKE, 16, 1, FAKE, 16, 4, None, FAKE, FAKE, 1 << 30, 0, None), ERR_ARG, "null"),

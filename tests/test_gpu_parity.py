@@ -223,7 +223,7 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     idx_q = to_dev(np.concatenate([h["idx_q"] for h in host]), "bf16")
     q = to_dev(np.concatenate([h["q"] for h in host]), "bf16")
     nb_max = max(h["n"] for h in host) // 4
-    scores = torch.zeros((m, nb_max + 4), dtype=torch.float32, device=DEV)
+    scores = torch.zeros((m, -(-(nb_max + 4) // 4) * 4), dtype=torch.float32, device=DEV)
     Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
     sel = torch.empty((m, k), dtype=torch.int32, device=DEV)
     n_sel = torch.empty((m,), dtype=torch.int32, device=DEV)
@@ -286,7 +286,7 @@ def test_batched_segmented_full_size(Q):
     q = to_dev(np.concatenate([h["q"] for h in data]), "bf16")
     nb_max = max(sp.n_ctx for sp in specs) // 4
     k = 512
-    scores = torch.zeros((n_seq, nb_max), dtype=torch.float32, device=DEV)
+    scores = torch.zeros((n_seq, -(-nb_max // 4) * 4), dtype=torch.float32, device=DEV)
     Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
     sel = torch.empty((n_seq, k), dtype=torch.int32, device=DEV)
     n_sel = torch.empty((n_seq,), dtype=torch.int32, device=DEV)
