@@ -440,6 +440,330 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
   }
 }
 
+// bf16 K/V: matrix-core kernel.  Grid and split plan as above; inside a
+// workgroup each wave owns one 16-token slice of every 64-token tile and
+// keeps its own online softmax state, so the tile loop has no workgroup
+// barrier:
+//   1. lanes resolve the slice's 16 tokens (lane % 16) to K and V rows; every
+//      load of the slice is issued before any is used;
+//   2. QK on v_mfma_f32_16x16x32_bf16: A = the group's 12 query heads (rows
+//      12..15 zero) held in VGPRs for the whole kernel, B = the 16 tokens' K
+//      rows loaded straight into the operand layout (lane: token lane % 16,
+//      8 consecutive dims per k-step);
+//   3. online softmax per head over the 16 lanes that hold a head's tokens
+//      (base-2 exponentials, bf16-rounded probabilities packed in token
+//      pairs into a wave-private LDS region);
+//   4. PV with packed bf16 dot2 from the wave's V rows, pair-interleaved in
+//      LDS: lane = D/64 dims of all 12 heads, float32 accumulation.
+// At the end the four wave partials are merged by log-sum-exp in LDS.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ const unsigned char* shfl_ptr(const unsigned char* p, int src) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
+  return reinterpret_cast<const unsigned char*>(((uint64_t)hi << 32) | lo);
+}
+
+// max / sum over the 16 lanes of a row (lanes 16r .. 16r+15)
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+template <int D>
+struct MfmaSmem {
+  static constexpr int kPairs = 8;  // token pairs of a 16-token slice
+  struct Wave {
+    uint32_t v[kPairs * D];         // [pair][dim]: (V[2 pair][dim], V[2 pair + 1][dim]) as bf16 x 2
+    uint32_t p[kPairs * kGroup];    // [pair][head]: bf16 probabilities of the pair
+  };
+  struct Merge {
+    float acc[4][kGroup * D];
+    float m[4][kGroup];
+    float l[4][kGroup];
+  };
+  union {
+    Wave w[4];
+    Merge mg;
+  };
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2,
+                 const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
+                 KvArgs kv, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
+                 int k_blocks, int tiles_per_split, int splits,
+                 uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                 float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  constexpr int KS = D / 32;               // QK k-steps
+  constexpr int DPL = D / kWave;           // PV dims per lane
+  constexpr int VCH = D * 2 / 16;          // 16-byte chunks per V row
+  constexpr int VIT = 8 * VCH / kWave;     // (token pair, chunk) V items per lane
+  constexpr int kRowBytes = D * 2;
+  static_assert(kWave % VCH == 0 || VCH % kWave == 0, "V item mapping");
+  __shared__ __align__(16) MfmaSmem<D> sm;
+  __shared__ SegDesc segs[kMaxSegments];
+  __shared__ int nseg_sh;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int m = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = uniform(tid / kWave);
+  const int n16 = lane & 15;   // token of the slice (QK operand and softmax row position)
+  const int g4 = lane >> 4;    // k-slice of the operands / head quad of the scores
+  const int tok_begin = split * tiles_per_split * kTileTok;
+  const int32_t* __restrict__ srow = sel + (int64_t)m * k_blocks;
+
+  // ---- independent loads, issued together
+  const int64_t p = row_pos[m];
+  const int ns_raw = n_sel[m];
+  const int sq_raw = row_seq ? row_seq[m] : 0;
+  int32_t bid;
+  {
+    const int j = tok_begin + wave * 16 + n16;
+    bid = (j >> 2) < k_blocks ? srow[j >> 2] : -1;
+  }
+  // query operand: head n16 (rows 12..15 are zero), dims 32 s + 8 g4 .. + 7
+  const unsigned char* qh = reinterpret_cast<const unsigned char*>(
+      q + ((int64_t)m * hq + (int64_t)g * kGroup + (n16 < kGroup ? n16 : 0)) * D);
+  uint4 qraw[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qraw[s] = ldg16(qh + (32 * s + 8 * g4) * 2);
+  int si_lo = 0, nseg_all = 0;
+  if (kv.n_seq == 1) {
+    nseg_all = kv.n_seg_total < kMaxSegments ? kv.n_seg_total : kMaxSegments;
+  } else {
+    const bool seq_ok = sq_raw >= 0 && sq_raw < kv.n_seq;
+    const int sq = seq_ok ? sq_raw : 0;
+    int s_begin = kv.seq_seg_begin[sq], s_end = kv.seq_seg_begin[sq + 1];
+    s_begin = s_begin < 0 ? 0 : s_begin;
+    s_end = s_end > kv.n_seg_total ? kv.n_seg_total : s_end;
+    si_lo = s_begin;
+    nseg_all = (seq_ok && s_end > s_begin) ? min(s_end - s_begin, kMaxSegments) : 0;
+  }
+  SegDesc mine{};
+  if (tid < nseg_all) {
+    const int si = si_lo + tid;
+    const int64_t st = kv.seg_start[si];
+    mine.lo = st;
+    mine.hi = st + kv.seg_len[si];
+    mine.cap = kv.seg_cap[si];
+    mine.k = static_cast<const unsigned char*>(kv.k_seg[si]);
+    mine.v = static_cast<const unsigned char*>(kv.v_seg[si]);
+  }
+  if (tid < nseg_all) segs[tid] = mine;
+  if (tid == 0) nseg_sh = nseg_all;
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint4 x = n16 < kGroup ? qraw[s] : make_uint4(0, 0, 0, 0);
+    qa[s] = __builtin_bit_cast(bf16x8_t, x);
+  }
+
+  const int64_t n_vis = p + 1 > 0 ? p + 1 : 0;
+  const int64_t nb = n_vis / kBlockTokens;
+  const int tail = (int)(n_vis - nb * kBlockTokens);
+  int ns = ns_raw < 0 ? 0 : ns_raw;
+  ns = ns > k_blocks ? k_blocks : ns;
+  ns = (int64_t)ns > nb ? (int)nb : ns;
+  const int total = ns * kBlockTokens + tail;
+  __syncthreads();
+  const int nseg = nseg_sh;
+
+  float m_run[4], l_run[4];  // heads 4 g4 + v (identical over the 16 lanes of a row)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m_run[v] = -INFINITY;
+    l_run[v] = 0.f;
+  }
+  float acc[kGroup][DPL];
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[h][d] = 0.f;
+  uint32_t* vl = sm.w[wave].v;
+  uint32_t* pl = sm.w[wave].p;
+
+  for (int t = 0; t < tiles_per_split; ++t) {
+    const int j0 = tok_begin + t * kTileTok + wave * 16;
+    if (j0 >= total) break;  // wave-uniform: the loop has no workgroup barrier
+    // 1. token of this lane's row position
+    const int j = j0 + n16;
+    int64_t tok = -1;
+    if (j < total) {
+      if (j < ns * kBlockTokens) {
+        if (bid >= 0 && bid < nb) tok = (int64_t)bid * kBlockTokens + (j & 3);
+      } else {
+        tok = nb * kBlockTokens + (j - ns * kBlockTokens);
+      }
+    }
+    const unsigned char* kr = qh;  // any readable address; masked below
+    const unsigned char* vr = qh;
+    int ok = 0;
+    for (int si = 0; si < nseg; ++si) {
+      const SegDesc sd = segs[si];
+      const int64_t rel = tok - sd.lo;
+      const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !ok;
+      const int64_t off = ((int64_t)g * sd.cap + rel) * kRowBytes;
+      kr = hit ? sd.k + off : kr;
+      vr = hit ? sd.v + off : vr;
+      ok |= hit ? 1 : 0;
+    }
+    // K operand rows: all k-steps
+    uint4 kb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kb[s] = ldg16(kr + (32 * s + 8 * g4) * 2);
+    // V items: (pair pp, chunk c) of the slice's token pairs
+    uint4 va[VIT], vb[VIT];
+    int vok[VIT];
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+      const int item = lane + kWave * u;
+      const int pp = item / VCH;
+      const int c = item % VCH;
+      const unsigned char* r0 = shfl_ptr(vr, 2 * pp);
+      const unsigned char* r1 = shfl_ptr(vr, 2 * pp + 1);
+      vok[u] = __shfl(ok, 2 * pp, kWave) | (__shfl(ok, 2 * pp + 1, kWave) << 1);
+      va[u] = ldg16(r0 + c * 16);
+      vb[u] = ldg16(r1 + c * 16);
+    }
+    // next slice's block id, in flight during this slice's compute
+    if (t + 1 < tiles_per_split) {
+      const int jn = j + kTileTok;
+      bid = (jn >> 2) < k_blocks ? srow[jn >> 2] : -1;
+    }
+
+    // 2. QK: sacc[v] = q[head 4 g4 + v] . K[token n16]
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, x), sacc, 0, 0, 0);
+    }
+
+    // 3. online softmax per head over the row's 16 tokens
+    float alpha[4];
+    uint32_t pw[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float s2 = ok ? sacc[v] * scale_log2 : -INFINITY;
+      const float m_new = fmaxf(m_run[v], row16_max(s2));
+      alpha[v] = (m_run[v] == m_new) ? 1.f : exp2f(m_run[v] - m_new);
+      const float pv = (s2 == -INFINITY) ? 0.f : exp2f(s2 - m_new);
+      const uint32_t pb = f32_to_bf16_bits(pv);  // PV consumes bf16: normalise by the same values
+      l_run[v] = l_run[v] * alpha[v] + row16_sum(__uint_as_float(pb << 16));
+      m_run[v] = m_new;
+      pw[v] = pb | ((uint32_t)__shfl_xor((int)pb, 1, kWave) << 16);
+    }
+    if ((n16 & 1) == 0 && g4 < 3)
+      *reinterpret_cast<uint4*>(pl + (n16 >> 1) * kGroup + 4 * g4) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    // V rows, pair-interleaved
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+      const int item = lane + kWave * u;
+      const int pp = item / VCH;
+      const int c = item % VCH;
+      const uint4 a = (vok[u] & 1) ? va[u] : make_uint4(0, 0, 0, 0);
+      const uint4 b = (vok[u] & 2) ? vb[u] : make_uint4(0, 0, 0, 0);
+      uint4 lo, hi;
+      interleave(a, b, lo, hi);
+      uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 8);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+    // rescale by every head's alpha (head h sits in row h / 4, slot h % 4)
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[h][d] *= a;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // 4. PV over the slice's 8 token pairs
+#pragma unroll 2
+    for (int pp = 0; pp < 8; ++pp) {
+      uint32_t w[DPL];
+      if constexpr (DPL == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(vl + pp * D + DPL * lane);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(vl + pp * D + DPL * lane);
+        w[0] = x.x; w[1] = x.y;
+      }
+      const uint4 p0 = *reinterpret_cast<const uint4*>(pl + pp * kGroup);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(pl + pp * kGroup + 4);
+      const uint4 p2 = *reinterpret_cast<const uint4*>(pl + pp * kGroup + 8);
+      const uint32_t ph[kGroup] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w, p2.x, p2.y, p2.z, p2.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[h][d] = dot2_bf16(ph[h], w[d], acc[h][d]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the four wave partials (log2 domain)
+  __syncthreads();  // every wave is done with its V / P region
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) {
+    if constexpr (DPL == 4) {
+      *reinterpret_cast<float4*>(&sm.mg.acc[wave][h * D + DPL * lane]) =
+          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    } else {
+      *reinterpret_cast<float2*>(&sm.mg.acc[wave][h * D + DPL * lane]) = make_float2(acc[h][0], acc[h][1]);
+    }
+  }
+  if (n16 == 0 && g4 < 3) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sm.mg.m[wave][4 * g4 + v] = m_run[v];
+      sm.mg.l[wave][4 * g4 + v] = l_run[v];
+    }
+  }
+  __syncthreads();
+  constexpr int kOut = kGroup * D / kThreads;  // outputs per thread
+#pragma unroll
+  for (int e = 0; e < kOut; ++e) {
+    const int o = tid + kThreads * e;
+    const int h = o / D;
+    const int d = o % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.mg.m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = sm.mg.m[w][h];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
+        L += sm.mg.l[w][h] * f;
+        O += sm.mg.acc[w][h * D + d] * f;
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    const int64_t head = (int64_t)m * hq + (int64_t)g * kGroup + h;
+    if (splits == 1) {
+      out[head * D + d] = (uint16_t)f32_to_bf16_bits(O * inv);
+      if (d == 0) lse_out[head] = lse;
+    } else {
+      ws_o[(head * splits + split) * D + d] = O * inv;
+      if (d == 0) ws_lse[head * splits + split] = lse;
+    }
+  }
+}
+
 // Merge split partials by log-sum-exp.  One workgroup per (row, head).
 template <class E, int D>
 __global__ void __launch_bounds__(D)
@@ -505,10 +829,17 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
   float* ws_o = static_cast<float*>(ws);
   float* ws_lse = ws_o ? ws_o + (size_t)M * hq * plan.splits * D : nullptr;
   dim3 grid(plan.splits, hkv, M), block(kThreads);
-  hipLaunchKernelGGL((attn_decode_kernel<E, D>), grid, block, 0, stream,
-                     static_cast<const typename E::T*>(q), M, hq, scale * kLog2e, row_pos, row_seq,
-                     kv, sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,
-                     static_cast<typename E::T*>(out), lse, ws_o, ws_lse);
+  if constexpr (E::kBytes == 2) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(q), M, hq, scale * kLog2e, row_pos, row_seq,
+                       kv, sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,
+                       static_cast<uint16_t*>(out), lse, ws_o, ws_lse);
+  } else {
+    hipLaunchKernelGGL((attn_decode_kernel<E, D>), grid, block, 0, stream,
+                       static_cast<const typename E::T*>(q), M, hq, scale * kLog2e, row_pos, row_seq,
+                       kv, sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,
+                       static_cast<typename E::T*>(out), lse, ws_o, ws_lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL((attn_combine_kernel<E, D>), dim3((unsigned)M * hq), dim3(D),

@@ -44,15 +44,22 @@ constexpr int kBlocksPerWave = kGroupBlocks * kGroupsPerWave;
 constexpr int kBlocksPerWG = kBlocksPerWave * kWavesPerWG;
 constexpr float kScoreScale = 0.08838834764831845f;  // 1/sqrt(128)
 
+// Index-query elements as loaded (4 per lane per chunk) and as MFMA operands.
+template <class EQ> struct QRaw;
+template <> struct QRaw<F32> { using T = uint4; };
+template <> struct QRaw<BF16> { using T = uint2; };
 template <class EQ>
-__device__ __forceinline__ float4 load_q4(const typename EQ::T* __restrict__ q);
+__device__ __forceinline__ typename QRaw<EQ>::T load_q_raw(const typename EQ::T* __restrict__ q) {
+  return *reinterpret_cast<const typename QRaw<EQ>::T*>(q);
+}
+template <class EQ>
+__device__ __forceinline__ float4 q_to_f4(typename QRaw<EQ>::T x);
 template <>
-__device__ __forceinline__ float4 load_q4<F32>(const float* __restrict__ q) {
-  return *reinterpret_cast<const float4*>(q);
+__device__ __forceinline__ float4 q_to_f4<F32>(uint4 x) {
+  return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
 }
 template <>
-__device__ __forceinline__ float4 load_q4<BF16>(const uint16_t* __restrict__ q) {
-  const uint2 x = *reinterpret_cast<const uint2*>(q);
+__device__ __forceinline__ float4 q_to_f4<BF16>(uint2 x) {
   return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
                      __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
 }
@@ -73,54 +80,66 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   const int m0 = blockIdx.y * RPG;
   const int rows = min(RPG, M - m0);
 
-  // The pooled loads depend only on nb_max (the host bound): they are issued
-  // before the row positions arrive.
+  // Everything is loaded up front.  The row positions (wave-uniform) and the
+  // index-query operand are small and cached; issued before the pooled
+  // stream, their waits leave the pooled loads in flight.  The pooled loads
+  // depend only on nb_max (the host bound), not on the row positions.
   const int64_t wave_b0 = (int64_t)blockIdx.x * kBlocksPerWG + wave * kBlocksPerWave;
   if (wave_b0 >= nb_max) return;
+  const int i16 = lane & 15;   // A row (block in group) / B column
+  const int kq = lane >> 4;    // k slot 0..3
+  int64_t pos_r[RPG];
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) pos_r[r] = row_pos[m0 + (r < rows ? r : 0)];
+  // index-query operand: column j = row*4 + head of set st, dims 16c + 4*kq + t
+  typename QRaw<EQ>::T qraw[NSET][kChunks];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    const int h = i16 & 3;
+    const typename EQ::T* qsrc = idx_q + ((int64_t)(m0 + (r < rows ? r : 0)) * kIndexHeads + h) * kIndexDim + 4 * kq;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) qraw[st][c] = load_q_raw<EQ>(qsrc + 16 * c);
+  }
   const int s = row_seq ? row_seq[m0] : 0;
   const bool seq_ok = s >= 0 && s < n_seq;
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
   const float* __restrict__ P = pooled + (int64_t)(seq_ok ? s : 0) * (capacity / kBlockTokens) * kIndexDim;
 
-  const int i16 = lane & 15;   // A row (block in group) / B column
-  const int kq = lane >> 4;    // k slot 0..3
-
-  // Pooled loads: all groups, all chunks, issued up front.
+  // Pooled loads: all groups, all chunks, unconditional (blocks past nb_max
+  // re-read the last block; their scores are never stored).
   float4 a[kGroupsPerWave][kChunks];
 #pragma unroll
   for (int g = 0; g < kGroupsPerWave; ++g) {
     const int64_t b = wave_b0 + g * kGroupBlocks + i16;
-    const float* src = P + b * kIndexDim + 4 * kq;
+    const float* src = P + (b < nb_max ? b : nb_max - 1) * kIndexDim + 4 * kq;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-      a[g][c] = b < nb_max ? *reinterpret_cast<const float4*>(src + 16 * c) : zero4();
-  }
-  // Index-query operand: column j = row*4 + head of set st, dims 16c + 4*kq + t.
-  float4 bq[NSET][kChunks];
-#pragma unroll
-  for (int st = 0; st < NSET; ++st) {
-    const int r = st * 4 + (i16 >> 2);
-    const int h = i16 & 3;
-    const bool live = r < rows;
-    const typename EQ::T* qsrc = idx_q + ((int64_t)(m0 + (live ? r : 0)) * kIndexHeads + h) * kIndexDim + 4 * kq;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? load_q4<EQ>(qsrc + 16 * c) : zero4();
+    for (int c = 0; c < kChunks; ++c) a[g][c] = *reinterpret_cast<const float4*>(src + 16 * c);
   }
 
+  int64_t nb_r[RPG];
   int64_t nb_hi = 0;
-  for (int r = 0; r < rows; ++r) {
-    const int64_t nb = clamp_nb(row_pos[m0 + r], nb_max);
-    nb_hi = nb > nb_hi ? nb : nb_hi;
+#pragma unroll
+  for (int r = 0; r < RPG; ++r) {
+    nb_r[r] = r < rows ? clamp_nb(pos_r[r], nb_max) : 0;
+    nb_hi = nb_r[r] > nb_hi ? nb_r[r] : nb_hi;
   }
   const bool active = wave_b0 < nb_hi && seq_ok;
   if (!active) return;
 
+  float4 bq[NSET][kChunks];
   int64_t nb_row[NSET];
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {
     const int r = st * 4 + (i16 >> 2);
-    nb_row[st] = r < rows ? clamp_nb(row_pos[m0 + r], nb_max) : 0;
+    const bool live = r < rows;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(qraw[st][c]) : zero4();
+    int64_t n = 0;
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) n = (r == rr) ? nb_r[rr] : n;  // no dynamic register indexing
+    nb_row[st] = n;
   }
 
   float sv[kGroupsPerWave][NSET][4];
