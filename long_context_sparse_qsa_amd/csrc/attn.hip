@@ -489,6 +489,8 @@ struct MfmaSmem {
     float acc[4][kGroup * D];
     float m[4][kGroup];
     float l[4][kGroup];
+    float wt[kGroup][4];   // weight of each wave's partial in the merged output
+    float lse[kGroup];
   };
   union {
     Wave w[4];
@@ -732,92 +734,105 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     }
   }
   __syncthreads();
+  if (tid < kGroup) {  // per-head merge weights, once
+    const int h = tid;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.mg.m[w][h]);
+    float f[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm.mg.m[w][h];
+      f[w] = (mx == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - mx);
+      L += sm.mg.l[w][h] * f[w];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sm.mg.wt[h][w] = f[w] * inv;
+    sm.mg.lse[h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
   constexpr int kOut = kGroup * D / kThreads;  // outputs per thread
 #pragma unroll
   for (int e = 0; e < kOut; ++e) {
     const int o = tid + kThreads * e;
     const int h = o / D;
     const int d = o % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.mg.m[w][h]);
-    float L = 0.f, O = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = sm.mg.m[w][h];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
-        L += sm.mg.l[w][h] * f;
-        O += sm.mg.acc[w][h * D + d] * f;
-      }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float lse = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    const float4 wt = *reinterpret_cast<const float4*>(sm.mg.wt[h]);
+    const float O = sm.mg.acc[0][o] * wt.x + sm.mg.acc[1][o] * wt.y + sm.mg.acc[2][o] * wt.z +
+                    sm.mg.acc[3][o] * wt.w;
     const int64_t head = (int64_t)m * hq + (int64_t)g * kGroup + h;
     if (splits == 1) {
-      out[head * D + d] = (uint16_t)f32_to_bf16_bits(O * inv);
-      if (d == 0) lse_out[head] = lse;
+      out[head * D + d] = (uint16_t)f32_to_bf16_bits(O);
+      if (d == 0) lse_out[head] = sm.mg.lse[h];
     } else {
-      ws_o[(head * splits + split) * D + d] = O * inv;
-      if (d == 0) ws_lse[head * splits + split] = lse;
+      ws_o[(head * splits + split) * D + d] = O;
+      if (d == 0) ws_lse[head * splits + split] = sm.mg.lse[h];
     }
   }
 }
 
-// Merge split partials by log-sum-exp.  One workgroup per (row, head).
+// Merge split partials by log-sum-exp.  One workgroup per (row, head), one
+// thread per output dimension.  Each thread's partial outputs (up to
+// kRegSplits) and its own split's lse are loaded at once; thread i computes
+// split i's weight once and the weights are shared through LDS, so the merge
+// takes one memory round trip.
+constexpr int kRegSplits = 40;
+
 template <class E, int D>
 __global__ void __launch_bounds__(D)
 attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int splits,
                     typename E::T* __restrict__ out, float* __restrict__ lse_out) {
-  extern __shared__ float w_lds[];  // [splits]
+  static_assert(D >= kRegSplits, "one thread per register-held split");
+  __shared__ float w_sh[kRegSplits];
   __shared__ float red[D / kWave];
-  __shared__ float mx_sh, tot_sh;
   const int64_t head = blockIdx.x;
   const int tid = threadIdx.x;
-  const float* L = ws_lse + head * splits;
-  float mx = -INFINITY;
-  for (int i = tid; i < splits; i += D) {
-    const float v = L[i];
-    w_lds[i] = v;
-    mx = fmaxf(mx, v);
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const float* __restrict__ L = ws_lse + head * splits;
+  const float* __restrict__ O = ws_o + head * splits * D + tid;
+  if (splits > kRegSplits) {  // long budgets: plain loops
+    float mx = -INFINITY, tot = 0.f, o = 0.f;
+    for (int i = 0; i < splits; ++i) mx = fmaxf(mx, L[i]);
+    if (mx != -INFINITY) {
+      for (int i = 0; i < splits; ++i) {
+        const float li = L[i];
+        const float w = li == -INFINITY ? 0.f : expf(li - mx);
+        tot += w;
+        o = fmaf(w, O[(int64_t)i * D], o);
+      }
+    }
+    const bool empty = (mx == -INFINITY) || tot == 0.f;
+    out[head * D + tid] = E::from_f(empty ? 0.f : o / tot);
+    if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot);
+    return;
   }
-  mx = wave_max(mx);
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
+  float ov[kRegSplits];
+#pragma unroll
+  for (int i = 0; i < kRegSplits; ++i) ov[i] = O[(int64_t)(i < splits ? i : splits - 1) * D];  // masked by w = 0
+  const float l_own = tid < splits ? L[tid] : -INFINITY;
+  float mx = wave_max(l_own);
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
-  if (tid == 0) {
-    float a = red[0];
-    for (int i = 1; i < D / kWave; ++i) a = fmaxf(a, red[i]);
-    mx_sh = a;
-  }
-  __syncthreads();
-  mx = mx_sh;
+#pragma unroll
+  for (int w = 0; w < D / kWave; ++w) mx = fmaxf(mx, red[w]);
   const bool empty = (mx == -INFINITY);
-  float tot = 0.f;
-  for (int i = tid; i < splits; i += D) {
-    const float w = (empty || w_lds[i] == -INFINITY) ? 0.f : expf(w_lds[i] - mx);
-    w_lds[i] = w;
-    tot += w;
-  }
-  tot = wave_sum(tot);
+  const float w_own = (empty || l_own == -INFINITY) ? 0.f : expf(l_own - mx);
+  if (tid < kRegSplits) w_sh[tid] = w_own;
+  float tot = wave_sum(w_own);
   __syncthreads();
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = tot;
+  if (lane == 0) red[wave] = tot;
   __syncthreads();
-  if (tid == 0) {
-    float a = 0.f;
-    for (int i = 0; i < D / kWave; ++i) a += red[i];
-    tot_sh = a;
-  }
-  __syncthreads();
-  tot = tot_sh;
-  // every partial is finite (an empty split stores zeros), so the loads are
-  // unconditional and independent
+  tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / kWave; ++w) tot += red[w];
   float o = 0.f;
-  const float* O = ws_o + head * splits * D + tid;
-#pragma unroll 8
-  for (int i = 0; i < splits; ++i) o = fmaf(w_lds[i], O[(int64_t)i * D], o);
-  o = (empty || tot == 0.f) ? 0.f : o / tot;
-  out[head * D + tid] = E::from_f(o);
-  if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot);
+#pragma unroll
+  for (int i = 0; i < kRegSplits; ++i) o = fmaf(w_sh[i], ov[i], o);  // every partial is finite
+  const bool none = empty || tot == 0.f;
+  out[head * D + tid] = E::from_f(none ? 0.f : o / tot);
+  if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot);
 }
 
 template <class E, int D>
@@ -842,8 +857,8 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<E, D>), dim3((unsigned)M * hq), dim3(D),
-                     plan.splits * sizeof(float), stream, ws_o, ws_lse, plan.splits,
+  hipLaunchKernelGGL((attn_combine_kernel<E, D>), dim3((unsigned)M * hq), dim3(D), 0, stream, ws_o, ws_lse,
+                     plan.splits,
                      static_cast<typename E::T*>(out), lse);
   return hipGetLastError();
 }

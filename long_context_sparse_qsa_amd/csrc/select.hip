@@ -76,34 +76,48 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   return before + incl - v;
 }
 
-// Counts cnt[0..nbins) in LDS (digit order ascending): find the digit where
+// Counts cnt[0..NBINS) in LDS (digit order ascending): find the digit where
 // the count from the top reaches `want`.  out3 = {digit, want - count above
-// the digit, 0}; out3[2] = 1 when the total stays below `want`.
-template <int NT>
-__device__ void find_digit_desc(const uint32_t* cnt, int nbins, uint32_t want, uint32_t* scan_sh,
-                                uint32_t* out3) {
-  const int per = (nbins + NT - 1) / NT;
-  const int hi = nbins - 1 - (int)threadIdx.x * per;
+// the digit, 0}; out3[2] = 1 when the total stays below `want`.  Thread t
+// owns a contiguous run of bins (thread 0 the top ones); the lanes that share
+// a bank read their runs in rotated order, so the sums are conflict-free.
+template <int NT, int NBINS>
+__device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* scan_sh, uint32_t* out3) {
+  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
+  static_assert(NBINS < NT || NBINS % NT == 0, "bins split evenly over threads");
+  static_assert((PER & (PER - 1)) == 0 && PER <= kWave, "power-of-two run per thread");
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const bool owns = NBINS >= NT || t < NBINS;
+  const int lo = NBINS - (t + 1) * PER;
   uint32_t mine = 0;
-  for (int j = 0; j < per; ++j)
-    if (hi - j >= 0) mine += cnt[hi - j];
-  if (threadIdx.x == 0) {
+  if (owns) {
+    const int rot = (lane * PER) / kWave;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) mine += cnt[lo + ((j + rot) & (PER - 1))];
+  }
+  if (t == 0) {
     out3[0] = 0u;
     out3[1] = want;
     out3[2] = 1u;
   }
   uint32_t tot;
-  uint32_t above = block_excl_scan<NT>(mine, scan_sh, tot);
-  for (int j = 0; j < per; ++j) {
-    const int b = hi - j;
-    if (b < 0) break;
-    const uint32_t c = cnt[b];
-    if (above < want && above + c >= want) {
-      out3[0] = (uint32_t)b;
-      out3[1] = want - above;
-      out3[2] = 0u;
+  const uint32_t above = block_excl_scan<NT>(mine, scan_sh, tot);
+  if (owns && above < want && above + mine >= want) {  // one thread: walk its run from the top
+    uint32_t c[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = cnt[lo + j];
+    uint32_t a = above;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      if (a + c[j] >= want) {
+        out3[0] = (uint32_t)(lo + j);
+        out3[1] = want - a;
+        out3[2] = 0u;
+        break;
+      }
+      a += c[j];
     }
-    above += c;
   }
   __syncthreads();
 }
@@ -142,7 +156,7 @@ __device__ void exact_row_select(const float* __restrict__ s, int64_t nb, int k,
       sm.tot[i] = t;
     }
     __syncthreads();
-    find_digit_desc<NT>(sm.tot, kBins, want, sm.scan_sh, sm.out3);
+    find_digit_desc<NT, kBins>(sm.tot, want, sm.scan_sh, sm.out3);
     prefix |= sm.out3[0] << shift;
     mask |= 0xffu << shift;
     want = sm.out3[1];
@@ -257,7 +271,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   }
   __syncthreads();
   // conservative threshold (not reached: every block is a candidate)
-  find_digit_desc<kChunkThreads>(h, kDigits, sel::sample_target((uint32_t)k), scan_sh, out3);
+  find_digit_desc<kChunkThreads, kDigits>(h, sel::sample_target((uint32_t)k), scan_sh, out3);
   const uint32_t B = out3[2] ? 0u : out3[0];
 
   uint32_t key[kChunkPer];
@@ -362,7 +376,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   __syncthreads();
   // The k-th largest candidate key TK, 12 + 10 + 10 bits at a time; each
   // level histograms only the candidates that share the bits found so far.
-  find_digit_desc<kFinThreads>(sm.hist16, kDigits, (uint32_t)k, sm.scan_sh, sm.out3);
+  find_digit_desc<kFinThreads, kDigits>(sm.hist16, (uint32_t)k, sm.scan_sh, sm.out3);
   const uint32_t t1 = sm.out3[0];
   uint32_t need = sm.out3[1];
 #pragma unroll
@@ -371,7 +385,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
     if (i < n_cand && (kk[e] >> kDigitShift) == t1) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
   }
   __syncthreads();
-  find_digit_desc<kFinThreads>(sm.h2, kLowBins, need, sm.scan_sh, sm.out3);
+  find_digit_desc<kFinThreads, kLowBins>(sm.h2, need, sm.scan_sh, sm.out3);
   const uint32_t t12 = (t1 << 10) | sm.out3[0];
   need = sm.out3[1];
 #pragma unroll
@@ -380,7 +394,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
     if (i < n_cand && (kk[e] >> 10) == t12) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
   }
   __syncthreads();
-  find_digit_desc<kFinThreads>(sm.h3, kLowBins, need, sm.scan_sh, sm.out3);
+  find_digit_desc<kFinThreads, kLowBins>(sm.h3, need, sm.scan_sh, sm.out3);
   const uint32_t TK = (t12 << 10) | sm.out3[0];
   need = sm.out3[1];  // keys equal to TK kept: the first `need` in block order
 
