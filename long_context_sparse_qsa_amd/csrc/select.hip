@@ -132,6 +132,7 @@ struct FinSmem {
   uint32_t coff[kMaxChunks + 1];     // chunk offsets into the candidate list
   uint32_t scan_sh[2 * (kFinThreads / kWave)];
   uint32_t out3[3];
+  uint32_t cmax;                     // largest chunk count
 };
 static_assert(kDigits == kBins * kCopies, "the digit histogram reuses the radix histogram");
 
@@ -314,10 +315,30 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   int32_t* __restrict__ out = sel + (int64_t)m * k;
   const uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
-  // every chunk count of the row is written by the collect pass whenever the
-  // candidate path runs: load them before the row position arrives
+  // Every chunk count of the row is written by the collect pass whenever the
+  // candidate path runs.  The counts and the first C slots of every chunk
+  // (C = 4096 / the chunk count rounded up to a power of two) are loaded
+  // before the row position arrives; only a chunk holding more than C
+  // candidates costs a second round trip.
   const int64_t nch_max = sel::n_chunks(nb_max);
-  const uint32_t cnt_raw = (tid < kWave && tid < kMaxChunks && tid < nch_max) ? W[tid] : 0u;
+  const int nchm = (int)(nch_max < kMaxChunks ? nch_max : kMaxChunks);
+  int lgc = 0;
+  while ((1 << lgc) < nchm) ++lgc;
+  const int lgC = 12 - lgc;  // log2 of C; kCandMax = 4096
+  static_assert(kCandMax == 4096, "speculative slot split");
+  const uint32_t* K = W + sel::key_off(nb_max);
+  const uint32_t* I = W + sel::id_off(nb_max);
+  uint32_t kk[kFinPer], ii[kFinPer];
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const int q = e * kFinThreads + tid;
+    const int c = q >> lgC;
+    const int64_t slot = (int64_t)c * kChunk + (q & ((1 << lgC) - 1));
+    const int64_t at = (c < nchm && slot < nb_max) ? slot : 0;
+    kk[e] = K[at];
+    ii[e] = I[at];
+  }
+  const uint32_t cnt_raw = (tid < kWave && tid < nchm) ? W[tid] : 0u;
   if (nb <= k) {
     for (int i = tid; i < k; i += kFinThreads) out[i] = i < nb ? i : -1;
     if (tid == 0) n_sel[m] = (int32_t)nb;
@@ -335,9 +356,12 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
     sm.h3[i] = 0u;
   }
   if (tid < kWave) {  // chunk offsets (nch <= 64: one wave)
-    const uint32_t incl = wave_incl_scan(tid < nch ? cnt_raw : 0u, lane);
+    const uint32_t cnt = tid < nch ? cnt_raw : 0u;
+    const uint32_t incl = wave_incl_scan(cnt, lane);
     sm.coff[lane + 1] = incl;
     if (lane == 0) sm.coff[0] = 0u;
+    const uint32_t mx = (uint32_t)wave_max((float)cnt);  // counts <= 4096: exact in float
+    if (lane == 0) sm.cmax = mx;
   }
   __syncthreads();
   const uint32_t n_cand = sm.coff[nch];
@@ -346,82 +370,129 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
     return;
   }
 
-  // gather the candidates (chunk order = ascending block order)
-  const uint32_t* K = W + sel::key_off(nb_max);
-  const uint32_t* I = W + sel::id_off(nb_max);
-  uint32_t kk[kFinPer], ii[kFinPer];
+  // place the candidates in chunk order (= ascending block order)
+  uint32_t vm = 0u;  // which of kk/ii hold a candidate
+  if (sm.cmax <= (1u << lgC)) {
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
-    // chunk of candidate i: the last c with coff[c] <= i
-    int lo = 0, hi = nch;  // coff[lo] <= i < coff[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.coff[mid] <= i) lo = mid; else hi = mid;
+    for (int e = 0; e < kFinPer; ++e) {
+      const int q = e * kFinThreads + tid;
+      const int c = q >> lgC;
+      const uint32_t j = (uint32_t)(q & ((1 << lgC) - 1));
+      if (c < nch && j < sm.coff[c + 1] - sm.coff[c]) {
+        const uint32_t i = sm.coff[c] + j;
+        sm.ck[i] = kk[e];
+        sm.ci[i] = ii[e];
+        atomicAdd(&sm.hist16[kk[e] >> kDigitShift], 1u);
+        vm |= 1u << e;
+      }
     }
-    const bool live = i < n_cand;
-    const int64_t slot = live ? (int64_t)lo * kChunk + (i - sm.coff[lo]) : 0;
-    kk[e] = live ? K[slot] : 0u;
-    ii[e] = live ? I[slot] : 0u;
-  }
+  } else {
+    // a chunk overflowed its speculative share: gather by candidate index
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
-    if (i < n_cand) {
-      sm.ck[i] = kk[e];
-      sm.ci[i] = ii[e];
-      atomicAdd(&sm.hist16[kk[e] >> kDigitShift], 1u);
+    for (int e = 0; e < kFinPer; ++e) {
+      const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+      // chunk of candidate i: the last c with coff[c] <= i
+      int lo = 0, hi = nch;  // coff[lo] <= i < coff[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.coff[mid] <= i) lo = mid; else hi = mid;
+      }
+      const bool live = i < n_cand;
+      const int64_t slot = live ? (int64_t)lo * kChunk + (i - sm.coff[lo]) : 0;
+      kk[e] = K[slot];
+      ii[e] = I[slot];
+      vm |= live ? (1u << e) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      const uint32_t i = (uint32_t)(e * kFinThreads + tid);
+      if ((vm >> e) & 1u) {
+        sm.ck[i] = kk[e];
+        sm.ci[i] = ii[e];
+        atomicAdd(&sm.hist16[kk[e] >> kDigitShift], 1u);
+      }
     }
   }
   __syncthreads();
-  // The k-th largest candidate key TK, 12 + 10 + 10 bits at a time; each
-  // level histograms only the candidates that share the bits found so far.
+  // The k-th largest candidate key, 12 + 10 + 10 bits at a time; each level
+  // histograms only the candidates that share the bits found so far, and the
+  // search stops as soon as the cut bin is kept whole.  Then a key is kept if
+  // (key >> shift) > prefix, or == prefix and (whole, or among the first
+  // `need` such keys in block order).
   find_digit_desc<kFinThreads, kDigits>(sm.hist16, (uint32_t)k, sm.scan_sh, sm.out3);
-  const uint32_t t1 = sm.out3[0];
+  uint32_t prefix = sm.out3[0];
   uint32_t need = sm.out3[1];
+  int shift = kDigitShift;
+  bool whole = sm.hist16[prefix] == need;
+  if (!whole) {
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
-    if (i < n_cand && (kk[e] >> kDigitShift) == t1) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
+    for (int e = 0; e < kFinPer; ++e) {
+      if (((vm >> e) & 1u) && (kk[e] >> kDigitShift) == prefix) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_desc<kFinThreads, kLowBins>(sm.h2, need, sm.scan_sh, sm.out3);
+    const uint32_t d2 = sm.out3[0];
+    prefix = (prefix << 10) | d2;
+    need = sm.out3[1];
+    shift = 10;
+    whole = sm.h2[d2] == need;
   }
-  __syncthreads();
-  find_digit_desc<kFinThreads, kLowBins>(sm.h2, need, sm.scan_sh, sm.out3);
-  const uint32_t t12 = (t1 << 10) | sm.out3[0];
-  need = sm.out3[1];
+  if (!whole) {
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    const uint32_t i = (uint32_t)(e * kFinThreads + tid);
-    if (i < n_cand && (kk[e] >> 10) == t12) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
+    for (int e = 0; e < kFinPer; ++e) {
+      if (((vm >> e) & 1u) && (kk[e] >> 10) == prefix) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_desc<kFinThreads, kLowBins>(sm.h3, need, sm.scan_sh, sm.out3);
+    const uint32_t d3 = sm.out3[0];
+    prefix = (prefix << 10) | d3;
+    need = sm.out3[1];
+    shift = 0;
+    whole = sm.h3[d3] == need;
   }
-  __syncthreads();
-  find_digit_desc<kFinThreads, kLowBins>(sm.h3, need, sm.scan_sh, sm.out3);
-  const uint32_t TK = (t12 << 10) | sm.out3[0];
-  need = sm.out3[1];  // keys equal to TK kept: the first `need` in block order
 
   // keep flags over contiguous ranges of the (ascending) candidate list
   const uint32_t r0 = (uint32_t)tid * kFinPer;
-  uint32_t n_eq = 0;
+  static_assert(kFinPer == 8, "two 16-byte LDS reads per thread");
+  uint32_t key[kFinPer], cid[kFinPer];
+  {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(&sm.ck[r0]);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(&sm.ck[r0 + 4]);
+    const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.ci[r0]);
+    const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.ci[r0 + 4]);
+    key[0] = a0.x; key[1] = a0.y; key[2] = a0.z; key[3] = a0.w;
+    key[4] = a1.x; key[5] = a1.y; key[6] = a1.z; key[7] = a1.w;
+    cid[0] = b0.x; cid[1] = b0.y; cid[2] = b0.z; cid[3] = b0.w;
+    cid[4] = b1.x; cid[5] = b1.y; cid[6] = b1.z; cid[7] = b1.w;
+  }
+  uint32_t keep = 0u, n_keep = 0u, tot;
+  if (whole) {
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) n_eq += (r0 + e < n_cand && sm.ck[r0 + e] == TK) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t eq_rank = block_excl_scan<kFinThreads>(n_eq, sm.scan_sh, tot);
-  uint32_t keep = 0u, n_keep = 0u;
+    for (int e = 0; e < kFinPer; ++e) {
+      const bool kp = r0 + e < n_cand && (key[e] >> shift) >= prefix;
+      keep |= kp ? (1u << e) : 0u;
+      n_keep += kp ? 1u : 0u;
+    }
+  } else {
+    // equal keys straddle the cut: the first `need` of them in block order
+    uint32_t n_eq = 0;
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    const uint32_t i = r0 + e;
-    if (i >= n_cand) break;
-    const uint32_t key = sm.ck[i];
-    bool kp = key > TK;
-    if (key == TK) kp = eq_rank++ < need;
-    keep |= kp ? (1u << e) : 0u;
-    n_keep += kp ? 1u : 0u;
+    for (int e = 0; e < kFinPer; ++e) n_eq += (r0 + e < n_cand && key[e] == prefix) ? 1u : 0u;
+    uint32_t eq_rank = block_excl_scan<kFinThreads>(n_eq, sm.scan_sh, tot);
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      bool kp = r0 + e < n_cand && key[e] > prefix;
+      if (r0 + e < n_cand && key[e] == prefix) kp = eq_rank++ < need;
+      keep |= kp ? (1u << e) : 0u;
+      n_keep += kp ? 1u : 0u;
+    }
   }
   // kept candidates are already in ascending block order: compact them
   uint32_t pos = block_excl_scan<kFinThreads>(n_keep, sm.scan_sh, tot);
 #pragma unroll
   for (int e = 0; e < kFinPer; ++e) {
     if ((keep >> e) & 1u) {
-      if (pos < (uint32_t)k) out[pos] = (int32_t)sm.ci[r0 + e];
+      if (pos < (uint32_t)k) out[pos] = (int32_t)cid[e];
       ++pos;
     }
   }

@@ -121,6 +121,28 @@ def test_decode_262k_full_size(Q):
     say(_check_layer(d, layer.run(), layer))
 
 
+def test_clustered_relevance_full_size(Q):
+    """Relevance concentrated in 1,000 consecutive blocks: one 4,096-block
+    chunk then holds most of the candidates, more than its share of the
+    selection's first (speculative) gather, so the second gather path runs."""
+    say("verify M=4 at 261122, relevance clustered in blocks 40000..40999")
+    d = dict(datagen.gen_layer("verify_262k"))
+    idx = d["idx"].copy()
+    u = datagen.planting_direction(d["idx_q"]).astype(np.float32)
+    lo, hi = 40000 * 4, 41000 * 4
+    idx[lo:hi] = datagen.round_bf16(idx[lo:hi] + np.float32(6.0) * u[None, :])
+    d["idx"] = idx
+    layer = Layer(d)
+    res = layer.run()
+    st = _check_layer(d, res, layer)
+    sel = res["sel"].cpu().numpy()
+    # chunk 9 = blocks 36,864..40,959; with 16 chunks each chunk's speculative
+    # share is 256 candidates, and every kept block was a candidate
+    in_chunk = ((sel >= 9 * 4096) & (sel < 10 * 4096)).sum(axis=1)
+    assert np.all(in_chunk > 256), in_chunk
+    say(st, in_chunk)
+
+
 def test_prefill_full_size_sampled(Q):
     say("prefill 2048 rows at 200000 bf16 (full size, sampled rows)")
     d = datagen.gen_layer("prefill")
