@@ -54,6 +54,16 @@ constexpr int kChunkPer = kChunk / kChunkThreads;  // 16 consecutive scores per 
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kCandMax / kFinThreads;    // 8 candidates per thread
 constexpr int kLowBins = 1024;                     // 10-bit digits below the 12-bit one
+// The collect pass histograms its sample over a window of 256 digits: scores
+// from 2^-16 to 2^16 at 8 bins per octave; lower digits share the first bin
+// and higher ones the last.  Its threshold is an estimate, so saturation only
+// makes it more conservative (the finalize pass is exact regardless).
+constexpr int kWinBins = 256;
+constexpr uint32_t kWinBase = 0x800u + (127u - 16u) * 8u;  // digit of 2^-16
+__device__ __forceinline__ uint32_t win_bin(uint32_t key) {
+  const uint32_t d = key >> kDigitShift;
+  return d < kWinBase ? 0u : (d - kWinBase < (uint32_t)kWinBins ? d - kWinBase : (uint32_t)kWinBins - 1u);
+}
 static_assert(kChunkPer % 4 == 0, "float4 score loads");
 
 template <int NT>
@@ -214,7 +224,7 @@ select_sample_kernel(const float* __restrict__ scores, int64_t ld, const int64_t
 __global__ void __launch_bounds__(kChunkThreads)
 select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
                       int64_t nb_max, int k, uint32_t* __restrict__ ws) {
-  __shared__ uint32_t h[kDigits];
+  __shared__ uint32_t h[kWinBins];
   __shared__ uint32_t scan_sh[2 * (kChunkThreads / kWave)];
   __shared__ uint32_t out3[3];
   const int m = blockIdx.y;
@@ -242,7 +252,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
     smpv[e] = gi < n_grp ? smp[gi] : 0.f;
   }
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
-  for (int i = tid; i < kDigits; i += kChunkThreads) h[i] = 0u;
+  for (int i = tid; i < kWinBins; i += kChunkThreads) h[i] = 0u;
   if (nb <= k) return;  // the finalize pass keeps every block
   if (base >= nb) {
     if (tid == 0) W[c] = 0u;
@@ -254,7 +264,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   for (int e = 0; e < kSampPer; ++e) {
     const int64_t gi = (int64_t)e * kChunkThreads + tid;
     if (gi < n_grp && gi * 16 + sel::sample_offset((uint32_t)gi) < nb)
-      atomicAdd(&h[order_key(smpv[e]) >> kDigitShift], 1u);
+      atomicAdd(&h[win_bin(order_key(smpv[e]))], 1u);
   }
   for (int64_t g0 = kChunk; g0 < n_grp; g0 += kChunk) {  // rows of more than 65,536 blocks
     float v[kSampPer];
@@ -267,13 +277,14 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
     for (int e = 0; e < kSampPer; ++e) {
       const int64_t gi = g0 + (int64_t)e * kChunkThreads + tid;
       if (gi < n_grp && gi * 16 + sel::sample_offset((uint32_t)gi) < nb)
-        atomicAdd(&h[order_key(v[e]) >> kDigitShift], 1u);
+        atomicAdd(&h[win_bin(order_key(v[e]))], 1u);
     }
   }
   __syncthreads();
   // conservative threshold (not reached: every block is a candidate)
-  find_digit_desc<kChunkThreads, kDigits>(h, sel::sample_target((uint32_t)k), scan_sh, out3);
-  const uint32_t B = out3[2] ? 0u : out3[0];
+  find_digit_desc<kChunkThreads, kWinBins>(h, sel::sample_target((uint32_t)k), scan_sh, out3);
+  // window bin 0 (or a target never reached): every block is a candidate
+  const uint32_t B = (out3[2] || out3[0] == 0u) ? 0u : kWinBase + out3[0];
 
   uint32_t key[kChunkPer];
   uint32_t flags = 0u;
