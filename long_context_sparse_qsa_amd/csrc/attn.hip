@@ -478,28 +478,29 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+constexpr int kMaxWaves = 8;  // waves (16-token slices) per workgroup
+
+// Dynamic LDS of the matrix-core kernel, in 32-bit words.  Phase 1, per wave:
+// V rows of its slice, [pair][dim] as (V[2 pair][dim], V[2 pair + 1][dim])
+// bf16 pairs, then the bf16 probabilities [pair][head].  Phase 2 (merge,
+// reusing the same memory): every wave's partial output, then the softmax
+// states and the per-head merge weights.
 template <int D>
-struct MfmaSmem {
+struct MfmaLds {
   static constexpr int kPairs = 8;  // token pairs of a 16-token slice
-  struct Wave {
-    uint32_t v[kPairs * D];         // [pair][dim]: (V[2 pair][dim], V[2 pair + 1][dim]) as bf16 x 2
-    uint32_t p[kPairs * kGroup];    // [pair][head]: bf16 probabilities of the pair
-  };
-  struct Merge {
-    float acc[4][kGroup * D];
-    float m[4][kGroup];
-    float l[4][kGroup];
-    float wt[kGroup][4];   // weight of each wave's partial in the merged output
-    float lse[kGroup];
-  };
-  union {
-    Wave w[4];
-    Merge mg;
-  };
+  static constexpr int kWaveWords = kPairs * D + kPairs * kGroup;
+  static constexpr int acc(int w) { return w * kGroup * D; }
+  static constexpr int m(int W, int w) { return W * kGroup * D + w * kGroup; }
+  static constexpr int l(int W, int w) { return W * kGroup * D + W * kGroup + w * kGroup; }
+  static constexpr int wt(int W, int h) { return W * kGroup * D + 2 * W * kGroup + h * kMaxWaves; }
+  static constexpr int lse(int W) { return W * kGroup * D + 2 * W * kGroup + kGroup * kMaxWaves; }
+  static constexpr size_t bytes(int W) {
+    return 4 * (size_t)(W * kWaveWords > lse(W) + kGroup ? W * kWaveWords : lse(W) + kGroup);
+  }
 };
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int D, int NW>
+__global__ void __launch_bounds__(kWave * NW)
 attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2,
                  const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                  KvArgs kv, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
@@ -512,19 +513,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   constexpr int VIT = 8 * VCH / kWave;     // (token pair, chunk) V items per lane
   constexpr int kRowBytes = D * 2;
   static_assert(kWave % VCH == 0 || VCH % kWave == 0, "V item mapping");
-  __shared__ __align__(16) MfmaSmem<D> sm;
+  using Lds = MfmaLds<D>;
+  extern __shared__ __align__(16) uint32_t lds[];
   __shared__ SegDesc segs[kMaxSegments];
   __shared__ int nseg_sh;
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int m = blockIdx.z;
+  constexpr int nw = NW;  // waves = 16-token slices per tile
+  constexpr int tile = 16 * nw;
+  const int g = blockIdx.x;  // grid (KV head, row, split)
+  const int m = blockIdx.y;
+  const int split = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = uniform(tid / kWave);
   const int n16 = lane & 15;   // token of the slice (QK operand and softmax row position)
   const int g4 = lane >> 4;    // k-slice of the operands / head quad of the scores
-  const int tok_begin = split * tiles_per_split * kTileTok;
+  const int tok_begin = split * tiles_per_split * tile;
   const int32_t* __restrict__ srow = sel + (int64_t)m * k_blocks;
 
   // ---- independent loads, issued together
@@ -594,11 +598,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   for (int h = 0; h < kGroup; ++h)
 #pragma unroll
     for (int d = 0; d < DPL; ++d) acc[h][d] = 0.f;
-  uint32_t* vl = sm.w[wave].v;
-  uint32_t* pl = sm.w[wave].p;
+  uint32_t* vl = lds + wave * Lds::kWaveWords;
+  uint32_t* pl = vl + Lds::kPairs * D;
 
   for (int t = 0; t < tiles_per_split; ++t) {
-    const int j0 = tok_begin + t * kTileTok + wave * 16;
+    const int j0 = tok_begin + t * tile + wave * 16;
     if (j0 >= total) break;  // wave-uniform: the loop has no workgroup barrier
     // 1. token of this lane's row position
     const int j = j0 + n16;
@@ -642,7 +646,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     }
     // next slice's block id, in flight during this slice's compute
     if (t + 1 < tiles_per_split) {
-      const int jn = j + kTileTok;
+      const int jn = j + tile;
       bid = (jn >> 2) < k_blocks ? srow[jn >> 2] : -1;
     }
 
@@ -715,22 +719,23 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- merge the four wave partials (log2 domain)
+  // ---- merge the wave partials (log2 domain)
   __syncthreads();  // every wave is done with its V / P region
+  float* fl = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int h = 0; h < kGroup; ++h) {
+    float* dst = fl + Lds::acc(wave) + h * D + DPL * lane;
     if constexpr (DPL == 4) {
-      *reinterpret_cast<float4*>(&sm.mg.acc[wave][h * D + DPL * lane]) =
-          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
     } else {
-      *reinterpret_cast<float2*>(&sm.mg.acc[wave][h * D + DPL * lane]) = make_float2(acc[h][0], acc[h][1]);
+      *reinterpret_cast<float2*>(dst) = make_float2(acc[h][0], acc[h][1]);
     }
   }
   if (n16 == 0 && g4 < 3) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      sm.mg.m[wave][4 * g4 + v] = m_run[v];
-      sm.mg.l[wave][4 * g4 + v] = l_run[v];
+      fl[Lds::m(nw, wave) + 4 * g4 + v] = m_run[v];
+      fl[Lds::l(nw, wave) + 4 * g4 + v] = l_run[v];
     }
   }
   __syncthreads();
@@ -738,36 +743,39 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     const int h = tid;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.mg.m[w][h]);
-    float f[4], L = 0.f;
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, fl[Lds::m(nw, w) + h]);
+    float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = sm.mg.m[w][h];
-      f[w] = (mx == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - mx);
-      L += sm.mg.l[w][h] * f[w];
+    for (int w = 0; w < nw; ++w) {
+      const float mw = fl[Lds::m(nw, w) + h];
+      const float f = (mx == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - mx);
+      fl[Lds::wt(nw, h) + w] = f;
+      L += fl[Lds::l(nw, w) + h] * f;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) sm.mg.wt[h][w] = f[w] * inv;
-    sm.mg.lse[h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    for (int w = 0; w < nw; ++w) fl[Lds::wt(nw, h) + w] *= inv;
+    fl[Lds::lse(nw) + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  constexpr int kOut = kGroup * D / kThreads;  // outputs per thread
+  constexpr int kOut = (kGroup * D + kWave * nw - 1) / (kWave * nw);  // outputs per thread
 #pragma unroll
   for (int e = 0; e < kOut; ++e) {
-    const int o = tid + kThreads * e;
+    const int o = tid + kWave * nw * e;
+    if (o >= kGroup * D) break;
     const int h = o / D;
     const int d = o % D;
-    const float4 wt = *reinterpret_cast<const float4*>(sm.mg.wt[h]);
-    const float O = sm.mg.acc[0][o] * wt.x + sm.mg.acc[1][o] * wt.y + sm.mg.acc[2][o] * wt.z +
-                    sm.mg.acc[3][o] * wt.w;
+    const float* wt = fl + Lds::wt(nw, h);
+    float O = 0.f;
+#pragma unroll
+    for (int w = 0; w < nw; ++w) O = fmaf(fl[Lds::acc(w) + o], wt[w], O);
     const int64_t head = (int64_t)m * hq + (int64_t)g * kGroup + h;
     if (splits == 1) {
       out[head * D + d] = (uint16_t)f32_to_bf16_bits(O);
-      if (d == 0) lse_out[head] = sm.mg.lse[h];
+      if (d == 0) lse_out[head] = fl[Lds::lse(nw) + h];
     } else {
       ws_o[(head * splits + split) * D + d] = O;
-      if (d == 0) ws_lse[head * splits + split] = sm.mg.lse[h];
+      if (d == 0) ws_lse[head * splits + split] = fl[Lds::lse(nw) + h];
     }
   }
 }
@@ -777,7 +785,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 // kRegSplits) and its own split's lse are loaded at once; thread i computes
 // split i's weight once and the weights are shared through LDS, so the merge
 // takes one memory round trip.
-constexpr int kRegSplits = 40;
+constexpr int kRegSplits = 72;
 
 template <class E, int D>
 __global__ void __launch_bounds__(D)
@@ -840,15 +848,30 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
                         const int64_t* row_pos, const int32_t* row_seq, const KvArgs& kv,
                         const int32_t* sel, const int32_t* n_sel, int k_blocks, void* out,
                         float* lse, void* ws, hipStream_t stream) {
-  const AttnPlan plan = attn_plan(M, hkv, k_blocks);
+  constexpr bool kMfma = (E::kBytes == 2);
+  const AttnPlan plan = kMfma ? attn_plan(M, hkv, k_blocks) : attn_plan_valu(M, hkv, k_blocks);
   float* ws_o = static_cast<float*>(ws);
   float* ws_lse = ws_o ? ws_o + (size_t)M * hq * plan.splits * D : nullptr;
-  dim3 grid(plan.splits, hkv, M), block(kThreads);
-  if constexpr (E::kBytes == 2) {
-    hipLaunchKernelGGL((attn_mfma_kernel<D>), grid, block, 0, stream,
-                       static_cast<const uint16_t*>(q), M, hq, scale * kLog2e, row_pos, row_seq,
-                       kv, sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,
-                       static_cast<uint16_t*>(out), lse, ws_o, ws_lse);
+  dim3 grid(plan.splits, hkv, M), block(kWave * plan.waves);
+  if constexpr (kMfma) {
+    grid = dim3(hkv, M, plan.splits);
+    const size_t lds = MfmaLds<D>::bytes(plan.waves);
+#define QSA_MFMA_LAUNCH(W)                                                                              \
+  case W:                                                                                             \
+    hipLaunchKernelGGL((attn_mfma_kernel<D, W>), grid, block, lds, stream,                            \
+                       static_cast<const uint16_t*>(q), M, hq, scale * kLog2e, row_pos, row_seq, kv,  \
+                       sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,                       \
+                       static_cast<uint16_t*>(out), lse, ws_o, ws_lse);                               \
+    break;
+    switch (plan.waves) {
+      QSA_MFMA_LAUNCH(4)
+      QSA_MFMA_LAUNCH(5)
+      QSA_MFMA_LAUNCH(6)
+      QSA_MFMA_LAUNCH(7)
+      QSA_MFMA_LAUNCH(8)
+      default: return hipErrorInvalidConfiguration;
+    }
+#undef QSA_MFMA_LAUNCH
   } else {
     hipLaunchKernelGGL((attn_decode_kernel<E, D>), grid, block, 0, stream,
                        static_cast<const typename E::T*>(q), M, hq, scale * kLog2e, row_pos, row_seq,
@@ -865,7 +888,38 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
 
 }  // namespace
 
+// Compute units of a gfx950 device (MI350X / MI355X).
+constexpr long kCUs = 256;
+
+// Matrix-core kernel: a workgroup holds `waves` 16-token slices of a tile.
+// Four waves (one per SIMD) when every (row, KV head, split) workgroup then
+// has a compute unit of its own; otherwise the fewest waves, up to 8, that
+// fit: a second workgroup on a unit slows both more than a fifth wave does,
+// and fewer waves than four only add split partials to merge.  When even 8
+// waves cannot fit, one tile per workgroup up to 4 workgroups per unit, then
+// several tiles each.
 AttnPlan attn_plan(int M, int hkv, int k_blocks) {
+  const int max_tokens = k_blocks * kBlockTokens + (kBlockTokens - 1);
+  const int slices = (max_tokens + 15) / 16;
+  const long rows = (long)M * hkv;
+  AttnPlan p;
+  int w = 4;
+  while (w < kMaxWaves && rows * ((slices + w - 1) / w) > kCUs) ++w;
+  const int tiles = (slices + w - 1) / w;
+  p.waves = w;
+  p.tile_tokens = 16 * w;
+  p.tiles_per_split = 1;
+  if (rows * tiles > 4 * kCUs) {
+    long want = 4 * kCUs / rows;
+    if (want < 1) want = 1;
+    p.tiles_per_split = (int)((tiles + want - 1) / want);
+  }
+  p.splits = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  return p;
+}
+
+// Vector kernel: 4-wave workgroups over 64-token tiles, about 512 of them.
+AttnPlan attn_plan_valu(int M, int hkv, int k_blocks) {
   const int max_tokens = k_blocks * kBlockTokens + (kBlockTokens - 1);
   const int max_tiles = (max_tokens + kTileTok - 1) / kTileTok;
   const long target_wg = 512;
@@ -874,6 +928,7 @@ AttnPlan attn_plan(int M, int hkv, int k_blocks) {
   if (want > max_tiles) want = max_tiles;
   AttnPlan p;
   p.tile_tokens = kTileTok;
+  p.waves = kThreads / kWave;
   p.tiles_per_split = (max_tiles + (int)want - 1) / (int)want;
   p.splits = (max_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
@@ -881,12 +936,16 @@ AttnPlan attn_plan(int M, int hkv, int k_blocks) {
 
 size_t attn_workspace_bytes(int max_M, int hq, int head_dim, int k_blocks) {
   size_t best = 0;
-  // partial count M * splits(M) is not monotone in M; take the maximum.
+  const int hkv = hq / kGroup > 0 ? hq / kGroup : 1;
+  // partial count M * splits(M) is not monotone in M; take the maximum over
+  // both kernels' plans.
   for (int m = 1; m <= max_M; ++m) {
-    const AttnPlan p = attn_plan(m, hq / kGroup > 0 ? hq / kGroup : 1, k_blocks);
-    if (p.splits == 1) continue;
-    const size_t need = (size_t)m * hq * p.splits * (head_dim + 1) * sizeof(float);
-    best = need > best ? need : best;
+    const AttnPlan pl[2] = {attn_plan(m, hkv, k_blocks), attn_plan_valu(m, hkv, k_blocks)};
+    for (const AttnPlan& p : pl) {
+      if (p.splits == 1) continue;
+      const size_t need = (size_t)m * hq * p.splits * (head_dim + 1) * sizeof(float);
+      best = need > best ? need : best;
+    }
   }
   return best;
 }

@@ -37,8 +37,11 @@ struct AttnPlan {
   int tile_tokens;     // tokens per inner tile
   int splits;          // split-K parts per (row, KV head)
   int tiles_per_split; // tiles walked by one workgroup
+  int waves;           // waves per workgroup
 };
+// bf16 K/V (matrix-core kernel) and float32 K/V (vector kernel) plans.
 AttnPlan attn_plan(int M, int hkv, int k_blocks);
+AttnPlan attn_plan_valu(int M, int hkv, int k_blocks);
 size_t attn_workspace_bytes(int max_M, int hq, int head_dim, int k_blocks);
 
 hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv, int head_dim,

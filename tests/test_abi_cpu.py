@@ -132,8 +132,13 @@ def test_attn_null_kv():
 
 
 def test_workspace_sizes():
-    # one row, 2 KV heads, budget 512 blocks: 33 tiles of 64 tokens -> 33 splits
+    # one row, 2 KV heads, budget 512 blocks = 2,051 tokens at most: 33
+    # splits of 64 tokens in both plans, one partial of 257 floats per head
     assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 33 * 257 * 4
+    # up to four rows: the bf16 plan needs at most 4 x 26 partials per head
+    # (four rows in 5-wave workgroups); the float32 plan keeps 33 splits of
+    # 64 tokens at four rows, which is the largest need
+    assert Q.qsa_attn_workspace_bytes(4, 24, 256, 512) == 4 * 24 * 33 * 257 * 4
     # sizing is monotone in max_M (a call with fewer rows always fits)
     prev = 0
     for m in (1, 2, 3, 4, 8, 16, 64, 256, 2048):
