@@ -31,6 +31,8 @@ CSRC = os.path.join(ROOT, "long_context_sparse_qsa_amd", "csrc")
 SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h")
 PMC_FILE = os.path.join(ROOT, "profiles", "score_fewrow_kernel.verify_262k.pmc.txt")
 COPY_BYTES = 256 << 20  # plain copy of known size used to scale the PMC byte counters
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PREFILL_MIN_ROWS = 64  # rows at which scoring takes the many-row matrix-core kernel
 
 
 def parse():
@@ -280,6 +282,21 @@ def main():
     score_us = kt["score"]
     score_bytes = nb_max * 128 * 4 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
     achieved = score_bytes / (score_us * 1e-6) / 1e9
+    if wl.m >= PREFILL_MIN_ROWS:
+        # many-row scoring runs on the bf16 matrix cores with three-plane
+        # pooled keys: report issued bf16 flops against the bf16 peak, and the
+        # float32-equivalent (algorithmic) rate beside it
+        alg_flops = sum(min((p + 1) // 4, nb_max) for p in wl.rows) * 4 * 128 * 2
+        roofline = {"bound": "mfma", "kernel": "score_prefill_kernel",
+                    "achieved": 3 * alg_flops / (score_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": 3 * alg_flops / (score_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": None, "algorithmic_tflops": alg_flops / (score_us * 1e-6) / 1e12,
+                    "flops_per_launch_bf16": 3 * alg_flops, "launch_us": score_us}
+    else:
+        roofline = {"bound": "hbm", "kernel": "score_fewrow_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": stored_traffic() if wl.name == "verify_262k" else None,
+                    "bytes_per_launch": score_bytes, "launch_us": score_us}
     # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries
     tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
     path_bytes = nb_max * 512 + tok * wl.hkv * 2 * wl.head_dim * 2 + wl.m * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2)
@@ -300,9 +317,7 @@ def main():
         "config": {"workload": wl.name, "n_ctx": wl.n_ctx, "rows": wl.m, "row_pos": [wl.rows[0], wl.rows[-1]],
                    "layers": layers, "budget_tokens": wl.k_blocks * 4, "hq": wl.hq, "hkv": wl.hkv,
                    "head_dim": wl.head_dim, "graph": not args.eager},
-        "roofline": {"bound": "hbm", "kernel": "score_fewrow_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                     "bytes_per_launch": score_bytes, "launch_us": score_us},
+        "roofline": roofline,
         "path": {"layer_us": layer_us, "bytes_per_layer_step": path_bytes,
                  "achieved_GBs": path_bytes / (layer_us * 1e-6) / 1e9,
                  "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,

@@ -21,6 +21,13 @@ hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_
                                int64_t capacity, int64_t nb_max, float* scores, int64_t ld,
                                uint32_t* sel_ws, hipStream_t stream);
 
+// Many-row scoring (bf16 index queries, one sequence): the bf16 matrix-core
+// kernel with three-plane pooled keys (score_prefill.hip).
+constexpr int kPrefillMinRows = 64;
+hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
+                                int64_t nb_max, float* scores, int64_t ld, uint32_t* sel_ws,
+                                hipStream_t stream);
+
 size_t select_workspace_bytes(int max_M, int64_t nb_max, int k_blocks);
 // Standalone selection: histogram, collect and finalize passes.
 hipError_t launch_select_topk(const float* scores, int64_t ld, int M, const int64_t* row_pos,

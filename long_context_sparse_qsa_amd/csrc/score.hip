@@ -212,8 +212,11 @@ hipError_t dispatch_rows(const void* idx_q, int M, const int64_t* row_pos, const
                          const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
                          float* scores, int64_t ld, uint32_t* ws, hipStream_t stream) {
   // Rows of different sequences read different pooled keys: one row per
-  // group.  Rows of one sequence share each pooled read, 4 or 8 at a time.
+  // group.  Rows of one sequence share each pooled read, 4 or 8 at a time;
+  // many bf16 rows go to the matrix-core many-row kernel.
   if (row_seq) return launch_fewrow<EQ, 1, 1, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
+  if (EQ::kBytes == 2 && M >= kPrefillMinRows)
+    return launch_score_prefill(idx_q, M, row_pos, pooled, nb_max, scores, ld, ws, stream);
   if (M <= 4) return launch_fewrow<EQ, 1, 4, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
   return launch_fewrow<EQ, 2, 8, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
 }

@@ -135,7 +135,10 @@ def check_attention(out_gpu: np.ndarray, lse_gpu: np.ndarray, d: dict, row_i: in
     tok = O.attended_tokens(sel, p + 1)
     ref, ref_lse = O.attend(d["q"][row_i], d["k"], d["v"], tok, 1.0 / math.sqrt(wl.head_dim))
     tol = 2e-2 if dtype == "bf16" else 1e-4
-    ltol = 1e-3 if dtype == "bf16" else 1e-5
+    # bf16 K/V: the kernel rounds each probability to bf16 (relative error at
+    # most 2^-9) and normalises by the sum of the rounded values, so lse may
+    # differ by up to log(1 + 2^-9) ~ 1.95e-3 when a few tokens dominate
+    ltol = 2.5e-3 if dtype == "bf16" else 1e-5
     err = float(np.max(np.abs(out_gpu - ref)))
     lerr = float(np.max(np.abs(lse_gpu - ref_lse)))
     assert err <= tol, f"attention max-abs {err} > {tol}"

@@ -153,6 +153,27 @@ def test_prefill_full_size_sampled(Q):
     say(_check_layer(d, res, layer, rows=rows))
 
 
+def test_many_rows_ragged(Q):
+    """131 bf16 rows of one sequence at scattered positions -- rows with fewer
+    blocks than one 64-block tile, rows ending inside a tile, a partial
+    second 128-row tile: the many-row matrix-core scoring path."""
+    say("many rows (131) at scattered positions of a 32,768-token context")
+    base = datagen.gen_layer("decode_32k")
+    d = dict(base)
+    rng = np.random.default_rng(7)
+    fixed = [0, 1, 2, 3, 4, 63, 64, 255, 256, 257, 2050]
+    rest = rng.choice(np.arange(5, 32768), 120, replace=False)
+    rows = np.sort(np.unique(np.concatenate([fixed, rest]))).astype(np.int64)
+    m = len(rows)
+    d["rows"] = rows
+    d["idx_q"] = datagen.round_bf16(rng.standard_normal((m, 4, 128)).astype(np.float32))
+    d["q"] = datagen.round_bf16(rng.standard_normal((m, 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=32768)
+    res = layer.run()
+    st = _check_layer(d, res, layer, attn_rows=[0, 4, 5, 10, m - 1])
+    say(len(st), "rows checked")
+
+
 @pytest.mark.parametrize("rows", [(0,), (1,), (2,), (3,), (4,), (5, 6, 7), (30, 100, 255),
                                   (1019, 1020, 1021, 1022)])
 def test_short_and_ragged_rows(Q, rows):
