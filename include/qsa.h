@@ -208,7 +208,13 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
                       void* workspace, size_t workspace_bytes, qsa_stream_t stream);
 
 /* Workspace bytes qsa_select_topk needs for up to max_M rows of up to
- * nb_max blocks (0 means no workspace is needed). */
+ * nb_max blocks (0 means no workspace is needed).  The workspace is one
+ * record per row, of qsa_select_workspace_bytes(1, nb_max, k_blocks) bytes;
+ * after a selection, 32-bit word 0 of row m's record tells how row m was
+ * selected (a diagnostic; every path gives the same exact result): 1 all
+ * blocks kept, 2 from the conservative candidates, 3 or 4 by the exact
+ * whole-row select (more than 64 chunks of 4,096 blocks; a candidate count
+ * below k_blocks or above 4,096). */
 size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks);
 
 /* Workspace bytes qsa_gathered_attn needs for up to max_M rows (split-K

@@ -253,11 +253,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   }
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
   for (int i = tid; i < kWinBins; i += kChunkThreads) h[i] = 0u;
-  if (nb <= k) return;  // the finalize pass keeps every block
-  if (base >= nb) {
-    if (tid == 0) W[c] = 0u;
-    return;
-  }
+  if (nb <= k || base >= nb) return;  // every block kept, or a chunk the finalize pass does not read
   __syncthreads();
   // histogram of the row's samples (blocks < nb only)
 #pragma unroll
@@ -311,7 +307,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
       ++pos;
     }
   }
-  if (tid == 0) W[c] = total;
+  if (tid == 0) W[sel::cnt_off(nb_max) + c] = total;
 }
 
 __global__ void __launch_bounds__(kFinThreads)
@@ -324,7 +320,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   const int lane = tid & (kWave - 1);
   const float* __restrict__ s = scores + (int64_t)m * ld;
   int32_t* __restrict__ out = sel + (int64_t)m * k;
-  const uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
+  uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
   // Every chunk count of the row is written by the collect pass whenever the
   // candidate path runs.  The counts and the first C slots of every chunk
@@ -349,15 +345,19 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
     kk[e] = K[at];
     ii[e] = I[at];
   }
-  const uint32_t cnt_raw = (tid < kWave && tid < nchm) ? W[tid] : 0u;
+  const uint32_t cnt_raw = (tid < kWave && tid < nchm) ? W[sel::cnt_off(nb_max) + tid] : 0u;
   if (nb <= k) {
     for (int i = tid; i < k; i += kFinThreads) out[i] = i < nb ? i : -1;
-    if (tid == 0) n_sel[m] = (int32_t)nb;
+    if (tid == 0) {
+      n_sel[m] = (int32_t)nb;
+      W[sel::kPathWord] = sel::kPathAll;
+    }
     return;
   }
   if (tid == 0) n_sel[m] = k;
   const int nch = (int)((nb + kChunk - 1) / kChunk);
   if (nch > kMaxChunks) {
+    if (tid == 0) W[sel::kPathWord] = sel::kPathExactChunks;
     exact_row_select(s, nb, k, out, sm);
     return;
   }
@@ -377,9 +377,11 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   __syncthreads();
   const uint32_t n_cand = sm.coff[nch];
   if (n_cand < (uint32_t)k || n_cand > (uint32_t)kCandMax) {
+    if (tid == 0) W[sel::kPathWord] = sel::kPathExactCount;
     exact_row_select(s, nb, k, out, sm);
     return;
   }
+  if (tid == 0) W[sel::kPathWord] = sel::kPathCandidates;
 
   // place the candidates in chunk order (= ascending block order)
   uint32_t vm = 0u;  // which of kk/ii hold a candidate

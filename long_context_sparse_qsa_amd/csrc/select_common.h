@@ -16,14 +16,25 @@ constexpr int kCandMax = 4096;                 // candidates the finalize pass h
 
 // Per-row workspace record (32-bit words, every part 256-byte aligned);
 // nothing in it needs to start at any particular value:
-//   [0, n_chunks)        candidate count of each 4,096-block chunk
+//   [0, kCtlWords)       word kPathWord: how the last selection of the row went
+//   cnt_off + c          candidate count of 4,096-block chunk c
 //   key_off + c*kChunk   candidate keys of chunk c, ascending block order
 //   id_off  + c*kChunk   their block ids
 //   sample_off + g       sampled score of 16-block group g
+constexpr int kCtlWords = 64;
+constexpr int kPathWord = 0;
+// Selection paths (a diagnostic: every path gives the same exact result).
+enum SelPath : uint32_t {
+  kPathAll = 1,         // at most k blocks: all kept
+  kPathCandidates = 2,  // from the conservative candidates
+  kPathExactChunks = 3, // exact whole-row select: more than kMaxChunks chunks
+  kPathExactCount = 4,  // exact whole-row select: candidate count below k or above kCandMax
+};
 __host__ __device__ constexpr int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 __host__ __device__ constexpr int64_t n_chunks(int64_t nb_max) { return (nb_max + kChunk - 1) / kChunk; }
 __host__ __device__ constexpr int64_t sample_groups(int64_t nb_max) { return (nb_max + 15) / 16; }
-__host__ __device__ constexpr int64_t key_off(int64_t nb_max) { return round64(n_chunks(nb_max)); }
+__host__ __device__ constexpr int64_t cnt_off(int64_t) { return kCtlWords; }
+__host__ __device__ constexpr int64_t key_off(int64_t nb_max) { return cnt_off(nb_max) + round64(n_chunks(nb_max)); }
 __host__ __device__ constexpr int64_t id_off(int64_t nb_max) { return key_off(nb_max) + round64(nb_max); }
 __host__ __device__ constexpr int64_t sample_off(int64_t nb_max) { return id_off(nb_max) + round64(nb_max); }
 __host__ __device__ constexpr int64_t row_words(int64_t nb_max) {

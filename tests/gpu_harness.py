@@ -90,6 +90,10 @@ class Layer:
             torch.cuda.synchronize()
             assert torch.equal(scores_f, scores), "prepared-path scores differ"
             assert torch.equal(sel_f, sel) and torch.equal(n_sel_f, n_sel), "prepared-path selection differs"
+        # word 0 of each row's workspace record: how the prepared selection went
+        rec_words = Q.qsa_select_workspace_bytes(1, self.nb_max, k) // 4
+        paths = ws_sel[: m * rec_words * 4].view(torch.int32).view(m, rec_words)[:, 0].cpu().numpy() \
+            if rec_words > 0 else np.ones(m, dtype=np.int32)
         out = torch.empty_like(self.q)
         lse = torch.empty((m, wl.hq), dtype=torch.float32, device=DEV)
         wsa = Q.qsa_attn_workspace_bytes(m, wl.hq, wl.head_dim, k)
@@ -97,7 +101,7 @@ class Layer:
         Q.qsa_gathered_attn(self.q, self.rows, self.kv, sel, n_sel, out, lse, wl.hkv,
                             scale=1.0 / math.sqrt(wl.head_dim), workspace=ws)
         torch.cuda.synchronize()
-        return {"scores": scores, "sel": sel, "n_sel": n_sel, "out": out, "lse": lse}
+        return {"scores": scores, "sel": sel, "n_sel": n_sel, "out": out, "lse": lse, "paths": paths}
 
 
 def band_mask(scores64: np.ndarray, k: int) -> tuple[np.ndarray, float]:

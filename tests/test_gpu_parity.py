@@ -97,6 +97,7 @@ def test_decode_32k(Q):
     layer = Layer(d)
     res = layer.run()
     say(_check_layer(d, res, layer))
+    _assert_candidate_path(res, layer)
 
 
 def test_decode_32k_layers_differ(Q):
@@ -106,19 +107,31 @@ def test_decode_32k_layers_differ(Q):
     say(_check_layer(d, layer.run(), layer))
 
 
+def _assert_candidate_path(res, layer, k=None):
+    """Every row longer than the budget was selected from the conservative
+    candidates (the exact whole-row fallback is correct but slow)."""
+    k = k or layer.wl.k_blocks
+    nb = (layer.rows.cpu().numpy() + 1) // 4
+    want = np.where(nb <= k, 1, 2)
+    assert np.array_equal(res["paths"], want), (res["paths"][:16], want[:16])
+
+
 def test_verify_262k_full_size(Q):
     say("verify M=4 at 261122 bf16 (full size)")
     d = datagen.gen_layer("verify_262k")
     layer = Layer(d)
     res = layer.run()
     say(_check_layer(d, res, layer))
+    _assert_candidate_path(res, layer)
 
 
 def test_decode_262k_full_size(Q):
     say("decode M=1 at 261122 bf16 (full size)")
     d = datagen.gen_layer("decode_262k")
     layer = Layer(d)
-    say(_check_layer(d, layer.run(), layer))
+    res = layer.run()
+    say(_check_layer(d, res, layer))
+    _assert_candidate_path(res, layer)
 
 
 def test_clustered_relevance_full_size(Q):
@@ -140,6 +153,7 @@ def test_clustered_relevance_full_size(Q):
     # share is 256 candidates, and every kept block was a candidate
     in_chunk = ((sel >= 9 * 4096) & (sel < 10 * 4096)).sum(axis=1)
     assert np.all(in_chunk > 256), in_chunk
+    _assert_candidate_path(res, layer)
     say(st, in_chunk)
 
 
@@ -151,6 +165,7 @@ def test_prefill_full_size_sampled(Q):
     rng = np.random.default_rng(0)
     rows = sorted(set([0, 1, 2, 3, 15, 16, 1023, 2046, 2047] + rng.choice(2048, 16, replace=False).tolist()))
     say(_check_layer(d, res, layer, rows=rows))
+    _assert_candidate_path(res, layer)
 
 
 def test_many_rows_ragged(Q):
@@ -171,6 +186,7 @@ def test_many_rows_ragged(Q):
     layer = Layer(d, prefix_split=32768)
     res = layer.run()
     st = _check_layer(d, res, layer, attn_rows=[0, 4, 5, 10, m - 1])
+    _assert_candidate_path(res, layer)
     say(len(st), "rows checked")
 
 
