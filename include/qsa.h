@@ -84,6 +84,13 @@ typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
  * idx_cache.  Contract: within one call, the tokens of one sequence are
  * consecutive in new_idx and in ascending position order.  Tokens whose
  * pos or seq is out of range are skipped.
+ *
+ * Rollback (a speculative verify whose tokens are partly rejected) needs no
+ * call and no snapshot: the caller lowers its length.  Rows past the length
+ * are never read, and a block's pooled key is rebuilt from its four cached
+ * keys whenever its last token is written again, so appending from the
+ * trimmed length gives the same bytes as if the rejected tokens had never
+ * been written.
  */
 int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
                     const int64_t* pos, const int32_t* seq,

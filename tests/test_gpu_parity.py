@@ -207,6 +207,57 @@ def test_short_and_ragged_rows(Q, rows):
     say(_check_layer(d, res, layer, k=16))
 
 
+@pytest.mark.parametrize("accepted", [0, 1, 2, 3])
+def test_verify_rollback_reappend(Q, accepted):
+    """Speculative verify with rollback (MTPLX PR #482, section 3,
+    optimization 1: in-place verify write, rollback by trimming).  A verify
+    writes 4 index keys in place, pooling the block they complete; only
+    ``accepted`` of them are kept and the length goes back; the next verify
+    writes 4 keys from there.  Nothing is restored: positions are explicit,
+    rows past the length are never read, and a block's pooled key is rebuilt
+    from its four cached keys whenever its last token is written, so the block
+    the rejected keys completed is pooled again when it completes again.  With
+    accepted = 0..3 the first verify starts at every block offset.  Cache and
+    pooled keys must equal a from-scratch build of the accepted history byte
+    for byte, and the layer on the rolled-back state must pass the oracle."""
+    say(f"verify rollback, {accepted} of 4 accepted, 32K context")
+    base = datagen.gen_layer("decode_32k")
+    n = base["idx"].shape[0] - 1          # accepted history after the second verify
+    n0 = n - 4 - accepted                 # length before the first verify
+    d = dict(base)
+    d["idx"] = np.ascontiguousarray(base["idx"][:n])
+    d["k"] = np.ascontiguousarray(base["k"][:, :n])
+    d["v"] = np.ascontiguousarray(base["v"][:, :n])
+    d["rows"] = np.asarray([n - 1], dtype=np.int64)
+    layer = Layer(d)                      # the accepted history, appended from scratch
+    rng = np.random.default_rng(100 + accepted)
+    rejected = datagen.round_bf16(rng.standard_normal((4 - accepted, 128)).astype(np.float32))
+    cache = torch.zeros_like(layer.idx_cache)
+    pooled = torch.zeros_like(layer.pooled)
+
+    def append(keys, lo):
+        pos = torch.arange(lo, lo + len(keys), dtype=torch.int64, device=DEV)
+        Q.qsa_append_pool(to_dev(np.ascontiguousarray(keys), "bf16"), pos, cache, pooled)
+
+    append(d["idx"][:n0], 0)
+    append(np.concatenate([d["idx"][n0:n0 + accepted], rejected]), n0)   # first verify
+    torch.cuda.synchronize()
+    last = n0 + (3 - n0) % 4              # the one position of the verify that ends a block
+    cb = last // 4                        # the block the first verify completed ...
+    assert last >= n0 + accepted          # ... holds a rejected key
+    stale = pooled[0, cb].clone()
+    append(d["idx"][n0 + accepted:n], n0 + accepted)                      # second verify
+    torch.cuda.synchronize()
+    nb = n // 4
+    assert not torch.equal(stale.view(torch.int32), pooled[0, cb].view(torch.int32)), "block not re-pooled"
+    assert torch.equal(cache[:, :n], layer.idx_cache[:, :n])
+    assert torch.equal(pooled[:, :nb].view(torch.int32), layer.pooled[:, :nb].view(torch.int32))
+    layer.idx_cache, layer.pooled = cache, pooled
+    res = layer.run()
+    say(_check_layer(d, res, layer))
+    _assert_candidate_path(res, layer)
+
+
 def test_row_without_visible_token_gives_zeros(Q):
     say("row at position -1")
     d = dict(datagen.gen_layer("tiny"))
