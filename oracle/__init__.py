@@ -11,9 +11,13 @@ from .qsa_oracle import (  # noqa: F401
     attend,
     attend_partitioned,
     attended_tokens,
+    dequantize_kv_fp8,
+    e4m3_decode,
+    e4m3_encode,
     merge_partials,
     n_blocks,
     pool_index_keys,
+    quantize_kv_fp8,
     qsa_row,
     score_blocks,
     select_blocks,

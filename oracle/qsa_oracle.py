@@ -24,7 +24,9 @@ IEEE round-to-nearest-even, no fused multiply-add).
 Pins (tests/test_oracle_pins.py) tie every function below to something other
 than itself: dense causal attention through torch SDPA, brute-force sorting,
 closed forms and hand-derived golden values.  No function here is
-"parity unpinned".
+"parity unpinned".  The fp8 K/V functions at the end follow the same page,
+section 03 ("State formats"), and are pinned to torch's own float8_e4m3fn
+conversions.
 """
 from __future__ import annotations
 
@@ -183,3 +185,68 @@ def attend_partitioned(q_row, k, v, tokens, scale, parts) -> tuple[np.ndarray, n
     for i, p in enumerate(parts):
         outs[i], lses[i] = attend(q_row, k, v, np.asarray(tokens)[np.asarray(p, dtype=np.int64)], scale)
     return merge_partials(lses, outs)
+
+
+# ----------------------------------------------------------- fp8 K/V state
+# hipfire page, section 03, "State formats": the fp8 state stores K and V as
+# E4M3 with one f16 scale per head and token, index keys staying bf16.  The
+# page names the format only.  Readings: E4M3 is the OCP "FN" variant (bias
+# 7, no infinities, largest finite value 448, S.1111.111 is NaN); a row's
+# scale is its largest magnitude divided by 448 in float32, rounded to f16;
+# each code is the E4M3 value nearest to the float32 quotient x / scale, ties
+# to the even code, magnitudes above 448 saturating to 448; a row whose scale
+# rounds to zero stores zero codes.
+
+E4M3_MAX = 448.0
+F16_MAX = 65504.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 value of each E4M3 code (uint8), from the format's fields:
+    sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+    subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_GRID = e4m3_decode(np.arange(127, dtype=np.uint8))  # codes 0..126, ascending magnitudes
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Code (uint8) of the E4M3 value nearest to each finite ``y``: ties go to
+    the even code, magnitudes above 448 saturate to 448 (code 0x7e), and the
+    sign bit is the input's (-0 and negative values that round to zero give
+    0x80)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    lo = np.searchsorted(_E4M3_GRID, a, side="right") - 1   # largest grid value <= a
+    hi = np.minimum(lo + 1, len(_E4M3_GRID) - 1)
+    d_lo = a - _E4M3_GRID[lo]
+    d_hi = _E4M3_GRID[hi] - a
+    up = (hi != lo) & ((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)))
+    code = np.where(up, hi, lo).astype(np.int64)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_kv_fp8(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """E4M3 codes and f16 scales of the rows of ``x`` [..., D] (float32, or
+    bf16-exact float32): one scale per row, i.e. per head and token."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float16)
+    scale = np.where(np.isinf(scale), np.float16(F16_MAX), scale)
+    sf = scale.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(sf > 0, x / np.where(sf > 0, sf, np.float32(1.0)), np.float32(0.0))
+    return e4m3_encode(y), scale
+
+
+def dequantize_kv_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """float64 K or V rows from E4M3 codes [..., D] and f16 scales [...]."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+

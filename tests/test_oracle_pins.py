@@ -333,3 +333,81 @@ def test_datagen_bf16_exact_and_shapes():
     for sp in specs:
         assert 4096 <= sp.n_ctx <= 131072 and 1 <= len(sp.seg_len) <= 5
         assert sum(sp.seg_len) == sp.n_ctx and sp.seg_start[0] == 0
+
+
+# ------------------------------------------------------- fp8 K/V (NEXT: fp8 state)
+
+def test_e4m3_decode_all_codes_match_torch():
+    """All 256 E4M3 codes decode as torch's float8_e4m3fn does (NaN at 0x7f/0xff)."""
+    c = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(c).view(torch.float8_e4m3fn).to(F64).numpy()
+    got = O.e4m3_decode(c)
+    assert np.array_equal(got, want, equal_nan=True)
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_including_ties():
+    """Nearest value, ties to the even code: against torch's float8_e4m3fn cast on
+    random values over every binade, the grid values and the exact midpoints."""
+    grid = O.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(11)
+    mags = rng.choice([2.0 ** -11, 2.0 ** -7, 0.01, 0.3, 1.0, 7.0, 60.0, 300.0], 20000)
+    rnd = rng.standard_normal(20000) * mags
+    y = np.concatenate([grid, -grid, mids, -mids, rnd, [0.0, -0.0, 2.0 ** -10, -2.0 ** -10]])
+    y = np.clip(y, -448.0, 448.0).astype(np.float32)
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(y), want)
+    # midpoints do split between the two neighbours (ties are exercised)
+    codes = O.e4m3_encode(mids.astype(np.float32))
+    assert np.all(codes % 2 == 0) and len(set(codes.tolist())) > 60
+
+
+def test_e4m3_encode_saturates():
+    """Finite magnitudes above 448 saturate to +-448 (codes 0x7e / 0xfe)."""
+    y = np.array([448.0, 449.0, 464.0, 479.9, 480.0, 1e4, 3e38], dtype=np.float32)
+    assert np.all(O.e4m3_encode(y) == 0x7E)
+    assert np.all(O.e4m3_encode(-y) == 0xFE)
+
+
+def test_quantize_kv_fp8_matches_torch_recipe():
+    """Per-row scale = f16(amax / 448) and codes = E4M3(x / scale), both through
+    torch (float32 quotients, torch's f16 and float8_e4m3fn casts)."""
+    rng = np.random.default_rng(5)
+    x = datagen.round_bf16(rng.standard_normal((64, 256)).astype(np.float32))
+    x[3] *= 1e-3
+    x[4] *= 1e-6            # scale in the f16 subnormal range
+    x[5] = 0.0              # zero row
+    x[6, 7] = 56.0          # an amax whose scale is exact (0.125)
+    x[6] = np.clip(x[6], -56.0, 56.0)
+    codes, scale = O.quantize_kv_fp8(x)
+    xt = torch.from_numpy(x)
+    amax = xt.abs().amax(dim=-1)
+    s = (amax / torch.tensor(448.0)).to(torch.float16)
+    sf = s.to(torch.float32)[:, None]
+    y = torch.where(sf > 0, xt / torch.where(sf > 0, sf, torch.ones_like(sf)), torch.zeros_like(xt))
+    want_codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(scale.view(np.uint16), s.numpy().view(np.uint16))
+    assert np.array_equal(codes, want_codes)
+    assert codes[6, 7] == 0x7E and scale[6] == np.float16(0.125)
+    assert scale[5] == 0 and np.all(codes[5] == 0)
+
+
+def test_quantize_kv_fp8_closed_forms():
+    """Sign symmetry, the largest magnitude maps to about 448, the round trip is
+    within half an E4M3 step, and a scale that overflows f16 clamps to 65504."""
+    rng = np.random.default_rng(9)
+    x = datagen.round_bf16(rng.standard_normal((32, 128)).astype(np.float32) * 3.0)
+    c, s = O.quantize_kv_fp8(x)
+    cn, sn = O.quantize_kv_fp8(-x)
+    assert np.array_equal(s, sn)
+    assert np.array_equal(cn, c ^ 0x80)
+    r = O.dequantize_kv_fp8(c, s)
+    sd = s.astype(np.float64)[:, None]
+    # E4M3: 3 mantissa bits (relative half-step 2^-4), subnormal step 2^-9
+    assert np.all(np.abs(r - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * sd) * (1 + 1e-6))
+    top = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(O.e4m3_decode(c[np.arange(32), top])) >= 416.0)
+    big = np.full((1, 16), 3.0e7, np.float32)
+    cb, sb = O.quantize_kv_fp8(big)
+    assert sb[0] == np.float16(65504.0) and np.all(cb == 0x7E)
