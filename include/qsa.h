@@ -59,6 +59,13 @@ typedef enum {
 
 typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
 
+/* K/V storage formats (qsa_kv_segments.kv_format).  QSA_KV_FP8_E4M3 is the
+ * fp8 state of the hipfire page, section 03 ("State formats"): E4M3 K and V
+ * (OCP E4M3FN: bias 7, largest finite 448, no infinities) with one f16 scale
+ * per KV head and token; a row's values are code * scale. */
+#define QSA_KV_SAME 0      /* K/V in the query dtype */
+#define QSA_KV_FP8_E4M3 1  /* E4M3 codes + f16 scales; queries bf16 */
+
 /*
  * qsa_append_pool -- write index keys in place and pool completed blocks.
  *
@@ -170,14 +177,18 @@ typedef struct qsa_kv_segments {
   int32_t n_seq;                /* sequences described (>= 1) */
   int32_t n_seg_total;          /* segments over all sequences (>= n_seq) */
   int32_t max_seg_per_seq;      /* host bound, 1..QSA_MAX_SEGMENTS */
-  int32_t reserved;
+  int32_t kv_format;            /* QSA_KV_SAME or QSA_KV_FP8_E4M3 */
   const int32_t* seq_seg_begin; /* int32 [n_seq+1]: sequence s owns segments
                                    seq_seg_begin[s] .. seq_seg_begin[s+1]-1 */
   const int64_t* seg_start;     /* int64 [n_seg_total]: first logical token held */
   const int64_t* seg_len;       /* int64 [n_seg_total]: tokens held */
   const int64_t* seg_cap;       /* int64 [n_seg_total]: token stride between KV heads */
-  const void* const* k_seg;     /* [n_seg_total] -> K [hkv][seg_cap][head_dim] dtype */
-  const void* const* v_seg;     /* [n_seg_total] -> V [hkv][seg_cap][head_dim] dtype */
+  const void* const* k_seg;     /* [n_seg_total] -> K [hkv][seg_cap][head_dim] dtype
+                                   (QSA_KV_FP8_E4M3: uint8 codes) */
+  const void* const* v_seg;     /* [n_seg_total] -> V, same layout */
+  const uint16_t* const* k_scale_seg; /* QSA_KV_FP8_E4M3: [n_seg_total] -> f16 bits
+                                   [hkv][seg_cap], the scale of each K row; else NULL */
+  const uint16_t* const* v_scale_seg; /* the same for V */
 } qsa_kv_segments;
 
 /*
@@ -205,6 +216,12 @@ typedef struct qsa_kv_segments {
  * Row m reads tokens 4b..4b+3 of every kept block b plus its tail tokens
  * 4*nb..p; query head h uses KV head h / (hq/hkv).  Logits, softmax and
  * partial outputs are float32; the output is rounded once to dtype.
+ *
+ * With kv->kv_format == QSA_KV_FP8_E4M3 (dtype QSA_BF16 only) K and V are
+ * E4M3 codes with f16 row scales (see qsa_quantize_kv_fp8): a logit is
+ * scale_k(t) * (q . code_k(t)) * scale, and token t's softmax weight is
+ * multiplied by scale_v(t) before it meets V's codes (rounded to bf16 as the
+ * weights of the bf16 path are).
  */
 int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
                       int32_t head_dim, float scale,
@@ -213,6 +230,35 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
                       const int32_t* sel, const int32_t* n_sel, int32_t k_blocks,
                       void* out, float* lse,
                       void* workspace, size_t workspace_bytes, qsa_stream_t stream);
+
+/*
+ * qsa_quantize_kv_fp8 -- write K or V rows into an fp8 (E4M3 + f16 scale)
+ * cache.
+ *
+ * Page: hipfire "QSA sparse attention ...", section 03, "State formats"
+ * (fp8 state: E4M3 K/V with an f16 scale per head and token, index keys
+ * staying bf16).  The page gives the format only; the rule here:
+ *   scale = f16(amax / 448), amax the row's largest magnitude, the quotient
+ *   in float32 and rounded to nearest even (an f16 overflow clamps to
+ *   65504); code = E4M3 value nearest to the float32 quotient x / scale,
+ *   ties to the even code, magnitudes above 448 saturating to 448, the sign
+ *   bit copied from x; a row whose scale rounds to zero gets zero codes.
+ *
+ *  src       bf16 rows: row (h, t) at src + (h * src_head_stride + t) * head_dim
+ *  n_head, n_tok >= 0   rows written: n_head * n_tok
+ *  head_dim  128 or 256
+ *  dst       uint8 codes: row (h, t) at dst + (h * dst_head_stride + t) * head_dim
+ *  dst_scale f16 bits: scale of row (h, t) at dst_scale[h * dst_head_stride + t]
+ *  src_head_stride >= n_tok, dst_head_stride >= n_tok (in rows)
+ * src and dst 16-byte aligned, dst_scale 2-byte aligned; the caller owns
+ * every buffer.  Typical use: the new tokens' K of one layer, [hkv][T][D],
+ * written at token t0 of a segment [hkv][cap][D]: dst = seg + t0 * head_dim,
+ * dst_scale = seg_scale + t0, dst_head_stride = cap.  In place, nothing
+ * allocated.  NaN or infinite inputs give undefined codes.
+ */
+int qsa_quantize_kv_fp8(const void* src, int32_t n_head, int32_t n_tok, int32_t head_dim,
+                        int64_t src_head_stride, void* dst, uint16_t* dst_scale,
+                        int64_t dst_head_stride, qsa_stream_t stream);
 
 /* Workspace bytes qsa_select_topk needs for up to max_M rows of up to
  * nb_max blocks (0 means no workspace is needed).  The workspace is one

@@ -25,6 +25,8 @@ QSA_ERR_LAUNCH = -4
 QSA_ERR_DEVICE = -5
 QSA_F32 = 0
 QSA_BF16 = 1
+QSA_KV_SAME = 0
+QSA_KV_FP8_E4M3 = 1
 INDEX_DIM = 128
 INDEX_HEADS = 4
 BLOCK_TOKENS = 4
@@ -33,8 +35,8 @@ MAX_SEGMENTS = 16
 
 EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes", "qsa_device_check",
-    "qsa_last_error", "qsa_version",
+    "qsa_quantize_kv_fp8", "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes",
+    "qsa_device_check", "qsa_last_error", "qsa_version",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -54,9 +56,9 @@ class QsaKvSegments(ctypes.Structure):
     """ctypes mirror of ``qsa_kv_segments`` (include/qsa.h)."""
 
     _fields_ = [
-        ("n_seq", _I32), ("n_seg_total", _I32), ("max_seg_per_seq", _I32), ("reserved", _I32),
+        ("n_seq", _I32), ("n_seg_total", _I32), ("max_seg_per_seq", _I32), ("kv_format", _I32),
         ("seq_seg_begin", _P), ("seg_start", _P), ("seg_len", _P), ("seg_cap", _P),
-        ("k_seg", _P), ("v_seg", _P),
+        ("k_seg", _P), ("v_seg", _P), ("k_scale_seg", _P), ("v_scale_seg", _P),
     ]
 
 
@@ -65,6 +67,7 @@ _lib.qsa_score_blocks.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, 
 _lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ, _I32, _P]
 _lib.qsa_gathered_attn.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P, _SZ, _P]
+_lib.qsa_quantize_kv_fp8.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
 _lib.qsa_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
 _lib.qsa_select_workspace_bytes.restype = _SZ
 _lib.qsa_attn_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
@@ -73,7 +76,7 @@ _lib.qsa_device_check.argtypes = []
 _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-           "qsa_device_check"):
+           "qsa_quantize_kv_fp8", "qsa_device_check"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -189,16 +192,22 @@ class KvSegments:
     """Device segment table of a batch of sequences for ``qsa_gathered_attn``.
 
     ``segments[s]`` is a list of (start, length, K, V) for sequence s, with
-    K/V tensors [hkv, cap, head_dim] (cap >= length).  The tensors must stay
-    alive (and in place) while the table is used; the table keeps references.
+    K/V tensors [hkv, cap, head_dim] (cap >= length) in the query dtype, or
+    (start, length, K, V, K_scale, V_scale) for fp8 K/V: uint8 E4M3 codes
+    [hkv, cap, head_dim] and float16 scales [hkv, cap] (see
+    ``qsa_quantize_kv_fp8``).  The tensors must stay alive (and in place)
+    while the table is used; the table keeps references.
     """
 
     def __init__(self, segments: list, device=None):
         dev = device or segments[0][0][2].device
         self._keep = []
-        begin, starts, lens, caps, kp, vp = [0], [], [], [], [], []
+        begin, starts, lens, caps, kp, vp, ksp, vsp = [0], [], [], [], [], [], [], []
+        fp8 = len(segments[0][0]) == 6
         for segs in segments:
-            for (st, ln, k, v) in segs:
+            for seg in segs:
+                _need(len(seg) == (6 if fp8 else 4), "all segments fp8 or none")
+                st, ln, k, v = seg[:4]
                 assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
                 starts.append(int(st))
                 lens.append(int(ln))
@@ -206,7 +215,17 @@ class KvSegments:
                 kp.append(k.data_ptr())
                 vp.append(v.data_ptr())
                 self._keep += [k, v]
+                if fp8:
+                    ks, vs = seg[4], seg[5]
+                    _need(k.dtype == torch.uint8 and ks.dtype == torch.float16 and vs.dtype == torch.float16,
+                          "fp8 segments: uint8 codes, float16 scales")
+                    _need(ks.is_contiguous() and vs.is_contiguous() and ks.shape == k.shape[:2] == vs.shape,
+                          "scale shape [hkv, cap]")
+                    ksp.append(ks.data_ptr())
+                    vsp.append(vs.data_ptr())
+                    self._keep += [ks, vs]
             begin.append(len(starts))
+        self.fp8 = fp8
         self.max_seg = max(len(s) for s in segments)
         self.seq_seg_begin = torch.tensor(begin, dtype=torch.int32, device=dev)
         self.seg_start = torch.tensor(starts, dtype=torch.int64, device=dev)
@@ -214,15 +233,39 @@ class KvSegments:
         self.seg_cap = torch.tensor(caps, dtype=torch.int64, device=dev)
         self.k_ptrs = torch.tensor(kp, dtype=torch.int64, device=dev)
         self.v_ptrs = torch.tensor(vp, dtype=torch.int64, device=dev)
+        self.ks_ptrs = torch.tensor(ksp, dtype=torch.int64, device=dev) if fp8 else None
+        self.vs_ptrs = torch.tensor(vsp, dtype=torch.int64, device=dev) if fp8 else None
         self.struct = QsaKvSegments(
-            len(segments), len(starts), self.max_seg, 0,
+            len(segments), len(starts), self.max_seg, QSA_KV_FP8_E4M3 if fp8 else QSA_KV_SAME,
             self.seq_seg_begin.data_ptr(), self.seg_start.data_ptr(), self.seg_len.data_ptr(),
-            self.seg_cap.data_ptr(), self.k_ptrs.data_ptr(), self.v_ptrs.data_ptr())
+            self.seg_cap.data_ptr(), self.k_ptrs.data_ptr(), self.v_ptrs.data_ptr(),
+            self.ks_ptrs.data_ptr() if fp8 else None, self.vs_ptrs.data_ptr() if fp8 else None)
 
     @classmethod
-    def single(cls, k: torch.Tensor, v: torch.Tensor, length: int | None = None):
-        """One sequence held in one [hkv, cap, D] buffer."""
-        return cls([[(0, k.shape[1] if length is None else length, k, v)]])
+    def single(cls, k: torch.Tensor, v: torch.Tensor, length: int | None = None,
+               k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None):
+        """One sequence held in one [hkv, cap, D] buffer (fp8: with its scales)."""
+        n = k.shape[1] if length is None else length
+        if k_scale is not None:
+            return cls([[(0, n, k, v, k_scale, v_scale)]])
+        return cls([[(0, n, k, v)]])
+
+
+def qsa_quantize_kv_fp8(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.Tensor, t0: int = 0,
+                        stream=None) -> None:
+    """E4M3 codes and f16 scales of ``src`` [n_head, T, D] bf16 written to rows
+    t0 .. t0+T-1 of ``dst`` uint8 [n_head, cap, D] and ``dst_scale`` float16
+    [n_head, cap]."""
+    _need(src.dtype == torch.bfloat16 and dst.dtype == torch.uint8 and dst_scale.dtype == torch.float16,
+          "src bf16, dst uint8, dst_scale float16")
+    _need(src.is_contiguous() and dst.is_contiguous() and dst_scale.is_contiguous(), "tensors must be contiguous")
+    h, t, d = src.shape
+    _need(dst.dim() == 3 and dst.shape[0] == h and dst.shape[2] == d and dst_scale.shape == dst.shape[:2],
+          "dst [n_head, cap, D], dst_scale [n_head, cap]")
+    cap = dst.shape[1]
+    _need(0 <= t0 and t0 + t <= cap, "rows t0..t0+T-1 must lie inside the cache")
+    _check(_lib.qsa_quantize_kv_fp8(_ptr(src), h, t, d, t, dst.data_ptr() + t0 * d,
+                                    dst_scale.data_ptr() + 2 * t0, cap, _stream(stream)))
 
 
 def qsa_gathered_attn(q: torch.Tensor, row_pos: torch.Tensor, kv: KvSegments, sel: torch.Tensor,

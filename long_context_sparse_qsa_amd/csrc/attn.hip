@@ -63,6 +63,8 @@ struct KvArgs {
   const int64_t* seg_cap;
   const void* const* k_seg;
   const void* const* v_seg;
+  const uint16_t* const* k_scale;  // fp8 K/V: f16 row scales per segment
+  const uint16_t* const* v_scale;
   int n_seq;
   int n_seg_total;
 };
@@ -71,6 +73,8 @@ struct SegDesc {
   int64_t lo, hi, cap;
   const unsigned char* k;
   const unsigned char* v;
+  const uint16_t* ks;  // fp8 K/V only
+  const uint16_t* vs;
 };
 
 // Element-type specific constants of the tile loop.
@@ -456,8 +460,35 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 //   4. PV with packed bf16 dot2 from the wave's V rows, pair-interleaved in
 //      LDS: lane = D/64 dims of all 12 heads, float32 accumulation.
 // At the end the four wave partials are merged by log-sum-exp in LDS.
+//
+// F8: K/V are E4M3 codes with an f16 scale per KV head and token (the fp8
+// state of the hipfire page, section 03).  Rows are D bytes; a lane reads
+// 16 contiguous K bytes per pair of k-steps, so k-step s of lane quad g4
+// covers dims 64 (s / 2) + 16 g4 + 8 (s % 2) .. + 7, and the query operand is
+// loaded with the same dim permutation (the dot product is unchanged).  The
+// codes become bf16 exactly; token t's logits are multiplied by its K scale,
+// and its softmax weight by its V scale before the bf16 rounding that PV
+// consumes (the normaliser sums the unscaled weights).  V goes to LDS as
+// bf16 pairs like the bf16 path.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// E4M3 codes -> bf16.  Every E4M3 value (4 significant bits, exponents
+// 2^-9 .. 2^8) is exact in bf16, so the hardware conversion to float32
+// followed by dropping the low 16 bits loses nothing.
+__device__ __forceinline__ uint32_t bf16_pair_of(f32x2_t v) {
+  return __builtin_amdgcn_perm(__float_as_uint(v.y), __float_as_uint(v.x), 0x07060302u);
+}
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return make_uint4(bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false)),
+                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true)),
+                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false)),
+                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true)));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
 
 __device__ __forceinline__ const unsigned char* shfl_ptr(const unsigned char* p, int src) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -499,7 +530,7 @@ struct MfmaLds {
   }
 };
 
-template <int D, int NW>
+template <int D, int NW, bool F8>
 __global__ void __launch_bounds__(kWave * NW)
 attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2,
                  const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
@@ -509,9 +540,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
                  float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int KS = D / 32;               // QK k-steps
   constexpr int DPL = D / kWave;           // PV dims per lane
-  constexpr int VCH = D * 2 / 16;          // 16-byte chunks per V row
+  constexpr int kRowBytes = F8 ? D : D * 2;
+  constexpr int VCH = kRowBytes / 16;      // 16-byte chunks per V row
   constexpr int VIT = 8 * VCH / kWave;     // (token pair, chunk) V items per lane
-  constexpr int kRowBytes = D * 2;
+  constexpr int KL = F8 ? KS / 2 : KS;     // 16-byte K loads per lane
   static_assert(kWave % VCH == 0 || VCH % kWave == 0, "V item mapping");
   using Lds = MfmaLds<D>;
   extern __shared__ __align__(16) uint32_t lds[];
@@ -545,7 +577,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       q + ((int64_t)m * hq + (int64_t)g * kGroup + (n16 < kGroup ? n16 : 0)) * D);
   uint4 qraw[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qraw[s] = ldg16(qh + (32 * s + 8 * g4) * 2);
+  for (int s = 0; s < KS; ++s) {
+    const int dim = F8 ? 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : 32 * s + 8 * g4;
+    qraw[s] = ldg16(qh + dim * 2);
+  }
   int si_lo = 0, nseg_all = 0;
   if (kv.n_seq == 1) {
     nseg_all = kv.n_seg_total < kMaxSegments ? kv.n_seg_total : kMaxSegments;
@@ -567,6 +602,10 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     mine.cap = kv.seg_cap[si];
     mine.k = static_cast<const unsigned char*>(kv.k_seg[si]);
     mine.v = static_cast<const unsigned char*>(kv.v_seg[si]);
+    if constexpr (F8) {
+      mine.ks = kv.k_scale[si];
+      mine.vs = kv.v_scale[si];
+    }
   }
   if (tid < nseg_all) segs[tid] = mine;
   if (tid == 0) nseg_sh = nseg_all;
@@ -616,20 +655,31 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     }
     const unsigned char* kr = qh;  // any readable address; masked below
     const unsigned char* vr = qh;
+    const uint16_t* ksp = reinterpret_cast<const uint16_t*>(qh);
+    const uint16_t* vsp = ksp;
     int ok = 0;
     for (int si = 0; si < nseg; ++si) {
       const SegDesc sd = segs[si];
       const int64_t rel = tok - sd.lo;
       const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !ok;
-      const int64_t off = ((int64_t)g * sd.cap + rel) * kRowBytes;
-      kr = hit ? sd.k + off : kr;
-      vr = hit ? sd.v + off : vr;
+      const int64_t row = (int64_t)g * sd.cap + rel;
+      kr = hit ? sd.k + row * kRowBytes : kr;
+      vr = hit ? sd.v + row * kRowBytes : vr;
+      if constexpr (F8) {
+        ksp = hit ? sd.ks + row : ksp;
+        vsp = hit ? sd.vs + row : vsp;
+      }
       ok |= hit ? 1 : 0;
     }
     // K operand rows: all k-steps
-    uint4 kb[KS];
+    uint4 kb[KL];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kb[s] = ldg16(kr + (32 * s + 8 * g4) * 2);
+    for (int s = 0; s < KL; ++s) kb[s] = ldg16(kr + (F8 ? 64 * s + 16 * g4 : (32 * s + 8 * g4) * 2));
+    uint32_t ks_bits = 0, vs_bits = 0;
+    if constexpr (F8) {
+      ks_bits = *ksp;
+      vs_bits = *vsp;
+    }
     // V items: (pair pp, chunk c) of the slice's token pairs
     uint4 va[VIT], vb[VIT];
     int vok[VIT];
@@ -652,25 +702,41 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 
     // 2. QK: sacc[v] = q[head 4 g4 + v] . K[token n16]
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F8) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, x), sacc, 0, 0, 0);
+      for (int s = 0; s < KL; ++s) {
+        const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
+        const uint4 lo = fp8x8_to_bf16x8(x.x, x.y);
+        const uint4 hi = fp8x8_to_bf16x8(x.z, x.w);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s], __builtin_bit_cast(bf16x8_t, lo), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s + 1], __builtin_bit_cast(bf16x8_t, hi), sacc, 0, 0,
+                                                       0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, x), sacc, 0, 0, 0);
+      }
     }
+    // fp8: this lane's token scales (0 for a masked token)
+    const float k_sc = F8 ? (ok ? f16_bits_to_f32(ks_bits) : 0.f) : 1.f;
+    const float v_sc = F8 ? (ok ? f16_bits_to_f32(vs_bits) : 0.f) : 1.f;
 
     // 3. online softmax per head over the row's 16 tokens
     float alpha[4];
     uint32_t pw[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float s2 = ok ? sacc[v] * scale_log2 : -INFINITY;
+      const float s2 = ok ? (F8 ? sacc[v] * k_sc : sacc[v]) * scale_log2 : -INFINITY;
       const float m_new = fmaxf(m_run[v], row16_max(s2));
       alpha[v] = (m_run[v] == m_new) ? 1.f : exp2f(m_run[v] - m_new);
       const float pv = (s2 == -INFINITY) ? 0.f : exp2f(s2 - m_new);
       const uint32_t pb = f32_to_bf16_bits(pv);  // PV consumes bf16: normalise by the same values
       l_run[v] = l_run[v] * alpha[v] + row16_sum(__uint_as_float(pb << 16));
       m_run[v] = m_new;
-      pw[v] = pb | ((uint32_t)__shfl_xor((int)pb, 1, kWave) << 16);
+      const uint32_t pbv = F8 ? (uint32_t)f32_to_bf16_bits(pv * v_sc) : pb;  // fp8: V's scale joins the weight
+      pw[v] = pbv | ((uint32_t)__shfl_xor((int)pbv, 1, kWave) << 16);
     }
     if ((n16 & 1) == 0 && g4 < 3)
       *reinterpret_cast<uint4*>(pl + (n16 >> 1) * kGroup + 4 * g4) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
@@ -682,11 +748,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       const int c = item % VCH;
       const uint4 a = (vok[u] & 1) ? va[u] : make_uint4(0, 0, 0, 0);
       const uint4 b = (vok[u] & 2) ? vb[u] : make_uint4(0, 0, 0, 0);
-      uint4 lo, hi;
-      interleave(a, b, lo, hi);
-      uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 8);
-      dst[0] = lo;
-      dst[1] = hi;
+      if constexpr (F8) {  // 16 codes of each token: dims 16 c .. 16 c + 15
+        uint4 lo, hi, lo2, hi2;
+        interleave(fp8x8_to_bf16x8(a.x, a.y), fp8x8_to_bf16x8(b.x, b.y), lo, hi);
+        interleave(fp8x8_to_bf16x8(a.z, a.w), fp8x8_to_bf16x8(b.z, b.w), lo2, hi2);
+        uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 16);
+        dst[0] = lo;
+        dst[1] = hi;
+        dst[2] = lo2;
+        dst[3] = hi2;
+      } else {
+        uint4 lo, hi;
+        interleave(a, b, lo, hi);
+        uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 8);
+        dst[0] = lo;
+        dst[1] = hi;
+      }
     }
     // rescale by every head's alpha (head h sits in row h / 4, slot h % 4)
 #pragma unroll
@@ -843,7 +920,7 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot);
 }
 
-template <class E, int D>
+template <class E, int D, bool F8 = false>
 hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
                         const int64_t* row_pos, const int32_t* row_seq, const KvArgs& kv,
                         const int32_t* sel, const int32_t* n_sel, int k_blocks, void* out,
@@ -858,7 +935,7 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
     const size_t lds = MfmaLds<D>::bytes(plan.waves);
 #define QSA_MFMA_LAUNCH(W)                                                                              \
   case W:                                                                                             \
-    hipLaunchKernelGGL((attn_mfma_kernel<D, W>), grid, block, lds, stream,                            \
+    hipLaunchKernelGGL((attn_mfma_kernel<D, W, F8>), grid, block, lds, stream,                        \
                        static_cast<const uint16_t*>(q), M, hq, scale * kLog2e, row_pos, row_seq, kv,  \
                        sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,                       \
                        static_cast<uint16_t*>(out), lse, ws_o, ws_lse);                               \
@@ -963,8 +1040,15 @@ hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv
   a.seg_cap = kv->seg_cap;
   a.k_seg = kv->k_seg;
   a.v_seg = kv->v_seg;
+  a.k_scale = kv->k_scale_seg;
+  a.v_scale = kv->v_scale_seg;
   a.n_seq = kv->n_seq;
   a.n_seg_total = kv->n_seg_total;
+  if (kv->kv_format == QSA_KV_FP8_E4M3) {  // bf16 queries (validated by the caller)
+    if (head_dim == 256)
+      return launch_typed<BF16, 256, true>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+    return launch_typed<BF16, 128, true>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+  }
   if (dtype == QSA_BF16) {
     if (head_dim == 256)
       return launch_typed<BF16, 256>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);

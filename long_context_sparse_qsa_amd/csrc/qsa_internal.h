@@ -51,6 +51,11 @@ AttnPlan attn_plan(int M, int hkv, int k_blocks);
 AttnPlan attn_plan_valu(int M, int hkv, int k_blocks);
 size_t attn_workspace_bytes(int max_M, int hq, int head_dim, int k_blocks);
 
+// fp8 K/V cache writes (kv_fp8.hip).
+hipError_t launch_quantize_kv_fp8(const void* src, int n_head, int n_tok, int head_dim, int64_t src_head_stride,
+                                  uint8_t* dst, uint16_t* dst_scale, int64_t dst_head_stride,
+                                  hipStream_t stream);
+
 hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv, int head_dim,
                                 float scale, const int64_t* row_pos, const int32_t* row_seq,
                                 const qsa_kv_segments* kv, const int32_t* sel,

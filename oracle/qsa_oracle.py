@@ -238,7 +238,8 @@ def quantize_kv_fp8(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     bf16-exact float32): one scale per row, i.e. per head and token."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x), axis=-1)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float16)
+    with np.errstate(over="ignore"):  # an f16 overflow is clamped just below
+        scale = (amax / np.float32(E4M3_MAX)).astype(np.float16)
     scale = np.where(np.isinf(scale), np.float16(F16_MAX), scale)
     sf = scale.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):

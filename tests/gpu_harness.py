@@ -32,7 +32,8 @@ def round_up(a: int, b: int) -> int:
 class Layer:
     """One sequence's QSA layer state on the device, filled from host data."""
 
-    def __init__(self, d: dict, capacity: int | None = None, prefix_split: int | None = None):
+    def __init__(self, d: dict, capacity: int | None = None, prefix_split: int | None = None,
+                 kv: str = "same"):
         import long_context_sparse_qsa_amd as Q
 
         wl = d["workload"]
@@ -58,6 +59,15 @@ class Layer:
         self.k[:, :n] = to_dev(d["k"], wl.dtype)
         self.v[:, :n] = to_dev(d["v"], wl.dtype)
         self.kv = Q.KvSegments.single(self.k, self.v, n)
+        self.kv_mode = kv
+        if kv == "fp8":  # E4M3 codes + f16 scales, quantized on the device
+            self.k8 = torch.zeros((wl.hkv, self.cap, wl.head_dim), dtype=torch.uint8, device=DEV)
+            self.v8 = torch.zeros_like(self.k8)
+            self.ks = torch.zeros((wl.hkv, self.cap), dtype=torch.float16, device=DEV)
+            self.vs = torch.zeros_like(self.ks)
+            Q.qsa_quantize_kv_fp8(to_dev(d["k"], "bf16"), self.k8, self.ks)
+            Q.qsa_quantize_kv_fp8(to_dev(d["v"], "bf16"), self.v8, self.vs)
+            self.kv = Q.KvSegments.single(self.k8, self.v8, n, self.ks, self.vs)
         self.q = to_dev(d["q"], wl.dtype)
         self.idx_q = to_dev(d["idx_q"], wl.dtype)
         self.rows = torch.from_numpy(d["rows"]).to(DEV)
@@ -131,6 +141,31 @@ def check_selection(sel_gpu: np.ndarray, n_sel_gpu: int, scores64: np.ndarray, k
     return {"band": int(band.sum()), "diff_in_band": len(g ^ o)}
 
 
+def check_attention_fp8(out_gpu: np.ndarray, lse_gpu: np.ndarray, layer, row_i: int, sel: np.ndarray):
+    """fp8 K/V: the device cache holds the oracle's codes and scales for every
+    attended token (bit for bit), and attention matches fp64 attention over
+    the oracle's dequantized rows within the bf16 tolerances."""
+    d = layer.d
+    wl = d["workload"]
+    p = int(d["rows"][row_i])
+    tok = O.attended_tokens(sel, p + 1)
+    ti = torch.from_numpy(tok).to(DEV)
+    deq = []
+    for src, codes, sc in ((d["k"], layer.k8, layer.ks), (d["v"], layer.v8, layer.vs)):
+        c_ref, s_ref = O.quantize_kv_fp8(src[:, tok])
+        assert np.array_equal(codes[:, ti].cpu().numpy(), c_ref), "fp8 codes differ from the oracle"
+        assert np.array_equal(sc[:, ti].cpu().numpy().view(np.uint16), s_ref.view(np.uint16)), "fp8 scales differ"
+        deq.append(O.dequantize_kv_fp8(c_ref, s_ref))
+    ref, ref_lse = O.attend(d["q"][row_i], deq[0], deq[1], np.arange(len(tok)), 1.0 / math.sqrt(wl.head_dim))
+    err = float(np.max(np.abs(out_gpu - ref)))
+    lerr = float(np.max(np.abs(lse_gpu - ref_lse)))
+    # as for bf16 K/V (probabilities rounded to bf16), plus one more bf16
+    # rounding of each weight times its V scale
+    assert err <= 2e-2, f"attention max-abs {err} > 2e-2"
+    assert lerr <= 2.5e-3, f"lse max-abs {lerr} > 2.5e-3"
+    return err, lerr
+
+
 def check_attention(out_gpu: np.ndarray, lse_gpu: np.ndarray, d: dict, row_i: int,
                     sel: np.ndarray, dtype: str):
     """Recompute attention in fp64 over the GPU's own selection (plus tail)."""
@@ -148,3 +183,54 @@ def check_attention(out_gpu: np.ndarray, lse_gpu: np.ndarray, d: dict, row_i: in
     assert err <= tol, f"attention max-abs {err} > {tol}"
     assert lerr <= ltol, f"lse max-abs {lerr} > {ltol}"
     return err, lerr
+
+
+def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
+    """Pooling bit-exact, scores within the fp64 band, selection exact on the
+    GPU's scores and equal to the oracle's outside the band, attention within
+    tolerance over the GPU's selection (fp8 K/V: over the oracle's
+    dequantized rows).  Returns per-row statistics."""
+    wl = d["workload"]
+    k = k or wl.k_blocks
+    n = d["idx"].shape[0]
+    # index keys copied bit for bit; pooled keys bit-exact
+    cache = layer.idx_cache[0, :n].float().cpu().numpy()
+    assert np.array_equal(cache, d["idx"])
+    pooled_gpu = layer.pooled[0, : n // 4].cpu().numpy()
+    pooled_ref = O.pool_index_keys(d["idx"])
+    assert np.array_equal(pooled_gpu.view(np.uint32), pooled_ref.view(np.uint32))
+    sc = res["scores"].cpu().numpy()
+    sel = res["sel"].cpu().numpy()
+    n_sel = res["n_sel"].cpu().numpy()
+    out = to_host_f32(res["out"])
+    lse = res["lse"].cpu().numpy()
+    rows = range(len(d["rows"])) if rows is None else rows
+    attn_rows = rows if attn_rows is None else attn_rows
+    stats = []
+    for i in rows:
+        p = int(d["rows"][i])
+        s64 = O.score_blocks(d["idx_q"][i], pooled_ref, p + 1)
+        nb = len(s64)
+        g32 = sc[i, :nb].astype(np.float64)
+        # scores: float32 accumulation against fp64
+        assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), float(np.max(np.abs(g32 - s64)))
+        # the select kernel is exact on its own input
+        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), "select != exact top-k of GPU scores"
+        st = check_selection(sel[i], int(n_sel[i]), s64, k)
+        if i in attn_rows and layer.kv_mode == "fp8":
+            err, lerr = check_attention_fp8(out[i], lse[i], layer, i, sel[i, : n_sel[i]])
+            st.update(err=err, lse_err=lerr)
+        elif i in attn_rows:
+            err, lerr = check_attention(out[i], lse[i], d, i, sel[i, : n_sel[i]], wl.dtype)
+            st.update(err=err, lse_err=lerr)
+        stats.append(st)
+    return stats
+
+
+def assert_candidate_path(res, layer, k=None):
+    """Every row longer than the budget was selected from the conservative
+    candidates (the exact whole-row fallback is correct but slow)."""
+    k = k or layer.wl.k_blocks
+    nb = (layer.rows.cpu().numpy() + 1) // 4
+    want = np.where(nb <= k, 1, 2)
+    assert np.array_equal(res["paths"], want), (res["paths"][:16], want[:16])

@@ -91,8 +91,10 @@ def test_select_validation(args, code, word):
     assert word in _err()
 
 
-def _kv(n_seq=1, n_seg=1, max_seg=1, null=False):
-    return Q.QsaKvSegments(n_seq, n_seg, max_seg, 0, None if null else FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+def _kv(n_seq=1, n_seg=1, max_seg=1, null=False, fmt=0, scales=False):
+    sc = FAKE if scales else None
+    return Q.QsaKvSegments(n_seq, n_seg, max_seg, fmt, None if null else FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           sc, sc)
 
 
 def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FAKE, wsb=1 << 30,
@@ -122,6 +124,37 @@ def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FA
 ])
 def test_attn_validation(kw, code, word):
     assert _attn(**kw) == code
+    assert word in _err()
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(kv=_kv(fmt=7)), ERR_ARG, "kv_format"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3)), ERR_ARG, "scale"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3, scales=True), dtype=0, d=128), Q.QSA_ERR_UNSUPPORTED, "bf16"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3, scales=True), wsb=0), Q.QSA_ERR_WORKSPACE, "workspace"),
+])
+def test_attn_fp8_validation(kw, code, word):
+    assert _attn(**kw) == code
+    assert word in _err()
+
+
+def _quant(src=FAKE, nh=2, nt=4, d=256, shs=4, dst=FAKE, dsc=FAKE, dhs=16):
+    return L.qsa_quantize_kv_fp8(src, nh, nt, d, shs, dst, dsc, dhs, None)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(nh=-1), ERR_ARG, "n_head"),
+    (dict(nt=-3), ERR_ARG, "n_tok"),
+    (dict(d=64), Q.QSA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(shs=3), ERR_ARG, "stride"),
+    (dict(dhs=2), ERR_ARG, "stride"),
+    (dict(src=None), ERR_ARG, "null"),
+    (dict(dst=FAKE + 8), ERR_ARG, "aligned"),
+    (dict(dsc=FAKE + 1), ERR_ARG, "aligned"),
+    (dict(nt=0, src=None, dst=None, dsc=None), Q.QSA_OK, ""),
+])
+def test_quantize_kv_fp8_validation(kw, code, word):
+    assert _quant(**kw) == code
     assert word in _err()
 
 

@@ -18,8 +18,9 @@ import oracle as O
 
 pytestmark = pytest.mark.gpu
 
-from gpu_harness import (DEV, Layer, check_attention, check_selection, to_dev,  # noqa: E402
-                         to_host_f32)
+from gpu_harness import DEV, Layer, check_attention, check_selection, to_dev, to_host_f32  # noqa: E402
+from gpu_harness import assert_candidate_path as _assert_candidate_path  # noqa: E402
+from gpu_harness import check_layer as _check_layer  # noqa: E402
 
 
 def say(*a):
@@ -33,41 +34,6 @@ def Q():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     Q.qsa_device_check()
     return Q
-
-
-def _check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
-    wl = d["workload"]
-    k = k or wl.k_blocks
-    n = d["idx"].shape[0]
-    # index keys copied bit for bit; pooled keys bit-exact
-    cache = layer.idx_cache[0, :n].float().cpu().numpy()
-    assert np.array_equal(cache, d["idx"])
-    pooled_gpu = layer.pooled[0, : n // 4].cpu().numpy()
-    pooled_ref = O.pool_index_keys(d["idx"])
-    assert np.array_equal(pooled_gpu.view(np.uint32), pooled_ref.view(np.uint32))
-    sc = res["scores"].cpu().numpy()
-    sel = res["sel"].cpu().numpy()
-    n_sel = res["n_sel"].cpu().numpy()
-    out = to_host_f32(res["out"])
-    lse = res["lse"].cpu().numpy()
-    rows = range(len(d["rows"])) if rows is None else rows
-    attn_rows = rows if attn_rows is None else attn_rows
-    stats = []
-    for i in rows:
-        p = int(d["rows"][i])
-        s64 = O.score_blocks(d["idx_q"][i], pooled_ref, p + 1)
-        nb = len(s64)
-        g32 = sc[i, :nb].astype(np.float64)
-        # scores: float32 accumulation against fp64
-        assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), float(np.max(np.abs(g32 - s64)))
-        # the select kernel is exact on its own input
-        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), "select != exact top-k of GPU scores"
-        st = check_selection(sel[i], int(n_sel[i]), s64, k)
-        if i in attn_rows:
-            err, lerr = check_attention(out[i], lse[i], d, i, sel[i, : n_sel[i]], wl.dtype)
-            st.update(err=err, lse_err=lerr)
-        stats.append(st)
-    return stats
 
 
 def test_tiny_fp32(Q):
@@ -105,15 +71,6 @@ def test_decode_32k_layers_differ(Q):
     d = datagen.gen_layer("decode_32k", layer=5)
     layer = Layer(d)
     say(_check_layer(d, layer.run(), layer))
-
-
-def _assert_candidate_path(res, layer, k=None):
-    """Every row longer than the budget was selected from the conservative
-    candidates (the exact whole-row fallback is correct but slow)."""
-    k = k or layer.wl.k_blocks
-    nb = (layer.rows.cpu().numpy() + 1) // 4
-    want = np.where(nb <= k, 1, 2)
-    assert np.array_equal(res["paths"], want), (res["paths"][:16], want[:16])
 
 
 def test_verify_262k_full_size(Q):
