@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 companion measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 K/V companion measurement")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (scales FETCH_SIZE / WRITE_SIZE)")
@@ -218,6 +219,72 @@ def cpu_baseline(wl_name: str, budget_s: float = 12.0) -> dict:
 
 # ------------------------------------------------------------------ main
 
+def fp8_leg(Q, L, sh, nb_max, wl, args, attn_bf16_us):
+    """The same layers with K/V in the fp8 state (E4M3 codes + f16 scale per
+    head and token), quantized on the device from the bf16 K/V: the whole
+    step through a graph, the attention launch beside the bf16 one, and the
+    quantize launch that writes one step's new K (or V) rows."""
+    import torch
+
+    for ly in L:
+        ly.k8 = torch.empty((wl.hkv, ly.cap, wl.head_dim), dtype=torch.uint8, device=ly.k.device)
+        ly.v8 = torch.empty_like(ly.k8)
+        ly.ks = torch.empty((wl.hkv, ly.cap), dtype=torch.float16, device=ly.k.device)
+        ly.vs = torch.empty_like(ly.ks)
+        Q.qsa_quantize_kv_fp8(ly.k, ly.k8, ly.ks)
+        Q.qsa_quantize_kv_fp8(ly.v, ly.v8, ly.vs)
+        ly.kv_bf16, ly.kv = ly.kv, Q.KvSegments.single(ly.k8, ly.v8, wl.n_ctx, ly.ks, ly.vs)
+        ly.new_k = ly.k[:, ly.rows[0]:ly.rows[0] + min(wl.m, 4)].contiguous()  # new K rows [hkv, T, D]
+    torch.cuda.synchronize()
+    run = step_fn(Q, L, sh, nb_max, wl)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    attn_us = per_launch_us(Q, L, sh, nb_max, wl, "attn")
+    # one step's K write: M rows x hkv heads quantized into the cache
+    t0 = int(wl.rows[0])
+    torch.cuda.synchronize()
+    try:  # queue every launch before the device reaches them (no host gaps in the interval)
+        torch.cuda._sleep(int(2e8))
+    except Exception:  # pragma: no cover
+        pass
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(4):
+        for ly in L:
+            Q.qsa_quantize_kv_fp8(ly.new_k, ly.k8, ly.ks, t0=t0)
+    b.record()
+    torch.cuda.synchronize()
+    quant_us = a.elapsed_time(b) * 1e3 / (4 * len(L))
+    tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
+    gather_fp8 = tok * wl.hkv * 2 * (wl.head_dim + 2)
+    gather_bf16 = tok * wl.hkv * 2 * wl.head_dim * 2
+    for ly in L:  # back to the bf16 state for whatever runs next
+        ly.kv = ly.kv_bf16
+        del ly.k8, ly.v8, ly.ks, ly.vs, ly.new_k
+    torch.cuda.synchronize()
+    return {"workload": wl.name + " fp8 K/V", "value": wl.m * len(L) * args.steps / (ms / 1e3),
+            "unit": "query-rows/s per layer", "ms_per_step": ms / args.steps,
+            "layer_us": ms * 1e3 / args.steps / len(L),
+            "attn_us": round(attn_us, 2), "attn_us_bf16": round(attn_bf16_us, 2),
+            "gather_bytes": gather_fp8, "gather_bytes_bf16": gather_bf16,
+            "quantize_us_per_kv_write": round(quant_us, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -323,6 +390,8 @@ def main():
                  "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                  "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}},
     }
+    if not args.no_fp8 and wl.name in ("verify_262k", "decode_262k", "decode_32k", "prefill"):
+        res["fp8"] = fp8_leg(Q, L, sh, nb_max, wl, args, kt["attn"])
     if not args.no_m1 and wl.name == "verify_262k":
         wl1 = datagen.WORKLOADS["decode_262k"]
         for ly in L:
