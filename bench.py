@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-m1", action="store_true", help="skip the M=1 companion measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 K/V companion measurement")
+    ap.add_argument("--no-flat", action="store_true", help="skip the memory-flat selection measurement (many rows)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (scales FETCH_SIZE / WRITE_SIZE)")
@@ -129,16 +130,22 @@ def build_single(Q, wl, layers, dev):
     return L, shared, nb_max
 
 
-def step_fn(Q, L, sh, nb_max, wl, only=None):
-    """Enqueue one step (all layers).  ``only`` restricts to one kernel family."""
+def step_fn(Q, L, sh, nb_max, wl, only=None, flat=False):
+    """Enqueue one step (all layers).  ``only`` restricts to one kernel family;
+    ``flat`` scores and selects through the memory-flat entry point."""
     def run():
         for ly in L:
             if only in (None, "append"):
                 Q.qsa_append_pool(ly.new_idx, ly.new_pos, ly.idx_cache, ly.pooled, seq=getattr(ly, "seq", None))
-            if only in (None, "score"):
+            if flat and only in (None, "flat"):
+                Q.qsa_score_select(ly.idx_q, ly.rows, ly.pooled, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"],
+                                   sh["ws_flat"])
+            elif flat:
+                pass
+            elif only in (None, "score"):
                 Q.qsa_score_blocks(ly.idx_q, ly.rows, ly.pooled, sh["scores"], nb_max, row_seq=ly.row_seq,
                                    sel_workspace=sh["ws_sel"])
-            if only in (None, "select"):
+            if not flat and only in (None, "select"):
                 Q.qsa_select_topk(sh["scores"], ly.rows, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"], sh["ws_sel"],
                                   prepared=True)
             if only in (None, "attn"):
@@ -218,6 +225,56 @@ def cpu_baseline(wl_name: str, budget_s: float = 12.0) -> dict:
 
 
 # ------------------------------------------------------------------ main
+
+def flat_leg(Q, L, sh, nb_max, wl, args, kt):
+    """Many rows scored and selected without the score matrix
+    (qsa_score_select): the whole step through a graph, the launch beside the
+    materialized score + select, and the memory each needs."""
+    import torch
+
+    sh = dict(sh)
+    wsb = Q.qsa_score_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
+    sh["ws_flat"] = torch.empty(wsb, dtype=torch.uint8, device=L[0].pooled.device)
+    run = step_fn(Q, L, sh, nb_max, wl, flat=True)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+
+    def one(only):
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(int(2e8))
+        except Exception:  # pragma: no cover
+            pass
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step_fn(Q, L, sh, nb_max, wl, only=only, flat=True)()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(L)
+
+    flat_us = one("flat")
+    ld = -(-nb_max // 4) * 4
+    return {"workload": wl.name + " memory-flat select", "value": wl.m * len(L) * args.steps / (ms / 1e3),
+            "unit": "query-rows/s per layer", "ms_per_step": ms / args.steps,
+            "layer_us": ms * 1e3 / args.steps / len(L),
+            "score_select_us": round(flat_us, 1), "score_plus_select_us": round(kt["score"] + kt["select"], 1),
+            "workspace_bytes": wsb, "score_matrix_bytes": wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)}
+
 
 def fp8_leg(Q, L, sh, nb_max, wl, args, attn_bf16_us):
     """The same layers with K/V in the fp8 state (E4M3 codes + f16 scale per
@@ -390,6 +447,8 @@ def main():
                  "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                  "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}},
     }
+    if not args.no_flat and wl.m >= PREFILL_MIN_ROWS:
+        res["flat"] = flat_leg(Q, L, sh, nb_max, wl, args, kt)
     if not args.no_fp8 and wl.name in ("verify_262k", "decode_262k", "decode_32k", "prefill"):
         res["fp8"] = fp8_leg(Q, L, sh, nb_max, wl, args, kt["attn"])
     if not args.no_m1 and wl.name == "verify_262k":

@@ -232,6 +232,46 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
                       void* workspace, size_t workspace_bytes, qsa_stream_t stream);
 
 /*
+ * qsa_score_select -- scores and top-k selection of many rows of one
+ * sequence without a score matrix (memory-flat prefill).
+ *
+ * Pages: hipfire "QSA sparse attention ...", section 02 (score and keep the
+ * best blocks within the budget, ties to the lower index) and section 06
+ * (long score rows outgrow the selector's on-chip memory); the chunked-
+ * prefill page, section 1 (the [rows x context] score buffer is a prefill
+ * chunk's memory peak).  Same result as qsa_score_blocks followed by
+ * qsa_select_topk on the many-row path, without writing the M x nb_max
+ * scores: a sampled threshold per row, candidates above it appended during
+ * scoring, an exact selection among them.
+ *
+ *  idx_q     bf16 [M][4][128]            index queries (one sequence)
+ *  M >= 0; row_pos int64 [M]; pooled float32 [nb_max][128] (the sequence's
+ *  pooled keys, e.g. the first sequence of qsa_append_pool's buffer)
+ *  nb_max    >= max blocks of any row (a host bound)
+ *  k_blocks  1..QSA_MAX_K_BLOCKS
+ *  sel       int32 [M][k_blocks], ascending block ids, -1 padded (written)
+ *  n_sel     int32 [M] = min(k_blocks, nb) (written)
+ *  workspace / workspace_bytes  >= qsa_score_select_workspace_bytes(M, nb_max,
+ *            k_blocks), 16-byte aligned; needs no initialisation.  For each
+ *            row m, 32-bit word 2 * round64(M) + m (round64: up to a multiple
+ *            of 64) tells how the row was selected (a diagnostic): 1 all
+ *            blocks kept, 2 from the candidates, 3/4/5 by an exact whole-row
+ *            select over scores recomputed in float32 (row longer than
+ *            262,144 blocks; candidate count outside [k, 4096]; more than 512
+ *            keys equal to the k-th).
+ *
+ * The scores are the many-row kernel's (bf16 matrix cores, float32 pooled
+ * keys as three bf16 planes); rows that take the exact path use float32
+ * vector arithmetic instead, so their scores may differ in the last bits.
+ * Workspace: about 4 B per 16 blocks plus 32 KiB per row, against 4 B per
+ * block per row for the score matrix.
+ */
+int qsa_score_select(const void* idx_q, int32_t M, const int64_t* row_pos, const float* pooled,
+                     int64_t nb_max, int32_t k_blocks, int32_t* sel, int32_t* n_sel,
+                     void* workspace, size_t workspace_bytes, qsa_stream_t stream);
+size_t qsa_score_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks);
+
+/*
  * qsa_quantize_kv_fp8 -- write K or V rows into an fp8 (E4M3 + f16 scale)
  * cache.
  *

@@ -35,7 +35,8 @@ MAX_SEGMENTS = 16
 
 EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-    "qsa_quantize_kv_fp8", "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes",
+    "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
+    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes",
     "qsa_device_check", "qsa_last_error", "qsa_version",
 )
 
@@ -68,6 +69,9 @@ _lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ
 _lib.qsa_gathered_attn.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P, _SZ, _P]
 _lib.qsa_quantize_kv_fp8.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
+_lib.qsa_score_select.argtypes = [_P, _I32, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
+_lib.qsa_score_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
+_lib.qsa_score_select_workspace_bytes.restype = _SZ
 _lib.qsa_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
 _lib.qsa_select_workspace_bytes.restype = _SZ
 _lib.qsa_attn_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
@@ -76,7 +80,7 @@ _lib.qsa_device_check.argtypes = []
 _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-           "qsa_quantize_kv_fp8", "qsa_device_check"):
+           "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_device_check"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -249,6 +253,25 @@ class KvSegments:
         if k_scale is not None:
             return cls([[(0, n, k, v, k_scale, v_scale)]])
         return cls([[(0, n, k, v)]])
+
+
+def qsa_score_select_workspace_bytes(max_m: int, nb_max: int, k_blocks: int) -> int:
+    return int(_lib.qsa_score_select_workspace_bytes(int(max_m), int(nb_max), int(k_blocks)))
+
+
+def qsa_score_select(idx_q: torch.Tensor, row_pos: torch.Tensor, pooled: torch.Tensor, nb_max: int,
+                     k_blocks: int, sel: torch.Tensor, n_sel: torch.Tensor, workspace: torch.Tensor,
+                     stream=None) -> None:
+    """``sel`` [M,k] / ``n_sel`` [M] <- top-k blocks of the bf16 rows ``idx_q``
+    [M,4,128] over ``pooled`` ([cap/4,128] or [1,cap/4,128]) without writing
+    the score matrix."""
+    _need(idx_q.dtype == torch.bfloat16 and idx_q.is_contiguous(), "idx_q: contiguous bf16 [M,4,128]")
+    _need(pooled.dtype == torch.float32 and pooled.is_contiguous(), "pooled: contiguous float32")
+    _need(row_pos.dtype == torch.int64 and sel.dtype == torch.int32 and n_sel.dtype == torch.int32, "dtypes")
+    m = idx_q.shape[0]
+    _need(sel.shape[0] >= m and sel.shape[1] == k_blocks and sel.is_contiguous(), "sel [M, k_blocks]")
+    _check(_lib.qsa_score_select(_ptr(idx_q), m, _ptr(row_pos), _ptr(pooled), int(nb_max), int(k_blocks),
+                                 _ptr(sel), _ptr(n_sel), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def qsa_quantize_kv_fp8(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.Tensor, t0: int = 0,

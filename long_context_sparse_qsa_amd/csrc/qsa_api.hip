@@ -164,6 +164,30 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
                        "qsa_gathered_attn");
 }
 
+int qsa_score_select(const void* idx_q, int32_t M, const int64_t* row_pos, const float* pooled,
+                     int64_t nb_max, int32_t k_blocks, int32_t* sel, int32_t* n_sel,
+                     void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
+  if (M < 0) return fail(QSA_ERR_ARG, "qsa_score_select: M = %d < 0", M);
+  if (nb_max < 0) return fail(QSA_ERR_ARG, "qsa_score_select: nb_max %lld < 0", (long long)nb_max);
+  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
+    return fail(QSA_ERR_ARG, "qsa_score_select: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
+  const size_t need = qsa::score_select_workspace_bytes(M, nb_max, k_blocks);
+  if (M > 0 && (workspace_bytes < need || !workspace))
+    return fail(QSA_ERR_WORKSPACE, "qsa_score_select: workspace %zu B < %zu B needed", workspace_bytes, need);
+  if (M == 0) return ok();
+  if (((uintptr_t)workspace & 15u) != 0) return fail(QSA_ERR_ARG, "qsa_score_select: workspace must be 16-byte aligned");
+  if (!idx_q || !row_pos || !sel || !n_sel || (nb_max > 0 && !pooled))
+    return fail(QSA_ERR_ARG, "qsa_score_select: null pointer (idx_q, row_pos, pooled, sel or n_sel)");
+  return launch_status(qsa::launch_score_select_flat(idx_q, M, row_pos, pooled, nb_max, k_blocks, sel, n_sel,
+                                                     workspace, (hipStream_t)stream),
+                       "qsa_score_select");
+}
+
+size_t qsa_score_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks) {
+  if (max_M <= 0 || nb_max < 0) return 0;
+  return qsa::score_select_workspace_bytes(max_M, nb_max, k_blocks);
+}
+
 int qsa_quantize_kv_fp8(const void* src, int32_t n_head, int32_t n_tok, int32_t head_dim,
                         int64_t src_head_stride, void* dst, uint16_t* dst_scale,
                         int64_t dst_head_stride, qsa_stream_t stream) {

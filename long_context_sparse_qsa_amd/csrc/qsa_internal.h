@@ -28,6 +28,15 @@ hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos
                                 int64_t nb_max, float* scores, int64_t ld, uint32_t* sel_ws,
                                 hipStream_t stream);
 
+// Memory-flat score -> top-k (select_flat.hip; its scoring modes in
+// score_prefill.hip).
+hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
+                                     int64_t nb_max, int k_blocks, uint32_t* ws, bool emit, hipStream_t stream);
+size_t score_select_workspace_bytes(int max_M, int64_t nb_max, int k_blocks);
+hipError_t launch_score_select_flat(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
+                                    int64_t nb_max, int k_blocks, int32_t* sel, int32_t* n_sel, void* ws,
+                                    hipStream_t stream);
+
 size_t select_workspace_bytes(int max_M, int64_t nb_max, int k_blocks);
 // Standalone selection: histogram, collect and finalize passes.
 hipError_t launch_select_topk(const float* scores, int64_t ld, int M, const int64_t* row_pos,

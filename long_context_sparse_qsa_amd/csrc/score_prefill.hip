@@ -23,6 +23,17 @@
 // block count are not stored.  With a selection workspace the epilogue
 // also stores the score sample of every 16-block group (as the few-row
 // variant does).
+//
+// Two more modes serve the memory-flat score -> top-k (no score matrix):
+//  - sample only: the tile's 64 A rows are the sampled blocks of 64
+//    consecutive 16-block groups, and their scores go to the rows' samples;
+//  - emit: after the full scoring, each row keeps only its blocks whose
+//    score digit reaches the row's threshold.  A wave counts its rows'
+//    candidates over the tile (ballots), reserves space with one atomic add
+//    per row (all issued together, one round trip) and appends the (key,
+//    block) pairs to the row's candidate slots in no particular order; slots
+//    past the capacity are dropped (the count still records them, which
+//    sends the row to the exact selection).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
@@ -33,6 +44,19 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+enum PfMode { kPfScores = 0, kPfScoresSample = 1, kPfSampleOnly = 2, kPfEmit = 3 };
+
+// Memory-flat workspace views of one call (select_common.h, FlatLayout).
+struct FlatArgs {
+  const uint32_t* thr;
+  uint32_t* cnt;
+  float* samples;
+  uint32_t* keys;
+  uint32_t* ids;
+  int64_t n_grp;
+  int k;
+};
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRowsPerWave = 32;
@@ -53,11 +77,11 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
-template <bool HIST>
+template <int MODE>
 __global__ void __launch_bounds__(kWave * kPfWaves, 2)
 score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
                      const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores,
-                     int64_t ld, uint32_t* __restrict__ ws) {
+                     int64_t ld, uint32_t* __restrict__ ws, FlatArgs fa) {
   __shared__ __align__(16) uint32_t planes[3][kPfBlocks * kPfRowWords];
   __shared__ int64_t nb_sh[kPfRows];
   const int tid = threadIdx.x;
@@ -65,7 +89,7 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   const int wave = tid / kWave;
   const int n16 = lane & 15;
   const int g4 = lane >> 4;
-  const int64_t b0 = (int64_t)blockIdx.x * kPfBlocks;
+  const int64_t b0 = (int64_t)blockIdx.x * kPfBlocks;  // first block (sample only: first sample group)
   const int r0 = blockIdx.y * kPfRows;
 
   // ---- loads: the tile's pooled keys (coalesced), this wave's index-query
@@ -75,7 +99,8 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
 #pragma unroll
   for (int i = 0; i < kF4; ++i) {
     const int idx = tid + i * kWave * kPfWaves;  // float4 index inside the tile
-    const int64_t b = b0 + idx / (kIndexDim / 4);
+    int64_t b = b0 + idx / (kIndexDim / 4);
+    if constexpr (MODE == kPfSampleOnly) b = b * 16 + sel::sample_offset((uint32_t)b);  // the group's sampled block
     const int64_t bl = b < nb_max ? b : nb_max - 1;  // past the last block: re-read it, never stored
     pk[i] = *reinterpret_cast<const float4*>(pooled + bl * kIndexDim + (idx % (kIndexDim / 4)) * 4);
   }
@@ -90,9 +115,11 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
 #pragma unroll
     for (int s = 0; s < kPfKs; ++s) bq[cg][s] = *reinterpret_cast<const uint4*>(src + 32 * s);
   }
+  __shared__ uint32_t thr_sh[kPfRows];
   if (tid < kPfRows) {
     const int r = r0 + tid;
     nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
+    if constexpr (MODE == kPfEmit) thr_sh[tid] = r < M ? fa.thr[r] : 0u;
   }
   // ---- split into planes, stage in LDS
 #pragma unroll
@@ -118,7 +145,18 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
 
-#pragma unroll 1
+  // emit mode: the key of the lane's block in every (16-block group, column
+  // group), which of them are candidates, and the candidates of the lane's
+  // row so far (the 16-block groups are unrolled so the keys stay in VGPRs)
+  uint32_t ekey[kPfGroups][kPfCg];
+  uint32_t eflag = 0u;
+  uint32_t run[kPfCg];
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) run[cg] = 0u;
+  const uint64_t rmask = 0x000F000F000F000Full << (4 * (n16 >> 2));  // the lane's row in a ballot
+  (void)ekey;
+
+#pragma unroll
   for (int bg = 0; bg < kPfGroups; ++bg) {
     f32x4_t acc[kPfCg];
 #pragma unroll
@@ -150,21 +188,69 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
         sv[v] = x * kScoreScale;
       }
       const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
-      if ((n16 & 3) == 0 && r < M) {
-        float* dst = scores + (int64_t)r * ld + bb;
-        if (bb + 3 < nb_row[cg]) {
-          *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
-        } else {
+      // sample-only and emit: lane t = n16 % 4 of the row's quad takes slot t
+      const int t = n16 & 3;
+      const float xt = t == 0 ? sv[0] : (t == 1 ? sv[1] : (t == 2 ? sv[2] : sv[3]));
+      if constexpr (MODE == kPfScores || MODE == kPfScoresSample) {
+        if ((n16 & 3) == 0 && r < M) {
+          float* dst = scores + (int64_t)r * ld + bb;
+          if (bb + 3 < nb_row[cg]) {
+            *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (bb + v < nb_row[cg]) dst[v] = sv[v];
-        }
-        if constexpr (HIST) {
+            for (int v = 0; v < 4; ++v)
+              if (bb + v < nb_row[cg]) dst[v] = sv[v];
+          }
+          if constexpr (MODE == kPfScoresSample) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (bb + v < nb_row[cg] && sel::sampled((uint32_t)(bb + v)))
-              reinterpret_cast<float*>(ws)[(size_t)r * rw + smp_off + ((bb + v) >> 4)] = sv[v];
+            for (int v = 0; v < 4; ++v)
+              if (bb + v < nb_row[cg] && sel::sampled((uint32_t)(bb + v)))
+                reinterpret_cast<float*>(ws)[(size_t)r * rw + smp_off + ((bb + v) >> 4)] = sv[v];
+          }
         }
+      }
+      if constexpr (MODE == kPfSampleOnly) {  // slot = sample group bb + t
+        const int64_t g = bb + t;
+        if (r < M && g < fa.n_grp && g * 16 + sel::sample_offset((uint32_t)g) < nb_row[cg])
+          fa.samples[(int64_t)r * fa.n_grp + g] = xt;
+      }
+      if constexpr (MODE == kPfEmit) {  // slot = block bb + t
+        const uint32_t key = sel::order_key(xt);
+        const int rl = wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
+        const bool c = r < M && bb + t < nb_row[cg] && nb_row[cg] > fa.k &&
+                       (key >> sel::kDigitShift) >= thr_sh[rl];
+        ekey[bg][cg] = key;
+        eflag |= c ? 1u << (bg * kPfCg + cg) : 0u;
+        run[cg] += (uint32_t)__popcll(__ballot(c) & rmask);
+      }
+    }
+  }
+
+  if constexpr (MODE == kPfEmit) {
+    // reserve each row's slots: one atomic per row, all in flight together
+    uint32_t base[kPfCg];
+#pragma unroll
+    for (int cg = 0; cg < kPfCg; ++cg) {
+      const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
+      uint32_t b = 0u;
+      if (g4 == 0 && (n16 & 3) == 0 && r < M && run[cg] > 0u) b = atomicAdd(fa.cnt + r, run[cg]);
+      base[cg] = b;
+    }
+    const uint64_t lane_lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int cg = 0; cg < kPfCg; ++cg) {
+      const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
+      uint32_t pos = (uint32_t)__shfl((int)base[cg], n16 & ~3, kWave);  // from lane 4 (n16 / 4)
+#pragma unroll
+      for (int bg = 0; bg < kPfGroups; ++bg) {
+        const bool c = (eflag >> (bg * kPfCg + cg)) & 1u;
+        const uint64_t mk = __ballot(c) & rmask;
+        const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
+        if (c && p < (uint32_t)sel::kFlatCap) {
+          fa.keys[(int64_t)r * sel::kFlatCap + p] = ekey[bg][cg];
+          fa.ids[(int64_t)r * sel::kFlatCap + p] = (uint32_t)(b0 + bg * 16 + 4 * g4 + (n16 & 3));
+        }
+        pos += (uint32_t)__popcll(mk);
       }
     }
   }
@@ -177,12 +263,38 @@ hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos
                                 hipStream_t stream) {
   if (M == 0 || nb_max == 0) return hipSuccess;
   dim3 grid((unsigned)((nb_max + kPfBlocks - 1) / kPfBlocks), (unsigned)((M + kPfRows - 1) / kPfRows));
+  const FlatArgs none{};
   if (sel_ws)
-    hipLaunchKernelGGL(score_prefill_kernel<true>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfScoresSample>, grid, dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws, none);
   else
-    hipLaunchKernelGGL(score_prefill_kernel<false>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfScores>, grid, dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
+                                     int64_t nb_max, int k_blocks, uint32_t* ws, bool emit, hipStream_t stream) {
+  if (M == 0 || nb_max == 0) return hipSuccess;
+  const sel::FlatLayout L = sel::flat_layout(M, nb_max);
+  FlatArgs fa;
+  fa.thr = ws + L.thr;
+  fa.cnt = ws + L.cnt;
+  fa.samples = reinterpret_cast<float*>(ws + L.samples);
+  fa.keys = ws + L.keys;
+  fa.ids = ws + L.ids;
+  fa.n_grp = sel::sample_groups(nb_max);
+  fa.k = k_blocks;
+  const unsigned gy = (unsigned)((M + kPfRows - 1) / kPfRows);
+  if (emit) {
+    dim3 grid((unsigned)((nb_max + kPfBlocks - 1) / kPfBlocks), gy);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfEmit>, grid, dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa);
+  } else {
+    dim3 grid((unsigned)((fa.n_grp + kPfBlocks - 1) / kPfBlocks), gy);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfSampleOnly>, grid, dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa);
+  }
   return hipGetLastError();
 }
 

@@ -54,83 +54,13 @@ constexpr int kChunkPer = kChunk / kChunkThreads;  // 16 consecutive scores per 
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kCandMax / kFinThreads;    // 8 candidates per thread
 constexpr int kLowBins = 1024;                     // 10-bit digits below the 12-bit one
-// The collect pass histograms its sample over a window of 256 digits: scores
-// from 2^-16 to 2^16 at 8 bins per octave; lower digits share the first bin
-// and higher ones the last.  Its threshold is an estimate, so saturation only
-// makes it more conservative (the finalize pass is exact regardless).
-constexpr int kWinBins = 256;
-constexpr uint32_t kWinBase = 0x800u + (127u - 16u) * 8u;  // digit of 2^-16
-__device__ __forceinline__ uint32_t win_bin(uint32_t key) {
-  const uint32_t d = key >> kDigitShift;
-  return d < kWinBase ? 0u : (d - kWinBase < (uint32_t)kWinBins ? d - kWinBase : (uint32_t)kWinBins - 1u);
-}
+using sel::kWinBase;
+using sel::kWinBins;
+using sel::win_bin;
 static_assert(kChunkPer % 4 == 0, "float4 score loads");
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
-  constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const uint32_t incl = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) sh[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < NW ? sh[lane] : 0u;
-    x = wave_incl_scan(x, lane);
-    if (lane < NW) sh[NW + lane] = x;
-  }
-  __syncthreads();
-  const uint32_t before = wave > 0 ? sh[NW + wave - 1] : 0u;
-  total = sh[2 * NW - 1];
-  __syncthreads();
-  return before + incl - v;
-}
-
-// Counts cnt[0..NBINS) in LDS (digit order ascending): find the digit where
-// the count from the top reaches `want`.  out3 = {digit, want - count above
-// the digit, 0}; out3[2] = 1 when the total stays below `want`.  Thread t
-// owns a contiguous run of bins (thread 0 the top ones); the lanes that share
-// a bank read their runs in rotated order, so the sums are conflict-free.
-template <int NT, int NBINS>
-__device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* scan_sh, uint32_t* out3) {
-  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
-  static_assert(NBINS < NT || NBINS % NT == 0, "bins split evenly over threads");
-  static_assert((PER & (PER - 1)) == 0 && PER <= kWave, "power-of-two run per thread");
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const bool owns = NBINS >= NT || t < NBINS;
-  const int lo = NBINS - (t + 1) * PER;
-  uint32_t mine = 0;
-  if (owns) {
-    const int rot = (lane * PER) / kWave;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) mine += cnt[lo + ((j + rot) & (PER - 1))];
-  }
-  if (t == 0) {
-    out3[0] = 0u;
-    out3[1] = want;
-    out3[2] = 1u;
-  }
-  uint32_t tot;
-  const uint32_t above = block_excl_scan<NT>(mine, scan_sh, tot);
-  if (owns && above < want && above + mine >= want) {  // one thread: walk its run from the top
-    uint32_t c[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) c[j] = cnt[lo + j];
-    uint32_t a = above;
-#pragma unroll
-    for (int j = PER - 1; j >= 0; --j) {
-      if (a + c[j] >= want) {
-        out3[0] = (uint32_t)(lo + j);
-        out3[1] = want - a;
-        out3[2] = 0u;
-        break;
-      }
-      a += c[j];
-    }
-  }
-  __syncthreads();
-}
+using sel::block_excl_scan;
+using sel::find_digit_desc;
 
 struct FinSmem {
   uint32_t hist16[kBins * kCopies];  // exact-path radix passes; also the 12-bit digit histogram
@@ -146,64 +76,10 @@ struct FinSmem {
 };
 static_assert(kDigits == kBins * kCopies, "the digit histogram reuses the radix histogram");
 
-// Exact path over the whole row: four 8-bit radix passes over all keys,
-// then an order-preserving compaction in index order.
-__device__ void exact_row_select(const float* __restrict__ s, int64_t nb, int k, int32_t* out, FinSmem& sm) {
-  constexpr int NT = kFinThreads;
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t prefix = 0, mask = 0, want = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < kBins * kCopies; i += NT) sm.hist16[i] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < nb; i += NT) {
-      const uint32_t u = order_key(s[i]);
-      if ((u & mask) == prefix) atomicAdd(&sm.hist16[((u >> shift) & 0xffu) * kCopies + (lane & (kCopies - 1))], 1u);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBins; i += NT) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int c = 0; c < kCopies; ++c) t += sm.hist16[i * kCopies + c];
-      sm.tot[i] = t;
-    }
-    __syncthreads();
-    find_digit_desc<NT, kBins>(sm.tot, want, sm.scan_sh, sm.out3);
-    prefix |= sm.out3[0] << shift;
-    mask |= 0xffu << shift;
-    want = sm.out3[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix, need = want;
-  uint32_t base_out = 0, base_eq = 0;
-  for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NT * 4) {
-    const int64_t i0 = c0 + (int64_t)threadIdx.x * 4;
-    uint32_t gt[4], eq[4], n_eq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = i0 + e;
-      const uint32_t u = i < nb ? order_key(s[i]) : 0u;
-      gt[e] = (i < nb) && (u > T);
-      eq[e] = (i < nb) && (u == T);
-      n_eq += eq[e];
-    }
-    uint32_t tot_eq, tot_take;
-    uint32_t eq_rank = base_eq + block_excl_scan<NT>(n_eq, sm.scan_sh, tot_eq);
-    uint32_t take[4], n_take = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      take[e] = gt[e] || (eq[e] && eq_rank < need);
-      eq_rank += eq[e];
-      n_take += take[e];
-    }
-    uint32_t pos = base_out + block_excl_scan<NT>(n_take, sm.scan_sh, tot_take);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (take[e] && pos < (uint32_t)k) out[pos] = (int32_t)(i0 + e);
-      pos += take[e];
-    }
-    base_out += tot_take;
-    base_eq += tot_eq;
-  }
+// Exact path over the whole row (select_common.h) reading the score array.
+__device__ __forceinline__ void exact_row_select(const float* __restrict__ s, int64_t nb, int k, int32_t* out,
+                                                 FinSmem& sm) {
+  sel::exact_select<kFinThreads>(sel::ScoreArray{s}, nb, k, out, sm);
 }
 
 // ---------------------------------------------------------------- kernels

@@ -182,3 +182,36 @@ def test_workspace_sizes():
     # select: one fixed-size record per row (histogram, candidate list)
     per_row = Q.qsa_select_workspace_bytes(1, 65280, 512)
     assert per_row > 0 and Q.qsa_select_workspace_bytes(4, 65280, 512) == 4 * per_row
+
+
+def _ssel(M=2, nb=100, k=16, ws=FAKE, wsb=1 << 30, idx=FAKE):
+    return L.qsa_score_select(idx, M, FAKE, FAKE, nb, k, FAKE, FAKE, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(M=-1), ERR_ARG, "M ="),
+    (dict(nb=-1), ERR_ARG, "nb_max"),
+    (dict(k=0), ERR_ARG, "k_blocks"),
+    (dict(k=5000), ERR_ARG, "k_blocks"),
+    (dict(wsb=100), ERR_WS, "workspace"),
+    (dict(ws=None), ERR_WS, "workspace"),
+    (dict(ws=FAKE + 4), ERR_ARG, "aligned"),
+    (dict(idx=None), ERR_ARG, "null"),
+    (dict(M=0, ws=None, wsb=0), Q.QSA_OK, ""),
+])
+def test_score_select_validation(kw, code, word):
+    assert _ssel(**kw) == code
+    assert word in _err()
+
+
+def test_score_select_workspace_bytes():
+    # per row: threshold, count, path (rounded to 64 rows), the sample (one
+    # word per 16 blocks, rounded to 64 words), 4,096 key and id slots
+    m, nb = 2048, 50512
+    n_grp = -(-nb // 16)
+    words = 3 * 2048 + (-(-(m * n_grp) // 64) * 64) + 2 * m * 4096
+    assert Q.qsa_score_select_workspace_bytes(m, nb, 512) == 4 * words
+    assert Q.qsa_score_select_workspace_bytes(0, nb, 512) == 0
+    # far below the M x nb score matrix it replaces
+    assert Q.qsa_score_select_workspace_bytes(m, nb, 512) < m * nb * 4 / 4
+
