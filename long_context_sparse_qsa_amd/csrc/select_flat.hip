@@ -26,6 +26,11 @@
 // LDS bitmap) the finalize workgroup selects exactly over the whole row,
 // recomputing each score from the index query and the pooled keys in float32
 // on the vector ALU: exact for those scores, slow, and rare.
+//
+// The chunked-prefill page (section 2.3) reaches a flat memory line by
+// blocking the key axis and merging per-block top-k lists; a per-row
+// threshold reaches it without holding a per-block top-k for every row of a
+// scoring workgroup, and with the same exactness.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
