@@ -135,12 +135,17 @@ def step_fn(Q, L, sh, nb_max, wl, only=None, flat=False):
     ``flat`` scores and selects through the memory-flat entry point."""
     def run():
         for ly in L:
-            if only in (None, "append"):
+            # one sequence: the append rides in the scoring launch
+            fused = only in (None, "append_score") and not flat and ly.row_seq is None
+            if fused:
+                Q.qsa_append_score(ly.new_idx, ly.new_pos, ly.idx_cache, ly.pooled, ly.idx_q, ly.rows, sh["scores"],
+                                   nb_max, sel_workspace=sh["ws_sel"])
+            elif only in (None, "append"):
                 Q.qsa_append_pool(ly.new_idx, ly.new_pos, ly.idx_cache, ly.pooled, seq=getattr(ly, "seq", None))
             if flat and only in (None, "flat"):
                 Q.qsa_score_select(ly.idx_q, ly.rows, ly.pooled, nb_max, wl.k_blocks, sh["sel"], sh["n_sel"],
                                    sh["ws_flat"])
-            elif flat:
+            elif flat or fused:
                 pass
             elif only in (None, "score"):
                 Q.qsa_score_blocks(ly.idx_q, ly.rows, ly.pooled, sh["scores"], nb_max, row_seq=ly.row_seq,
@@ -403,6 +408,8 @@ def main():
 
     # per-kernel device time (dominant kernel: scoring, HBM-bound)
     kt = {kind: per_launch_us(Q, L, sh, nb_max, wl, kind) for kind in ("score", "select", "attn", "append")}
+    if L[0].row_seq is None:
+        kt["append_score"] = per_launch_us(Q, L, sh, nb_max, wl, "append_score")
     score_us = kt["score"]
     score_bytes = nb_max * 128 * 4 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
     achieved = score_bytes / (score_us * 1e-6) / 1e9

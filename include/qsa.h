@@ -137,6 +137,31 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M,
                      void* sel_workspace, size_t sel_workspace_bytes, qsa_stream_t stream);
 
 /*
+ * qsa_append_score -- qsa_append_pool followed by qsa_score_blocks for one
+ * sequence, in one launch where possible.
+ *
+ * Pages: as qsa_append_pool and qsa_score_blocks (hipfire "QSA sparse
+ * attention ...", section 02).  One launch instead of two when the few-row
+ * scoring kernel serves the rows (fewer than 64 bf16 rows, or float32) and
+ * 1..64 tokens are appended: one workgroup writes the new keys and pools the
+ * blocks they complete, and the scoring of such a block pools it in
+ * registers from the same keys.  Otherwise the two launches.  Results are
+ * bit-identical to the two calls.
+ *
+ *  new_idx, n_new, new_pos   as qsa_append_pool's new_idx, n_new, pos (seq NULL)
+ *  idx_cache, pooled         [capacity][128] dtype, float32 [capacity/4][128]
+ *  capacity                  > 0, multiple of 4
+ *  idx_q, dtype, M, row_pos  as qsa_score_blocks (row_seq NULL, n_seq 1)
+ *  nb_max, scores, ld        as qsa_score_blocks
+ *  sel_workspace, ..._bytes  as qsa_score_blocks
+ * Errors: those of either call.
+ */
+int qsa_append_score(const void* new_idx, int32_t n_new, const int64_t* new_pos, void* idx_cache,
+                     float* pooled, int64_t capacity, const void* idx_q, int32_t dtype, int32_t M,
+                     const int64_t* row_pos, int64_t nb_max, float* scores, int64_t ld,
+                     void* sel_workspace, size_t sel_workspace_bytes, qsa_stream_t stream);
+
+/*
  * qsa_select_topk -- keep the best blocks of each row within the budget.
  *
  * Page: hipfire "QSA sparse attention ...", section 02 (top-scoring blocks

@@ -35,7 +35,7 @@ MAX_SEGMENTS = 16
 
 EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-    "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
+    "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
     "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes",
     "qsa_device_check", "qsa_last_error", "qsa_version",
 )
@@ -68,6 +68,7 @@ _lib.qsa_score_blocks.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, 
 _lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ, _I32, _P]
 _lib.qsa_gathered_attn.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P, _SZ, _P]
+_lib.qsa_append_score.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]
 _lib.qsa_quantize_kv_fp8.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
 _lib.qsa_score_select.argtypes = [_P, _I32, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
 _lib.qsa_score_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
@@ -80,7 +81,7 @@ _lib.qsa_device_check.argtypes = []
 _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-           "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_device_check"):
+           "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_device_check"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -253,6 +254,26 @@ class KvSegments:
         if k_scale is not None:
             return cls([[(0, n, k, v, k_scale, v_scale)]])
         return cls([[(0, n, k, v)]])
+
+
+def qsa_append_score(new_idx: torch.Tensor, new_pos: torch.Tensor, idx_cache: torch.Tensor, pooled: torch.Tensor,
+                     idx_q: torch.Tensor, row_pos: torch.Tensor, scores: torch.Tensor, nb_max: int,
+                     sel_workspace: torch.Tensor | None = None, stream=None) -> None:
+    """``qsa_append_pool`` of ``new_idx`` at ``new_pos`` into one sequence's
+    ``idx_cache`` [cap,128] / ``pooled`` [cap/4,128], then ``qsa_score_blocks``
+    of the rows ``idx_q`` over it: one launch where possible."""
+    cache = idx_cache[0] if idx_cache.dim() == 3 else idx_cache
+    pl = pooled[0] if pooled.dim() == 3 else pooled
+    _need(new_idx.is_contiguous() and cache.is_contiguous() and pl.is_contiguous() and idx_q.is_contiguous()
+          and scores.is_contiguous(), "tensors must be contiguous")
+    _need(new_idx.dtype == cache.dtype == idx_q.dtype and pl.dtype == torch.float32, "dtype mismatch")
+    _need(new_pos.dtype == torch.int64 and row_pos.dtype == torch.int64, "positions int64")
+    cap = cache.shape[0]
+    _need(pl.shape[0] == cap // BLOCK_TOKENS, "pooled shape mismatch")
+    _check(_lib.qsa_append_score(_ptr(new_idx), new_idx.shape[0], _ptr(new_pos), _ptr(cache), _ptr(pl), cap,
+                                 _ptr(idx_q), _dtype_code(idx_q), idx_q.shape[0], _ptr(row_pos), int(nb_max),
+                                 _ptr(scores), scores.shape[1], _ptr(sel_workspace), _nbytes(sel_workspace),
+                                 _stream(stream)))
 
 
 def qsa_score_select_workspace_bytes(max_m: int, nb_max: int, k_blocks: int) -> int:

@@ -11,6 +11,7 @@
 // so no workgroup reads a row another workgroup of this launch writes.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "append_common.h"
 
 namespace qsa {
 
@@ -20,33 +21,7 @@ append_pool_kernel(const typename E::T* __restrict__ new_idx, int n_new,
                    const int64_t* __restrict__ pos, const int32_t* __restrict__ seq,
                    typename E::T* __restrict__ cache, float* __restrict__ pooled,
                    int n_seq, int64_t capacity) {
-  using T = typename E::T;
-  const int i = blockIdx.x;
-  const int d = threadIdx.x;
-  const int64_t p = pos[i];
-  const int s = seq ? seq[i] : 0;
-  if (p < 0 || p >= capacity || s < 0 || s >= n_seq) return;
-  const int64_t seq_base = (int64_t)s * capacity;
-  const T x = new_idx[(int64_t)i * kIndexDim + d];
-  cache[(seq_base + p) * kIndexDim + d] = x;
-  if ((p & 3) != 3) return;
-
-  float v[kBlockTokens];
-#pragma unroll
-  for (int j = 0; j < kBlockTokens; ++j) {
-    const int back = kBlockTokens - 1 - j;  // tokens before the completing one
-    const int64_t pj = p - back;
-    const int ij = i - back;
-    bool here = (back == 0);
-    if (!here && ij >= 0) here = (pos[ij] == pj) && ((seq ? seq[ij] : 0) == s);
-    const T xj = here ? new_idx[(int64_t)ij * kIndexDim + d] : cache[(seq_base + pj) * kIndexDim + d];
-    v[j] = E::to_f(xj);
-  }
-  // Fixed order, IEEE round-to-nearest-even, no contraction.
-  float acc = __fadd_rn(v[0], v[1]);
-  acc = __fadd_rn(acc, v[2]);
-  acc = __fadd_rn(acc, v[3]);
-  pooled[((int64_t)s * (capacity / kBlockTokens) + (p >> 2)) * kIndexDim + d] = __fmul_rn(acc, 0.25f);
+  append_token_dim<E>(new_idx, pos, seq, cache, pooled, n_seq, capacity, blockIdx.x, threadIdx.x);
 }
 
 hipError_t launch_append_pool(const void* new_idx, int dtype, int n_new, const int64_t* pos,

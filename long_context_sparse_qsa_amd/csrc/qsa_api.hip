@@ -81,6 +81,35 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t*
                        "qsa_score_blocks");
 }
 
+int qsa_append_score(const void* new_idx, int32_t n_new, const int64_t* new_pos, void* idx_cache,
+                     float* pooled, int64_t capacity, const void* idx_q, int32_t dtype, int32_t M,
+                     const int64_t* row_pos, int64_t nb_max, float* scores, int64_t ld,
+                     void* sel_workspace, size_t sel_workspace_bytes, qsa_stream_t stream) {
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_append_score: dtype %d is not QSA_F32 or QSA_BF16", dtype);
+  if (n_new < 0) return fail(QSA_ERR_ARG, "qsa_append_score: n_new = %d < 0", n_new);
+  if (M < 0) return fail(QSA_ERR_ARG, "qsa_append_score: M = %d < 0", M);
+  if (capacity <= 0 || capacity % QSA_BLOCK_TOKENS != 0)
+    return fail(QSA_ERR_ARG, "qsa_append_score: capacity %lld must be a positive multiple of 4", (long long)capacity);
+  if (nb_max < 0 || nb_max > capacity / QSA_BLOCK_TOKENS)
+    return fail(QSA_ERR_ARG, "qsa_append_score: nb_max %lld outside [0, capacity/4 = %lld]", (long long)nb_max,
+                (long long)(capacity / QSA_BLOCK_TOKENS));
+  if (ld < nb_max) return fail(QSA_ERR_ARG, "qsa_append_score: ld %lld < nb_max %lld", (long long)ld, (long long)nb_max);
+  if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
+    return fail(QSA_ERR_ARG, "qsa_append_score: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
+                (long long)ld);
+  if (sel_workspace && sel_workspace_bytes < qsa::select_workspace_bytes(M, nb_max, 1))
+    return fail(QSA_ERR_WORKSPACE, "qsa_append_score: selection workspace %zu B < %zu B needed",
+                sel_workspace_bytes, qsa::select_workspace_bytes(M, nb_max, 1));
+  if (n_new > 0 && (!new_idx || !new_pos || !idx_cache || !pooled))
+    return fail(QSA_ERR_ARG, "qsa_append_score: null pointer (new_idx, new_pos, idx_cache or pooled)");
+  if (M > 0 && nb_max > 0 && (!idx_q || !row_pos || !pooled || !scores))
+    return fail(QSA_ERR_ARG, "qsa_append_score: null pointer (idx_q, row_pos, pooled or scores)");
+  return launch_status(qsa::launch_append_score(new_idx, n_new, new_pos, idx_cache, pooled, capacity, idx_q, dtype,
+                                                M, row_pos, nb_max, scores, ld,
+                                                static_cast<uint32_t*>(sel_workspace), (hipStream_t)stream),
+                       "qsa_append_score");
+}
+
 size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_blocks) {
   if (max_M <= 0 || nb_max < 0 || k_blocks <= 0) return 0;
   return qsa::select_workspace_bytes(max_M, nb_max, k_blocks);

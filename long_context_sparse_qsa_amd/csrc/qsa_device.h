@@ -67,6 +67,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 // that loads addressed by it become scalar loads.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Pooled key element of one block: (((x0 + x1) + x2) + x3) * 0.25 in float32,
+// fixed order, IEEE round-to-nearest-even, no contraction.
+__device__ __forceinline__ float pool4(float x0, float x1, float x2, float x3) {
+  float acc = __fadd_rn(x0, x1);
+  acc = __fadd_rn(acc, x2);
+  acc = __fadd_rn(acc, x3);
+  return __fmul_rn(acc, 0.25f);
+}
+
 __device__ __forceinline__ int64_t clamp_nb(int64_t pos, int64_t nb_max) {
   int64_t nb = (pos + 1) / kBlockTokens;
   if (nb < 0) nb = 0;

@@ -21,6 +21,16 @@ hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_
                                int64_t capacity, int64_t nb_max, float* scores, int64_t ld,
                                uint32_t* sel_ws, hipStream_t stream);
 
+// qsa_append_pool followed by qsa_score_blocks (one sequence) in one launch
+// when the few-row kernel scores and at most kMaxFoldedTokens tokens are
+// appended; otherwise the two launches.
+constexpr int kMaxFoldedTokens = 64;
+bool append_folds_into_scoring(int dtype, int M, int n_new, int64_t nb_max);
+hipError_t launch_append_score(const void* new_idx, int n_new, const int64_t* new_pos, void* idx_cache,
+                               float* pooled, int64_t capacity, const void* idx_q, int dtype, int M,
+                               const int64_t* row_pos, int64_t nb_max, float* scores, int64_t ld,
+                               uint32_t* sel_ws, hipStream_t stream);
+
 // Many-row scoring (bf16 index queries, one sequence): the bf16 matrix-core
 // kernel with three-plane pooled keys (score_prefill.hip).
 constexpr int kPrefillMinRows = 64;

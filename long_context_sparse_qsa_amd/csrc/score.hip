@@ -26,8 +26,16 @@
 // With HIST, the epilogue also feeds the top-k selection: the score of one
 // block per 16-block group (at a hashed offset) is stored in the row's sample
 // slots in the selection workspace (plain stores, no atomics).
+//
+// With APPEND the launch also does the index-key append of the new tokens
+// (one sequence): one extra workgroup writes their keys to the cache and
+// pools every block they complete, as the append kernel does; the wave that scores
+// such a block recomputes its pooled key in registers from the same four keys
+// (new ones from the call, earlier ones from the cache, which this launch
+// does not write there) instead of reading the value being written.
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "append_common.h"
 #include "select_common.h"
 
 namespace qsa {
@@ -66,15 +74,47 @@ __device__ __forceinline__ float4 q_to_f4<BF16>(uint2 x) {
 
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// NSET column sets of 16 (row, head) columns (4 rows per set); RPG rows per
-// group (RPG = 1 when every row has its own sequence).
-template <class EQ, int NSET, int RPG, bool HIST>
+// The append folded into the launch (one sequence).
+struct AppendArgs {
+  const void* new_idx;  // [n_new][128] in the query dtype
+  const int64_t* pos;   // [n_new]
+  void* cache;          // [capacity][128]
+  float* pooled;        // the pooled keys the scoring reads (written for completed blocks)
+  int n_new;
+  int64_t capacity;
+};
+
+// Pooled elements dims dim..dim+3 of a block from its four key rows,
+// exactly as the append computes them.
+template <class EQ>
+__device__ __forceinline__ float4 pooled4_of(const typename EQ::T* const* rows, int dim) {
+  float4 x[kBlockTokens];
+#pragma unroll
+  for (int j = 0; j < kBlockTokens; ++j) x[j] = q_to_f4<EQ>(load_q_raw<EQ>(rows[j] + dim));
+  return make_float4(pool4(x[0].x, x[1].x, x[2].x, x[3].x), pool4(x[0].y, x[1].y, x[2].y, x[3].y),
+                     pool4(x[0].z, x[1].z, x[2].z, x[3].z), pool4(x[0].w, x[1].w, x[2].w, x[3].w));
+}
+
+template <class EQ, int NSET, int RPG, bool HIST, bool APPEND>
 __global__ void __launch_bounds__(kWave * kWavesPerWG)
 score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
                     const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                     const float* __restrict__ pooled, int n_seq, int64_t capacity,
-                    int64_t nb_max, float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ ws) {
+                    int64_t nb_max, float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ ws,
+                    AppendArgs ap) {
   static_assert(RPG <= 4 * NSET, "rows per group exceed the column sets");
+  if constexpr (APPEND) {
+    // the grid's extra last column of workgroups: row group 0's does the
+    // append (cache rows and completed blocks), alongside the scoring
+    if (blockIdx.x == gridDim.x - 1) {
+      if (blockIdx.y == 0)
+        for (int e = threadIdx.x; e < ap.n_new * kIndexDim; e += kWave * kWavesPerWG)
+          append_token_dim<EQ>(static_cast<const typename EQ::T*>(ap.new_idx), ap.pos, nullptr,
+                               static_cast<typename EQ::T*>(ap.cache), ap.pooled, 1, ap.capacity, e / kIndexDim,
+                               e % kIndexDim);
+      return;
+    }
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m0 = blockIdx.y * RPG;
@@ -116,6 +156,47 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     const float* src = P + (b < nb_max ? b : nb_max - 1) * kIndexDim + 4 * kq;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) a[g][c] = *reinterpret_cast<const float4*>(src + 16 * c);
+  }
+  if constexpr (APPEND) {
+    // blocks this call completes inside the wave's range: their pooled keys
+    // come from the keys, not from memory (wave-uniform loop; few tokens).
+    // Issued after the pooled stream: waiting for the positions first would
+    // hold back every wave's stream for the sake of one wave.
+    using T = typename EQ::T;
+    const T* nw = static_cast<const T*>(ap.new_idx);
+    const T* ca = static_cast<const T*>(ap.cache);
+    int64_t w1 = -1, w2 = -1, w3 = -1;  // positions of tokens i-1, i-2, i-3
+    for (int i0 = 0; i0 < ap.n_new; i0 += 4) {
+      int64_t pb[4];  // four positions per round trip
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pb[u] = i0 + u < ap.n_new ? ap.pos[i0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u;
+        const int64_t p = pb[u];
+        const int64_t rel = (p >> 2) - wave_b0;
+        if (i < ap.n_new && (p & 3) == 3 && p < ap.capacity && rel >= 0 && rel < kBlocksPerWave &&
+            (p >> 2) < nb_max && i16 == (int)(rel & 15)) {
+          // key rows of the block: from this call when the token is in it
+          // (consecutive ascending positions), else from the cache
+          const int64_t b4 = p - 3;
+          const T* rows[kBlockTokens] = {
+              w3 == b4 ? nw + (int64_t)(i - 3) * kIndexDim : ca + b4 * kIndexDim,
+              w2 == b4 + 1 ? nw + (int64_t)(i - 2) * kIndexDim : ca + (b4 + 1) * kIndexDim,
+              w1 == b4 + 2 ? nw + (int64_t)(i - 1) * kIndexDim : ca + (b4 + 2) * kIndexDim,
+              nw + (int64_t)i * kIndexDim};
+#pragma unroll
+          for (int g = 0; g < kGroupsPerWave; ++g) {
+            if (g != (int)(rel >> 4)) continue;
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) a[g][c] = pooled4_of<EQ>(rows, 16 * c + 4 * kq);
+          }
+        }
+        w3 = w2;
+        w2 = w1;
+        w1 = p;
+      }
+    }
   }
 
   int64_t nb_r[RPG];
@@ -197,28 +278,33 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
 template <class EQ, int NSET, int RPG, bool HIST>
 hipError_t launch_fewrow(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
                          const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
-                         float* scores, int64_t ld, uint32_t* ws, hipStream_t stream) {
+                         float* scores, int64_t ld, uint32_t* ws, const AppendArgs* ap, hipStream_t stream) {
   const int64_t wgs = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
   if (wgs == 0) return hipSuccess;
   dim3 grid((unsigned)wgs, (unsigned)((M + RPG - 1) / RPG));
-  hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST>), grid, dim3(kWave * kWavesPerWG), 0, stream,
-                     static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled,
-                     n_seq, capacity, nb_max, scores, ld, ws);
+  if (ap)
+    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true>), dim3(grid.x + 1, grid.y),
+                       dim3(kWave * kWavesPerWG), 0, stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
+                       capacity, nb_max, scores, ld, ws, *ap);
+  else
+    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, false>), grid, dim3(kWave * kWavesPerWG), 0,
+                       stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
+                       capacity, nb_max, scores, ld, ws, AppendArgs{});
   return hipGetLastError();
 }
 
 template <class EQ, bool HIST>
 hipError_t dispatch_rows(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
                          const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
-                         float* scores, int64_t ld, uint32_t* ws, hipStream_t stream) {
+                         float* scores, int64_t ld, uint32_t* ws, const AppendArgs* ap, hipStream_t stream) {
   // Rows of different sequences read different pooled keys: one row per
   // group.  Rows of one sequence share each pooled read, 4 or 8 at a time;
   // many bf16 rows go to the matrix-core many-row kernel.
-  if (row_seq) return launch_fewrow<EQ, 1, 1, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
-  if (EQ::kBytes == 2 && M >= kPrefillMinRows)
+  if (row_seq) return launch_fewrow<EQ, 1, 1, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, ap, stream);
+  if (EQ::kBytes == 2 && M >= kPrefillMinRows)  // (the append is never folded into this path)
     return launch_score_prefill(idx_q, M, row_pos, pooled, nb_max, scores, ld, ws, stream);
-  if (M <= 4) return launch_fewrow<EQ, 1, 4, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
-  return launch_fewrow<EQ, 2, 8, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, stream);
+  if (M <= 4) return launch_fewrow<EQ, 1, 4, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, ap, stream);
+  return launch_fewrow<EQ, 2, 8, HIST>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, ws, ap, stream);
 }
 
 }  // namespace
@@ -230,12 +316,37 @@ hipError_t launch_score_blocks(const void* idx_q, int dtype, int M, const int64_
   if (M == 0 || nb_max == 0) return hipSuccess;
   if (sel_ws) {
     if (dtype == QSA_BF16)
-      return dispatch_rows<BF16, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, stream);
-    return dispatch_rows<F32, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, stream);
+      return dispatch_rows<BF16, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, nullptr, stream);
+    return dispatch_rows<F32, true>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, sel_ws, nullptr, stream);
   }
   if (dtype == QSA_BF16)
-    return dispatch_rows<BF16, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, stream);
-  return dispatch_rows<F32, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, stream);
+    return dispatch_rows<BF16, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, nullptr, stream);
+  return dispatch_rows<F32, false>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity, nb_max, scores, ld, nullptr, nullptr, stream);
+}
+
+bool append_folds_into_scoring(int dtype, int M, int n_new, int64_t nb_max) {
+  return M > 0 && nb_max > 0 && n_new > 0 && n_new <= kMaxFoldedTokens && !(dtype == QSA_BF16 && M >= kPrefillMinRows);
+}
+
+hipError_t launch_append_score(const void* new_idx, int n_new, const int64_t* new_pos, void* idx_cache,
+                               float* pooled, int64_t capacity, const void* idx_q, int dtype, int M,
+                               const int64_t* row_pos, int64_t nb_max, float* scores, int64_t ld,
+                               uint32_t* sel_ws, hipStream_t stream) {
+  if (!append_folds_into_scoring(dtype, M, n_new, nb_max)) {  // two launches
+    hipError_t e = launch_append_pool(new_idx, dtype, n_new, new_pos, nullptr, idx_cache, pooled, 1, capacity, stream);
+    if (e != hipSuccess) return e;
+    return launch_score_blocks(idx_q, dtype, M, row_pos, nullptr, pooled, 1, capacity, nb_max, scores, ld, sel_ws,
+                               stream);
+  }
+  const AppendArgs ap{new_idx, new_pos, idx_cache, pooled, n_new, capacity};
+  if (dtype == QSA_BF16) {
+    if (sel_ws)
+      return dispatch_rows<BF16, true>(idx_q, M, row_pos, nullptr, pooled, 1, capacity, nb_max, scores, ld, sel_ws, &ap, stream);
+    return dispatch_rows<BF16, false>(idx_q, M, row_pos, nullptr, pooled, 1, capacity, nb_max, scores, ld, nullptr, &ap, stream);
+  }
+  if (sel_ws)
+    return dispatch_rows<F32, true>(idx_q, M, row_pos, nullptr, pooled, 1, capacity, nb_max, scores, ld, sel_ws, &ap, stream);
+  return dispatch_rows<F32, false>(idx_q, M, row_pos, nullptr, pooled, 1, capacity, nb_max, scores, ld, nullptr, &ap, stream);
 }
 
 }  // namespace qsa

@@ -215,3 +215,25 @@ def test_score_select_workspace_bytes():
     # far below the M x nb score matrix it replaces
     assert Q.qsa_score_select_workspace_bytes(m, nb, 512) < m * nb * 4 / 4
 
+
+def _apsc(dtype=1, n_new=4, M=1, cap=64, nb=16, ld=16, scores=FAKE, ws=None, wsb=0, new=FAKE, idx_q=FAKE):
+    return L.qsa_append_score(new, n_new, FAKE, FAKE, FAKE, cap, idx_q, dtype, M, FAKE, nb, scores, ld, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(dtype=4), ERR_ARG, "dtype"),
+    (dict(n_new=-1), ERR_ARG, "n_new"),
+    (dict(M=-1), ERR_ARG, "M ="),
+    (dict(cap=62), ERR_ARG, "capacity"),
+    (dict(nb=17), ERR_ARG, "nb_max"),
+    (dict(ld=8), ERR_ARG, "ld"),
+    (dict(ld=18), ERR_ARG, "aligned"),
+    (dict(ws=FAKE, wsb=100), ERR_WS, "workspace"),
+    (dict(new=None), ERR_ARG, "null"),
+    (dict(idx_q=None), ERR_ARG, "null"),
+    (dict(n_new=0, M=0, new=None, idx_q=None), Q.QSA_OK, ""),
+])
+def test_append_score_validation(kw, code, word):
+    assert _apsc(**kw) == code
+    assert word in _err()
+
