@@ -108,10 +108,70 @@ class SeqLayer:
         self.row_seq = None
 
 
+class BatchedLayer:
+    """One layer of a batched decode: one row per sequence, each sequence's
+    K/V in 1..5 separately allocated segments (seeded lengths and cut points),
+    resident on the device."""
+
+    def __init__(self, Q, specs, layer, dev):
+        import torch
+        import datagen
+        from datagen.synth import BATCHED
+
+        bf = torch.bfloat16
+        n_seq = len(specs)
+        self.cap = max(-(-(sp.n_ctx + 4) // 256) * 256 for sp in specs)
+        self.idx_cache = torch.zeros((n_seq, self.cap, 128), dtype=bf, device=dev)
+        self.pooled = torch.zeros((n_seq, self.cap // 4, 128), dtype=torch.float32, device=dev)
+        self.idx_q = torch.empty((n_seq, 4, 128), dtype=bf, device=dev)
+        self.q = torch.empty((n_seq, 24, 256), dtype=bf, device=dev)
+        segs, new_idx = [], []
+        for s, sp in enumerate(specs):
+            wl_s = datagen.Workload(f"batched_seq{s}", 3, sp.n_ctx, (sp.row,), "bf16", 256,
+                                    plant=BATCHED["plant"], seed=s)
+            idx32 = torch.empty((sp.n_ctx, 128), dtype=torch.float32, device=dev)
+            k = torch.empty((2, sp.n_ctx, 256), dtype=bf, device=dev)
+            v = torch.empty_like(k)
+            datagen.fill_layer_device(wl_s, layer, idx32, self.idx_q[s:s + 1], self.q[s:s + 1], k, v)
+            idx = idx32.to(bf)
+            del idx32
+            Q.qsa_append_pool(idx, torch.arange(sp.n_ctx, dtype=torch.int64, device=dev),
+                              self.idx_cache[s:s + 1], self.pooled[s:s + 1])
+            new_idx.append(idx[sp.row:sp.row + 1])
+            seq_segs = []
+            for st, ln, cp in zip(sp.seg_start, sp.seg_len, sp.seg_cap):
+                kt = torch.zeros((2, cp, 256), dtype=bf, device=dev)
+                vt = torch.zeros_like(kt)
+                kt[:, :ln] = k[:, st:st + ln]
+                vt[:, :ln] = v[:, st:st + ln]
+                seq_segs.append((st, ln, kt, vt))
+            segs.append(seq_segs)
+            del k, v
+        self.kv = Q.KvSegments(segs)
+        self.rows = torch.tensor([sp.row for sp in specs], dtype=torch.int64, device=dev)
+        self.row_seq = torch.arange(n_seq, dtype=torch.int32, device=dev)
+        self.seq = self.row_seq
+        self.new_idx = torch.cat(new_idx).contiguous()  # each row's own key, re-appended each step
+        self.new_pos = self.rows.clone()
+
+
+def build_batched(Q, layers, dev):
+    import datagen
+
+    specs = datagen.batched_specs()
+    wl = datagen.Workload("batched", 3, max(sp.n_ctx for sp in specs), tuple(sp.row for sp in specs), "bf16", 256)
+    L = [BatchedLayer(Q, specs, i, dev) for i in range(layers)]
+    return wl, L, shared_buffers(Q, wl, dev), (max(wl.rows) + 1) // 4, [sp.n_ctx // 4 for sp in specs]
+
+
 def build_single(Q, wl, layers, dev):
+    L = [SeqLayer(Q, wl, i, dev) for i in range(layers)]
+    return L, shared_buffers(Q, wl, dev), (max(wl.rows) + 1) // 4
+
+
+def shared_buffers(Q, wl, dev):
     import torch
 
-    L = [SeqLayer(Q, wl, i, dev) for i in range(layers)]
     nb_max = (max(wl.rows) + 1) // 4
     m = wl.m
     k = wl.k_blocks
@@ -127,7 +187,7 @@ def build_single(Q, wl, layers, dev):
     wsb = Q.qsa_select_workspace_bytes(m, nb_max, k)
     if wsb:
         shared["ws_sel"] = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-    return L, shared, nb_max
+    return shared
 
 
 def step_fn(Q, L, sh, nb_max, wl, only=None, flat=False):
@@ -361,10 +421,14 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     Q.qsa_device_check()
-    wl = datagen.WORKLOADS[args.workload]
     layers = args.layers
     t_setup = time.time()
-    L, sh, nb_max = build_single(Q, wl, layers, dev)
+    if args.workload == "batched":
+        wl, L, sh, nb_max, seq_nb = build_batched(Q, layers, dev)
+    else:
+        wl = datagen.WORKLOADS[args.workload]
+        L, sh, nb_max = build_single(Q, wl, layers, dev)
+        seq_nb = None  # one sequence: its pooled keys are read once for all rows
     torch.cuda.synchronize()
     print(f"[bench] set-up {wl.name}: {layers} layers, n_ctx {wl.n_ctx}, M {wl.m} in "
           f"{time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
@@ -411,7 +475,8 @@ def main():
     if L[0].row_seq is None:
         kt["append_score"] = per_launch_us(Q, L, sh, nb_max, wl, "append_score")
     score_us = kt["score"]
-    score_bytes = nb_max * 128 * 4 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
+    pooled_bytes = nb_max * 512 if seq_nb is None else sum(seq_nb) * 512
+    score_bytes = pooled_bytes + wl.m * 4 * 128 * 2 + (wl.m * nb_max if seq_nb is None else sum(seq_nb)) * 4
     achieved = score_bytes / (score_us * 1e-6) / 1e9
     if wl.m >= PREFILL_MIN_ROWS:
         # many-row scoring runs on the bf16 matrix cores with three-plane
@@ -424,13 +489,14 @@ def main():
                     "traffic": None, "algorithmic_tflops": alg_flops / (score_us * 1e-6) / 1e12,
                     "flops_per_launch_bf16": 3 * alg_flops, "launch_us": score_us}
     else:
-        roofline = {"bound": "hbm", "kernel": "score_fewrow_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "kernel": "score_fewrow_kernel" if seq_nb is None else "score_fewrow_kernel (one row per sequence)",
                     "traffic": stored_traffic() if wl.name == "verify_262k" else None,
                     "bytes_per_launch": score_bytes, "launch_us": score_us}
     # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries
     tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
-    path_bytes = nb_max * 512 + tok * wl.hkv * 2 * wl.head_dim * 2 + wl.m * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2)
+    path_bytes = pooled_bytes + tok * wl.hkv * 2 * wl.head_dim * 2 + wl.m * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2)
     layer_us = ms_step * 1e3 / layers
     res = {
         "metric": "QSA query-rows/s per layer at 262K ctx (M=1,4) + achieved HBM GB/s / MFMA %",
