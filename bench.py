@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 CSRC = os.path.join(ROOT, "long_context_sparse_qsa_amd", "csrc")
 # sources of the scoring kernel (the dominant kernel): PMC figures taken on
 # another build of them are not reported
-SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h")
+SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h", "append_common.h")
 PMC_FILE = os.path.join(ROOT, "profiles", "score_fewrow_kernel.verify_262k.pmc.txt")
 COPY_BYTES = 256 << 20  # plain copy of known size used to scale the PMC byte counters
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -59,6 +59,19 @@ def score_source_hash() -> str:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def append_alg_bytes(new_pos, elt: int) -> int:
+    """Algorithmic bytes of appending index keys at positions ``new_pos``
+    (``elt`` bytes per element): new keys read and written to the cache, the
+    earlier keys of every completed block read from the cache, the pooled
+    key (float32) written."""
+    pos = set(int(p) for p in new_pos)
+    b = len(pos) * 128 * elt * 2
+    for p in pos:
+        if p % 4 == 3:
+            b += 128 * 4 + sum(128 * elt for q in range(p - 3, p) if q not in pos)
+    return b
 
 
 def stored_traffic() -> int | None:
@@ -474,9 +487,14 @@ def main():
     kt = {kind: per_launch_us(Q, L, sh, nb_max, wl, kind) for kind in ("score", "select", "attn", "append")}
     if L[0].row_seq is None:
         kt["append_score"] = per_launch_us(Q, L, sh, nb_max, wl, "append_score")
-    score_us = kt["score"]
     pooled_bytes = nb_max * 512 if seq_nb is None else sum(seq_nb) * 512
     score_bytes = pooled_bytes + wl.m * 4 * 128 * 2 + (wl.m * nb_max if seq_nb is None else sum(seq_nb)) * 4
+    # the step scores through the launch that also appends (one sequence,
+    # few rows): its bytes include the append's
+    folded = L[0].row_seq is None and wl.m < PREFILL_MIN_ROWS
+    score_us = kt["append_score"] if folded else kt["score"]
+    if folded:
+        score_bytes += append_alg_bytes(L[0].new_pos.cpu().tolist(), 2)
     achieved = score_bytes / (score_us * 1e-6) / 1e9
     if wl.m >= PREFILL_MIN_ROWS:
         # many-row scoring runs on the bf16 matrix cores with three-plane
@@ -491,7 +509,9 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                    "kernel": "score_fewrow_kernel" if seq_nb is None else "score_fewrow_kernel (one row per sequence)",
+                    "kernel": ("score_fewrow_kernel (append folded in)" if folded else
+                               "score_fewrow_kernel" if seq_nb is None else
+                               "score_fewrow_kernel (one row per sequence)"),
                     "traffic": stored_traffic() if wl.name == "verify_262k" else None,
                     "bytes_per_launch": score_bytes, "launch_us": score_us}
     # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries

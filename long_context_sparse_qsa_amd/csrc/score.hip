@@ -28,11 +28,15 @@
 // slots in the selection workspace (plain stores, no atomics).
 //
 // With APPEND the launch also does the index-key append of the new tokens
-// (one sequence): one extra workgroup writes their keys to the cache and
-// pools every block they complete, as the append kernel does; the wave that scores
-// such a block recomputes its pooled key in registers from the same four keys
-// (new ones from the call, earlier ones from the cache, which this launch
-// does not write there) instead of reading the value being written.
+// (one sequence) in two extra columns of workgroups: one writes their keys to
+// the cache and pools every block they complete, as the append kernel does;
+// the other scores those blocks for its row group, pooling each in registers
+// from the same four keys (new ones from the call, earlier ones from the
+// cache, which this launch does not write there) and running the scoring
+// waves' exact MFMA sequence on it, so every score is bit-identical to an
+// append followed by a plain scoring launch.  The scoring waves skip those
+// blocks' stores; they learn which blocks they are from one position per
+// lane, loaded with the index queries ahead of the pooled stream.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "append_common.h"
@@ -84,15 +88,160 @@ struct AppendArgs {
   int64_t capacity;
 };
 
-// Pooled elements dims dim..dim+3 of a block from its four key rows,
-// exactly as the append computes them.
-template <class EQ>
-__device__ __forceinline__ float4 pooled4_of(const typename EQ::T* const* rows, int dim) {
-  float4 x[kBlockTokens];
+// A new token at position p completes a block whose score this launch
+// writes from the keys rather than from the pooled stream.
+__device__ __forceinline__ bool completes_scored_block(int64_t p, int64_t capacity, int64_t nb_max) {
+  return p >= 0 && p < capacity && (p & 3) == 3 && (p >> 2) < nb_max;
+}
+
+// Index-query operand of a row group, as loaded: column i16 = (row 4 st +
+// i16 / 4, head i16 % 4) of set st, dims 16c + 4 kq .. + 3.
+template <class EQ, int NSET>
+__device__ __forceinline__ void load_q_operand(const typename EQ::T* __restrict__ idx_q, int m0, int rows, int i16,
+                                               int kq, typename QRaw<EQ>::T (&qraw)[NSET][kChunks]) {
 #pragma unroll
-  for (int j = 0; j < kBlockTokens; ++j) x[j] = q_to_f4<EQ>(load_q_raw<EQ>(rows[j] + dim));
-  return make_float4(pool4(x[0].x, x[1].x, x[2].x, x[3].x), pool4(x[0].y, x[1].y, x[2].y, x[3].y),
-                     pool4(x[0].z, x[1].z, x[2].z, x[3].z), pool4(x[0].w, x[1].w, x[2].w, x[3].w));
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    const int h = i16 & 3;
+    const typename EQ::T* qsrc = idx_q + ((int64_t)(m0 + (r < rows ? r : 0)) * kIndexHeads + h) * kIndexDim + 4 * kq;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) qraw[st][c] = load_q_raw<EQ>(qsrc + 16 * c);
+  }
+}
+
+template <class EQ, int NSET>
+__device__ __forceinline__ void q_operand(const typename QRaw<EQ>::T (&qraw)[NSET][kChunks], int rows, int i16,
+                                          float4 (&bq)[NSET][kChunks]) {
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const bool live = st * 4 + (i16 >> 2) < rows;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(qraw[st][c]) : zero4();
+  }
+}
+
+// Scores of one 16-block group against every column set: sv[st][v] is the
+// score of block 4 kq + v of the group for row 4 st + i16 / 4 (the 4 heads'
+// ReLU'd dot products summed by two lane shuffles, then scaled).
+template <int NSET>
+__device__ __forceinline__ void group_scores(const float4 (&a)[kChunks], const float4 (&bq)[NSET][kChunks],
+                                             float (&sv)[NSET][4]) {
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].x, bq[st][c].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].y, bq[st][c].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].z, bq[st][c].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c].w, bq[st][c].w, acc, 0, 0, 0);
+    }
+    // acc[v] = D[4*kq + v][i16]: block 4kq + v of the group, column i16
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = fmaxf(acc[v], 0.f);
+      x += __shfl_xor(x, 1, kWave);
+      x += __shfl_xor(x, 2, kWave);
+      sv[st][v] = x * kScoreScale;
+    }
+  }
+}
+
+// The folded append's second extra workgroup of each row group: scores of
+// the blocks the new tokens complete, one block per wave at a time.  The
+// block's pooled key is built in every A row and goes through the scoring
+// waves' MFMA sequence (an output element depends only on its own A row and
+// B column), so the score equals theirs on the stored pooled key.
+template <class EQ, int NSET, int RPG, bool HIST>
+__device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int M,
+                                   const int64_t* __restrict__ row_pos, int64_t nb_max, float* __restrict__ scores,
+                                   int64_t ld, uint32_t* __restrict__ ws, const AppendArgs& ap) {
+  using T = typename EQ::T;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int i16 = lane & 15;
+  const int kq = lane >> 4;
+  const int m0 = blockIdx.y * RPG;
+  const int rows = min(RPG, M - m0);
+  // positions of tokens i-3..i in one vector load: lane j % 4 loads token
+  // i-3+j (index clamped into the call); issued first, so the wave's first
+  // block needs one round trip for positions and one for its keys
+  auto load_pos4 = [&](int i) -> int64_t {
+    int il = i - (kBlockTokens - 1) + (lane & 3);
+    il = il < 0 ? 0 : (il < ap.n_new ? il : ap.n_new - 1);
+    return ap.pos[il];
+  };
+  int i = __builtin_amdgcn_readfirstlane(wave);
+  int64_t pl = load_pos4(i);
+  typename QRaw<EQ>::T qraw[NSET][kChunks];
+  load_q_operand<EQ, NSET>(idx_q, m0, rows, i16, kq, qraw);
+  int64_t nb_row[NSET];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    nb_row[st] = r < rows ? clamp_nb(row_pos[m0 + r], nb_max) : 0;
+  }
+  float4 bq[NSET][kChunks];
+  q_operand<EQ, NSET>(qraw, rows, i16, bq);
+  const T* nw = static_cast<const T*>(ap.new_idx);
+  const T* ca = static_cast<const T*>(ap.cache);
+  const int64_t rw = sel::row_words(nb_max);
+  const int64_t smp_off = sel::sample_off(nb_max);
+  for (; i < ap.n_new; i += kWavesPerWG) {
+    const int64_t cur = pl;
+    pl = load_pos4(i + kWavesPerWG);  // the wave's next token, in flight meanwhile
+    int64_t pw[kBlockTokens];  // wave-uniform copies
+#pragma unroll
+    for (int j = 0; j < kBlockTokens; ++j) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cur, j);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)cur >> 32), j);
+      pw[j] = (int64_t)(((uint64_t)hi << 32) | lo);
+    }
+    const int64_t p = pw[kBlockTokens - 1];
+    // key rows: from this call when the token is in it, else from the cache
+    // (the append kernel's rule)
+    const T* krow[kBlockTokens];
+#pragma unroll
+    for (int j = 0; j < kBlockTokens; ++j) {
+      const int back = kBlockTokens - 1 - j;
+      const int ij = i - back;
+      const bool here = back == 0 || (ij >= 0 && pw[j] == p - back);
+      krow[j] = here ? nw + (int64_t)ij * kIndexDim : ca + (p - back) * kIndexDim;
+    }
+    if (!completes_scored_block(p, ap.capacity, nb_max)) continue;
+    const int64_t b = p >> 2;
+    // the block's pooled key in every A row (all loads in flight together)
+    typename QRaw<EQ>::T kraw[kChunks][kBlockTokens];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+      for (int j = 0; j < kBlockTokens; ++j) kraw[c][j] = load_q_raw<EQ>(krow[j] + 16 * c + 4 * kq);
+    __builtin_amdgcn_sched_barrier(0);  // keep every key load ahead of the first use
+    float4 a[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      float4 x[kBlockTokens];
+#pragma unroll
+      for (int j = 0; j < kBlockTokens; ++j) x[j] = q_to_f4<EQ>(kraw[c][j]);
+      a[c] = make_float4(pool4(x[0].x, x[1].x, x[2].x, x[3].x), pool4(x[0].y, x[1].y, x[2].y, x[3].y),
+                         pool4(x[0].z, x[1].z, x[2].z, x[3].z), pool4(x[0].w, x[1].w, x[2].w, x[3].w));
+    }
+    float sv[NSET][4];
+    group_scores<NSET>(a, bq, sv);
+    const int64_t bb = (b & ~(int64_t)15) + 4 * kq;
+#pragma unroll
+    for (int st = 0; st < NSET; ++st) {
+      const int r = st * 4 + (i16 >> 2);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if ((i16 & 3) == 0 && r < rows && bb + v == b && b < nb_row[st]) {
+          scores[(int64_t)(m0 + r) * ld + b] = sv[st][v];
+          if (HIST && sel::sampled((uint32_t)b))
+            reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + smp_off + (b >> 4)] = sv[st][v];
+        }
+      }
+    }
+  }
 }
 
 template <class EQ, int NSET, int RPG, bool HIST, bool APPEND>
@@ -103,17 +252,25 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
                     int64_t nb_max, float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ ws,
                     AppendArgs ap) {
   static_assert(RPG <= 4 * NSET, "rows per group exceed the column sets");
+  int bx = blockIdx.x;
   if constexpr (APPEND) {
-    // the grid's extra last column of workgroups: row group 0's does the
-    // append (cache rows and completed blocks), alongside the scoring
-    if (blockIdx.x == gridDim.x - 1) {
-      if (blockIdx.y == 0)
+    // the grid's two extra first columns (dispatched first, so that their
+    // dependent loads start before the pooled stream fills the memory
+    // queues): the append (row group 0's workgroup writes the cache rows and
+    // the completed blocks' pooled keys) and the completed blocks' scores
+    // (every row group's)
+    if (bx < 2) {
+      if (bx == 1) {
+        score_fresh_blocks<EQ, NSET, RPG, HIST>(idx_q, M, row_pos, nb_max, scores, ld, ws, ap);
+      } else if (blockIdx.y == 0) {
         for (int e = threadIdx.x; e < ap.n_new * kIndexDim; e += kWave * kWavesPerWG)
           append_token_dim<EQ>(static_cast<const typename EQ::T*>(ap.new_idx), ap.pos, nullptr,
                                static_cast<typename EQ::T*>(ap.cache), ap.pooled, 1, ap.capacity, e / kIndexDim,
                                e % kIndexDim);
+      }
       return;
     }
+    bx -= 2;
   }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -124,23 +281,19 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   // index-query operand are small and cached; issued before the pooled
   // stream, their waits leave the pooled loads in flight.  The pooled loads
   // depend only on nb_max (the host bound), not on the row positions.
-  const int64_t wave_b0 = (int64_t)blockIdx.x * kBlocksPerWG + wave * kBlocksPerWave;
+  const int64_t wave_b0 = (int64_t)bx * kBlocksPerWG + wave * kBlocksPerWave;
   if (wave_b0 >= nb_max) return;
   const int i16 = lane & 15;   // A row (block in group) / B column
   const int kq = lane >> 4;    // k slot 0..3
   int64_t pos_r[RPG];
 #pragma unroll
   for (int r = 0; r < RPG; ++r) pos_r[r] = row_pos[m0 + (r < rows ? r : 0)];
-  // index-query operand: column j = row*4 + head of set st, dims 16c + 4*kq + t
   typename QRaw<EQ>::T qraw[NSET][kChunks];
-#pragma unroll
-  for (int st = 0; st < NSET; ++st) {
-    const int r = st * 4 + (i16 >> 2);
-    const int h = i16 & 3;
-    const typename EQ::T* qsrc = idx_q + ((int64_t)(m0 + (r < rows ? r : 0)) * kIndexHeads + h) * kIndexDim + 4 * kq;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) qraw[st][c] = load_q_raw<EQ>(qsrc + 16 * c);
-  }
+  load_q_operand<EQ, NSET>(idx_q, m0, rows, i16, kq, qraw);
+  // folded append: one new token's position per lane (lanes past the count
+  // repeat the last; 1 <= n_new <= 64)
+  int64_t new_p = -1;
+  if constexpr (APPEND) new_p = ap.pos[lane < ap.n_new ? lane : ap.n_new - 1];
   const int s = row_seq ? row_seq[m0] : 0;
   const bool seq_ok = s >= 0 && s < n_seq;
   const int64_t rw = sel::row_words(nb_max);
@@ -157,47 +310,6 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) a[g][c] = *reinterpret_cast<const float4*>(src + 16 * c);
   }
-  if constexpr (APPEND) {
-    // blocks this call completes inside the wave's range: their pooled keys
-    // come from the keys, not from memory (wave-uniform loop; few tokens).
-    // Issued after the pooled stream: waiting for the positions first would
-    // hold back every wave's stream for the sake of one wave.
-    using T = typename EQ::T;
-    const T* nw = static_cast<const T*>(ap.new_idx);
-    const T* ca = static_cast<const T*>(ap.cache);
-    int64_t w1 = -1, w2 = -1, w3 = -1;  // positions of tokens i-1, i-2, i-3
-    for (int i0 = 0; i0 < ap.n_new; i0 += 4) {
-      int64_t pb[4];  // four positions per round trip
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pb[u] = i0 + u < ap.n_new ? ap.pos[i0 + u] : -1;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u;
-        const int64_t p = pb[u];
-        const int64_t rel = (p >> 2) - wave_b0;
-        if (i < ap.n_new && (p & 3) == 3 && p < ap.capacity && rel >= 0 && rel < kBlocksPerWave &&
-            (p >> 2) < nb_max && i16 == (int)(rel & 15)) {
-          // key rows of the block: from this call when the token is in it
-          // (consecutive ascending positions), else from the cache
-          const int64_t b4 = p - 3;
-          const T* rows[kBlockTokens] = {
-              w3 == b4 ? nw + (int64_t)(i - 3) * kIndexDim : ca + b4 * kIndexDim,
-              w2 == b4 + 1 ? nw + (int64_t)(i - 2) * kIndexDim : ca + (b4 + 1) * kIndexDim,
-              w1 == b4 + 2 ? nw + (int64_t)(i - 1) * kIndexDim : ca + (b4 + 2) * kIndexDim,
-              nw + (int64_t)i * kIndexDim};
-#pragma unroll
-          for (int g = 0; g < kGroupsPerWave; ++g) {
-            if (g != (int)(rel >> 4)) continue;
-#pragma unroll
-            for (int c = 0; c < kChunks; ++c) a[g][c] = pooled4_of<EQ>(rows, 16 * c + 4 * kq);
-          }
-        }
-        w3 = w2;
-        w2 = w1;
-        w1 = p;
-      }
-    }
-  }
 
   int64_t nb_r[RPG];
   int64_t nb_hi = 0;
@@ -210,68 +322,49 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   if (!active) return;
 
   float4 bq[NSET][kChunks];
+  q_operand<EQ, NSET>(qraw, rows, i16, bq);
   int64_t nb_row[NSET];
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {
     const int r = st * 4 + (i16 >> 2);
-    const bool live = r < rows;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(qraw[st][c]) : zero4();
     int64_t n = 0;
 #pragma unroll
     for (int rr = 0; rr < RPG; ++rr) n = (r == rr) ? nb_r[rr] : n;  // no dynamic register indexing
     nb_row[st] = n;
   }
 
-  float sv[kGroupsPerWave][NSET][4];
+  // blocks of this wave whose scores the fresh-block workgroup writes
+  uint32_t fresh = 0u;
+  if constexpr (APPEND) {
+    const int64_t rel = (new_p >> 2) - wave_b0;
+    fresh = completes_scored_block(new_p, ap.capacity, nb_max) && rel >= 0 && rel < kBlocksPerWave
+                ? 1u << rel : 0u;
 #pragma unroll
-  for (int g = 0; g < kGroupsPerWave; ++g) {
-#pragma unroll
-    for (int st = 0; st < NSET; ++st) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].x, bq[st][c].x, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].y, bq[st][c].y, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].z, bq[st][c].z, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][c].w, bq[st][c].w, acc, 0, 0, 0);
-        }
-      }
-      // acc[v] = D[4*kq + v][i16]: block wave_b0 + 16g + 4kq + v, column i16.
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = fmaxf(acc[v], 0.f);
-        x += __shfl_xor(x, 1, kWave);
-        x += __shfl_xor(x, 2, kWave);
-        sv[g][st][v] = x * kScoreScale;
-      }
-      const int r = st * 4 + (i16 >> 2);
-      if (active && (i16 & 3) == 0 && r < rows) {
-        float* dst = scores + (int64_t)(m0 + r) * ld;
-        const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (bb + v < nb_row[st]) dst[bb + v] = sv[g][st][v];
-      }
-    }
+    for (int off = kWave / 2; off > 0; off >>= 1) fresh |= (uint32_t)__shfl_xor((int)fresh, off, kWave);
   }
 
-  if constexpr (HIST) {
-    // one sampled block per 16-block group: its score goes to the group's slot
+  // group by group, so that the first group's matrix work and stores
+  // proceed while the second group's pooled loads are still arriving
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
+  for (int g = 0; g < kGroupsPerWave; ++g) {
+    float sv[NSET][4];
+    group_scores<NSET>(a[g], bq, sv);
+    const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
 #pragma unroll
-      for (int st = 0; st < NSET; ++st) {
-        const int r = st * 4 + (i16 >> 2);
-        const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
+    for (int st = 0; st < NSET; ++st) {
+      const int r = st * 4 + (i16 >> 2);
+      if ((i16 & 3) != 0 || r >= rows) continue;
+      float* dst = scores + (int64_t)(m0 + r) * ld;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if ((i16 & 3) == 0 && r < rows && bb + v < nb_row[st] && sel::sampled((uint32_t)(bb + v)))
-            reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + smp_off + ((bb + v) >> 4)] =
-                sv[g][st][v];
+      for (int v = 0; v < 4; ++v) {
+        const bool keep = bb + v < nb_row[st] && !((fresh >> (g * kGroupBlocks + 4 * kq + v)) & 1u);
+        if (keep) dst[bb + v] = sv[st][v];
+        // one sampled block per 16-block group: its score goes to the group's slot
+        if (HIST && keep && sel::sampled((uint32_t)(bb + v)))
+          reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + smp_off + ((bb + v) >> 4)] = sv[st][v];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -283,7 +376,7 @@ hipError_t launch_fewrow(const void* idx_q, int M, const int64_t* row_pos, const
   if (wgs == 0) return hipSuccess;
   dim3 grid((unsigned)wgs, (unsigned)((M + RPG - 1) / RPG));
   if (ap)
-    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true>), dim3(grid.x + 1, grid.y),
+    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true>), dim3(grid.x + 2, grid.y),
                        dim3(kWave * kWavesPerWG), 0, stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
                        capacity, nb_max, scores, ld, ws, *ap);
   else
