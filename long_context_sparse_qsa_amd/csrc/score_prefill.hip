@@ -5,35 +5,41 @@
 //
 // Prefill chunks score thousands of rows of one sequence against the same
 // pooled keys, a dense contraction: (rows x 4 heads) x 128 dims against
-// blocks.  It runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with
-// float32 accumulation.  Index queries are bf16 already.  Each float32
-// pooled key x is split into three bf16 planes, hi = bf16(x), mid =
-// bf16(x - hi), lo = bf16(x - hi - mid), whose sum is x (24 significand
-// bits); bf16 x bf16 products are exact in float32, so the three-plane sum
-// matches a float32 dot product to float32 accumulation error, at three bf16
-// matrix ops per float32 one (the bf16 rate is 16 times the float32 rate).
+// blocks.  It runs on the bf16 matrix cores with float32 accumulation, on
+// v_mfma_f32_32x32x16_bf16 (on this chip it sustains twice the rate of the
+// 16x16x32 form).  Index queries are bf16 already.  Each float32 pooled key
+// x is split into three bf16 planes, hi = bf16(x), mid = bf16(x - hi), lo =
+// bf16(x - hi - mid), whose sum is x (24 significand bits); bf16 x bf16
+// products are exact in float32, so the three-plane sum matches a float32
+// dot product to float32 accumulation error, at three bf16 matrix ops per
+// float32 one.
 //
-// Workgroup tile: 64 consecutive blocks x 128 rows.  The tile's pooled keys
-// are loaded once (coalesced), split into planes and staged in LDS with
-// padded 272-byte rows (A-operand reads are then free of bank conflicts).
-// Each of the 4 waves owns 32 rows = 8 column groups of (4 rows x 4 heads)
-// whose index-query operands stay in VGPRs; per 16-block group it runs
-// 8 groups x 4 k-steps x 3 planes MFMAs, then ReLU's, sums the 4 heads with
-// two lane shuffles and stores the scores.  Blocks at or past a row's own
-// block count are not stored.  With a selection workspace the epilogue
-// also stores the score sample of every 16-block group (as the few-row
-// variant does).
+// Operands: A = 32 (row, head) pairs (8 rows x 4 heads) x 16 dims of index
+// queries, B = 16 dims x 32 blocks of one pooled plane.  An output lane then
+// holds, for its block, the 4 heads of each of its rows in consecutive
+// accumulator registers, so the ReLU'd head sum needs no lane exchange.
+//
+// Work: tiles of 64 consecutive blocks x 128 rows.  A workgroup (4 waves,
+// 32 rows each) keeps its rows' index-query operands in VGPRs and walks a
+// contiguous run of block tiles (about two workgroups per compute unit in
+// all).  Per tile the pooled keys are split into planes and staged in LDS
+// with padded 272-byte rows; the next tile's loads are issued right after,
+// so they arrive during the tile's matrix work.  Per 32-block group a wave
+// runs 4 column groups x 8 k-steps x 3 planes MFMAs, then ReLU's and sums
+// the heads and stores.  Blocks at or past a row's own block count are not
+// stored.  With a selection workspace the epilogue also stores the score
+// sample of every 16-block group (as the few-row variant does).
 //
 // Two more modes serve the memory-flat score -> top-k (no score matrix):
-//  - sample only: the tile's 64 A rows are the sampled blocks of 64
+//  - sample only: the tile's 64 B columns are the sampled blocks of 64
 //    consecutive 16-block groups, and their scores go to the rows' samples;
-//  - emit: after the full scoring, each row keeps only its blocks whose
-//    score digit reaches the row's threshold.  A wave counts its rows'
-//    candidates over the tile (ballots), reserves space with one atomic add
-//    per row (all issued together, one round trip) and appends the (key,
-//    block) pairs to the row's candidate slots in no particular order; slots
-//    past the capacity are dropped (the count still records them, which
-//    sends the row to the exact selection).
+//  - emit: after scoring a tile, each row keeps only its blocks whose score
+//    digit reaches the row's threshold.  A wave counts its rows' candidates
+//    (ballots), reserves space with one atomic add per row (all issued
+//    together, one round trip) and appends the (key, block) pairs to the
+//    row's candidate slots in no particular order; slots past the capacity
+//    are dropped (the count still records them, which sends the row to the
+//    exact selection).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
@@ -43,7 +49,7 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 enum PfMode { kPfScores = 0, kPfScoresSample = 1, kPfSampleOnly = 2, kPfEmit = 3 };
 
@@ -58,14 +64,16 @@ struct FlatArgs {
   int k;
 };
 
-constexpr int kPfWaves = 4;
-constexpr int kPfRowsPerWave = 32;
+constexpr int kPfWaves = 8;
+constexpr int kPfRowsPerWave = 16;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // 128 rows per workgroup
-constexpr int kPfCg = kPfRowsPerWave / 4;           // 8 column groups per wave
-constexpr int kPfBlocks = 64;                       // blocks per workgroup
-constexpr int kPfGroups = kPfBlocks / 16;           // 16-block MFMA row groups
-constexpr int kPfKs = kIndexDim / 32;               // 4 k-steps of 32 dims
+constexpr int kPfCg = kPfRowsPerWave / 8;           // 2 groups of 8 rows (32 (row, head) pairs) per wave
+constexpr int kPfBlocks = 64;                       // blocks per tile
+constexpr int kPfBg = kPfBlocks / 32;               // 32-block MFMA column groups per tile
+constexpr int kPfKs = kIndexDim / 16;               // 8 k-steps of 16 dims
 constexpr int kPfRowWords = kIndexDim / 2 + 4;      // bf16 plane row + 16 B pad, in 32-bit words
+constexpr int kPfSlots = 256;                       // workgroups in flight: 1 per compute unit
+constexpr int kPfF4 = kPfBlocks * kIndexDim / 4 / (kWave * kPfWaves);  // 4 float4 per thread per tile
 constexpr float kScoreScale = 0.08838834764831845f; // 1/sqrt(128)
 
 // Three bf16 planes of a float32 value (round to nearest even each time).
@@ -77,183 +85,224 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
   lo = f32_to_bf16_bits(r2);
 }
 
+// The pooled keys of tile t (coalesced: float4 idx of the tile per thread
+// and step); in sample-only mode the tile's blocks are the sampled blocks of
+// 64 consecutive 16-block groups.
 template <int MODE>
-__global__ void __launch_bounds__(kWave * kPfWaves, 2)
-score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
-                     const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores,
-                     int64_t ld, uint32_t* __restrict__ ws, FlatArgs fa) {
-  __shared__ __align__(16) uint32_t planes[3][kPfBlocks * kPfRowWords];
-  __shared__ int64_t nb_sh[kPfRows];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int n16 = lane & 15;
-  const int g4 = lane >> 4;
-  const int64_t b0 = (int64_t)blockIdx.x * kPfBlocks;  // first block (sample only: first sample group)
-  const int r0 = blockIdx.y * kPfRows;
-
-  // ---- loads: the tile's pooled keys (coalesced), this wave's index-query
-  // operands, the tile's row positions
-  constexpr int kF4 = kPfBlocks * kIndexDim / 4 / (kWave * kPfWaves);  // 8 float4 per thread
-  float4 pk[kF4];
+__device__ __forceinline__ void load_tile(const float* __restrict__ pooled, int64_t nb_max, int64_t t, int tid,
+                                          float4 (&pk)[kPfF4]) {
 #pragma unroll
-  for (int i = 0; i < kF4; ++i) {
-    const int idx = tid + i * kWave * kPfWaves;  // float4 index inside the tile
-    int64_t b = b0 + idx / (kIndexDim / 4);
-    if constexpr (MODE == kPfSampleOnly) b = b * 16 + sel::sample_offset((uint32_t)b);  // the group's sampled block
+  for (int i = 0; i < kPfF4; ++i) {
+    const int idx = tid + i * kWave * kPfWaves;
+    int64_t b = t * kPfBlocks + idx / (kIndexDim / 4);
+    if constexpr (MODE == kPfSampleOnly) b = b * 16 + sel::sample_offset((uint32_t)b);
     const int64_t bl = b < nb_max ? b : nb_max - 1;  // past the last block: re-read it, never stored
     pk[i] = *reinterpret_cast<const float4*>(pooled + bl * kIndexDim + (idx % (kIndexDim / 4)) * 4);
   }
-  // B operand of column group cg: column n16 = (row 4 cg + n16 / 4, head n16 % 4),
-  // k-step s: dims 32 s + 8 g4 .. + 7
-  uint4 bq[kPfCg][kPfKs];
+}
+
+// Splits a tile's pooled keys (as load_tile leaves them) into the three
+// planes and stages them in LDS.
+__device__ __forceinline__ void stage_tile(const float4 (&pk)[kPfF4], int tid, uint32_t (*planes)[kPfBlocks * kPfRowWords]) {
+#pragma unroll
+  for (int i = 0; i < kPfF4; ++i) {
+    const int idx = tid + i * kWave * kPfWaves;
+    const int blk = idx / (kIndexDim / 4);
+    const int d4 = idx % (kIndexDim / 4);
+    uint32_t hi[4], md[4], lo[4];
+    split3(pk[i].x, hi[0], md[0], lo[0]);
+    split3(pk[i].y, hi[1], md[1], lo[1]);
+    split3(pk[i].z, hi[2], md[2], lo[2]);
+    split3(pk[i].w, hi[3], md[3], lo[3]);
+    const int w = blk * kPfRowWords + d4 * 2;  // 4 bf16 = 2 words
+    *reinterpret_cast<uint2*>(&planes[0][w]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    *reinterpret_cast<uint2*>(&planes[1][w]) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
+    *reinterpret_cast<uint2*>(&planes[2][w]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+  }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(kWave * kPfWaves, 1)
+score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
+                     const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores,
+                     int64_t ld, uint32_t* __restrict__ ws, FlatArgs fa, int n_rt, int64_t n_tiles, int n_chunks) {
+  __shared__ __align__(16) uint32_t planes[2][3][kPfBlocks * kPfRowWords];  // two tiles in turn
+  __shared__ int64_t nb_sh[kPfRows];
+  __shared__ uint32_t thr_sh[kPfRows];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int j32 = lane & 31;  // A row ((row, head) pair) / B column (block) / D column
+  const int h = lane >> 5;    // k half of the operands; row parity of the outputs
+  // this workgroup: row tile rt, block tiles [t_begin, t_end)
+  const int rt = blockIdx.x % n_rt;
+  const int chunk = blockIdx.x / n_rt;
+  const int64_t t_begin = n_tiles * chunk / n_chunks;
+  const int64_t t_end = n_tiles * (chunk + 1) / n_chunks;
+  if (t_begin >= t_end) return;
+  const int r0 = rt * kPfRows;
+
+  float4 pk[kPfF4];
+  load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);
+  // A operand of row group cg: A row j32 = (row 8 cg + j32 / 4 of the wave's
+  // 32, head j32 % 4), k-step s: dims 16 s + 8 h .. + 7
+  uint4 aq[kPfCg][kPfKs];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg) {
-    int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
+    int r = r0 + wave * kPfRowsPerWave + 8 * cg + (j32 >> 2);
     r = r < M ? r : M - 1;
-    const uint16_t* src = idx_q + ((int64_t)r * kIndexHeads + (n16 & 3)) * kIndexDim + 8 * g4;
+    const uint16_t* src = idx_q + ((int64_t)r * kIndexHeads + (j32 & 3)) * kIndexDim + 8 * h;
 #pragma unroll
-    for (int s = 0; s < kPfKs; ++s) bq[cg][s] = *reinterpret_cast<const uint4*>(src + 32 * s);
+    for (int s = 0; s < kPfKs; ++s) aq[cg][s] = *reinterpret_cast<const uint4*>(src + 16 * s);
   }
-  __shared__ uint32_t thr_sh[kPfRows];
   if (tid < kPfRows) {
     const int r = r0 + tid;
     nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
     if constexpr (MODE == kPfEmit) thr_sh[tid] = r < M ? fa.thr[r] : 0u;
   }
-  // ---- split into planes, stage in LDS
-#pragma unroll
-  for (int i = 0; i < kF4; ++i) {
-    const int idx = tid + i * kWave * kPfWaves;
-    const int blk = idx / (kIndexDim / 4);
-    const int d4 = idx % (kIndexDim / 4);
-    uint32_t h[4], md[4], lo[4];
-    split3(pk[i].x, h[0], md[0], lo[0]);
-    split3(pk[i].y, h[1], md[1], lo[1]);
-    split3(pk[i].z, h[2], md[2], lo[2]);
-    split3(pk[i].w, h[3], md[3], lo[3]);
-    const int w = blk * kPfRowWords + d4 * 2;  // 4 bf16 = 2 words
-    *reinterpret_cast<uint2*>(&planes[0][w]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    *reinterpret_cast<uint2*>(&planes[1][w]) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
-    *reinterpret_cast<uint2*>(&planes[2][w]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-  }
-  __syncthreads();
-
-  int64_t nb_row[kPfCg];
-#pragma unroll
-  for (int cg = 0; cg < kPfCg; ++cg) nb_row[cg] = nb_sh[wave * kPfRowsPerWave + 4 * cg + (n16 >> 2)];
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
+  const uint64_t half = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;  // the lane's row in a ballot
+  const uint64_t lane_lt = (1ull << lane) - 1ull;
 
-  // emit mode: the key of the lane's block in every (16-block group, column
-  // group), which of them are candidates, and the candidates of the lane's
-  // row so far (the 16-block groups are unrolled so the keys stay in VGPRs)
-  uint32_t ekey[kPfGroups][kPfCg];
-  uint32_t eflag = 0u;
-  uint32_t run[kPfCg];
+  // Pipeline: tile t's planes are in buffer (t - t_begin) % 2 when its
+  // matrix work starts; meanwhile tile t+1's raw keys (loaded during tile
+  // t-1) are split into the other buffer and tile t+2's loads are in flight.
+  // Loads past the run re-read its last tile (never used).
+  stage_tile(pk, tid, planes[0]);
+  load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
+  __syncthreads();
+  // block count of each output row of the lane (row 8 cg + 2q + h of the
+  // wave's 32; 0 past the last row), held in registers for every tile
+  int64_t nbq[kPfCg][4];
 #pragma unroll
-  for (int cg = 0; cg < kPfCg; ++cg) run[cg] = 0u;
-  const uint64_t rmask = 0x000F000F000F000Full << (4 * (n16 >> 2));  // the lane's row in a ballot
-  (void)ekey;
+  for (int cg = 0; cg < kPfCg; ++cg)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int cur = (int)((t - t_begin) & 1);
+    float4 pn[kPfF4];
+    load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pn);
+    const int64_t b0 = t * kPfBlocks;
+    // emit mode: the keys of the lane's (block, row) outputs and which of
+    // them are candidates, and each row's candidate count in the tile
+    uint32_t ekey[kPfBg][kPfCg][4];
+    uint32_t eflag = 0u;
+    uint32_t run = 0u;  // lane L < 32: candidates of row 8 (L / 8) + L % 8 of the wave
+    (void)ekey;
 
+    // one accumulator set per 32-block group, so that a group's epilogue
+    // can overlap the next group's matrix work
+    f32x16_t accs[kPfBg][kPfCg];
 #pragma unroll
-  for (int bg = 0; bg < kPfGroups; ++bg) {
-    f32x4_t acc[kPfCg];
+    for (int bg = 0; bg < kPfBg; ++bg) {
+      f32x16_t (&acc)[kPfCg] = accs[bg];
 #pragma unroll
-    for (int cg = 0; cg < kPfCg; ++cg) acc[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
-    for (int s = 0; s < kPfKs; ++s) {
+        for (int e = 0; e < 16; ++e) acc[cg][e] = 0.f;
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        // A operand: block bg*16 + n16, dims 32 s + 8 g4 .. + 7 of plane pl
-        const uint4 a = *reinterpret_cast<const uint4*>(
-            &planes[pl][(bg * 16 + n16) * kPfRowWords + (32 * s + 8 * g4) / 2]);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+      for (int s = 0; s < kPfKs; ++s) {
 #pragma unroll
-        for (int cg = 0; cg < kPfCg; ++cg)
-          acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[cg][s]), acc[cg],
-                                                           0, 0, 0);
+        for (int pl = 0; pl < 3; ++pl) {
+          // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
+          const uint4 bv = *reinterpret_cast<const uint4*>(
+              &planes[cur][pl][(bg * 32 + j32) * kPfRowWords + (16 * s + 8 * h) / 2]);
+#pragma unroll
+          for (int cg = 0; cg < kPfCg; ++cg)
+            acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
+                                                             __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
+        }
       }
-    }
-    // acc[cg][v] = D[4 g4 + v][n16]: block b0 + 16 bg + 4 g4 + v, column n16
-    const int64_t bb = b0 + bg * 16 + 4 * g4;
+      // acc[cg][4q + hd] = D[8q + 4h + hd][j32]: head hd of row 8 cg + 2q + h
+      // (of the wave's 32), block b0 + 32 bg + j32
+      const int64_t b = b0 + bg * 32 + j32;
+      const bool smp = sel::sampled((uint32_t)b);
 #pragma unroll
-    for (int cg = 0; cg < kPfCg; ++cg) {
-      float sv[4];
+      for (int cg = 0; cg < kPfCg; ++cg) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = fmaxf(acc[cg][v], 0.f);
-        x += __shfl_xor(x, 1, kWave);
-        x += __shfl_xor(x, 2, kWave);
-        sv[v] = x * kScoreScale;
-      }
-      const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
-      // sample-only and emit: lane t = n16 % 4 of the row's quad takes slot t
-      const int t = n16 & 3;
-      const float xt = t == 0 ? sv[0] : (t == 1 ? sv[1] : (t == 2 ? sv[2] : sv[3]));
-      if constexpr (MODE == kPfScores || MODE == kPfScoresSample) {
-        if ((n16 & 3) == 0 && r < M) {
-          float* dst = scores + (int64_t)r * ld + bb;
-          if (bb + 3 < nb_row[cg]) {
-            *reinterpret_cast<float4*>(dst) = make_float4(sv[0], sv[1], sv[2], sv[3]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (bb + v < nb_row[cg]) dst[v] = sv[v];
+        for (int q = 0; q < 4; ++q) {
+          float x = fmaxf(acc[cg][4 * q], 0.f) + fmaxf(acc[cg][4 * q + 1], 0.f);
+          x += fmaxf(acc[cg][4 * q + 2], 0.f) + fmaxf(acc[cg][4 * q + 3], 0.f);
+          x *= kScoreScale;
+          const int rl = wave * kPfRowsPerWave + 8 * cg + 2 * q + h;
+          const int r = r0 + rl;
+          const int64_t nbr = nbq[cg][q];  // 0 for rows past M
+          if constexpr (MODE == kPfScores || MODE == kPfScoresSample) {
+            if (b < nbr) {
+              scores[(int64_t)r * ld + b] = x;
+              if (MODE == kPfScoresSample && smp) reinterpret_cast<float*>(ws)[(size_t)r * rw + smp_off + (b >> 4)] = x;
+            }
           }
-          if constexpr (MODE == kPfScoresSample) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (bb + v < nb_row[cg] && sel::sampled((uint32_t)(bb + v)))
-                reinterpret_cast<float*>(ws)[(size_t)r * rw + smp_off + ((bb + v) >> 4)] = sv[v];
+          if constexpr (MODE == kPfSampleOnly) {  // b is the sample group
+            if (b < fa.n_grp && b * 16 + sel::sample_offset((uint32_t)b) < nbr)
+              fa.samples[(int64_t)r * fa.n_grp + b] = x;
+          }
+          if constexpr (MODE == kPfEmit) {
+            const uint32_t key = sel::order_key(x);
+            const bool c = b < nbr && nbr > fa.k && (key >> sel::kDigitShift) >= thr_sh[rl];
+            ekey[bg][cg][q] = key;
+            eflag |= c ? 1u << ((bg * kPfCg + cg) * 4 + q) : 0u;
+            const uint64_t m = __ballot(c);
+            const uint32_t n0 = (uint32_t)__popcll(m & 0x00000000FFFFFFFFull);  // row 8 cg + 2q
+            const uint32_t n1 = (uint32_t)__popcll(m & 0xFFFFFFFF00000000ull);  // row 8 cg + 2q + 1
+            run += lane == 8 * cg + 2 * q ? n0 : (lane == 8 * cg + 2 * q + 1 ? n1 : 0u);
           }
         }
       }
-      if constexpr (MODE == kPfSampleOnly) {  // slot = sample group bb + t
-        const int64_t g = bb + t;
-        if (r < M && g < fa.n_grp && g * 16 + sel::sample_offset((uint32_t)g) < nb_row[cg])
-          fa.samples[(int64_t)r * fa.n_grp + g] = xt;
-      }
-      if constexpr (MODE == kPfEmit) {  // slot = block bb + t
-        const uint32_t key = sel::order_key(xt);
-        const int rl = wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
-        const bool c = r < M && bb + t < nb_row[cg] && nb_row[cg] > fa.k &&
-                       (key >> sel::kDigitShift) >= thr_sh[rl];
-        ekey[bg][cg] = key;
-        eflag |= c ? 1u << (bg * kPfCg + cg) : 0u;
-        run[cg] += (uint32_t)__popcll(__ballot(c) & rmask);
-      }
     }
-  }
 
-  if constexpr (MODE == kPfEmit) {
-    // reserve each row's slots: one atomic per row, all in flight together
-    uint32_t base[kPfCg];
+    if constexpr (MODE == kPfEmit) {
+      // reserve each row's slots: one atomic per row, all in flight together
+      uint32_t base = 0u;
+      {
+        const int r = r0 + wave * kPfRowsPerWave + lane;
+        if (lane < kPfRowsPerWave && r < M && run > 0u) base = atomicAdd(fa.cnt + r, run);
+      }
 #pragma unroll
-    for (int cg = 0; cg < kPfCg; ++cg) {
-      const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
-      uint32_t b = 0u;
-      if (g4 == 0 && (n16 & 3) == 0 && r < M && run[cg] > 0u) b = atomicAdd(fa.cnt + r, run[cg]);
-      base[cg] = b;
-    }
-    const uint64_t lane_lt = (1ull << lane) - 1ull;
+      for (int cg = 0; cg < kPfCg; ++cg) {
 #pragma unroll
-    for (int cg = 0; cg < kPfCg; ++cg) {
-      const int r = r0 + wave * kPfRowsPerWave + 4 * cg + (n16 >> 2);
-      uint32_t pos = (uint32_t)__shfl((int)base[cg], n16 & ~3, kWave);  // from lane 4 (n16 / 4)
+        for (int q = 0; q < 4; ++q) {
+          const int rw8 = 8 * cg + 2 * q + h;
+          const int r = r0 + wave * kPfRowsPerWave + rw8;
+          uint32_t pos = (uint32_t)__shfl((int)base, rw8, kWave);
 #pragma unroll
-      for (int bg = 0; bg < kPfGroups; ++bg) {
-        const bool c = (eflag >> (bg * kPfCg + cg)) & 1u;
-        const uint64_t mk = __ballot(c) & rmask;
-        const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
-        if (c && p < (uint32_t)sel::kFlatCap) {
-          fa.keys[(int64_t)r * sel::kFlatCap + p] = ekey[bg][cg];
-          fa.ids[(int64_t)r * sel::kFlatCap + p] = (uint32_t)(b0 + bg * 16 + 4 * g4 + (n16 & 3));
+          for (int bg = 0; bg < kPfBg; ++bg) {
+            const bool c = (eflag >> ((bg * kPfCg + cg) * 4 + q)) & 1u;
+            const uint64_t mk = __ballot(c) & half;
+            const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
+            if (c && p < (uint32_t)sel::kFlatCap) {
+              fa.keys[(int64_t)r * sel::kFlatCap + p] = ekey[bg][cg][q];
+              fa.ids[(int64_t)r * sel::kFlatCap + p] = (uint32_t)(b0 + bg * 32 + j32);
+            }
+            pos += (uint32_t)__popcll(mk);
+          }
         }
-        pos += (uint32_t)__popcll(mk);
       }
     }
+    if (t + 1 < t_end) stage_tile(pk, tid, planes[cur ^ 1]);
+#pragma unroll
+    for (int i = 0; i < kPfF4; ++i) pk[i] = pn[i];
+    __syncthreads();  // tile t+1 staged; every wave is done with buffer cur
   }
+}
+
+// Grid of the persistent form: row tiles x runs of block tiles, about
+// kPfSlots workgroups in all.
+struct PfGrid {
+  int n_rt;
+  int64_t n_tiles;
+  int n_chunks;
+  unsigned wgs() const { return (unsigned)(n_rt * n_chunks); }
+};
+PfGrid pf_grid(int M, int64_t n_cols) {
+  PfGrid g;
+  g.n_rt = (M + kPfRows - 1) / kPfRows;
+  g.n_tiles = (n_cols + kPfBlocks - 1) / kPfBlocks;
+  const int64_t want = (kPfSlots + g.n_rt - 1) / g.n_rt;
+  g.n_chunks = (int)(want < g.n_tiles ? want : g.n_tiles);
+  if (g.n_chunks < 1) g.n_chunks = 1;
+  return g;
 }
 
 }  // namespace
@@ -262,14 +311,16 @@ hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos
                                 int64_t nb_max, float* scores, int64_t ld, uint32_t* sel_ws,
                                 hipStream_t stream) {
   if (M == 0 || nb_max == 0) return hipSuccess;
-  dim3 grid((unsigned)((nb_max + kPfBlocks - 1) / kPfBlocks), (unsigned)((M + kPfRows - 1) / kPfRows));
+  const PfGrid g = pf_grid(M, nb_max);
   const FlatArgs none{};
   if (sel_ws)
-    hipLaunchKernelGGL(score_prefill_kernel<kPfScoresSample>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws, none);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfScoresSample>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws, none,
+                       g.n_rt, g.n_tiles, g.n_chunks);
   else
-    hipLaunchKernelGGL(score_prefill_kernel<kPfScores>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr, none);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfScores>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr, none,
+                       g.n_rt, g.n_tiles, g.n_chunks);
   return hipGetLastError();
 }
 
@@ -285,15 +336,16 @@ hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* ro
   fa.ids = ws + L.ids;
   fa.n_grp = sel::sample_groups(nb_max);
   fa.k = k_blocks;
-  const unsigned gy = (unsigned)((M + kPfRows - 1) / kPfRows);
   if (emit) {
-    dim3 grid((unsigned)((nb_max + kPfBlocks - 1) / kPfBlocks), gy);
-    hipLaunchKernelGGL(score_prefill_kernel<kPfEmit>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa);
+    const PfGrid g = pf_grid(M, nb_max);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfEmit>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa,
+                       g.n_rt, g.n_tiles, g.n_chunks);
   } else {
-    dim3 grid((unsigned)((fa.n_grp + kPfBlocks - 1) / kPfBlocks), gy);
-    hipLaunchKernelGGL(score_prefill_kernel<kPfSampleOnly>, grid, dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa);
+    const PfGrid g = pf_grid(M, fa.n_grp);
+    hipLaunchKernelGGL(score_prefill_kernel<kPfSampleOnly>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa,
+                       g.n_rt, g.n_tiles, g.n_chunks);
   }
   return hipGetLastError();
 }
