@@ -76,14 +76,30 @@ constexpr int kPfSlots = 256;                       // workgroups in flight: 1 p
 constexpr int kPfF4 = kPfBlocks * kIndexDim / 4 / (kWave * kPfWaves);  // 4 float4 per thread per tile
 constexpr float kScoreScale = 0.08838834764831845f; // 1/sqrt(128)
 
-// Three bf16 planes of a float32 value (round to nearest even each time).
-__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = f32_to_bf16_bits(x);
-  const float r1 = x - __uint_as_float(hi << 16);
-  mid = f32_to_bf16_bits(r1);
-  const float r2 = r1 - __uint_as_float(mid << 16);
-  lo = f32_to_bf16_bits(r2);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two float32 values to packed bf16 (first in the low half), rounded to
+// nearest even by the hardware conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+
+// Three bf16 planes of two float32 values, packed in pairs: hi = bf16(x),
+// mid = bf16(x - hi), lo = bf16(x - hi - mid).  Each difference is exact in
+// float32 (it keeps at most 16, then 8, significant bits), so hi + mid + lo
+// = x for every finite x.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  const float ra = a - __uint_as_float(hi << 16);
+  const float rb = b - __uint_as_float(hi & 0xffff0000u);
+  mid = pack_bf16x2(ra, rb);
+  lo = pack_bf16x2(ra - __uint_as_float(mid << 16), rb - __uint_as_float(mid & 0xffff0000u));
+}
+
+// max(x, 0) on the bit pattern: a float with the sign bit set is a negative
+// integer (one instruction; -0 gives +0).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // The pooled keys of tile t (coalesced: float4 idx of the tile per thread
 // and step); in sample-only mode the tile's blocks are the sampled blocks of
@@ -109,15 +125,13 @@ __device__ __forceinline__ void stage_tile(const float4 (&pk)[kPfF4], int tid, u
     const int idx = tid + i * kWave * kPfWaves;
     const int blk = idx / (kIndexDim / 4);
     const int d4 = idx % (kIndexDim / 4);
-    uint32_t hi[4], md[4], lo[4];
-    split3(pk[i].x, hi[0], md[0], lo[0]);
-    split3(pk[i].y, hi[1], md[1], lo[1]);
-    split3(pk[i].z, hi[2], md[2], lo[2]);
-    split3(pk[i].w, hi[3], md[3], lo[3]);
+    uint2 hi, md, lo;
+    split3_pair(pk[i].x, pk[i].y, hi.x, md.x, lo.x);
+    split3_pair(pk[i].z, pk[i].w, hi.y, md.y, lo.y);
     const int w = blk * kPfRowWords + d4 * 2;  // 4 bf16 = 2 words
-    *reinterpret_cast<uint2*>(&planes[0][w]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    *reinterpret_cast<uint2*>(&planes[1][w]) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
-    *reinterpret_cast<uint2*>(&planes[2][w]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    *reinterpret_cast<uint2*>(&planes[0][w]) = hi;
+    *reinterpret_cast<uint2*>(&planes[1][w]) = md;
+    *reinterpret_cast<uint2*>(&planes[2][w]) = lo;
   }
 }
 
@@ -142,10 +156,8 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   if (t_begin >= t_end) return;
   const int r0 = rt * kPfRows;
 
-  float4 pk[kPfF4];
-  load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);
   // A operand of row group cg: A row j32 = (row 8 cg + j32 / 4 of the wave's
-  // 32, head j32 % 4), k-step s: dims 16 s + 8 h .. + 7
+  // 16, head j32 % 4), k-step s: dims 16 s + 8 h .. + 7
   uint4 aq[kPfCg][kPfKs];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg) {
@@ -155,6 +167,10 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
 #pragma unroll
     for (int s = 0; s < kPfKs; ++s) aq[cg][s] = *reinterpret_cast<const uint4*>(src + 16 * s);
   }
+  // issued after the query operands: the first staging's wait then covers
+  // them as well, and the tile loop never waits for them
+  float4 pk[kPfF4];
+  load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);
   if (tid < kPfRows) {
     const int r = r0 + tid;
     nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
@@ -166,14 +182,17 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   const uint64_t lane_lt = (1ull << lane) - 1ull;
 
   // Pipeline: tile t's planes are in buffer (t - t_begin) % 2 when its
-  // matrix work starts; meanwhile tile t+1's raw keys (loaded during tile
-  // t-1) are split into the other buffer and tile t+2's loads are in flight.
-  // Loads past the run re-read its last tile (never used).
+  // matrix work starts.  After it, tile t+1's raw keys (loaded during tile
+  // t-1) are split into the other buffer, tile t+2's loads are issued, and
+  // only then are tile t's scores stored: a wait for a load also waits for
+  // every memory operation issued before it, so no store sits between a
+  // load and its wait.  Loads past the run re-read its last tile (never
+  // used).
   stage_tile(pk, tid, planes[0]);
   load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
   __syncthreads();
   // block count of each output row of the lane (row 8 cg + 2q + h of the
-  // wave's 32; 0 past the last row), held in registers for every tile
+  // wave's 16; 0 past the last row), held in registers for every tile
   int64_t nbq[kPfCg][4];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg)
@@ -181,18 +200,14 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
     for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int cur = (int)((t - t_begin) & 1);
-    float4 pn[kPfF4];
-    load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pn);
     const int64_t b0 = t * kPfBlocks;
     // emit mode: the keys of the lane's (block, row) outputs and which of
     // them are candidates, and each row's candidate count in the tile
     uint32_t ekey[kPfBg][kPfCg][4];
     uint32_t eflag = 0u;
-    uint32_t run = 0u;  // lane L < 32: candidates of row 8 (L / 8) + L % 8 of the wave
+    uint32_t run = 0u;  // lane L < 16: candidates of row L of the wave
     (void)ekey;
 
-    // one accumulator set per 32-block group, so that a group's epilogue
-    // can overlap the next group's matrix work
     f32x16_t accs[kPfBg][kPfCg];
 #pragma unroll
     for (int bg = 0; bg < kPfBg; ++bg) {
@@ -214,16 +229,24 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
                                                              __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
         }
       }
+    }
+    if (t + 1 < t_end) stage_tile(pk, tid, planes[cur ^ 1]);
+    // (emit mode waits for its atomics' results below: its loads go last)
+    if constexpr (MODE != kPfEmit) load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
+
+#pragma unroll
+    for (int bg = 0; bg < kPfBg; ++bg) {
+      const f32x16_t (&acc)[kPfCg] = accs[bg];
       // acc[cg][4q + hd] = D[8q + 4h + hd][j32]: head hd of row 8 cg + 2q + h
-      // (of the wave's 32), block b0 + 32 bg + j32
+      // (of the wave's 16), block b0 + 32 bg + j32
       const int64_t b = b0 + bg * 32 + j32;
       const bool smp = sel::sampled((uint32_t)b);
 #pragma unroll
       for (int cg = 0; cg < kPfCg; ++cg) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float x = fmaxf(acc[cg][4 * q], 0.f) + fmaxf(acc[cg][4 * q + 1], 0.f);
-          x += fmaxf(acc[cg][4 * q + 2], 0.f) + fmaxf(acc[cg][4 * q + 3], 0.f);
+          float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
+          x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
           x *= kScoreScale;
           const int rl = wave * kPfRowsPerWave + 8 * cg + 2 * q + h;
           const int r = r0 + rl;
@@ -279,10 +302,8 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
           }
         }
       }
+      load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
     }
-    if (t + 1 < t_end) stage_tile(pk, tid, planes[cur ^ 1]);
-#pragma unroll
-    for (int i = 0; i < kPfF4; ++i) pk[i] = pn[i];
     __syncthreads();  // tile t+1 staged; every wave is done with buffer cur
   }
 }
