@@ -125,6 +125,10 @@ int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
  * for b < min(nb(row_pos[m]), nb_max), accumulated in float32.  Entries past
  * a row's block count are left untouched.
  *
+ * 64 or more bf16 rows of one sequence (row_seq NULL) take the many-row
+ * kernel, which needs 64 * ld bytes and 64 * (selection-workspace bytes per
+ * row, about 8 * nb_max) under 2 GiB; larger shapes give QSA_ERR_UNSUPPORTED.
+ *
  *  sel_workspace  NULL, or a qsa_select_topk workspace: the scoring pass then
  *                 also stores the score sample the selection starts from, and
  *                 the following qsa_select_topk on these scores may be called

@@ -69,6 +69,11 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t*
   if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
     return fail(QSA_ERR_ARG, "qsa_score_blocks: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
                 (long long)ld);
+  if (dtype == QSA_BF16 && M >= qsa::kPrefillMinRows && row_seq == nullptr && !qsa::prefill_views_fit(nb_max, ld))
+    return fail(QSA_ERR_UNSUPPORTED,
+                "qsa_score_blocks: %d bf16 rows with ld %lld, nb_max %lld: the many-row kernel needs 64 * ld and 64 * "
+                "(selection-workspace words per row) under 2 GiB",
+                M, (long long)ld, (long long)nb_max);
   if (sel_workspace && sel_workspace_bytes < qsa::select_workspace_bytes(M, nb_max, 1))
     return fail(QSA_ERR_WORKSPACE, "qsa_score_blocks: selection workspace %zu B < %zu B needed",
                 sel_workspace_bytes, qsa::select_workspace_bytes(M, nb_max, 1));
@@ -97,6 +102,11 @@ int qsa_append_score(const void* new_idx, int32_t n_new, const int64_t* new_pos,
   if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
     return fail(QSA_ERR_ARG, "qsa_append_score: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
                 (long long)ld);
+  if (dtype == QSA_BF16 && M >= qsa::kPrefillMinRows && nullptr == nullptr && !qsa::prefill_views_fit(nb_max, ld))
+    return fail(QSA_ERR_UNSUPPORTED,
+                "qsa_append_score: %d bf16 rows with ld %lld, nb_max %lld: the many-row kernel needs 64 * ld and 64 * "
+                "(selection-workspace words per row) under 2 GiB",
+                M, (long long)ld, (long long)nb_max);
   if (sel_workspace && sel_workspace_bytes < qsa::select_workspace_bytes(M, nb_max, 1))
     return fail(QSA_ERR_WORKSPACE, "qsa_append_score: selection workspace %zu B < %zu B needed",
                 sel_workspace_bytes, qsa::select_workspace_bytes(M, nb_max, 1));

@@ -34,6 +34,10 @@ hipError_t launch_append_score(const void* new_idx, int n_new, const int64_t* ne
 // Many-row scoring (bf16 index queries, one sequence): the bf16 matrix-core
 // kernel with three-plane pooled keys (score_prefill.hip).
 constexpr int kPrefillMinRows = 64;
+// The many-row kernel stores through buffer views of 16 score rows and 16
+// selection-workspace rows, each under 2 GiB: false when ld or nb_max is
+// too large for them.
+bool prefill_views_fit(int64_t nb_max, int64_t ld);
 hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
                                 int64_t nb_max, float* scores, int64_t ld, uint32_t* sel_ws,
                                 hipStream_t stream);

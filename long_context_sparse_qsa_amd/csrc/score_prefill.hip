@@ -73,8 +73,12 @@ constexpr int kPfBg = kPfBlocks / 32;               // 32-block MFMA column grou
 constexpr int kPfKs = kIndexDim / 16;               // 8 k-steps of 16 dims
 constexpr int kPfRowWords = kIndexDim / 2 + 4;      // bf16 plane row + 16 B pad, in 32-bit words
 constexpr int kPfSlots = 256;                       // workgroups in flight: 1 per compute unit
+constexpr int kXcds = 8;                            // accelerator dies (each with its own L2)
 constexpr int kPfF4 = kPfBlocks * kIndexDim / 4 / (kWave * kPfWaves);  // 4 float4 per thread per tile
 constexpr float kScoreScale = 0.08838834764831845f; // 1/sqrt(128)
+constexpr int kBufferWord3 = 0x00020000;            // raw buffer view (gfx9 family)
+constexpr int kBufferDrop = (int)0x80000000u;       // an offset past any view: the store is dropped
+constexpr int64_t kPfMaxView = (int64_t)1 << 31;    // bytes of a buffer view
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -135,6 +139,151 @@ __device__ __forceinline__ void stage_tile(const float4 (&pk)[kPfF4], int tid, u
   }
 }
 
+// One 32-block group's matrix work: acc[cg] += A(row group cg) x B(group
+// bg of the staged tile), over 8 k-steps x 3 planes.
+__device__ __forceinline__ void group_mfma(const uint32_t (*planes)[kPfBlocks * kPfRowWords], int bg, int j32, int h,
+                                           const uint4 (&aq)[kPfCg][kPfKs], f32x16_t (&acc)[kPfCg]) {
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[cg][e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kPfKs; ++s) {
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
+      const uint4 bv = *reinterpret_cast<const uint4*>(&planes[pl][(bg * 32 + j32) * kPfRowWords + (16 * s + 8 * h) / 2]);
+#pragma unroll
+      for (int cg = 0; cg < kPfCg; ++cg)
+        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
+                                                         __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
+    }
+  }
+}
+
+// Epilogue of one 32-block group in the score-writing modes: the lane's
+// block b, rows 8 cg + 2q + h of the wave (acc[cg][4q + hd] = head hd), all
+// stores through the wave's buffer views (masked lanes dropped, no branch).
+template <bool HIST>
+__device__ __forceinline__ void group_store(const f32x16_t (&acc)[kPfCg], int64_t b, bool valid, int h,
+                                            const int64_t (&nbq)[kPfCg][4], __amdgpu_buffer_rsrc_t srs,
+                                            __amdgpu_buffer_rsrc_t wrs, int64_t ld, int64_t rw, int64_t smp_off) {
+  const bool smp = sel::sampled((uint32_t)b);
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
+      x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
+      x *= kScoreScale;
+      const int rr = 8 * cg + 2 * q + h;
+      const bool keep = valid && b < nbq[cg][q];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srs, keep ? (int)((rr * ld + b) * 4) : kBufferDrop,
+                                            0, 0);
+      if constexpr (HIST)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), wrs,
+                                              keep && smp ? (int)((rr * rw + smp_off + (b >> 4)) * 4) : kBufferDrop,
+                                              0, 0);
+    }
+  }
+}
+
+// The score-writing modes, software-pipelined: each 32-block group's
+// matrix work is issued next to the previous group's epilogue (and, for a
+// tile's second group, next to the staging of the following tile), so the
+// vector ALU and memory work hides behind the matrix instructions.  Two
+// accumulator sets alternate: accA takes a tile's first group, accB its
+// second, which is stored during the next tile's first group.  The two LDS
+// buffers are separate arrays and the tile loop is unrolled by two, so the
+// compiler sees that staging and matrix reads never touch the same words.
+template <bool HIST>
+__global__ void __launch_bounds__(kWave * kPfWaves, 1)
+score_prefill_store_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
+                           const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores, int64_t ld,
+                           uint32_t* __restrict__ ws, int n_rt, int64_t n_tiles, int n_chunks) {
+  constexpr int MODE = HIST ? kPfScoresSample : kPfScores;
+  __shared__ __align__(16) uint32_t planes0[3][kPfBlocks * kPfRowWords];
+  __shared__ __align__(16) uint32_t planes1[3][kPfBlocks * kPfRowWords];
+  __shared__ int64_t nb_sh[kPfRows];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int j32 = lane & 31;
+  const int h = lane >> 5;
+  int rt, chunk;
+  if (n_chunks % kXcds == 0) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    rt = slot % n_rt;
+    chunk = (slot / n_rt) * kXcds + xcd;
+  } else {
+    rt = blockIdx.x % n_rt;
+    chunk = blockIdx.x / n_rt;
+  }
+  const int64_t t_begin = n_tiles * chunk / n_chunks;
+  const int64_t t_end = n_tiles * (chunk + 1) / n_chunks;
+  if (t_begin >= t_end) return;
+  const int r0 = rt * kPfRows;
+
+  uint4 aq[kPfCg][kPfKs];
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) {
+    int r = r0 + wave * kPfRowsPerWave + 8 * cg + (j32 >> 2);
+    r = r < M ? r : M - 1;
+    const uint16_t* src = idx_q + ((int64_t)r * kIndexHeads + (j32 & 3)) * kIndexDim + 8 * h;
+#pragma unroll
+    for (int s = 0; s < kPfKs; ++s) aq[cg][s] = *reinterpret_cast<const uint4*>(src + 16 * s);
+  }
+  float4 pk[kPfF4];
+  load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);  // after the queries: its wait covers them
+  if (tid < kPfRows) {
+    const int r = r0 + tid;
+    nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
+  }
+  const int64_t rw = sel::row_words(nb_max);
+  const int64_t smp_off = sel::sample_off(nb_max);
+  const int64_t wrow0 = r0 + __builtin_amdgcn_readfirstlane(wave) * kPfRowsPerWave;  // wave-uniform
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(scores + wrow0 * ld, 0, (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<float*>(ws) + wrow0 * rw, 0, (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
+
+  stage_tile(pk, tid, planes0);
+  load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
+  __syncthreads();
+  int64_t nbq[kPfCg][4];
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
+
+  f32x16_t accA[kPfCg], accB[kPfCg];
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accB[cg][e] = 0.f;
+  // one tile: matrix reads from cur, staging (of tile t+1) into nxt
+  auto tile = [&](int64_t t, const uint32_t (*cur)[kPfBlocks * kPfRowWords], uint32_t (*nxt)[kPfBlocks * kPfRowWords]) {
+    const int64_t b0 = t * kPfBlocks;
+    group_mfma(cur, 0, j32, h, aq, accA);
+    group_store<HIST>(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, wrs, ld, rw, smp_off);  // previous tile, group 1
+    group_mfma(cur, 1, j32, h, aq, accB);
+    group_store<HIST>(accA, b0 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
+    stage_tile(pk, tid, nxt);  // tile t+1 (past the run: the last tile again, never read)
+    load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
+    __syncthreads();
+  };
+  int64_t t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    tile(t, planes0, planes1);
+    tile(t + 1, planes1, planes0);
+  }
+  if (t < t_end) {
+    tile(t, planes0, planes1);
+    ++t;
+  }
+  group_store<HIST>(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);  // last tile, group 1
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(kWave * kPfWaves, 1)
 score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
@@ -148,9 +297,19 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   const int wave = tid / kWave;
   const int j32 = lane & 31;  // A row ((row, head) pair) / B column (block) / D column
   const int h = lane >> 5;    // k half of the operands; row parity of the outputs
-  // this workgroup: row tile rt, block tiles [t_begin, t_end)
-  const int rt = blockIdx.x % n_rt;
-  const int chunk = blockIdx.x / n_rt;
+  // this workgroup: row tile rt, block tiles [t_begin, t_end).  Workgroups
+  // go to the 8 XCDs round-robin by index; when the run count allows, all
+  // row tiles of a run land on one XCD, so its L2 fetches each pooled tile
+  // once for all of them.
+  int rt, chunk;
+  if (n_chunks % kXcds == 0) {
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    rt = slot % n_rt;
+    chunk = (slot / n_rt) * kXcds + xcd;
+  } else {
+    rt = blockIdx.x % n_rt;
+    chunk = blockIdx.x / n_rt;
+  }
   const int64_t t_begin = n_tiles * chunk / n_chunks;
   const int64_t t_end = n_tiles * (chunk + 1) / n_chunks;
   if (t_begin >= t_end) return;
@@ -178,6 +337,18 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
   }
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
+  // Score and sample stores go through buffer views of the wave's 16 rows:
+  // a masked lane gets an offset past the view's end, which the hardware
+  // drops, so every store instruction issues on every tile and the wait for
+  // the next tile's loads can count past them (the launcher keeps both
+  // views under 2 GiB).
+  const int64_t wrow0 = r0 + __builtin_amdgcn_readfirstlane(wave) * kPfRowsPerWave;  // wave-uniform
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(scores + wrow0 * ld, 0, (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<float*>(ws) + wrow0 * rw, 0, (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
+  (void)srs;
+  (void)wrs;
   const uint64_t half = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;  // the lane's row in a ballot
   const uint64_t lane_lt = (1ull << lane) - 1ull;
 
@@ -208,26 +379,32 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
     uint32_t run = 0u;  // lane L < 16: candidates of row L of the wave
     (void)ekey;
 
+    // both 32-block groups at once: four independent accumulators, and
+    // each k-step's B reads have the other group's MFMAs to hide behind
     f32x16_t accs[kPfBg][kPfCg];
 #pragma unroll
-    for (int bg = 0; bg < kPfBg; ++bg) {
-      f32x16_t (&acc)[kPfCg] = accs[bg];
+    for (int bg = 0; bg < kPfBg; ++bg)
 #pragma unroll
       for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[cg][e] = 0.f;
+        for (int e = 0; e < 16; ++e) accs[bg][cg][e] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kPfKs; ++s) {
+    for (int s = 0; s < kPfKs; ++s) {
 #pragma unroll
-        for (int pl = 0; pl < 3; ++pl) {
-          // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
-          const uint4 bv = *reinterpret_cast<const uint4*>(
+      for (int pl = 0; pl < 3; ++pl) {
+        // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
+        uint4 bv[kPfBg];
+#pragma unroll
+        for (int bg = 0; bg < kPfBg; ++bg)
+          bv[bg] = *reinterpret_cast<const uint4*>(
               &planes[cur][pl][(bg * 32 + j32) * kPfRowWords + (16 * s + 8 * h) / 2]);
 #pragma unroll
+        for (int bg = 0; bg < kPfBg; ++bg)
+#pragma unroll
           for (int cg = 0; cg < kPfCg; ++cg)
-            acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
-                                                             __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
-        }
+            accs[bg][cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
+                                                                  __builtin_bit_cast(bf16x8_t, bv[bg]),
+                                                                  accs[bg][cg], 0, 0, 0);
       }
     }
     if (t + 1 < t_end) stage_tile(pk, tid, planes[cur ^ 1]);
@@ -252,10 +429,13 @@ score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* _
           const int r = r0 + rl;
           const int64_t nbr = nbq[cg][q];  // 0 for rows past M
           if constexpr (MODE == kPfScores || MODE == kPfScoresSample) {
-            if (b < nbr) {
-              scores[(int64_t)r * ld + b] = x;
-              if (MODE == kPfScoresSample && smp) reinterpret_cast<float*>(ws)[(size_t)r * rw + smp_off + (b >> 4)] = x;
-            }
+            const int rr = 8 * cg + 2 * q + h;  // row in the wave's views
+            const bool keep = b < nbr;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srs,
+                                                  keep ? (int)((rr * ld + b) * 4) : kBufferDrop, 0, 0);
+            if constexpr (MODE == kPfScoresSample)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(x), wrs, keep && smp ? (int)((rr * rw + smp_off + (b >> 4)) * 4) : kBufferDrop, 0, 0);
           }
           if constexpr (MODE == kPfSampleOnly) {  // b is the sample group
             if (b < fa.n_grp && b * 16 + sel::sample_offset((uint32_t)b) < nbr)
@@ -320,7 +500,8 @@ PfGrid pf_grid(int M, int64_t n_cols) {
   PfGrid g;
   g.n_rt = (M + kPfRows - 1) / kPfRows;
   g.n_tiles = (n_cols + kPfBlocks - 1) / kPfBlocks;
-  const int64_t want = (kPfSlots + g.n_rt - 1) / g.n_rt;
+  int64_t want = (kPfSlots + g.n_rt - 1) / g.n_rt;
+  if (want >= kXcds) want -= want % kXcds;  // a multiple of the XCD count where possible
   g.n_chunks = (int)(want < g.n_tiles ? want : g.n_tiles);
   if (g.n_chunks < 1) g.n_chunks = 1;
   return g;
@@ -328,19 +509,26 @@ PfGrid pf_grid(int M, int64_t n_cols) {
 
 }  // namespace
 
+bool prefill_views_fit(int64_t nb_max, int64_t ld) {
+  return (int64_t)kPfRowsPerWave * ld * 4 < kPfMaxView &&
+         (int64_t)kPfRowsPerWave * sel::row_words(nb_max) * 4 < kPfMaxView;
+}
+
 hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos, const float* pooled,
                                 int64_t nb_max, float* scores, int64_t ld, uint32_t* sel_ws,
                                 hipStream_t stream) {
   if (M == 0 || nb_max == 0) return hipSuccess;
+  if (!prefill_views_fit(nb_max, ld)) return hipErrorInvalidValue;
   const PfGrid g = pf_grid(M, nb_max);
   const FlatArgs none{};
+  (void)none;
   if (sel_ws)
-    hipLaunchKernelGGL(score_prefill_kernel<kPfScoresSample>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws, none,
+    hipLaunchKernelGGL(score_prefill_store_kernel<true>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws,
                        g.n_rt, g.n_tiles, g.n_chunks);
   else
-    hipLaunchKernelGGL(score_prefill_kernel<kPfScores>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr, none,
+    hipLaunchKernelGGL(score_prefill_store_kernel<false>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr,
                        g.n_rt, g.n_tiles, g.n_chunks);
   return hipGetLastError();
 }

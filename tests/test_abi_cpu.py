@@ -67,6 +67,9 @@ def test_append_pool_validation(args, code, word):
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE + 4, 16, None, 0, None), ERR_ARG, "aligned"),
     ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "null"),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, FAKE, 100, None), ERR_WS, "workspace"),
+    # 64 bf16 rows take the many-row kernel, whose buffer views of 16 score
+    # rows must stay under 2 GiB
+    ((FAKE, 1, 64, FAKE, None, FAKE, 1, 64, 16, FAKE, 1 << 25, None, 0, None), ERR_UNS, "many-row"),
     ((None, 1, 0, None, None, None, 1, 64, 16, None, 16, None, 0, None), Q.QSA_OK, ""),
 ])
 def test_score_validation(args, code, word):
@@ -229,6 +232,7 @@ def _apsc(dtype=1, n_new=4, M=1, cap=64, nb=16, ld=16, scores=FAKE, ws=None, wsb
     (dict(ld=8), ERR_ARG, "ld"),
     (dict(ld=18), ERR_ARG, "aligned"),
     (dict(ws=FAKE, wsb=100), ERR_WS, "workspace"),
+    (dict(M=64, ld=1 << 25), ERR_UNS, "many-row"),
     (dict(new=None), ERR_ARG, "null"),
     (dict(idx_q=None), ERR_ARG, "null"),
     (dict(n_new=0, M=0, new=None, idx_q=None), Q.QSA_OK, ""),
