@@ -457,9 +457,13 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 //   3. online softmax per head over the 16 lanes that hold a head's tokens
 //      (base-2 exponentials, bf16-rounded probabilities packed in token
 //      pairs into a wave-private LDS region);
-//   4. PV with packed bf16 dot2 from the wave's V rows, pair-interleaved in
-//      LDS: lane = D/64 dims of all 12 heads, float32 accumulation.
-// At the end the four wave partials are merged by log-sum-exp in LDS.
+//   4. PV on v_mfma_f32_16x16x16_bf16, D/16 instructions per slice: A = the
+//      probabilities (12 heads x 16 tokens, read back from LDS in operand
+//      layout), B = V staged in LDS as 4-token quads per dim (lane group g
+//      reads tokens 4g .. 4g+3 of its dim in one 8-byte load); the output
+//      lane holds heads 4 g .. 4 g + 3, the heads of its softmax state, so
+//      the online rescale needs no lane exchange.
+// At the end the wave partials are merged by log-sum-exp in LDS.
 //
 // F8: K/V are E4M3 codes with an f16 scale per KV head and token (the fp8
 // state of the hipfire page, section 03).  Rows are D bytes; a lane reads
@@ -469,9 +473,10 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 // codes become bf16 exactly; token t's logits are multiplied by its K scale,
 // and its softmax weight by its V scale before the bf16 rounding that PV
 // consumes (the normaliser sums the unscaled weights).  V goes to LDS as
-// bf16 pairs like the bf16 path.
+// bf16 quads like the bf16 path.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 operand of the 16x16x16 MFMA
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // E4M3 codes -> bf16.  Every E4M3 value (4 significant bits, exponents
@@ -512,14 +517,17 @@ __device__ __forceinline__ float row16_sum(float x) {
 constexpr int kMaxWaves = 8;  // waves (16-token slices) per workgroup
 
 // Dynamic LDS of the matrix-core kernel, in 32-bit words.  Phase 1, per wave:
-// V rows of its slice, [pair][dim] as (V[2 pair][dim], V[2 pair + 1][dim])
-// bf16 pairs, then the bf16 probabilities [pair][head].  Phase 2 (merge,
+// V of its 16-token slice as [token quad q][dim] -> 4 bf16 (tokens 4q ..
+// 4q+3 of the dim, 8 bytes; quad rows padded), the PV B operand of lane
+// group q; then the bf16 probabilities as [quad q][token parity p][head]
+// words (tokens 4q+2p, 4q+2p+1 of the head), the A operand.  Phase 2 (merge,
 // reusing the same memory): every wave's partial output, then the softmax
 // states and the per-head merge weights.
 template <int D>
 struct MfmaLds {
-  static constexpr int kPairs = 8;  // token pairs of a 16-token slice
-  static constexpr int kWaveWords = kPairs * D + kPairs * kGroup;
+  static constexpr int kQuadWords = 2 * D + 32;  // one token quad of V (+ pad)
+  static constexpr int kPWords = 4 * 2 * 16;     // probabilities, heads 0..15
+  static constexpr int kWaveWords = 4 * kQuadWords + kPWords;
   static constexpr int acc(int w) { return w * kGroup * D; }
   static constexpr int m(int W, int w) { return W * kGroup * D + w * kGroup; }
   static constexpr int l(int W, int w) { return W * kGroup * D + W * kGroup + w * kGroup; }
@@ -539,12 +547,12 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
                  uint16_t* __restrict__ out, float* __restrict__ lse_out,
                  float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int KS = D / 32;               // QK k-steps
-  constexpr int DPL = D / kWave;           // PV dims per lane
+  constexpr int NT = D / 16;               // PV output tiles of 16 dims
   constexpr int kRowBytes = F8 ? D : D * 2;
   constexpr int VCH = kRowBytes / 16;      // 16-byte chunks per V row
-  constexpr int VIT = 8 * VCH / kWave;     // (token pair, chunk) V items per lane
+  constexpr int VITEMS = 4 * VCH;          // (token quad, chunk) V staging items
+  constexpr int VIT = (VITEMS + kWave - 1) / kWave;  // per lane
   constexpr int KL = F8 ? KS / 2 : KS;     // 16-byte K loads per lane
-  static_assert(kWave % VCH == 0 || VCH % kWave == 0, "V item mapping");
   using Lds = MfmaLds<D>;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ SegDesc segs[kMaxSegments];
@@ -632,13 +640,13 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     m_run[v] = -INFINITY;
     l_run[v] = 0.f;
   }
-  float acc[kGroup][DPL];
+  // PV accumulators: pacc[n][r] = O[head 4 g4 + r][dim 16 n + n16] (heads
+  // 12..15 of lane group 3 are padding)
+  f32x4_t pacc[NT];
 #pragma unroll
-  for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[h][d] = 0.f;
+  for (int n = 0; n < NT; ++n) pacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t* vl = lds + wave * Lds::kWaveWords;
-  uint32_t* pl = vl + Lds::kPairs * D;
+  uint32_t* pl = vl + 4 * Lds::kQuadWords;
 
   for (int t = 0; t < tiles_per_split; ++t) {
     const int j0 = tok_begin + t * tile + wave * 16;
@@ -680,19 +688,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       ks_bits = *ksp;
       vs_bits = *vsp;
     }
-    // V items: (pair pp, chunk c) of the slice's token pairs
-    uint4 va[VIT], vb[VIT];
+    // V items: (token quad vq, chunk c) of the slice; lanes past the item
+    // count (fp8 at head_dim 128) load a valid chunk and write nothing
+    uint4 vt[VIT][4];
     int vok[VIT];
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
-      const int item = lane + kWave * u;
-      const int pp = item / VCH;
+      const int item = (lane + kWave * u) % VITEMS;
+      const int vq = item / VCH;
       const int c = item % VCH;
-      const unsigned char* r0 = shfl_ptr(vr, 2 * pp);
-      const unsigned char* r1 = shfl_ptr(vr, 2 * pp + 1);
-      vok[u] = __shfl(ok, 2 * pp, kWave) | (__shfl(ok, 2 * pp + 1, kWave) << 1);
-      va[u] = ldg16(r0 + c * 16);
-      vb[u] = ldg16(r1 + c * 16);
+      vok[u] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned char* r = shfl_ptr(vr, 4 * vq + e);
+        vok[u] |= __shfl(ok, 4 * vq + e, kWave) << e;
+        vt[u][e] = ldg16(r + c * 16);
+      }
     }
     // next slice's block id, in flight during this slice's compute
     if (t + 1 < tiles_per_split) {
@@ -738,60 +749,56 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       const uint32_t pbv = F8 ? (uint32_t)f32_to_bf16_bits(pv * v_sc) : pb;  // fp8: V's scale joins the weight
       pw[v] = pbv | ((uint32_t)__shfl_xor((int)pbv, 1, kWave) << 16);
     }
+    // probabilities of token pair n16/2 (quad n16/4, parity (n16/2)%2),
+    // heads 4 g4 .. 4 g4 + 3
     if ((n16 & 1) == 0 && g4 < 3)
-      *reinterpret_cast<uint4*>(pl + (n16 >> 1) * kGroup + 4 * g4) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-    // V rows, pair-interleaved
+      *reinterpret_cast<uint4*>(pl + (n16 >> 2) * 32 + ((n16 >> 1) & 1) * 16 + 4 * g4) =
+          make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    // V as [quad][dim] -> 4 tokens: per dim the words (t0, t1) and (t2, t3)
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
+      if (VITEMS % kWave != 0 && lane + kWave * u >= VITEMS) continue;
       const int item = lane + kWave * u;
-      const int pp = item / VCH;
+      const int vq = item / VCH;
       const int c = item % VCH;
-      const uint4 a = (vok[u] & 1) ? va[u] : make_uint4(0, 0, 0, 0);
-      const uint4 b = (vok[u] & 2) ? vb[u] : make_uint4(0, 0, 0, 0);
-      if constexpr (F8) {  // 16 codes of each token: dims 16 c .. 16 c + 15
-        uint4 lo, hi, lo2, hi2;
-        interleave(fp8x8_to_bf16x8(a.x, a.y), fp8x8_to_bf16x8(b.x, b.y), lo, hi);
-        interleave(fp8x8_to_bf16x8(a.z, a.w), fp8x8_to_bf16x8(b.z, b.w), lo2, hi2);
-        uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 16);
-        dst[0] = lo;
-        dst[1] = hi;
-        dst[2] = lo2;
-        dst[3] = hi2;
-      } else {
-        uint4 lo, hi;
-        interleave(a, b, lo, hi);
-        uint4* dst = reinterpret_cast<uint4*>(vl + pp * D + c * 8);
-        dst[0] = lo;
-        dst[1] = hi;
+      uint4 t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = ((vok[u] >> e) & 1) ? vt[u][e] : make_uint4(0, 0, 0, 0);
+      // one 8-dim bf16 half: tokens' words -> 8 dims x (t0 t1, t2 t3)
+      auto put8 = [&](uint4 a, uint4 b, uint4 cc, uint4 d, uint32_t* dst) {
+        uint4 lo01, hi01, lo23, hi23;
+        interleave(a, b, lo01, hi01);
+        interleave(cc, d, lo23, hi23);
+        uint4* o = reinterpret_cast<uint4*>(dst);
+        o[0] = make_uint4(lo01.x, lo23.x, lo01.y, lo23.y);
+        o[1] = make_uint4(lo01.z, lo23.z, lo01.w, lo23.w);
+        o[2] = make_uint4(hi01.x, hi23.x, hi01.y, hi23.y);
+        o[3] = make_uint4(hi01.z, hi23.z, hi01.w, hi23.w);
+      };
+      uint32_t* dst = vl + vq * Lds::kQuadWords;
+      if constexpr (F8) {  // 16 codes per token: dims 16 c .. 16 c + 15
+        put8(fp8x8_to_bf16x8(t[0].x, t[0].y), fp8x8_to_bf16x8(t[1].x, t[1].y), fp8x8_to_bf16x8(t[2].x, t[2].y),
+             fp8x8_to_bf16x8(t[3].x, t[3].y), dst + 32 * c);
+        put8(fp8x8_to_bf16x8(t[0].z, t[0].w), fp8x8_to_bf16x8(t[1].z, t[1].w), fp8x8_to_bf16x8(t[2].z, t[2].w),
+             fp8x8_to_bf16x8(t[3].z, t[3].w), dst + 32 * c + 16);
+      } else {  // 8 dims per chunk: dims 8 c .. 8 c + 7
+        put8(t[0], t[1], t[2], t[3], dst + 16 * c);
       }
     }
-    // rescale by every head's alpha (head h sits in row h / 4, slot h % 4)
+    // rescale: the lane's heads 4 g4 + r are its softmax heads
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[h][d] *= a;
-    }
+      for (int r = 0; r < 4; ++r) pacc[n][r] *= alpha[r];
     __builtin_amdgcn_wave_barrier();
-    // 4. PV over the slice's 8 token pairs
-#pragma unroll 2
-    for (int pp = 0; pp < 8; ++pp) {
-      uint32_t w[DPL];
-      if constexpr (DPL == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vl + pp * D + DPL * lane);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(vl + pp * D + DPL * lane);
-        w[0] = x.x; w[1] = x.y;
-      }
-      const uint4 p0 = *reinterpret_cast<const uint4*>(pl + pp * kGroup);
-      const uint4 p1 = *reinterpret_cast<const uint4*>(pl + pp * kGroup + 4);
-      const uint4 p2 = *reinterpret_cast<const uint4*>(pl + pp * kGroup + 8);
-      const uint32_t ph[kGroup] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w, p2.x, p2.y, p2.z, p2.w};
+    // 4. PV on v_mfma_f32_16x16x16_bf16: A = P (head n16, tokens 4 g4 .. + 3),
+    // B = V (tokens 4 g4 .. + 3, dim 16 n + n16)
+    const uint2 pa = n16 < kGroup ? make_uint2(pl[g4 * 32 + n16], pl[g4 * 32 + 16 + n16]) : make_uint2(0, 0);
+    const s16x4_t pa4 = __builtin_bit_cast(s16x4_t, pa);
 #pragma unroll
-      for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[h][d] = dot2_bf16(ph[h], w[d], acc[h][d]);
+    for (int n = 0; n < NT; ++n) {
+      const uint2 vb2 = *reinterpret_cast<const uint2*>(vl + g4 * Lds::kQuadWords + (16 * n + n16) * 2);
+      pacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, __builtin_bit_cast(s16x4_t, vb2), pacc[n], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -799,14 +806,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   // ---- merge the wave partials (log2 domain)
   __syncthreads();  // every wave is done with its V / P region
   float* fl = reinterpret_cast<float*>(lds);
+  if (g4 < 3) {
 #pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    float* dst = fl + Lds::acc(wave) + h * D + DPL * lane;
-    if constexpr (DPL == 4) {
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-    } else {
-      *reinterpret_cast<float2*>(dst) = make_float2(acc[h][0], acc[h][1]);
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) fl[Lds::acc(wave) + (4 * g4 + r) * D + 16 * n + n16] = pacc[n][r];
   }
   if (n16 == 0 && g4 < 3) {
 #pragma unroll
