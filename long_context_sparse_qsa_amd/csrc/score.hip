@@ -335,6 +335,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
 
   // blocks of this wave whose scores the fresh-block workgroup writes
   uint32_t fresh = 0u;
+  static_assert(kBlocksPerWave <= 32, "one mask bit per block of the wave");
   if constexpr (APPEND) {
     const int64_t rel = (new_p >> 2) - wave_b0;
     fresh = completes_scored_block(new_p, ap.capacity, nb_max) && rel >= 0 && rel < kBlocksPerWave
