@@ -219,6 +219,7 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 
   __syncthreads();
   const int nseg = nseg_sh;
+  const SegDesc seg0 = segs[0];
 
   for (int t = 0; t < tiles_per_split; ++t) {
     const int j0 = tok_begin + t * kTileTok;
@@ -502,19 +503,37 @@ __device__ __forceinline__ const unsigned char* shfl_ptr(const unsigned char* p,
   return reinterpret_cast<const unsigned char*>(((uint64_t)hi << 32) | lo);
 }
 
+// Lane exchange inside a 16-lane row through the DPP modifier (no LDS
+// traffic): quad_perm [1,0,3,2] and [2,3,0,1] (xor 1, xor 2), then
+// row_half_mirror and row_mirror, which after the quad steps pair every
+// lane with the other quad, then the other half.  Every lane of the row
+// ends with the same bits (each step adds two equal-order operands).
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 // max / sum over the 16 lanes of a row (lanes 16r .. 16r+15)
 __device__ __forceinline__ float row16_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = fmaxf(x, __int_as_float(dpp_row<kDppXor1>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_row<kDppXor2>(__float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_row<kDppHalfMirror>(__float_as_int(x))));
+  return fmaxf(x, __int_as_float(dpp_row<kDppMirror>(__float_as_int(x))));
 }
 __device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x += __int_as_float(dpp_row<kDppXor1>(__float_as_int(x)));
+  x += __int_as_float(dpp_row<kDppXor2>(__float_as_int(x)));
+  x += __int_as_float(dpp_row<kDppHalfMirror>(__float_as_int(x)));
+  return x + __int_as_float(dpp_row<kDppMirror>(__float_as_int(x)));
 }
 
 constexpr int kMaxWaves = 8;  // waves (16-token slices) per workgroup
+
+// Word offset, inside a V quad row, of piece k (dims 8 u8 + 2k, + 1; 16
+// bytes) of 8-dim unit u8.  The pieces of a unit are rotated by (u8 / 4) % 4
+// so that the staging writes (one unit per lane, 64 bytes apart) spread over
+// the LDS banks; the readers use the same map.
+__device__ __forceinline__ constexpr int vslot(int u8, int k) { return 16 * u8 + 4 * ((k + (u8 >> 2)) & 3); }
 
 // Dynamic LDS of the matrix-core kernel, in 32-bit words.  Phase 1, per wave:
 // V of its 16-token slice as [token quad q][dim] -> 4 bf16 (tokens 4q ..
@@ -633,6 +652,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   const int total = ns * kBlockTokens + tail;
   __syncthreads();
   const int nseg = nseg_sh;
+  const SegDesc seg0 = segs[0];
 
   float m_run[4], l_run[4];  // heads 4 g4 + v (identical over the 16 lanes of a row)
 #pragma unroll
@@ -666,8 +686,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     const uint16_t* ksp = reinterpret_cast<const uint16_t*>(qh);
     const uint16_t* vsp = ksp;
     int ok = 0;
-    for (int si = 0; si < nseg; ++si) {
-      const SegDesc sd = segs[si];
+    auto resolve = [&](const SegDesc& sd) {
       const int64_t rel = tok - sd.lo;
       const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !ok;
       const int64_t row = (int64_t)g * sd.cap + rel;
@@ -678,6 +697,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
         vsp = hit ? sd.vs + row : vsp;
       }
       ok |= hit ? 1 : 0;
+    };
+    if (nseg == 1) {
+      resolve(seg0);  // one segment (the common case): its descriptor stays in registers
+    } else {
+      for (int si = 0; si < nseg; ++si) resolve(segs[si]);
     }
     // K operand rows: all k-steps
     uint4 kb[KL];
@@ -725,10 +749,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, x), sacc, 0, 0, 0);
-      }
+      for (int s = 0; s < KS; ++s)  // a masked token's logit is replaced below: its K needs no mask
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, kb[s]), sacc, 0, 0, 0);
     }
     // fp8: this lane's token scales (0 for a masked token)
     const float k_sc = F8 ? (ok ? f16_bits_to_f32(ks_bits) : 0.f) : 1.f;
@@ -741,13 +763,13 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     for (int v = 0; v < 4; ++v) {
       const float s2 = ok ? (F8 ? sacc[v] * k_sc : sacc[v]) * scale_log2 : -INFINITY;
       const float m_new = fmaxf(m_run[v], row16_max(s2));
-      alpha[v] = (m_run[v] == m_new) ? 1.f : exp2f(m_run[v] - m_new);
-      const float pv = (s2 == -INFINITY) ? 0.f : exp2f(s2 - m_new);
+      alpha[v] = (m_run[v] == m_new) ? 1.f : __builtin_amdgcn_exp2f(m_run[v] - m_new);
+      const float pv = (s2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2 - m_new);
       const uint32_t pb = f32_to_bf16_bits(pv);  // PV consumes bf16: normalise by the same values
       l_run[v] = l_run[v] * alpha[v] + row16_sum(__uint_as_float(pb << 16));
       m_run[v] = m_new;
       const uint32_t pbv = F8 ? (uint32_t)f32_to_bf16_bits(pv * v_sc) : pb;  // fp8: V's scale joins the weight
-      pw[v] = pbv | ((uint32_t)__shfl_xor((int)pbv, 1, kWave) << 16);
+      pw[v] = pbv | ((uint32_t)dpp_row<kDppXor1>((int)pbv) << 16);
     }
     // probabilities of token pair n16/2 (quad n16/4, parity (n16/2)%2),
     // heads 4 g4 .. 4 g4 + 3
@@ -764,32 +786,35 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       uint4 t[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = ((vok[u] >> e) & 1) ? vt[u][e] : make_uint4(0, 0, 0, 0);
-      // one 8-dim bf16 half: tokens' words -> 8 dims x (t0 t1, t2 t3)
-      auto put8 = [&](uint4 a, uint4 b, uint4 cc, uint4 d, uint32_t* dst) {
+      // one 8-dim unit u8 (dims 8 u8 .. + 7): tokens' words -> 8 dims x
+      // (t0 t1, t2 t3); its four 16-byte pieces are rotated by vslot
+      auto put8 = [&](uint4 a, uint4 b, uint4 cc, uint4 d, uint32_t* quad, int u8) {
         uint4 lo01, hi01, lo23, hi23;
         interleave(a, b, lo01, hi01);
         interleave(cc, d, lo23, hi23);
-        uint4* o = reinterpret_cast<uint4*>(dst);
-        o[0] = make_uint4(lo01.x, lo23.x, lo01.y, lo23.y);
-        o[1] = make_uint4(lo01.z, lo23.z, lo01.w, lo23.w);
-        o[2] = make_uint4(hi01.x, hi23.x, hi01.y, hi23.y);
-        o[3] = make_uint4(hi01.z, hi23.z, hi01.w, hi23.w);
+        const uint4 piece[4] = {make_uint4(lo01.x, lo23.x, lo01.y, lo23.y), make_uint4(lo01.z, lo23.z, lo01.w, lo23.w),
+                                make_uint4(hi01.x, hi23.x, hi01.y, hi23.y), make_uint4(hi01.z, hi23.z, hi01.w, hi23.w)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(quad + vslot(u8, k)) = piece[k];
       };
-      uint32_t* dst = vl + vq * Lds::kQuadWords;
+      uint32_t* quad = vl + vq * Lds::kQuadWords;
       if constexpr (F8) {  // 16 codes per token: dims 16 c .. 16 c + 15
         put8(fp8x8_to_bf16x8(t[0].x, t[0].y), fp8x8_to_bf16x8(t[1].x, t[1].y), fp8x8_to_bf16x8(t[2].x, t[2].y),
-             fp8x8_to_bf16x8(t[3].x, t[3].y), dst + 32 * c);
+             fp8x8_to_bf16x8(t[3].x, t[3].y), quad, 2 * c);
         put8(fp8x8_to_bf16x8(t[0].z, t[0].w), fp8x8_to_bf16x8(t[1].z, t[1].w), fp8x8_to_bf16x8(t[2].z, t[2].w),
-             fp8x8_to_bf16x8(t[3].z, t[3].w), dst + 32 * c + 16);
+             fp8x8_to_bf16x8(t[3].z, t[3].w), quad, 2 * c + 1);
       } else {  // 8 dims per chunk: dims 8 c .. 8 c + 7
-        put8(t[0], t[1], t[2], t[3], dst + 16 * c);
+        put8(t[0], t[1], t[2], t[3], quad, c);
       }
     }
-    // rescale: the lane's heads 4 g4 + r are its softmax heads
+    // rescale: the lane's heads 4 g4 + r are its softmax heads (skipped when
+    // no head's running maximum moved, the common case after the first tiles)
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+      for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pacc[n][r] *= alpha[r];
+        for (int r = 0; r < 4; ++r) pacc[n][r] *= alpha[r];
+    }
     __builtin_amdgcn_wave_barrier();
     // 4. PV on v_mfma_f32_16x16x16_bf16: A = P (head n16, tokens 4 g4 .. + 3),
     // B = V (tokens 4 g4 .. + 3, dim 16 n + n16)
@@ -797,7 +822,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     const s16x4_t pa4 = __builtin_bit_cast(s16x4_t, pa);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const uint2 vb2 = *reinterpret_cast<const uint2*>(vl + g4 * Lds::kQuadWords + (16 * n + n16) * 2);
+      const int dim = 16 * n + n16;
+      const uint2 vb2 =
+          *reinterpret_cast<const uint2*>(vl + g4 * Lds::kQuadWords + vslot(dim >> 3, (dim & 7) >> 1) + 2 * (dim & 1));
       pacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, __builtin_bit_cast(s16x4_t, vb2), pacc[n], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
