@@ -166,7 +166,7 @@ __device__ __forceinline__ void group_mfma(const uint32_t (*planes)[kPfBlocks * 
 // stores through the wave's buffer views (masked lanes dropped, no branch).
 template <bool HIST>
 __device__ __forceinline__ void group_store(const f32x16_t (&acc)[kPfCg], int64_t b, bool valid, int h,
-                                            const int64_t (&nbq)[kPfCg][4], __amdgpu_buffer_rsrc_t srs,
+                                            const int (&nbq)[kPfCg][4], __amdgpu_buffer_rsrc_t srs,
                                             __amdgpu_buffer_rsrc_t wrs, int64_t ld, int64_t rw, int64_t smp_off) {
   const bool smp = sel::sampled((uint32_t)b);
 #pragma unroll
@@ -188,23 +188,88 @@ __device__ __forceinline__ void group_store(const f32x16_t (&acc)[kPfCg], int64_
   }
 }
 
-// The score-writing modes, software-pipelined: each 32-block group's
-// matrix work is issued next to the previous group's epilogue (and, for a
-// tile's second group, next to the staging of the following tile), so the
-// vector ALU and memory work hides behind the matrix instructions.  Two
-// accumulator sets alternate: accA takes a tile's first group, accB its
-// second, which is stored during the next tile's first group.  The two LDS
-// buffers are separate arrays and the tile loop is unrolled by two, so the
-// compiler sees that staging and matrix reads never touch the same words.
-template <bool HIST>
+// Emit mode's record of one 32-block group: the keys of the lane's 8
+// outputs (row group cg, row pair q), which of them are candidates, and
+// (lane L < 16) the candidate count of row L of the wave.
+struct EmitRec {
+  uint32_t key[kPfCg * 4];
+  uint32_t flags;
+  uint32_t run;
+};
+
+// Emit mode's epilogue of one 32-block group: keys, candidate flags (score
+// digit at or above the row's threshold) and per-row counts by ballot.
+__device__ __forceinline__ void group_emit(const f32x16_t (&acc)[kPfCg], int64_t b, bool valid, int h, int lane,
+                                           const int (&nbq)[kPfCg][4], const uint32_t* thr_w, int k, EmitRec& rec) {
+  rec.flags = 0u;
+  rec.run = 0u;
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
+      x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
+      x *= kScoreScale;
+      const uint32_t key = sel::order_key(x);
+      const int nbr = nbq[cg][q];
+      const bool c = valid && b < nbr && nbr > k && (key >> sel::kDigitShift) >= thr_w[8 * cg + 2 * q + h];
+      rec.key[cg * 4 + q] = key;
+      rec.flags |= c ? 1u << (cg * 4 + q) : 0u;
+      const uint64_t m = __ballot(c);
+      const uint32_t n0 = (uint32_t)__popcll(m & 0x00000000FFFFFFFFull);  // row 8 cg + 2q
+      const uint32_t n1 = (uint32_t)__popcll(m & 0xFFFFFFFF00000000ull);  // row 8 cg + 2q + 1
+      rec.run += lane == 8 * cg + 2 * q ? n0 : (lane == 8 * cg + 2 * q + 1 ? n1 : 0u);
+    }
+  }
+}
+
+// Emit mode: appends a finished group's candidates (lane block b) to their
+// rows' slots from the bases its reservation returned.
+__device__ __forceinline__ void scatter_emit(const EmitRec& rec, uint32_t base, int64_t b, int h, int lane,
+                                             int wrow0_rel, int r0, const FlatArgs& fa) {
+  const uint64_t half = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;  // the lane's row in a ballot
+  const uint64_t lane_lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rw8 = 8 * cg + 2 * q + h;
+      const int64_t r = r0 + wrow0_rel + rw8;
+      const uint32_t pos = (uint32_t)__shfl((int)base, rw8, kWave);
+      const bool c = (rec.flags >> (cg * 4 + q)) & 1u;
+      const uint64_t mk = __ballot(c) & half;
+      const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
+      if (c && p < (uint32_t)sel::kFlatCap) {
+        fa.keys[r * sel::kFlatCap + p] = rec.key[cg * 4 + q];
+        fa.ids[r * sel::kFlatCap + p] = (uint32_t)b;
+      }
+    }
+  }
+}
+
+// The score-writing modes and the emit mode, software-pipelined: each
+// 32-block group's matrix work is issued next to the previous group's
+// epilogue (and, for a tile's second group, next to the staging of the
+// following tile), so the vector ALU and memory work hides behind the
+// matrix instructions.  Two accumulator sets alternate: accA takes a tile's
+// first group, accB its second, whose epilogue runs during the next tile's
+// first group.  The two LDS buffers are separate arrays and the tile loop is
+// unrolled by two, so the compiler sees that staging and matrix reads never
+// touch the same words.  In emit mode a tile's slot reservation (one atomic
+// per row) is issued once its second group is done and consumed a group of
+// matrix work later, so the atomics' round trip hides behind it too.
+template <int MODE>
 __global__ void __launch_bounds__(kWave * kPfWaves, 1)
-score_prefill_store_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
-                           const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores, int64_t ld,
-                           uint32_t* __restrict__ ws, int n_rt, int64_t n_tiles, int n_chunks) {
-  constexpr int MODE = HIST ? kPfScoresSample : kPfScores;
+score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
+                          const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores, int64_t ld,
+                          uint32_t* __restrict__ ws, FlatArgs fa, int n_rt, int64_t n_tiles, int n_chunks) {
+  constexpr bool HIST = MODE == kPfScoresSample;
+  constexpr bool EMIT = MODE == kPfEmit;
+  static_assert(MODE != kPfSampleOnly, "sample-only mode runs on score_prefill_kernel");
   __shared__ __align__(16) uint32_t planes0[3][kPfBlocks * kPfRowWords];
   __shared__ __align__(16) uint32_t planes1[3][kPfBlocks * kPfRowWords];
-  __shared__ int64_t nb_sh[kPfRows];
+  __shared__ int nb_sh[kPfRows];
+  __shared__ uint32_t thr_sh[kPfRows];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -237,37 +302,68 @@ score_prefill_store_kernel(const uint16_t* __restrict__ idx_q, int M, const int6
   load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);  // after the queries: its wait covers them
   if (tid < kPfRows) {
     const int r = r0 + tid;
-    nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
+    nb_sh[tid] = r < M ? (int)clamp_nb(row_pos[r], nb_max) : 0;  // nb_max < 2^31 (launcher)
+    if constexpr (EMIT) thr_sh[tid] = r < M ? fa.thr[r] : 0u;
   }
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
-  const int64_t wrow0 = r0 + __builtin_amdgcn_readfirstlane(wave) * kPfRowsPerWave;  // wave-uniform
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc(scores + wrow0 * ld, 0, (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+  const int64_t wrow0 = r0 + wave_u * kPfRowsPerWave;
+  // (emit mode: no score matrix or sample; the views are empty and unused)
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      EMIT ? nullptr : scores + wrow0 * ld, 0, EMIT ? 0 : (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<float*>(ws) + wrow0 * rw, 0, (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
+      EMIT || !ws ? nullptr : reinterpret_cast<float*>(ws) + wrow0 * rw, 0,
+      EMIT || !ws ? 0 : (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
 
   stage_tile(pk, tid, planes0);
   load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
   __syncthreads();
-  int64_t nbq[kPfCg][4];
+  int nbq[kPfCg][4];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
     for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
+  const uint32_t* thr_w = thr_sh + wave * kPfRowsPerWave;  // emit mode: the wave's row thresholds (LDS)
 
   f32x16_t accA[kPfCg], accB[kPfCg];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
     for (int e = 0; e < 16; ++e) accB[cg][e] = 0.f;
-  // one tile: matrix reads from cur, staging (of tile t+1) into nxt
-  auto tile = [&](int64_t t, const uint32_t (*cur)[kPfBlocks * kPfRowWords], uint32_t (*nxt)[kPfBlocks * kPfRowWords]) {
+  // emit mode: each group's record is reserved right after its epilogue and
+  // scattered after the next group's matrix work (recA: a tile's first
+  // group, recB: its second)
+  EmitRec recA{}, recB{};
+  uint32_t baseA = 0u;
+  // reserve a finished record's slots: one atomic per row (lane L < 16: row L)
+  auto reserve = [&](const EmitRec& rec) -> uint32_t {
+    const int64_t r = wrow0 + lane;
+    uint32_t base = 0u;
+    if (lane < kPfRowsPerWave && r < M && rec.run > 0u) base = atomicAdd(fa.cnt + r, rec.run);
+    return base;
+  };
+  // one tile: matrix reads from cur_planes, staging (of tile t+1) into nxt
+  auto tile = [&](int64_t t, const uint32_t (*cur_planes)[kPfBlocks * kPfRowWords],
+                  uint32_t (*nxt)[kPfBlocks * kPfRowWords]) {
     const int64_t b0 = t * kPfBlocks;
-    group_mfma(cur, 0, j32, h, aq, accA);
-    group_store<HIST>(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, wrs, ld, rw, smp_off);  // previous tile, group 1
-    group_mfma(cur, 1, j32, h, aq, accB);
-    group_store<HIST>(accA, b0 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
+    group_mfma(cur_planes, 0, j32, h, aq, accA);
+    uint32_t baseB = 0u;
+    if constexpr (EMIT) {
+      group_emit(accB, b0 - 32 + j32, t > t_begin, h, lane, nbq, thr_w, fa.k, recB);  // previous tile, group 1
+      baseB = reserve(recB);
+      if (t > t_begin) scatter_emit(recA, baseA, b0 - kPfBlocks + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    } else {
+      group_store<HIST>(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, wrs, ld, rw, smp_off);
+    }
+    group_mfma(cur_planes, 1, j32, h, aq, accB);
+    if constexpr (EMIT) {
+      group_emit(accA, b0 + j32, true, h, lane, nbq, thr_w, fa.k, recA);
+      baseA = reserve(recA);
+      if (t > t_begin) scatter_emit(recB, baseB, b0 - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    } else {
+      group_store<HIST>(accA, b0 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
+    }
     stage_tile(pk, tid, nxt);  // tile t+1 (past the run: the last tile again, never read)
     load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
     __syncthreads();
@@ -281,7 +377,15 @@ score_prefill_store_kernel(const uint16_t* __restrict__ idx_q, int M, const int6
     tile(t, planes0, planes1);
     ++t;
   }
-  group_store<HIST>(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);  // last tile, group 1
+  // last tile, group 1
+  if constexpr (EMIT) {
+    scatter_emit(recA, baseA, t * kPfBlocks - kPfBlocks + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    group_emit(accB, t * kPfBlocks - 32 + j32, true, h, lane, nbq, thr_w, fa.k, recB);
+    const uint32_t base = reserve(recB);
+    scatter_emit(recB, base, t * kPfBlocks - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+  } else {
+    group_store<HIST>(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
+  }
 }
 
 template <int MODE>
@@ -521,14 +625,13 @@ hipError_t launch_score_prefill(const void* idx_q, int M, const int64_t* row_pos
   if (!prefill_views_fit(nb_max, ld)) return hipErrorInvalidValue;
   const PfGrid g = pf_grid(M, nb_max);
   const FlatArgs none{};
-  (void)none;
   if (sel_ws)
-    hipLaunchKernelGGL(score_prefill_store_kernel<true>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws,
+    hipLaunchKernelGGL(score_prefill_pipe_kernel<kPfScoresSample>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, sel_ws, none,
                        g.n_rt, g.n_tiles, g.n_chunks);
   else
-    hipLaunchKernelGGL(score_prefill_store_kernel<false>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
-                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr,
+    hipLaunchKernelGGL(score_prefill_pipe_kernel<kPfScores>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+                       static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, scores, ld, nullptr, none,
                        g.n_rt, g.n_tiles, g.n_chunks);
   return hipGetLastError();
 }
@@ -547,7 +650,7 @@ hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* ro
   fa.k = k_blocks;
   if (emit) {
     const PfGrid g = pf_grid(M, nb_max);
-    hipLaunchKernelGGL(score_prefill_kernel<kPfEmit>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+    hipLaunchKernelGGL(score_prefill_pipe_kernel<kPfEmit>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
                        static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa,
                        g.n_rt, g.n_tiles, g.n_chunks);
   } else {
