@@ -212,6 +212,8 @@ def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
         s64 = O.score_blocks(d["idx_q"][i], pooled_ref, p + 1)
         nb = len(s64)
         g32 = sc[i, :nb].astype(np.float64)
+        # entries past the row's block count are left untouched (the fill value)
+        assert np.all(sc[i, nb:] == -7.0), "scores written past the row's block count"
         # scores: float32 accumulation against fp64
         assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), float(np.max(np.abs(g32 - s64)))
         # the select kernel is exact on its own input
