@@ -219,7 +219,23 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 
   __syncthreads();
   const int nseg = nseg_sh;
-  const SegDesc seg0 = segs[0];
+  // the first segment's descriptor, wave-uniform: held in scalar registers
+  SegDesc seg0;
+  {
+    const SegDesc d0 = segs[0];
+    auto u64 = [](uint64_t x) -> uint64_t {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+      return ((uint64_t)hi << 32) | lo;
+    };
+    seg0.lo = (int64_t)u64((uint64_t)d0.lo);
+    seg0.hi = (int64_t)u64((uint64_t)d0.hi);
+    seg0.cap = (int64_t)u64((uint64_t)d0.cap);
+    seg0.k = reinterpret_cast<const unsigned char*>(u64(reinterpret_cast<uint64_t>(d0.k)));
+    seg0.v = reinterpret_cast<const unsigned char*>(u64(reinterpret_cast<uint64_t>(d0.v)));
+    seg0.ks = reinterpret_cast<const uint16_t*>(u64(reinterpret_cast<uint64_t>(d0.ks)));
+    seg0.vs = reinterpret_cast<const uint16_t*>(u64(reinterpret_cast<uint64_t>(d0.vs)));
+  }
 
   for (int t = 0; t < tiles_per_split; ++t) {
     const int j0 = tok_begin + t * kTileTok;
@@ -652,7 +668,23 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   const int total = ns * kBlockTokens + tail;
   __syncthreads();
   const int nseg = nseg_sh;
-  const SegDesc seg0 = segs[0];
+  // the first segment's descriptor, wave-uniform: held in scalar registers
+  SegDesc seg0;
+  {
+    const SegDesc d0 = segs[0];
+    auto u64 = [](uint64_t x) -> uint64_t {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+      return ((uint64_t)hi << 32) | lo;
+    };
+    seg0.lo = (int64_t)u64((uint64_t)d0.lo);
+    seg0.hi = (int64_t)u64((uint64_t)d0.hi);
+    seg0.cap = (int64_t)u64((uint64_t)d0.cap);
+    seg0.k = reinterpret_cast<const unsigned char*>(u64(reinterpret_cast<uint64_t>(d0.k)));
+    seg0.v = reinterpret_cast<const unsigned char*>(u64(reinterpret_cast<uint64_t>(d0.v)));
+    seg0.ks = reinterpret_cast<const uint16_t*>(u64(reinterpret_cast<uint64_t>(d0.ks)));
+    seg0.vs = reinterpret_cast<const uint16_t*>(u64(reinterpret_cast<uint64_t>(d0.vs)));
+  }
 
   float m_run[4], l_run[4];  // heads 4 g4 + v (identical over the 16 lanes of a row)
 #pragma unroll
@@ -668,54 +700,71 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   uint32_t* vl = lds + wave * Lds::kWaveWords;
   uint32_t* pl = vl + 4 * Lds::kQuadWords;
 
-  for (int t = 0; t < tiles_per_split; ++t) {
-    const int j0 = tok_begin + t * tile + wave * 16;
-    if (j0 >= total) break;  // wave-uniform: the loop has no workgroup barrier
-    // 1. token of this lane's row position
-    const int j = j0 + n16;
+  // Slice pipeline: slice t+1's K loads are issued right after slice t's QK
+  // and its V loads right after slice t's V staging, into the same
+  // registers, so they are in flight during slice t's softmax and P.V.
+  struct SliceAddr {
+    const unsigned char* kr;
+    const unsigned char* vr;
+    const uint16_t* ksp;
+    const uint16_t* vsp;
+    int ok;
+  };
+  // 1. token of this lane's position in slice t (block id bidv) -> K/V rows
+  auto resolve_slice = [&](int t, int32_t bidv) -> SliceAddr {
+    const int j = tok_begin + t * tile + wave * 16 + n16;
     int64_t tok = -1;
     if (j < total) {
       if (j < ns * kBlockTokens) {
-        if (bid >= 0 && bid < nb) tok = (int64_t)bid * kBlockTokens + (j & 3);
+        if (bidv >= 0 && bidv < nb) tok = (int64_t)bidv * kBlockTokens + (j & 3);
       } else {
         tok = nb * kBlockTokens + (j - ns * kBlockTokens);
       }
     }
-    const unsigned char* kr = qh;  // any readable address; masked below
-    const unsigned char* vr = qh;
-    const uint16_t* ksp = reinterpret_cast<const uint16_t*>(qh);
-    const uint16_t* vsp = ksp;
-    int ok = 0;
+    // any readable address for a masked token (its logit is replaced, its
+    // V row zeroed)
+    SliceAddr a{qh, qh, reinterpret_cast<const uint16_t*>(qh), reinterpret_cast<const uint16_t*>(qh), 0};
     auto resolve = [&](const SegDesc& sd) {
       const int64_t rel = tok - sd.lo;
-      const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !ok;
+      const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !a.ok;
       const int64_t row = (int64_t)g * sd.cap + rel;
-      kr = hit ? sd.k + row * kRowBytes : kr;
-      vr = hit ? sd.v + row * kRowBytes : vr;
+      a.kr = hit ? sd.k + row * kRowBytes : a.kr;
+      a.vr = hit ? sd.v + row * kRowBytes : a.vr;
       if constexpr (F8) {
-        ksp = hit ? sd.ks + row : ksp;
-        vsp = hit ? sd.vs + row : vsp;
+        a.ksp = hit ? sd.ks + row : a.ksp;
+        a.vsp = hit ? sd.vs + row : a.vsp;
       }
-      ok |= hit ? 1 : 0;
+      a.ok |= hit ? 1 : 0;
     };
     if (nseg == 1) {
       resolve(seg0);  // one segment (the common case): its descriptor stays in registers
     } else {
       for (int si = 0; si < nseg; ++si) resolve(segs[si]);
     }
-    // K operand rows: all k-steps
-    uint4 kb[KL];
+    return a;
+  };
+  // block id of the lane's token in slice t (index clamped, so the load is
+  // unconditional)
+  auto block_id = [&](int t) -> int32_t {
+    const int jb = (tok_begin + t * tile + wave * 16 + n16) >> 2;
+    const int32_t v = srow[jb < k_blocks ? jb : k_blocks - 1];
+    return jb < k_blocks ? v : -1;
+  };
+  uint4 kb[KL];  // K operand rows: all k-steps
+  uint32_t ks_bits = 0, vs_bits = 0;
+  auto load_k = [&](const SliceAddr& a) {
 #pragma unroll
-    for (int s = 0; s < KL; ++s) kb[s] = ldg16(kr + (F8 ? 64 * s + 16 * g4 : (32 * s + 8 * g4) * 2));
-    uint32_t ks_bits = 0, vs_bits = 0;
+    for (int s = 0; s < KL; ++s) kb[s] = ldg16(a.kr + (F8 ? 64 * s + 16 * g4 : (32 * s + 8 * g4) * 2));
     if constexpr (F8) {
-      ks_bits = *ksp;
-      vs_bits = *vsp;
+      ks_bits = *a.ksp;
+      vs_bits = *a.vsp;
     }
-    // V items: (token quad vq, chunk c) of the slice; lanes past the item
-    // count (fp8 at head_dim 128) load a valid chunk and write nothing
-    uint4 vt[VIT][4];
-    int vok[VIT];
+  };
+  // V items: (token quad vq, chunk c) of the slice; lanes past the item
+  // count (fp8 at head_dim 128) load a valid chunk and write nothing
+  uint4 vt[VIT][4];
+  int vok[VIT];
+  auto load_v = [&](const SliceAddr& a) {
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
       const int item = (lane + kWave * u) % VITEMS;
@@ -724,37 +773,49 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       vok[u] = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const unsigned char* r = shfl_ptr(vr, 4 * vq + e);
-        vok[u] |= __shfl(ok, 4 * vq + e, kWave) << e;
+        const unsigned char* r = shfl_ptr(a.vr, 4 * vq + e);
+        vok[u] |= __shfl(a.ok, 4 * vq + e, kWave) << e;
         vt[u][e] = ldg16(r + c * 16);
       }
     }
-    // next slice's block id, in flight during this slice's compute
-    if (t + 1 < tiles_per_split) {
-      const int jn = j + tile;
-      bid = (jn >> 2) < k_blocks ? srow[jn >> 2] : -1;
-    }
+  };
+  SliceAddr cur = resolve_slice(0, bid);
+  int32_t bid_n = block_id(1);  // slice 1
+  load_k(cur);
+  load_v(cur);
 
-    // 2. QK: sacc[v] = q[head 4 g4 + v] . K[token n16]
+  for (int t = 0; t < tiles_per_split; ++t) {
+    const int j0 = tok_begin + t * tile + wave * 16;
+    if (j0 >= total) break;  // wave-uniform: the loop has no workgroup barrier
+    const int ok = cur.ok;
+    // 2. QK: sacc[v] = q[head 4 g4 + v] . K[token n16] (a masked token's
+    // logit is replaced below: its K needs no mask)
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (F8) {
 #pragma unroll
       for (int s = 0; s < KL; ++s) {
-        const uint4 x = ok ? kb[s] : make_uint4(0, 0, 0, 0);
-        const uint4 lo = fp8x8_to_bf16x8(x.x, x.y);
-        const uint4 hi = fp8x8_to_bf16x8(x.z, x.w);
+        const uint4 lo = fp8x8_to_bf16x8(kb[s].x, kb[s].y);
+        const uint4 hi = fp8x8_to_bf16x8(kb[s].z, kb[s].w);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s], __builtin_bit_cast(bf16x8_t, lo), sacc, 0, 0, 0);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s + 1], __builtin_bit_cast(bf16x8_t, hi), sacc, 0, 0,
                                                        0);
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)  // a masked token's logit is replaced below: its K needs no mask
+      for (int s = 0; s < KS; ++s)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, kb[s]), sacc, 0, 0, 0);
     }
     // fp8: this lane's token scales (0 for a masked token)
     const float k_sc = F8 ? (ok ? f16_bits_to_f32(ks_bits) : 0.f) : 1.f;
     const float v_sc = F8 ? (ok ? f16_bits_to_f32(vs_bits) : 0.f) : 1.f;
+    // next slice of this split (if any): its rows and K loads
+    const bool more = t + 1 < tiles_per_split;
+    SliceAddr nxt = cur;
+    if (more) {
+      nxt = resolve_slice(t + 1, bid_n);
+      load_k(nxt);
+      bid_n = block_id(t + 2);
+    }
 
     // 3. online softmax per head over the row's 16 tokens
     float alpha[4];
@@ -807,6 +868,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
         put8(t[0], t[1], t[2], t[3], quad, c);
       }
     }
+    if (more) load_v(nxt);  // the V registers are free again
+    cur = nxt;
     // rescale: the lane's heads 4 g4 + r are its softmax heads (skipped when
     // no head's running maximum moved, the common case after the first tiles)
     if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
