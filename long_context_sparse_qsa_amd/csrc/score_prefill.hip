@@ -19,27 +19,30 @@
 // holds, for its block, the 4 heads of each of its rows in consecutive
 // accumulator registers, so the ReLU'd head sum needs no lane exchange.
 //
-// Work: tiles of 64 consecutive blocks x 128 rows.  A workgroup (4 waves,
-// 32 rows each) keeps its rows' index-query operands in VGPRs and walks a
-// contiguous run of block tiles (about two workgroups per compute unit in
-// all).  Per tile the pooled keys are split into planes and staged in LDS
-// with padded 272-byte rows; the next tile's loads are issued right after,
-// so they arrive during the tile's matrix work.  Per 32-block group a wave
-// runs 4 column groups x 8 k-steps x 3 planes MFMAs, then ReLU's and sums
-// the heads and stores.  Blocks at or past a row's own block count are not
-// stored.  With a selection workspace the epilogue also stores the score
-// sample of every 16-block group (as the few-row variant does).
+// Work: tiles of 64 consecutive blocks x 128 rows.  A workgroup (8 waves,
+// 16 rows each, one workgroup per compute unit) keeps its rows' index-query
+// operands in VGPRs and walks a contiguous run of block tiles.  LDS holds
+// two tiles' planes (padded 272-byte rows): while a tile is multiplied, the
+// next one is split and staged and the one after it is loading.  Per
+// 32-block group a wave runs 2 row groups x 8 k-steps x 3 planes MFMAs; the
+// group's epilogue runs next to the following group's matrix work (two
+// accumulator sets alternate).  Blocks at or past a row's own block count
+// are not stored: stores go through buffer views of the wave's rows, and a
+// masked lane's offset lies past the view, which the hardware drops.
 //
-// Two more modes serve the memory-flat score -> top-k (no score matrix):
-//  - sample only: the tile's 64 B columns are the sampled blocks of 64
-//    consecutive 16-block groups, and their scores go to the rows' samples;
-//  - emit: after scoring a tile, each row keeps only its blocks whose score
-//    digit reaches the row's threshold.  A wave counts its rows' candidates
-//    (ballots), reserves space with one atomic add per row (all issued
-//    together, one round trip) and appends the (key, block) pairs to the
-//    row's candidate slots in no particular order; slots past the capacity
-//    are dropped (the count still records them, which sends the row to the
-//    exact selection).
+// Modes:
+//  - scores (and, with a selection workspace, the score sample of every
+//    16-block group, as the few-row variant stores it);
+//  - sample only (memory-flat selection): the tile's 64 B columns are the
+//    sampled blocks of 64 consecutive 16-block groups, and their scores go
+//    to the rows' samples;
+//  - emit (memory-flat selection): each row keeps only its blocks whose
+//    score digit reaches the row's threshold.  Per 32-block group a wave
+//    counts its rows' candidates (ballots), reserves space with one atomic
+//    add per row (all issued together; the result is used a group of matrix
+//    work later) and appends the (key, block) pairs to the row's candidate
+//    slots in no particular order; slots past the capacity are dropped (the
+//    count still records them, which sends the row to the exact selection).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
@@ -188,6 +191,27 @@ __device__ __forceinline__ void group_store(const f32x16_t (&acc)[kPfCg], int64_
   }
 }
 
+// Sample-only mode's epilogue of one 32-block group: column b is sample
+// group b (its sampled block), whose score goes to the row's sample slot
+// through the wave's buffer view of the sample rows.
+__device__ __forceinline__ void group_sample(const f32x16_t (&acc)[kPfCg], int64_t b, bool valid, int h,
+                                             const int (&nbq)[kPfCg][4], __amdgpu_buffer_rsrc_t srs, int64_t n_grp) {
+  const int64_t blk = b * 16 + sel::sample_offset((uint32_t)b);
+#pragma unroll
+  for (int cg = 0; cg < kPfCg; ++cg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
+      x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
+      x *= kScoreScale;
+      const int rr = 8 * cg + 2 * q + h;
+      const bool keep = valid && b < n_grp && blk < nbq[cg][q];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srs, keep ? (int)((rr * n_grp + b) * 4) : kBufferDrop,
+                                            0, 0);
+    }
+  }
+}
+
 // Emit mode's record of one 32-block group: the keys of the lane's 8
 // outputs (row group cg, row pair q), which of them are candidates, and
 // (lane L < 16) the candidate count of row L of the wave.
@@ -265,7 +289,7 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
                           uint32_t* __restrict__ ws, FlatArgs fa, int n_rt, int64_t n_tiles, int n_chunks) {
   constexpr bool HIST = MODE == kPfScoresSample;
   constexpr bool EMIT = MODE == kPfEmit;
-  static_assert(MODE != kPfSampleOnly, "sample-only mode runs on score_prefill_kernel");
+  constexpr bool SAMPLE = MODE == kPfSampleOnly;
   __shared__ __align__(16) uint32_t planes0[3][kPfBlocks * kPfRowWords];
   __shared__ __align__(16) uint32_t planes1[3][kPfBlocks * kPfRowWords];
   __shared__ int nb_sh[kPfRows];
@@ -309,9 +333,11 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
   const int64_t smp_off = sel::sample_off(nb_max);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
   const int64_t wrow0 = r0 + wave_u * kPfRowsPerWave;
-  // (emit mode: no score matrix or sample; the views are empty and unused)
+  // score rows (sample-only mode: sample rows; emit mode: none, the views
+  // are empty and unused)
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      EMIT ? nullptr : scores + wrow0 * ld, 0, EMIT ? 0 : (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
+      EMIT ? nullptr : SAMPLE ? static_cast<void*>(fa.samples + wrow0 * fa.n_grp) : scores + wrow0 * ld, 0,
+      EMIT ? 0 : SAMPLE ? (int)(kPfRowsPerWave * fa.n_grp * 4) : (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       EMIT || !ws ? nullptr : reinterpret_cast<float*>(ws) + wrow0 * rw, 0,
       EMIT || !ws ? 0 : (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
@@ -353,6 +379,8 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
       group_emit(accB, b0 - 32 + j32, t > t_begin, h, lane, nbq, thr_w, fa.k, recB);  // previous tile, group 1
       baseB = reserve(recB);
       if (t > t_begin) scatter_emit(recA, baseA, b0 - kPfBlocks + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    } else if constexpr (SAMPLE) {
+      group_sample(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, fa.n_grp);
     } else {
       group_store<HIST>(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, wrs, ld, rw, smp_off);
     }
@@ -361,6 +389,8 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
       group_emit(accA, b0 + j32, true, h, lane, nbq, thr_w, fa.k, recA);
       baseA = reserve(recA);
       if (t > t_begin) scatter_emit(recB, baseB, b0 - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    } else if constexpr (SAMPLE) {
+      group_sample(accA, b0 + j32, true, h, nbq, srs, fa.n_grp);
     } else {
       group_store<HIST>(accA, b0 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
     }
@@ -383,212 +413,10 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
     group_emit(accB, t * kPfBlocks - 32 + j32, true, h, lane, nbq, thr_w, fa.k, recB);
     const uint32_t base = reserve(recB);
     scatter_emit(recB, base, t * kPfBlocks - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+  } else if constexpr (SAMPLE) {
+    group_sample(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, fa.n_grp);
   } else {
     group_store<HIST>(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, wrs, ld, rw, smp_off);
-  }
-}
-
-template <int MODE>
-__global__ void __launch_bounds__(kWave * kPfWaves, 1)
-score_prefill_kernel(const uint16_t* __restrict__ idx_q, int M, const int64_t* __restrict__ row_pos,
-                     const float* __restrict__ pooled, int64_t nb_max, float* __restrict__ scores,
-                     int64_t ld, uint32_t* __restrict__ ws, FlatArgs fa, int n_rt, int64_t n_tiles, int n_chunks) {
-  __shared__ __align__(16) uint32_t planes[2][3][kPfBlocks * kPfRowWords];  // two tiles in turn
-  __shared__ int64_t nb_sh[kPfRows];
-  __shared__ uint32_t thr_sh[kPfRows];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int j32 = lane & 31;  // A row ((row, head) pair) / B column (block) / D column
-  const int h = lane >> 5;    // k half of the operands; row parity of the outputs
-  // this workgroup: row tile rt, block tiles [t_begin, t_end).  Workgroups
-  // go to the 8 XCDs round-robin by index; when the run count allows, all
-  // row tiles of a run land on one XCD, so its L2 fetches each pooled tile
-  // once for all of them.
-  int rt, chunk;
-  if (n_chunks % kXcds == 0) {
-    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    rt = slot % n_rt;
-    chunk = (slot / n_rt) * kXcds + xcd;
-  } else {
-    rt = blockIdx.x % n_rt;
-    chunk = blockIdx.x / n_rt;
-  }
-  const int64_t t_begin = n_tiles * chunk / n_chunks;
-  const int64_t t_end = n_tiles * (chunk + 1) / n_chunks;
-  if (t_begin >= t_end) return;
-  const int r0 = rt * kPfRows;
-
-  // A operand of row group cg: A row j32 = (row 8 cg + j32 / 4 of the wave's
-  // 16, head j32 % 4), k-step s: dims 16 s + 8 h .. + 7
-  uint4 aq[kPfCg][kPfKs];
-#pragma unroll
-  for (int cg = 0; cg < kPfCg; ++cg) {
-    int r = r0 + wave * kPfRowsPerWave + 8 * cg + (j32 >> 2);
-    r = r < M ? r : M - 1;
-    const uint16_t* src = idx_q + ((int64_t)r * kIndexHeads + (j32 & 3)) * kIndexDim + 8 * h;
-#pragma unroll
-    for (int s = 0; s < kPfKs; ++s) aq[cg][s] = *reinterpret_cast<const uint4*>(src + 16 * s);
-  }
-  // issued after the query operands: the first staging's wait then covers
-  // them as well, and the tile loop never waits for them
-  float4 pk[kPfF4];
-  load_tile<MODE>(pooled, nb_max, t_begin, tid, pk);
-  if (tid < kPfRows) {
-    const int r = r0 + tid;
-    nb_sh[tid] = r < M ? clamp_nb(row_pos[r], nb_max) : 0;
-    if constexpr (MODE == kPfEmit) thr_sh[tid] = r < M ? fa.thr[r] : 0u;
-  }
-  const int64_t rw = sel::row_words(nb_max);
-  const int64_t smp_off = sel::sample_off(nb_max);
-  // Score and sample stores go through buffer views of the wave's 16 rows:
-  // a masked lane gets an offset past the view's end, which the hardware
-  // drops, so every store instruction issues on every tile and the wait for
-  // the next tile's loads can count past them (the launcher keeps both
-  // views under 2 GiB).
-  const int64_t wrow0 = r0 + __builtin_amdgcn_readfirstlane(wave) * kPfRowsPerWave;  // wave-uniform
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc(scores + wrow0 * ld, 0, (int)(kPfRowsPerWave * ld * 4), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<float*>(ws) + wrow0 * rw, 0, (int)(kPfRowsPerWave * rw * 4), kBufferWord3);
-  (void)srs;
-  (void)wrs;
-  const uint64_t half = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;  // the lane's row in a ballot
-  const uint64_t lane_lt = (1ull << lane) - 1ull;
-
-  // Pipeline: tile t's planes are in buffer (t - t_begin) % 2 when its
-  // matrix work starts.  After it, tile t+1's raw keys (loaded during tile
-  // t-1) are split into the other buffer, tile t+2's loads are issued, and
-  // only then are tile t's scores stored: a wait for a load also waits for
-  // every memory operation issued before it, so no store sits between a
-  // load and its wait.  Loads past the run re-read its last tile (never
-  // used).
-  stage_tile(pk, tid, planes[0]);
-  load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
-  __syncthreads();
-  // block count of each output row of the lane (row 8 cg + 2q + h of the
-  // wave's 16; 0 past the last row), held in registers for every tile
-  int64_t nbq[kPfCg][4];
-#pragma unroll
-  for (int cg = 0; cg < kPfCg; ++cg)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const int cur = (int)((t - t_begin) & 1);
-    const int64_t b0 = t * kPfBlocks;
-    // emit mode: the keys of the lane's (block, row) outputs and which of
-    // them are candidates, and each row's candidate count in the tile
-    uint32_t ekey[kPfBg][kPfCg][4];
-    uint32_t eflag = 0u;
-    uint32_t run = 0u;  // lane L < 16: candidates of row L of the wave
-    (void)ekey;
-
-    // both 32-block groups at once: four independent accumulators, and
-    // each k-step's B reads have the other group's MFMAs to hide behind
-    f32x16_t accs[kPfBg][kPfCg];
-#pragma unroll
-    for (int bg = 0; bg < kPfBg; ++bg)
-#pragma unroll
-      for (int cg = 0; cg < kPfCg; ++cg)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) accs[bg][cg][e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kPfKs; ++s) {
-#pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
-        uint4 bv[kPfBg];
-#pragma unroll
-        for (int bg = 0; bg < kPfBg; ++bg)
-          bv[bg] = *reinterpret_cast<const uint4*>(
-              &planes[cur][pl][(bg * 32 + j32) * kPfRowWords + (16 * s + 8 * h) / 2]);
-#pragma unroll
-        for (int bg = 0; bg < kPfBg; ++bg)
-#pragma unroll
-          for (int cg = 0; cg < kPfCg; ++cg)
-            accs[bg][cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
-                                                                  __builtin_bit_cast(bf16x8_t, bv[bg]),
-                                                                  accs[bg][cg], 0, 0, 0);
-      }
-    }
-    if (t + 1 < t_end) stage_tile(pk, tid, planes[cur ^ 1]);
-    // (emit mode waits for its atomics' results below: its loads go last)
-    if constexpr (MODE != kPfEmit) load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
-
-#pragma unroll
-    for (int bg = 0; bg < kPfBg; ++bg) {
-      const f32x16_t (&acc)[kPfCg] = accs[bg];
-      // acc[cg][4q + hd] = D[8q + 4h + hd][j32]: head hd of row 8 cg + 2q + h
-      // (of the wave's 16), block b0 + 32 bg + j32
-      const int64_t b = b0 + bg * 32 + j32;
-      const bool smp = sel::sampled((uint32_t)b);
-#pragma unroll
-      for (int cg = 0; cg < kPfCg; ++cg) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
-          x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
-          x *= kScoreScale;
-          const int rl = wave * kPfRowsPerWave + 8 * cg + 2 * q + h;
-          const int r = r0 + rl;
-          const int64_t nbr = nbq[cg][q];  // 0 for rows past M
-          if constexpr (MODE == kPfScores || MODE == kPfScoresSample) {
-            const int rr = 8 * cg + 2 * q + h;  // row in the wave's views
-            const bool keep = b < nbr;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srs,
-                                                  keep ? (int)((rr * ld + b) * 4) : kBufferDrop, 0, 0);
-            if constexpr (MODE == kPfScoresSample)
-              __builtin_amdgcn_raw_buffer_store_b32(
-                  __float_as_uint(x), wrs, keep && smp ? (int)((rr * rw + smp_off + (b >> 4)) * 4) : kBufferDrop, 0, 0);
-          }
-          if constexpr (MODE == kPfSampleOnly) {  // b is the sample group
-            if (b < fa.n_grp && b * 16 + sel::sample_offset((uint32_t)b) < nbr)
-              fa.samples[(int64_t)r * fa.n_grp + b] = x;
-          }
-          if constexpr (MODE == kPfEmit) {
-            const uint32_t key = sel::order_key(x);
-            const bool c = b < nbr && nbr > fa.k && (key >> sel::kDigitShift) >= thr_sh[rl];
-            ekey[bg][cg][q] = key;
-            eflag |= c ? 1u << ((bg * kPfCg + cg) * 4 + q) : 0u;
-            const uint64_t m = __ballot(c);
-            const uint32_t n0 = (uint32_t)__popcll(m & 0x00000000FFFFFFFFull);  // row 8 cg + 2q
-            const uint32_t n1 = (uint32_t)__popcll(m & 0xFFFFFFFF00000000ull);  // row 8 cg + 2q + 1
-            run += lane == 8 * cg + 2 * q ? n0 : (lane == 8 * cg + 2 * q + 1 ? n1 : 0u);
-          }
-        }
-      }
-    }
-
-    if constexpr (MODE == kPfEmit) {
-      // reserve each row's slots: one atomic per row, all in flight together
-      uint32_t base = 0u;
-      {
-        const int r = r0 + wave * kPfRowsPerWave + lane;
-        if (lane < kPfRowsPerWave && r < M && run > 0u) base = atomicAdd(fa.cnt + r, run);
-      }
-#pragma unroll
-      for (int cg = 0; cg < kPfCg; ++cg) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rw8 = 8 * cg + 2 * q + h;
-          const int r = r0 + wave * kPfRowsPerWave + rw8;
-          uint32_t pos = (uint32_t)__shfl((int)base, rw8, kWave);
-#pragma unroll
-          for (int bg = 0; bg < kPfBg; ++bg) {
-            const bool c = (eflag >> ((bg * kPfCg + cg) * 4 + q)) & 1u;
-            const uint64_t mk = __ballot(c) & half;
-            const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
-            if (c && p < (uint32_t)sel::kFlatCap) {
-              fa.keys[(int64_t)r * sel::kFlatCap + p] = ekey[bg][cg][q];
-              fa.ids[(int64_t)r * sel::kFlatCap + p] = (uint32_t)(b0 + bg * 32 + j32);
-            }
-            pos += (uint32_t)__popcll(mk);
-          }
-        }
-      }
-      load_tile<MODE>(pooled, nb_max, t + 2 < t_end ? t + 2 : t_end - 1, tid, pk);
-    }
-    __syncthreads();  // tile t+1 staged; every wave is done with buffer cur
   }
 }
 
@@ -655,7 +483,7 @@ hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* ro
                        g.n_rt, g.n_tiles, g.n_chunks);
   } else {
     const PfGrid g = pf_grid(M, fa.n_grp);
-    hipLaunchKernelGGL(score_prefill_kernel<kPfSampleOnly>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
+    hipLaunchKernelGGL(score_prefill_pipe_kernel<kPfSampleOnly>, dim3(g.wgs()), dim3(kWave * kPfWaves), 0, stream,
                        static_cast<const uint16_t*>(idx_q), M, row_pos, pooled, nb_max, nullptr, 0, nullptr, fa,
                        g.n_rt, g.n_tiles, g.n_chunks);
   }
