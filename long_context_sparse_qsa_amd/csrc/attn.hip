@@ -496,6 +496,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 operand of the 16x16x16 MFMA
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Two float32 values to packed bf16 (first in the low half), rounded to
+// nearest even by the hardware conversion.
+typedef __bf16 bf16x2e_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2e_t));
+}
+
 // E4M3 codes -> bf16.  Every E4M3 value (4 significant bits, exponents
 // 2^-9 .. 2^8) is exact in bf16, so the hardware conversion to float32
 // followed by dropping the low 16 bits loses nothing.
@@ -526,15 +533,22 @@ __device__ __forceinline__ const unsigned char* shfl_ptr(const unsigned char* p,
 // ends with the same bits (each step adds two equal-order operands).
 template <int CTRL>
 __device__ __forceinline__ int dpp_row(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);  // full-row patterns: every source lane exists
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// larger of two finite or -inf values (a compare and a select: no NaN
+// canonicalisation, which fmaxf needs around lane exchanges)
+__device__ __forceinline__ float max2(float a, float b) { return b > a ? b : a; }
+template <int CTRL>
+__device__ __forceinline__ float row_max_step(float x) {
+  return max2(x, __int_as_float(dpp_row<CTRL>(__float_as_int(x))));
+}
 // max / sum over the 16 lanes of a row (lanes 16r .. 16r+15)
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, __int_as_float(dpp_row<kDppXor1>(__float_as_int(x))));
-  x = fmaxf(x, __int_as_float(dpp_row<kDppXor2>(__float_as_int(x))));
-  x = fmaxf(x, __int_as_float(dpp_row<kDppHalfMirror>(__float_as_int(x))));
-  return fmaxf(x, __int_as_float(dpp_row<kDppMirror>(__float_as_int(x))));
+  x = row_max_step<kDppXor1>(x);
+  x = row_max_step<kDppXor2>(x);
+  x = row_max_step<kDppHalfMirror>(x);
+  return row_max_step<kDppMirror>(x);
 }
 __device__ __forceinline__ float row16_sum(float x) {
   x += __int_as_float(dpp_row<kDppXor1>(__float_as_int(x)));
@@ -823,13 +837,16 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float s2 = ok ? (F8 ? sacc[v] * k_sc : sacc[v]) * scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m_run[v], row16_max(s2));
+      const float m_new = max2(m_run[v], row16_max(s2));
       alpha[v] = (m_run[v] == m_new) ? 1.f : __builtin_amdgcn_exp2f(m_run[v] - m_new);
       const float pv = (s2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2 - m_new);
-      const uint32_t pb = f32_to_bf16_bits(pv);  // PV consumes bf16: normalise by the same values
+      // PV consumes bf16 (rounded to nearest even): normalise by the same
+      // values; fp8: V's scale joins the PV weight (the high half)
+      const uint32_t both = bf16x2_bits(pv, F8 ? pv * v_sc : pv);
+      const uint32_t pb = both & 0xffffu;
       l_run[v] = l_run[v] * alpha[v] + row16_sum(__uint_as_float(pb << 16));
       m_run[v] = m_new;
-      const uint32_t pbv = F8 ? (uint32_t)f32_to_bf16_bits(pv * v_sc) : pb;  // fp8: V's scale joins the weight
+      const uint32_t pbv = both >> 16;
       pw[v] = pbv | ((uint32_t)dpp_row<kDppXor1>((int)pbv) << 16);
     }
     // probabilities of token pair n16/2 (quad n16/4, parity (n16/2)%2),
