@@ -501,7 +501,7 @@ def main():
         # pooled keys: report issued bf16 flops against the bf16 peak, and the
         # float32-equivalent (algorithmic) rate beside it
         alg_flops = sum(min((p + 1) // 4, nb_max) for p in wl.rows) * 4 * 128 * 2
-        roofline = {"bound": "mfma", "kernel": "score_prefill_kernel",
+        roofline = {"bound": "mfma", "kernel": "score_prefill_pipe_kernel",
                     "achieved": 3 * alg_flops / (score_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": 3 * alg_flops / (score_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                     "traffic": None, "algorithmic_tflops": alg_flops / (score_us * 1e-6) / 1e12,
