@@ -468,12 +468,15 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
 //   1. lanes resolve the slice's 16 tokens (lane % 16) to K and V rows; every
 //      load of the slice is issued before any is used;
 //   2. QK on v_mfma_f32_16x16x32_bf16: A = the group's 12 query heads (rows
-//      12..15 zero) held in VGPRs for the whole kernel, B = the 16 tokens' K
+//      12..15 zero) staged once in LDS in operand layout and read back per
+//      slice (16 bytes per lane and k-step: no VGPRs held), B = the 16 tokens' K
 //      rows loaded straight into the operand layout (lane: token lane % 16,
 //      8 consecutive dims per k-step);
 //   3. online softmax per head over the 16 lanes that hold a head's tokens
 //      (base-2 exponentials, bf16-rounded probabilities packed in token
-//      pairs into a wave-private LDS region);
+//      pairs into a wave-private LDS region); a running maximum moves only
+//      when a logit exceeds it by more than kMaxSlack, and each lane sums
+//      its own tokens' probabilities, added over the row after the loop;
 //   4. PV on v_mfma_f32_16x16x16_bf16, D/16 instructions per slice: A = the
 //      probabilities (12 heads x 16 tokens, read back from LDS in operand
 //      layout), B = V staged in LDS as 4-token quads per dim (lane group g
@@ -558,6 +561,15 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 constexpr int kMaxWaves = 8;  // waves (16-token slices) per workgroup
+// How far (log2 units) a logit may exceed its head's running maximum before
+// the maximum moves: probabilities stay below 2^8, and rounding them to bf16
+// keeps the same relative error whatever maximum they are taken against.
+constexpr float kMaxSlack = 8.f;
+
+// Where a masked token's K and V are read from: a row of zeros (its logit is
+// replaced by -inf, and a zero V row adds nothing to P.V), so V needs no
+// masking after the load.  Also its fp8 scales (0).
+__device__ __align__(16) const unsigned char kZeroRow[512] = {};
 
 // Word offset, inside a V quad row, of piece k (dims 8 u8 + 2k, + 1; 16
 // bytes) of 8-dim unit u8.  The pieces of a unit are rotated by (u8 / 4) % 4
@@ -577,18 +589,22 @@ struct MfmaLds {
   static constexpr int kQuadWords = 2 * D + 32;  // one token quad of V (+ pad)
   static constexpr int kPWords = 4 * 2 * 16;     // probabilities, heads 0..15
   static constexpr int kWaveWords = 4 * kQuadWords + kPWords;
+  // the QK A operand (query heads), shared by the workgroup's waves: 16 bytes
+  // per lane and k-step, after the wave regions
+  static constexpr int kQWords = (D / 32) * kWave * 4;
+  static constexpr int qop(int W) { return W * kWaveWords; }
   static constexpr int acc(int w) { return w * kGroup * D; }
   static constexpr int m(int W, int w) { return W * kGroup * D + w * kGroup; }
   static constexpr int l(int W, int w) { return W * kGroup * D + W * kGroup + w * kGroup; }
   static constexpr int wt(int W, int h) { return W * kGroup * D + 2 * W * kGroup + h * kMaxWaves; }
   static constexpr int lse(int W) { return W * kGroup * D + 2 * W * kGroup + kGroup * kMaxWaves; }
   static constexpr size_t bytes(int W) {
-    return 4 * (size_t)(W * kWaveWords > lse(W) + kGroup ? W * kWaveWords : lse(W) + kGroup);
+    return 4 * (size_t)(qop(W) + kQWords > lse(W) + kGroup ? qop(W) + kQWords : lse(W) + kGroup);
   }
 };
 
 template <int D, int NW, bool F8>
-__global__ void __launch_bounds__(kWave * NW)
+__global__ void __launch_bounds__(kWave * NW, NW < 8 ? 8 / NW : 1)  // at least 8 waves per CU: registers for 2 per SIMD
 attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2,
                  const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                  KvArgs kv, const int32_t* __restrict__ sel, const int32_t* __restrict__ n_sel,
@@ -602,6 +618,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   constexpr int VITEMS = 4 * VCH;          // (token quad, chunk) V staging items
   constexpr int VIT = (VITEMS + kWave - 1) / kWave;  // per lane
   constexpr int KL = F8 ? KS / 2 : KS;     // 16-byte K loads per lane
+  static_assert(kRowBytes <= (int)sizeof(kZeroRow), "zero row shorter than a K/V row");
   using Lds = MfmaLds<D>;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ SegDesc segs[kMaxSegments];
@@ -629,14 +646,21 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     const int j = tok_begin + wave * 16 + n16;
     bid = (j >> 2) < k_blocks ? srow[j >> 2] : -1;
   }
-  // query operand: head n16 (rows 12..15 are zero), dims 32 s + 8 g4 .. + 7
-  const unsigned char* qh = reinterpret_cast<const unsigned char*>(
-      q + ((int64_t)m * hq + (int64_t)g * kGroup + (n16 < kGroup ? n16 : 0)) * D);
-  uint4 qraw[KS];
+  // query operand, staged once in LDS for all waves: chunk i is k-step i / 64
+  // of lane i % 64, i.e. head (i % 64) % 16 (heads 12..15 are zero), dims
+  // 32 s + 8 g .. + 7 for lane group g (fp8: the permuted dims below)
+  constexpr int kQChunks = KS * kWave;
+  constexpr int kQPer = (kQChunks + kWave * NW - 1) / (kWave * NW);
+  uint4 qraw[kQPer];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int dim = F8 ? 64 * (s >> 1) + 16 * g4 + 8 * (s & 1) : 32 * s + 8 * g4;
-    qraw[s] = ldg16(qh + dim * 2);
+  for (int e = 0; e < kQPer; ++e) {
+    const int i = tid + kWave * NW * e;
+    const int ic = i < kQChunks ? i : 0;
+    const int s = ic / kWave, h = ic & 15, gq = (ic % kWave) >> 4;
+    const int dim = F8 ? 64 * (s >> 1) + 16 * gq + 8 * (s & 1) : 32 * s + 8 * gq;
+    qraw[e] = ldg16(reinterpret_cast<const unsigned char*>(
+                        q + ((int64_t)m * hq + (int64_t)g * kGroup + (h < kGroup ? h : 0)) * D) +
+                    dim * 2);
   }
   int si_lo = 0, nseg_all = 0;
   if (kv.n_seq == 1) {
@@ -666,12 +690,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   }
   if (tid < nseg_all) segs[tid] = mine;
   if (tid == 0) nseg_sh = nseg_all;
-  bf16x8_t qa[KS];
+  uint4* qop = reinterpret_cast<uint4*>(lds + Lds::qop(nw));
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint4 x = n16 < kGroup ? qraw[s] : make_uint4(0, 0, 0, 0);
-    qa[s] = __builtin_bit_cast(bf16x8_t, x);
+  for (int e = 0; e < kQPer; ++e) {
+    const int i = tid + kWave * NW * e;
+    if (i < kQChunks) qop[i] = (i & 15) < kGroup ? qraw[e] : make_uint4(0, 0, 0, 0);
   }
+  // k-step s of this lane's query operand (read per slice: no VGPRs held)
+  auto qa = [&](int s) { return __builtin_bit_cast(bf16x8_t, qop[s * kWave + lane]); };
 
   const int64_t n_vis = p + 1 > 0 ? p + 1 : 0;
   const int64_t nb = n_vis / kBlockTokens;
@@ -700,11 +726,14 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     seg0.vs = reinterpret_cast<const uint16_t*>(u64(reinterpret_cast<uint64_t>(d0.vs)));
   }
 
-  float m_run[4], l_run[4];  // heads 4 g4 + v (identical over the 16 lanes of a row)
+  // running maxima of heads 4 g4 + v (identical over the 16 lanes of a row)
+  // and this lane's share of their normalisers (its tokens' probabilities;
+  // summed over the row after the loop)
+  float m_run[4], l_part[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     m_run[v] = -INFINITY;
-    l_run[v] = 0.f;
+    l_part[v] = 0.f;
   }
   // PV accumulators: pacc[n][r] = O[head 4 g4 + r][dim 16 n + n16] (heads
   // 12..15 of lane group 3 are padding)
@@ -724,20 +753,21 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     const uint16_t* vsp;
     int ok;
   };
-  // 1. token of this lane's position in slice t (block id bidv) -> K/V rows
-  auto resolve_slice = [&](int t, int32_t bidv) -> SliceAddr {
+  // 1. token of this lane's position in slice t (block id bidv) -> K/V rows;
+  // with live false every token is masked
+  auto resolve_slice = [&](int t, int32_t bidv, bool live) -> SliceAddr {
     const int j = tok_begin + t * tile + wave * 16 + n16;
     int64_t tok = -1;
-    if (j < total) {
+    if (live && j < total) {
       if (j < ns * kBlockTokens) {
         if (bidv >= 0 && bidv < nb) tok = (int64_t)bidv * kBlockTokens + (j & 3);
       } else {
         tok = nb * kBlockTokens + (j - ns * kBlockTokens);
       }
     }
-    // any readable address for a masked token (its logit is replaced, its
-    // V row zeroed)
-    SliceAddr a{qh, qh, reinterpret_cast<const uint16_t*>(qh), reinterpret_cast<const uint16_t*>(qh), 0};
+    // a masked token reads the zero row
+    const unsigned char* zr = kZeroRow;
+    SliceAddr a{zr, zr, reinterpret_cast<const uint16_t*>(zr), reinterpret_cast<const uint16_t*>(zr), 0};
     auto resolve = [&](const SegDesc& sd) {
       const int64_t rel = tok - sd.lo;
       const bool hit = tok >= 0 && rel >= 0 && tok < sd.hi && rel < sd.cap && !a.ok;
@@ -758,11 +788,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     return a;
   };
   // block id of the lane's token in slice t (index clamped, so the load is
-  // unconditional)
+  // unconditional; resolve_slice reads it only for tokens of the first ns
+  // blocks, ns <= k_blocks, so the value is used raw: no select waits on it)
   auto block_id = [&](int t) -> int32_t {
     const int jb = (tok_begin + t * tile + wave * 16 + n16) >> 2;
-    const int32_t v = srow[jb < k_blocks ? jb : k_blocks - 1];
-    return jb < k_blocks ? v : -1;
+    return srow[jb < k_blocks ? jb : k_blocks - 1];
   };
   uint4 kb[KL];  // K operand rows: all k-steps
   uint32_t ks_bits = 0, vs_bits = 0;
@@ -777,25 +807,21 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   // V items: (token quad vq, chunk c) of the slice; lanes past the item
   // count (fp8 at head_dim 128) load a valid chunk and write nothing
   uint4 vt[VIT][4];
-  int vok[VIT];
   auto load_v = [&](const SliceAddr& a) {
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
       const int item = (lane + kWave * u) % VITEMS;
       const int vq = item / VCH;
       const int c = item % VCH;
-      vok[u] = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned char* r = shfl_ptr(a.vr, 4 * vq + e);
-        vok[u] |= __shfl(a.ok, 4 * vq + e, kWave) << e;
-        vt[u][e] = ldg16(r + c * 16);
-      }
+      for (int e = 0; e < 4; ++e) vt[u][e] = ldg16(shfl_ptr(a.vr, 4 * vq + e) + c * 16);
     }
   };
-  SliceAddr cur = resolve_slice(0, bid);
+  SliceAddr cur = resolve_slice(0, bid, true);
   int32_t bid_n = block_id(1);  // slice 1
   load_k(cur);
+  // K before V, as in the loop body: the loop head then waits for K only
+  __builtin_amdgcn_sched_barrier(0);
   load_v(cur);
 
   for (int t = 0; t < tiles_per_split; ++t) {
@@ -810,41 +836,44 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       for (int s = 0; s < KL; ++s) {
         const uint4 lo = fp8x8_to_bf16x8(kb[s].x, kb[s].y);
         const uint4 hi = fp8x8_to_bf16x8(kb[s].z, kb[s].w);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s], __builtin_bit_cast(bf16x8_t, lo), sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2 * s + 1], __builtin_bit_cast(bf16x8_t, hi), sacc, 0, 0,
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa(2 * s), __builtin_bit_cast(bf16x8_t, lo), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa(2 * s + 1), __builtin_bit_cast(bf16x8_t, hi), sacc, 0, 0,
                                                        0);
       }
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, kb[s]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa(s), __builtin_bit_cast(bf16x8_t, kb[s]), sacc, 0, 0, 0);
     }
     // fp8: this lane's token scales (0 for a masked token)
     const float k_sc = F8 ? (ok ? f16_bits_to_f32(ks_bits) : 0.f) : 1.f;
     const float v_sc = F8 ? (ok ? f16_bits_to_f32(vs_bits) : 0.f) : 1.f;
-    // next slice of this split (if any): its rows and K loads
+    // next slice of this split: its rows and K loads.  Past the split's last
+    // slice every token is masked and the loads read the zero row: the loads
+    // stay unconditional, so every path through the loop has the same loads
+    // in flight and each wait counts only the loads it needs.
     const bool more = t + 1 < tiles_per_split;
-    SliceAddr nxt = cur;
-    if (more) {
-      nxt = resolve_slice(t + 1, bid_n);
-      load_k(nxt);
-      bid_n = block_id(t + 2);
-    }
+    const SliceAddr nxt = resolve_slice(t + 1, bid_n, more);
+    load_k(nxt);
+    bid_n = block_id(t + 2);
 
-    // 3. online softmax per head over the row's 16 tokens
+    // 3. online softmax per head over the row's 16 tokens (base-2 logits).
+    // A head's running maximum moves only when the row's maximum exceeds it
+    // by more than kMaxSlack (always on a wave's first slice, rarely after),
+    // so the accumulator rescale below is usually skipped.
     float alpha[4];
     uint32_t pw[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float s2 = ok ? (F8 ? sacc[v] * k_sc : sacc[v]) * scale_log2 : -INFINITY;
-      const float m_new = max2(m_run[v], row16_max(s2));
+      const float rmax = row16_max(s2);
+      const float m_new = rmax > m_run[v] + kMaxSlack ? rmax : m_run[v];
       alpha[v] = (m_run[v] == m_new) ? 1.f : __builtin_amdgcn_exp2f(m_run[v] - m_new);
       const float pv = (s2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s2 - m_new);
       // PV consumes bf16 (rounded to nearest even): normalise by the same
       // values; fp8: V's scale joins the PV weight (the high half)
       const uint32_t both = bf16x2_bits(pv, F8 ? pv * v_sc : pv);
-      const uint32_t pb = both & 0xffffu;
-      l_run[v] = l_run[v] * alpha[v] + row16_sum(__uint_as_float(pb << 16));
+      l_part[v] = l_part[v] * alpha[v] + __uint_as_float(both << 16);
       m_run[v] = m_new;
       const uint32_t pbv = both >> 16;
       pw[v] = pbv | ((uint32_t)dpp_row<kDppXor1>((int)pbv) << 16);
@@ -861,9 +890,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       const int item = lane + kWave * u;
       const int vq = item / VCH;
       const int c = item % VCH;
-      uint4 t[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = ((vok[u] >> e) & 1) ? vt[u][e] : make_uint4(0, 0, 0, 0);
+      const uint4* t = vt[u];  // a masked token's row is the zero row
       // one 8-dim unit u8 (dims 8 u8 .. + 7): tokens' words -> 8 dims x
       // (t0 t1, t2 t3); its four 16-byte pieces are rotated by vslot
       auto put8 = [&](uint4 a, uint4 b, uint4 cc, uint4 d, uint32_t* quad, int u8) {
@@ -885,15 +912,13 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
         put8(t[0], t[1], t[2], t[3], quad, c);
       }
     }
-    if (more) load_v(nxt);  // the V registers are free again
+    load_v(nxt);  // the V registers are free again
     cur = nxt;
-    // rescale: the lane's heads 4 g4 + r are its softmax heads (skipped when
-    // no head's running maximum moved, the common case after the first tiles)
     if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pacc[n][r] *= alpha[r];
+        for (int r = 0; r < 4; ++r) pacc[n][r] *= alpha[r];  // the lane's heads are its softmax heads
     }
     __builtin_amdgcn_wave_barrier();
     // 4. PV on v_mfma_f32_16x16x16_bf16: A = P (head n16, tokens 4 g4 .. + 3),
@@ -907,9 +932,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
           *reinterpret_cast<const uint2*>(vl + g4 * Lds::kQuadWords + vslot(dim >> 3, (dim & 7) >> 1) + 2 * (dim & 1));
       pacc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, __builtin_bit_cast(s16x4_t, vb2), pacc[n], 0, 0, 0);
     }
+    // interleave the B reads (paired 8-byte reads) with the matrix
+    // instructions, a few reads ahead, instead of holding all D/16 operands
+    // in registers at once
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < NT / 2 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_wave_barrier();
   }
 
+  float l_run[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) l_run[v] = row16_sum(l_part[v]);
   // ---- merge the wave partials (log2 domain)
   __syncthreads();  // every wave is done with its V / P region
   float* fl = reinterpret_cast<float*>(lds);
