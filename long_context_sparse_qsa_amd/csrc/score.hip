@@ -356,10 +356,19 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
       const int r = st * 4 + (i16 >> 2);
       if ((i16 & 3) != 0 || r >= rows) continue;
       float* dst = scores + (int64_t)(m0 + r) * ld;
+      // the lane's 4 consecutive blocks in one 16-byte store when all four
+      // are stored here (every span but a row's last and a fresh block's)
+      const uint32_t fr = (fresh >> (g * kGroupBlocks + 4 * kq)) & 0xfu;
+      if (bb + 3 < nb_row[st] && fr == 0u) {
+        *reinterpret_cast<float4*>(dst + bb) = make_float4(sv[st][0], sv[st][1], sv[st][2], sv[st][3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (bb + v < nb_row[st] && !((fr >> v) & 1u)) dst[bb + v] = sv[st][v];
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const bool keep = bb + v < nb_row[st] && !((fresh >> (g * kGroupBlocks + 4 * kq + v)) & 1u);
-        if (keep) dst[bb + v] = sv[st][v];
+        const bool keep = bb + v < nb_row[st] && !((fr >> v) & 1u);
         // one sampled block per 16-block group: its score goes to the group's slot
         if (HIST && keep && sel::sampled((uint32_t)(bb + v)))
           reinterpret_cast<float*>(ws)[(size_t)(m0 + r) * rw + smp_off + ((bb + v) >> 4)] = sv[st][v];
