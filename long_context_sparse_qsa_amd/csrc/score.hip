@@ -281,8 +281,9 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   // index-query operand are small and cached; issued before the pooled
   // stream, their waits leave the pooled loads in flight.  The pooled loads
   // depend only on nb_max (the host bound), not on the row positions.
+  // (a wave past nb_max issues its clamped loads and leaves below: no
+  // early branch holds the argument loads back)
   const int64_t wave_b0 = (int64_t)bx * kBlocksPerWG + wave * kBlocksPerWave;
-  if (wave_b0 >= nb_max) return;
   const int i16 = lane & 15;   // A row (block in group) / B column
   const int kq = lane >> 4;    // k slot 0..3
   int64_t pos_r[RPG];
@@ -294,7 +295,9 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   // repeat the last; 1 <= n_new <= 64)
   int64_t new_p = -1;
   if constexpr (APPEND) new_p = ap.pos[lane < ap.n_new ? lane : ap.n_new - 1];
-  const int s = row_seq ? row_seq[m0] : 0;
+  // rows of several sequences come one per row group; a group of several
+  // rows is one sequence's, so only the one-row kernel looks its sequence up
+  const int s = (RPG == 1 && row_seq) ? row_seq[m0] : 0;
   const bool seq_ok = s >= 0 && s < n_seq;
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
