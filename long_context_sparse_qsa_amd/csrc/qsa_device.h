@@ -53,14 +53,22 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
-  return v;
+// Inclusive prefix sum over the 64 lanes of a wave, through DPP moves (no
+// LDS round trips): row_shr 1, 2, 4, 8 scan each 16-lane row (a lane whose
+// source lies outside its row adds the old value 0), then row_bcast 15 adds
+// row 0's total to row 1 and row 2's to row 3, and row_bcast 31 adds the
+// total of rows 0-1 to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_add_step(uint32_t v) {
+  return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/) {
+  v = dpp_add_step<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add_step<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add_step<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add_step<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  return dpp_add_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
 }
 
 // Make a value known to be wave-uniform visible as such to the compiler, so

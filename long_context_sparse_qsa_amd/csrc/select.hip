@@ -64,7 +64,6 @@ using sel::find_digit_desc;
 
 struct FinSmem {
   uint32_t hist16[kBins * kCopies];  // exact-path radix passes; also the 12-bit digit histogram
-  uint32_t tot[kBins];
   uint32_t h2[kLowBins];             // bits 19..10 of the cut-digit keys
   uint32_t h3[kLowBins];             // bits 9..0 of the cut keys
   uint32_t ck[kCandMax];             // candidate keys, ascending block order
@@ -154,7 +153,7 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   }
   __syncthreads();
   // conservative threshold (not reached: every block is a candidate)
-  find_digit_desc<kChunkThreads, kWinBins>(h, sel::sample_target((uint32_t)k), scan_sh, out3);
+  find_digit_desc<kWinBins>(h, sel::sample_target((uint32_t)k), out3);
   // window bin 0 (or a target never reached): every block is a candidate
   const uint32_t B = (out3[2] || out3[0] == 0u) ? 0u : kWinBase + out3[0];
 
@@ -178,8 +177,10 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
 #pragma unroll
   for (int e = 0; e < kChunkPer; ++e) {
     if ((flags >> e) & 1u) {
-      K[pos] = key[e];
-      I[pos] = (uint32_t)(i0 + e);
+      if (pos < (uint32_t)kChunk) {  // the chunk's own slots (a scan result never leaves them)
+        K[pos] = key[e];
+        I[pos] = (uint32_t)(i0 + e);
+      }
       ++pos;
     }
   }
@@ -308,7 +309,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   // search stops as soon as the cut bin is kept whole.  Then a key is kept if
   // (key >> shift) > prefix, or == prefix and (whole, or among the first
   // `need` such keys in block order).
-  find_digit_desc<kFinThreads, kDigits>(sm.hist16, (uint32_t)k, sm.scan_sh, sm.out3);
+  find_digit_desc<kDigits>(sm.hist16, (uint32_t)k, sm.out3);
   uint32_t prefix = sm.out3[0];
   uint32_t need = sm.out3[1];
   int shift = kDigitShift;
@@ -319,7 +320,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
       if (((vm >> e) & 1u) && (kk[e] >> kDigitShift) == prefix) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
     }
     __syncthreads();
-    find_digit_desc<kFinThreads, kLowBins>(sm.h2, need, sm.scan_sh, sm.out3);
+    find_digit_desc<kLowBins>(sm.h2, need, sm.out3);
     const uint32_t d2 = sm.out3[0];
     prefix = (prefix << 10) | d2;
     need = sm.out3[1];
@@ -332,7 +333,7 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
       if (((vm >> e) & 1u) && (kk[e] >> 10) == prefix) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
     }
     __syncthreads();
-    find_digit_desc<kFinThreads, kLowBins>(sm.h3, need, sm.scan_sh, sm.out3);
+    find_digit_desc<kLowBins>(sm.h3, need, sm.out3);
     const uint32_t d3 = sm.out3[0];
     prefix = (prefix << 10) | d3;
     need = sm.out3[1];

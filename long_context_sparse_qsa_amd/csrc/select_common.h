@@ -93,59 +93,74 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, ui
   const uint32_t incl = wave_incl_scan(v, lane);
   if (lane == kWave - 1) sh[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < NW ? sh[lane] : 0u;
-    x = wave_incl_scan(x, lane);
-    if (lane < NW) sh[NW + lane] = x;
+  // every wave reads the wave totals itself (no second scan pass)
+  uint32_t before = 0u, tot = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = sh[w];
+    before += w < wave ? t : 0u;
+    tot += t;
   }
-  __syncthreads();
-  const uint32_t before = wave > 0 ? sh[NW + wave - 1] : 0u;
-  total = sh[2 * NW - 1];
-  __syncthreads();
+  total = tot;
+  __syncthreads();  // sh is free for the next scan
   return before + incl - v;
 }
 
-// Counts cnt[0..NBINS) in LDS (digit order ascending): find the digit where
-// the count from the top reaches `want`.  out3 = {digit, want - count above
-// the digit, 0}; out3[2] = 1 when the total stays below `want`.  Thread t
-// owns a contiguous run of bins (thread 0 the top ones); the lanes that share
-// a bank read their runs in rotated order, so the sums are conflict-free.
-template <int NT, int NBINS>
-__device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* scan_sh, uint32_t* out3) {
-  constexpr int PER = NBINS >= NT ? NBINS / NT : 1;
-  static_assert(NBINS < NT || NBINS % NT == 0, "bins split evenly over threads");
-  static_assert((PER & (PER - 1)) == 0 && PER <= kWave, "power-of-two run per thread");
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const bool owns = NBINS >= NT || t < NBINS;
-  const int lo = NBINS - (t + 1) * PER;
-  uint32_t mine = 0;
-  if (owns) {
-    const int rot = (lane * PER) / kWave;
+// Counts in LDS, C copies per bin (cnt[bin * C + copy]; digit order
+// ascending): find the digit where the count from the top reaches `want`.
+// out3 = {digit, want - count above the digit, 0}; out3[2] = 1 when the
+// total stays below `want`.  One wave does it, with no workgroup barrier
+// inside: lane l sums the run of NBINS / 64 bins l-th from the top (its
+// reads rotated by lane, so lanes spread over the banks), a wave scan finds
+// the run that crosses `want`, and the lanes then take that run's bins one
+// each.  The caller makes the counts visible first (a barrier); the function
+// ends with one.
+template <int NBINS, int C = 1>
+__device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* out3) {
+  static_assert(NBINS % kWave == 0 && NBINS / kWave <= kWave, "one run of bins per lane");
+  constexpr int R = NBINS / kWave;  // bins per lane
+  constexpr int W = R * C;          // words per lane
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    const uint32_t* run = cnt + (NBINS - (l + 1) * R) * C;
+    uint32_t c = 0u;
+    if constexpr (W % 4 == 0) {
+      constexpr int Q = W / 4;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) mine += cnt[lo + ((j + rot) & (PER - 1))];
-  }
-  if (t == 0) {
-    out3[0] = 0u;
-    out3[1] = want;
-    out3[2] = 1u;
-  }
-  uint32_t tot;
-  const uint32_t above = block_excl_scan<NT>(mine, scan_sh, tot);
-  if (owns && above < want && above + mine >= want) {  // one thread: walk its run from the top
-    uint32_t c[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) c[j] = cnt[lo + j];
-    uint32_t a = above;
-#pragma unroll
-    for (int j = PER - 1; j >= 0; --j) {
-      if (a + c[j] >= want) {
-        out3[0] = (uint32_t)(lo + j);
-        out3[1] = want - a;
-        out3[2] = 0u;
-        break;
+      for (int j = 0; j < Q; ++j) {
+        const uint4 x = reinterpret_cast<const uint4*>(run)[(j + l) % Q];
+        c += (x.x + x.y) + (x.z + x.w);
       }
-      a += c[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j) c += run[j];
+    }
+    const uint32_t incl = wave_incl_scan(c, l);
+    // counts are non-negative: the first lane whose inclusive count reaches
+    // want holds the digit
+    const uint64_t hit = __ballot(incl >= want);
+    if (hit == 0u) {
+      if (l == 0) {
+        out3[0] = 0u;
+        out3[1] = want;
+        out3[2] = 1u;
+      }
+    } else {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      const uint32_t above = (uint32_t)__shfl((int)(incl - c), L, kWave);
+      const int top = NBINS - L * R - 1;  // the run's top bin
+      uint32_t v = 0u;
+      if (l < R) {
+#pragma unroll
+        for (int e = 0; e < C; ++e) v += cnt[(top - l) * C + e];
+      }
+      const uint32_t vi = wave_incl_scan(v, l);
+      const uint64_t h2 = __ballot(l < R && above + vi >= want);
+      if (l == __ffsll((unsigned long long)h2) - 1) {
+        out3[0] = (uint32_t)(top - l);
+        out3[1] = want - (above + vi - v);
+        out3[2] = 0u;
+      }
     }
   }
   __syncthreads();
@@ -154,7 +169,7 @@ __device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* sc
 // Exact top-k of a whole row: four 8-bit radix passes over all keys (16
 // copies of each 256-bin histogram against atomic contention), then an
 // order-preserving compaction in index order (ties go to the lower index).
-// Src(i) gives block i's score; Sm provides hist16[4096], tot[256], scan_sh
+// Src(i) gives block i's score; Sm provides hist16[4096], scan_sh
 // and out3 in LDS.
 struct ScoreArray {
   const float* __restrict__ s;
@@ -174,14 +189,7 @@ __device__ void exact_select(const Src& src, int64_t nb, int k, int32_t* out, Sm
       if ((u & mask) == prefix) atomicAdd(&sm.hist16[((u >> shift) & 0xffu) * kCopies + (lane & (kCopies - 1))], 1u);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kBins; i += NT) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int c = 0; c < kCopies; ++c) t += sm.hist16[i * kCopies + c];
-      sm.tot[i] = t;
-    }
-    __syncthreads();
-    find_digit_desc<NT, kBins>(sm.tot, want, sm.scan_sh, sm.out3);
+    find_digit_desc<kBins, kCopies>(sm.hist16, want, sm.out3);
     prefix |= sm.out3[0] << shift;
     mask |= 0xffu << shift;
     want = sm.out3[1];

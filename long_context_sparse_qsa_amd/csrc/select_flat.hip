@@ -69,7 +69,6 @@ __global__ void __launch_bounds__(kThrThreads)
 flat_threshold_kernel(const int64_t* __restrict__ row_pos, int64_t nb_max, int k, uint32_t* __restrict__ ws,
                       int M) {
   __shared__ uint32_t h[sel::kWinBins];
-  __shared__ uint32_t scan_sh[2 * (kThrThreads / kWave)];
   __shared__ uint32_t out3[3];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
@@ -82,7 +81,7 @@ flat_threshold_kernel(const int64_t* __restrict__ row_pos, int64_t nb_max, int k
   for (int64_t g = tid; g < n_grp; g += kThrThreads)
     if (g * 16 + sel::sample_offset((uint32_t)g) < nb) atomicAdd(&h[sel::win_bin(order_key(smp[g]))], 1u);
   __syncthreads();
-  find_digit_desc<kThrThreads, sel::kWinBins>(h, sel::sample_target((uint32_t)k), scan_sh, out3);
+  find_digit_desc<sel::kWinBins>(h, sel::sample_target((uint32_t)k), out3);
   if (tid == 0) {
     // window bin 0 (or a target never reached): every block is a candidate
     ws[L.thr + m] = (out3[2] || out3[0] == 0u) ? 0u : sel::kWinBase + out3[0];
@@ -92,7 +91,6 @@ flat_threshold_kernel(const int64_t* __restrict__ row_pos, int64_t nb_max, int k
 
 struct FlatSmem {
   uint32_t hist16[256 * 16];  // the 12-bit digit histogram; the exact path's radix passes
-  uint32_t tot[256];
   uint32_t h2[kLowBins];
   uint32_t h3[kLowBins];
   uint32_t bits[kBitWords];   // kept blocks of the row
@@ -193,7 +191,7 @@ flat_finalize_kernel(const uint16_t* __restrict__ idx_q, const int64_t* __restri
   // The k-th largest candidate key, 12 + 10 + 10 bits at a time; each level
   // counts only the candidates that share the bits found so far, and the
   // search stops once the cut bin is kept whole.
-  find_digit_desc<kFinThreads, kDigits>(sm.hist16, (uint32_t)k, sm.scan_sh, sm.out3);
+  find_digit_desc<kDigits>(sm.hist16, (uint32_t)k, sm.out3);
   uint32_t prefix = sm.out3[0];
   uint32_t need = sm.out3[1];
   int shift = kDigitShift;
@@ -203,7 +201,7 @@ flat_finalize_kernel(const uint16_t* __restrict__ idx_q, const int64_t* __restri
     for (int e = 0; e < kFinPer; ++e)
       if (((vm >> e) & 1u) && (kk[e] >> kDigitShift) == prefix) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
     __syncthreads();
-    find_digit_desc<kFinThreads, kLowBins>(sm.h2, need, sm.scan_sh, sm.out3);
+    find_digit_desc<kLowBins>(sm.h2, need, sm.out3);
     const uint32_t d2 = sm.out3[0];
     prefix = (prefix << 10) | d2;
     need = sm.out3[1];
@@ -215,7 +213,7 @@ flat_finalize_kernel(const uint16_t* __restrict__ idx_q, const int64_t* __restri
     for (int e = 0; e < kFinPer; ++e)
       if (((vm >> e) & 1u) && (kk[e] >> 10) == prefix) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
     __syncthreads();
-    find_digit_desc<kFinThreads, kLowBins>(sm.h3, need, sm.scan_sh, sm.out3);
+    find_digit_desc<kLowBins>(sm.h3, need, sm.out3);
     const uint32_t d3 = sm.out3[0];
     prefix = (prefix << 10) | d3;
     need = sm.out3[1];
