@@ -236,11 +236,12 @@ typedef struct qsa_kv_segments {
  *  row_pos    int64 [M]; row_seq int32 [M] or NULL (all sequence 0)
  *  kv         K/V segment table of the sequences
  *  sel/n_sel  as written by qsa_select_topk; k_blocks its budget
- *  out        [M][hq][head_dim] dtype   (written)
+ *  out        [M][hq][head_dim] dtype   (written; 16-byte aligned)
  *  lse        float32 [M][hq]           natural-log sum of exp of the
  *                                       scaled logits; -inf for a row with no
  *                                       visible token (written)
- *  workspace / workspace_bytes          >= qsa_attn_workspace_bytes(...)
+ *  workspace / workspace_bytes          >= qsa_attn_workspace_bytes(...),
+ *                                       16-byte aligned
  *
  * Row m reads tokens 4b..4b+3 of every kept block b plus its tail tokens
  * 4*nb..p; query head h uses KV head h / (hq/hkv).  Logits, softmax and

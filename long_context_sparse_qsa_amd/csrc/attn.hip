@@ -984,23 +984,28 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     fl[Lds::lse(nw) + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  constexpr int kOut = (kGroup * D + kWave * nw - 1) / (kWave * nw);  // outputs per thread
-#pragma unroll
-  for (int e = 0; e < kOut; ++e) {
-    const int o = tid + kWave * nw * e;
-    if (o >= kGroup * D) break;
+  // 4 consecutive dims of one head per thread and step: 16-byte LDS reads
+  // and stores
+  for (int o = 4 * tid; o < kGroup * D; o += 4 * kWave * nw) {
     const int h = o / D;
     const int d = o % D;
     const float* wt = fl + Lds::wt(nw, h);
-    float O = 0.f;
+    f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < nw; ++w) O = fmaf(fl[Lds::acc(w) + o], wt[w], O);
+    for (int w = 0; w < nw; ++w) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(fl + Lds::acc(w) + o);
+      const float ww = wt[w];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[r] = fmaf(a[r], ww, O[r]);
+    }
     const int64_t head = (int64_t)m * hq + (int64_t)g * kGroup + h;
     if (splits == 1) {
-      out[head * D + d] = (uint16_t)f32_to_bf16_bits(O);
+      *reinterpret_cast<uint2*>(out + head * D + d) =
+          make_uint2((uint32_t)f32_to_bf16_bits(O[0]) | ((uint32_t)f32_to_bf16_bits(O[1]) << 16),
+                     (uint32_t)f32_to_bf16_bits(O[2]) | ((uint32_t)f32_to_bf16_bits(O[3]) << 16));
       if (d == 0) lse_out[head] = fl[Lds::lse(nw) + h];
     } else {
-      ws_o[(head * splits + split) * D + d] = O;
+      *reinterpret_cast<f32x4_t*>(ws_o + (head * splits + split) * D + d) = O;
       if (d == 0) ws_lse[head * splits + split] = fl[Lds::lse(nw) + h];
     }
   }

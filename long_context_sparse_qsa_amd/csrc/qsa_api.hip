@@ -197,6 +197,8 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
   if (M == 0) return ok();
   if (!q || !row_pos || !sel || !n_sel || !out || !lse)
     return fail(QSA_ERR_ARG, "qsa_gathered_attn: null pointer (q, row_pos, sel, n_sel, out or lse)");
+  if (((uintptr_t)out & 15u) || ((uintptr_t)workspace & 15u))
+    return fail(QSA_ERR_ARG, "qsa_gathered_attn: out and workspace must be 16-byte aligned");
   return launch_status(qsa::launch_gathered_attn(q, dtype, M, hq, hkv, head_dim, scale, row_pos,
                                                  row_seq, kv, sel, n_sel, k_blocks, out, lse,
                                                  workspace, workspace_bytes, (hipStream_t)stream),

@@ -123,6 +123,8 @@ def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FA
     (dict(ws=None, wsb=0), ERR_WS, "workspace"),
     (dict(wsb=100), ERR_WS, "workspace"),
     (dict(out=None), ERR_ARG, "null"),
+    (dict(out=FAKE + 8), ERR_ARG, "aligned"),
+    (dict(ws=FAKE + 4), ERR_ARG, "aligned"),
     (dict(M=0, ws=None, wsb=0), Q.QSA_OK, ""),
 ])
 def test_attn_validation(kw, code, word):
