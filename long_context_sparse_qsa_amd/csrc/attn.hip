@@ -1018,12 +1018,15 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 // takes one memory round trip.
 constexpr int kRegSplits = 72;
 
-template <class E, int D>
+// NS: the splits one thread holds in registers (the launch picks the
+// smallest of 16, 32, 72 that covers the plan, so no load is spent on
+// padding); more splits than 72 take plain loops.
+template <class E, int D, int NS>
 __global__ void __launch_bounds__(D)
 attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int splits,
                     typename E::T* __restrict__ out, float* __restrict__ lse_out) {
-  static_assert(D >= kRegSplits, "one thread per register-held split");
-  __shared__ float w_sh[kRegSplits];
+  static_assert(D >= NS && NS <= kRegSplits, "one thread per register-held split");
+  __shared__ float w_sh[NS];
   __shared__ float red[D / kWave];
   const int64_t head = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1031,7 +1034,7 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   const int wave = tid / kWave;
   const float* __restrict__ L = ws_lse + head * splits;
   const float* __restrict__ O = ws_o + head * splits * D + tid;
-  if (splits > kRegSplits) {  // long budgets: plain loops
+  if (splits > NS) {  // long budgets: plain loops
     float mx = -INFINITY, tot = 0.f, o = 0.f;
     for (int i = 0; i < splits; ++i) mx = fmaxf(mx, L[i]);
     if (mx != -INFINITY) {
@@ -1047,9 +1050,9 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot);
     return;
   }
-  float ov[kRegSplits];
+  float ov[NS];
 #pragma unroll
-  for (int i = 0; i < kRegSplits; ++i) ov[i] = O[(int64_t)(i < splits ? i : splits - 1) * D];  // masked by w = 0
+  for (int i = 0; i < NS; ++i) ov[i] = O[(int64_t)(i < splits ? i : splits - 1) * D];  // masked by w = 0
   const float l_own = tid < splits ? L[tid] : -INFINITY;
   float mx = wave_max(l_own);
   if (lane == 0) red[wave] = mx;
@@ -1058,7 +1061,7 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   for (int w = 0; w < D / kWave; ++w) mx = fmaxf(mx, red[w]);
   const bool empty = (mx == -INFINITY);
   const float w_own = (empty || l_own == -INFINITY) ? 0.f : expf(l_own - mx);
-  if (tid < kRegSplits) w_sh[tid] = w_own;
+  if (tid < NS) w_sh[tid] = w_own;
   float tot = wave_sum(w_own);
   __syncthreads();
   if (lane == 0) red[wave] = tot;
@@ -1068,7 +1071,7 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   for (int w = 0; w < D / kWave; ++w) tot += red[w];
   float o = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRegSplits; ++i) o = fmaf(w_sh[i], ov[i], o);  // every partial is finite
+  for (int i = 0; i < NS; ++i) o = fmaf(w_sh[i], ov[i], o);  // every partial is finite
   const bool none = empty || tot == 0.f;
   out[head * D + tid] = E::from_f(none ? 0.f : o / tot);
   if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot);
@@ -1111,9 +1114,15 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<E, D>), dim3((unsigned)M * hq), dim3(D), 0, stream, ws_o, ws_lse,
-                     plan.splits,
-                     static_cast<typename E::T*>(out), lse);
+  const dim3 cgrid((unsigned)M * hq), cblock(D);
+  typename E::T* o = static_cast<typename E::T*>(out);
+  if (plan.splits <= 16)
+    hipLaunchKernelGGL((attn_combine_kernel<E, D, 16>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits, o, lse);
+  else if (plan.splits <= 32)
+    hipLaunchKernelGGL((attn_combine_kernel<E, D, 32>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits, o, lse);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<E, D, kRegSplits>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits,
+                       o, lse);
   return hipGetLastError();
 }
 
