@@ -164,6 +164,25 @@ def test_short_and_ragged_rows(Q, rows):
     say(_check_layer(d, res, layer, k=16))
 
 
+def test_thirteen_rows_two_row_groups(Q):
+    """13 bf16 rows of one sequence at scattered positions of a 32K context:
+    the few-row scorer's 8-row groups (a full one and a ragged one of 5, two
+    column sets each), the selection and the attention plan for M = 13."""
+    say("13 rows, decode_32k context")
+    d = dict(datagen.gen_layer("decode_32k"))
+    n = d["idx"].shape[0]
+    rows = np.asarray([n - 1, n - 2, n - 3, n - 4, n - 5, n - 9, n - 17, n - 100, n - 777, n - 2048, n - 4097,
+                       n - 9001, 5000], dtype=np.int64)
+    d["rows"] = rows
+    rng = np.random.default_rng(13)
+    d["idx_q"] = datagen.round_bf16(rng.standard_normal((len(rows), 4, 128)).astype(np.float32))
+    d["q"] = datagen.round_bf16(rng.standard_normal((len(rows), 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=n - 4)
+    res = layer.run()
+    say(_check_layer(d, res, layer))
+    _assert_candidate_path(res, layer)
+
+
 @pytest.mark.parametrize("accepted", [0, 1, 2, 3])
 def test_verify_rollback_reappend(Q, accepted):
     """Speculative verify with rollback (MTPLX PR #482, section 3,
