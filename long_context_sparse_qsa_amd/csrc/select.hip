@@ -30,9 +30,6 @@
 //           than 64 chunks takes an exact radix select over the whole row in
 //           the same workgroup, so the result is exact in every case.
 //
-// Calls of 256 rows and more take a one-launch variant with one workgroup
-// per row instead of collect + finalize (below).
-//
 // The workspace holds one record per row (sel::row_words); no part of it
 // needs initialising.
 #include "qsa_device.h"
@@ -391,316 +388,6 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
   }
 }
 
-// ---------------------------------------------------------------- one workgroup per row
-//
-// For many rows (a workgroup per row fills the GPU) the collect and
-// finalize passes run in one launch, one workgroup per row: every
-// load is issued first (the row's sample and up to 65,536 scores, 16 bytes per
-// load, 32 per thread); the sample's window histogram gives the threshold
-// digit B as in the collect pass; each thread marks which of its loads hold a
-// block at or above B, those loads go to a list, the workgroup re-reads them
-// (cached) and appends their candidates (key, id) in LDS with their 12-bit
-// digit counts; the 12/10/10-bit levels find the k-th key TK; keys above TK
-// and the lowest-id keys equal to TK are marked in a bitmap of the row's
-// blocks, which gives the kept ids in ascending order.  A candidate count
-// outside [k, kCandMax], more keys equal to TK than the tie list holds, or a
-// row longer than the bitmap take the exact whole-row select.  With few rows
-// the two-pass path is faster: one compute unit streams a row at only
-// ~40 GB/s (19 vs 13 us at 4 rows of 65,280 blocks), and a short row's
-// zeroing and level passes outweigh the saved launch.
-constexpr int kRowThreads = 512;
-constexpr int kRowF4 = 32;                         // 16-byte score loads per thread per round
-constexpr int kRoundBlocks = kRowThreads * kRowF4 * 4;  // 65,536
-constexpr int kSmpPer = 8;                         // sample loads per thread per round (4,096 groups)
-constexpr int kPairPer = sel::kCandMax / kRowThreads;  // listed loads per thread (8)
-constexpr int kRowLowBins = 1024;                  // 10-bit digits below the 12-bit one
-constexpr int kMaxTies = 512;                      // keys equal to TK ranked on chip
-constexpr int64_t kRowMaxBlocks = (int64_t)kMaxChunks * kChunk;  // 262,144
-constexpr int kBitWords = (int)(kRowMaxBlocks / 32);
-constexpr int kSmpCopies = 16;                     // copies of the sample histogram against contention
-
-struct RowSmem {
-  uint32_t hist16[sel::kDigits];                  // the 12-bit digit histogram; the exact path's radix passes
-  uint32_t smp_h[sel::kWinBins * kSmpCopies];   // the sample histogram
-  uint32_t h2[kRowLowBins];                     // bits 19..10 of the cut-digit keys
-  uint32_t h3[kRowLowBins];                     // bits 9..0 of the cut keys
-  uint32_t ck[sel::kCandMax];                     // candidate keys (no particular order)
-  uint32_t ci[sel::kCandMax];                     // their block ids
-  uint32_t loads[sel::kCandMax];                  // 16-byte loads (index in the row) holding a candidate
-  uint32_t bits[kBitWords];                  // kept blocks of the row
-  uint32_t teq[kMaxTies];                    // ids of the keys equal to TK
-  uint32_t scan_sh[2 * (kRowThreads / kWave)];
-  uint32_t out3[3];
-  uint32_t n_loads, n_cand, n_placed, n_eq;
-};
-static_assert(sizeof(RowSmem) <= 160 * 1024, "fits the LDS of one compute unit");
-
-// 16-byte loads of one round: load j of thread t covers blocks
-// 4 (r0 / 4 + j * kRowThreads + t) .. + 3 (rows are padded to 4 floats).
-__device__ __forceinline__ void load_round(const float* __restrict__ s, int64_t nb_max, int64_t r0, int tid,
-                                           float4 (&sv)[kRowF4]) {
-#pragma unroll
-  for (int j = 0; j < kRowF4; ++j) {
-    const int64_t b = r0 + ((int64_t)j * kRowThreads + tid) * 4;
-    sv[j] = b < nb_max ? *reinterpret_cast<const float4*>(s + b) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// Which of the 4 blocks from b on are candidates: score >= f_min and block < nb.
-__device__ __forceinline__ uint32_t cand4(const float4& v, float f_min, int64_t b, int64_t nb) {
-  uint32_t m4 = (v.x >= f_min ? 1u : 0u) | (v.y >= f_min ? 2u : 0u) | (v.z >= f_min ? 4u : 0u) |
-                (v.w >= f_min ? 8u : 0u);
-  if (b + 4 > nb) m4 &= b >= nb ? 0u : (1u << (uint32_t)(nb - b)) - 1u;
-  return m4;
-}
-
-// Wave-aggregated append: this lane's first slot of `n` in a list whose
-// length counter lives in LDS.
-__device__ __forceinline__ uint32_t wave_append(uint32_t n, uint32_t* counter) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t incl = wave_incl_scan(n, lane);
-  const uint32_t wtot = (uint32_t)__shfl((int)incl, kWave - 1, kWave);
-  uint32_t base = 0u;
-  if (lane == 0 && wtot) base = atomicAdd(counter, wtot);
-  return (uint32_t)__shfl((int)base, 0, kWave) + incl - n;
-}
-
-__global__ void __launch_bounds__(kRowThreads)
-select_row_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
-                  int64_t nb_max, int k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-                  uint32_t* __restrict__ ws) {
-  extern __shared__ __align__(16) unsigned char row_lds[];
-  RowSmem& sm = *reinterpret_cast<RowSmem*>(row_lds);
-  const int m = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float* __restrict__ s = scores + (int64_t)m * ld;
-  int32_t* __restrict__ out = sel + (int64_t)m * k;
-  uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
-  uint32_t* path = W + sel::kPathWord;
-  const float* __restrict__ smp = reinterpret_cast<const float*>(W + sel::sample_off(nb_max));
-  const int64_t n_grp = sel::sample_groups(nb_max);
-
-  // every load of the first round at once: the position, the sample, the scores
-  const int64_t p = row_pos[m];
-  float smpv[kSmpPer];
-#pragma unroll
-  for (int e = 0; e < kSmpPer; ++e) {
-    const int64_t gi = (int64_t)e * kRowThreads + tid;
-    smpv[e] = gi < n_grp ? smp[gi] : 0.f;
-  }
-  float4 sv[kRowF4];
-  load_round(s, nb_max, 0, tid, sv);
-  const int64_t nb = clamp_nb(p, nb_max);
-  if (nb <= k) {
-    for (int i = tid; i < k; i += kRowThreads) out[i] = i < nb ? i : -1;
-    if (tid == 0) {
-      n_sel[m] = (int32_t)nb;
-      *path = sel::kPathAll;
-    }
-    return;
-  }
-  if (tid == 0) n_sel[m] = k;
-  if (nb > kRowMaxBlocks) {
-    if (tid == 0) *path = sel::kPathExactChunks;
-    sel::exact_select<kRowThreads>(sel::ScoreArray{s}, nb, k, out, sm);
-    return;
-  }
-  const int bit_words = (int)((nb + 31) / 32);
-  for (int i = tid; i < sel::kDigits; i += kRowThreads) {
-    sm.hist16[i] = 0u;
-    sm.smp_h[i] = 0u;
-  }
-  for (int i = tid; i < kRowLowBins; i += kRowThreads) {
-    sm.h2[i] = 0u;
-    sm.h3[i] = 0u;
-  }
-  for (int i = tid; i < bit_words; i += kRowThreads) sm.bits[i] = 0u;
-  if (tid == 0) {
-    sm.n_loads = 0u;
-    sm.n_cand = 0u;
-    sm.n_placed = 0u;
-    sm.n_eq = 0u;
-  }
-  __syncthreads();
-
-  // 1. the threshold digit B from the sample (blocks < nb only)
-  for (int64_t g0 = 0; g0 < n_grp; g0 += (int64_t)kSmpPer * kRowThreads) {
-    if (g0 > 0) {  // rows of more than 65,536 blocks
-#pragma unroll
-      for (int e = 0; e < kSmpPer; ++e) {
-        const int64_t gi = g0 + (int64_t)e * kRowThreads + tid;
-        smpv[e] = gi < n_grp ? smp[gi] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < kSmpPer; ++e) {
-      const int64_t gi = g0 + (int64_t)e * kRowThreads + tid;
-      if (gi < n_grp && gi * 16 + sel::sample_offset((uint32_t)gi) < nb)
-        atomicAdd(&sm.smp_h[sel::win_bin(order_key(smpv[e])) * kSmpCopies + (tid & (kSmpCopies - 1))], 1u);
-    }
-  }
-  __syncthreads();
-  find_digit_desc<sel::kWinBins, kSmpCopies>(sm.smp_h, sel::sample_target((uint32_t)k), sm.out3);
-  // window bin 0 (or a target never reached): every block is a candidate;
-  // otherwise a block is one when its key's digit reaches B, i.e. its score
-  // is at least the smallest positive float of digit B
-  const uint32_t B = (sm.out3[2] || sm.out3[0] == 0u) ? 0u : sel::kWinBase + sm.out3[0];
-  const float f_min = B == 0u ? -INFINITY : __uint_as_float((B << kDigitShift) & 0x7fffffffu);
-
-  // 2. the 16-byte loads holding a candidate, round by round
-  for (int64_t r0 = 0; r0 < nb; r0 += kRoundBlocks) {
-    if (r0 > 0) load_round(s, nb_max, r0, tid, sv);
-    uint32_t any = 0u, cnt = 0u;
-#pragma unroll
-    for (int j = 0; j < kRowF4; ++j) {
-      const uint32_t m4 = cand4(sv[j], f_min, r0 + ((int64_t)j * kRowThreads + tid) * 4, nb);
-      any |= (m4 != 0u ? 1u : 0u) << j;
-      cnt += (uint32_t)__popc(m4);
-    }
-    wave_append(cnt, &sm.n_cand);
-    uint32_t pos = wave_append((uint32_t)__popc(any), &sm.n_loads);
-    while (any) {
-      const int j = __ffs(any) - 1;
-      any &= any - 1u;
-      if (pos < (uint32_t)sel::kCandMax) sm.loads[pos] = (uint32_t)(r0 / 4 + (int64_t)j * kRowThreads + tid);
-      ++pos;
-    }
-  }
-  __syncthreads();
-  const uint32_t n_cand = sm.n_cand;
-  if (n_cand < (uint32_t)k || n_cand > (uint32_t)sel::kCandMax) {
-    if (tid == 0) *path = sel::kPathExactCount;
-    sel::exact_select<kRowThreads>(sel::ScoreArray{s}, nb, k, out, sm);
-    return;
-  }
-  // 3. the listed loads again (cached now): their candidates into LDS, and
-  // the candidates' 12-bit digit histogram (n_loads <= n_cand <= sel::kCandMax)
-  const uint32_t n_loads = sm.n_loads;
-  {
-    uint32_t li[kPairPer];
-    float4 lv[kPairPer];
-#pragma unroll
-    for (int e = 0; e < kPairPer; ++e) {
-      const uint32_t i = (uint32_t)(e * kRowThreads + tid);
-      li[e] = i < n_loads ? sm.loads[i] : 0u;
-      lv[e] = *reinterpret_cast<const float4*>(s + 4 * (int64_t)li[e]);
-    }
-    uint32_t m4[kPairPer], cnt = 0u;
-#pragma unroll
-    for (int e = 0; e < kPairPer; ++e) {
-      const uint32_t i = (uint32_t)(e * kRowThreads + tid);
-      m4[e] = i < n_loads ? cand4(lv[e], f_min, 4 * (int64_t)li[e], nb) : 0u;
-      cnt += (uint32_t)__popc(m4[e]);
-    }
-    uint32_t pos = wave_append(cnt, &sm.n_placed);
-#pragma unroll
-    for (int e = 0; e < kPairPer; ++e) {
-      if ((uint32_t)(e * kRowThreads) >= n_loads) break;  // uniform
-      const float c4[4] = {lv[e].x, lv[e].y, lv[e].z, lv[e].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (((m4[e] >> c) & 1u) && pos < (uint32_t)sel::kCandMax) {  // pos < n_cand: the same count as step 2
-          const uint32_t key = order_key(c4[c]);
-          sm.ck[pos] = key;
-          sm.ci[pos] = 4u * li[e] + (uint32_t)c;
-          atomicAdd(&sm.hist16[key >> kDigitShift], 1u);
-          ++pos;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // 4. the k-th largest candidate key, 12 + 10 + 10 bits at a time; each
-  // level counts only the candidates that share the bits found so far, and
-  // the search stops once the cut bin is kept whole
-  find_digit_desc<sel::kDigits>(sm.hist16, (uint32_t)k, sm.out3);
-  uint32_t prefix = sm.out3[0];
-  uint32_t need = sm.out3[1];
-  int shift = kDigitShift;
-  bool whole = sm.hist16[prefix] == need;
-  if (!whole) {
-    for (uint32_t i = tid; i < n_cand; i += kRowThreads) {
-      const uint32_t key = sm.ck[i];
-      if ((key >> kDigitShift) == prefix) atomicAdd(&sm.h2[(key >> 10) & (kRowLowBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_digit_desc<kRowLowBins>(sm.h2, need, sm.out3);
-    const uint32_t d2 = sm.out3[0];
-    prefix = (prefix << 10) | d2;
-    need = sm.out3[1];
-    shift = 10;
-    whole = sm.h2[d2] == need;
-  }
-  if (!whole) {
-    for (uint32_t i = tid; i < n_cand; i += kRowThreads) {
-      const uint32_t key = sm.ck[i];
-      if ((key >> 10) == prefix) atomicAdd(&sm.h3[key & (kRowLowBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_digit_desc<kRowLowBins>(sm.h3, need, sm.out3);
-    const uint32_t d3 = sm.out3[0];
-    prefix = (prefix << 10) | d3;
-    need = sm.out3[1];
-    shift = 0;
-    whole = sm.h3[d3] == need;
-  }
-  // 5. kept: keys above the cut, the whole cut bin when it fits; otherwise
-  // the keys equal to TK (shift is 0 then) go to the tie list
-  for (uint32_t i = tid; i < n_cand; i += kRowThreads) {
-    const uint32_t kh = sm.ck[i] >> shift;
-    const uint32_t id = sm.ci[i];
-    if (kh > prefix || (kh == prefix && whole)) {
-      atomicOr(&sm.bits[id >> 5], 1u << (id & 31u));
-    } else if (kh == prefix) {
-      const uint32_t j = atomicAdd(&sm.n_eq, 1u);
-      if (j < (uint32_t)kMaxTies) sm.teq[j] = id;
-    }
-  }
-  __syncthreads();
-  if (!whole) {
-    const uint32_t n_eq = sm.n_eq;
-    if (n_eq > (uint32_t)kMaxTies) {
-      if (tid == 0) *path = sel::kPathExactTies;
-      sel::exact_select<kRowThreads>(sel::ScoreArray{s}, nb, k, out, sm);
-      return;
-    }
-    // equal keys: the `need` lowest block ids (ids are distinct)
-    if ((uint32_t)tid < n_eq) {
-      const uint32_t me = sm.teq[tid];
-      uint32_t below = 0u;
-      for (uint32_t j = 0; j < n_eq; ++j) below += sm.teq[j] < me ? 1u : 0u;
-      if (below < need) atomicOr(&sm.bits[me >> 5], 1u << (me & 31u));
-    }
-    __syncthreads();
-  }
-  // 6. kept ids in ascending order: each thread owns a run of bitmap words
-  const int per = (bit_words + kRowThreads - 1) / kRowThreads;
-  const int w0 = tid * per;
-  uint32_t mine = 0u;
-  for (int w = w0; w < w0 + per && w < bit_words; ++w) mine += (uint32_t)__popc(sm.bits[w]);
-  uint32_t total;
-  uint32_t pos = block_excl_scan<kRowThreads>(mine, sm.scan_sh, total);
-  for (int w = w0; w < w0 + per && w < bit_words; ++w) {
-    uint32_t b = sm.bits[w];
-    while (b) {
-      const int bit = __ffs(b) - 1;
-      b &= b - 1u;
-      if (pos < (uint32_t)k) out[pos] = w * 32 + bit;
-      ++pos;
-    }
-  }
-  if (tid == 0) *path = sel::kPathCandidates;
-}
-
-hipError_t select_rows(const float* scores, int64_t ld, int M, const int64_t* row_pos, int64_t nb_max, int k,
-                       int32_t* sel, int32_t* n_sel, uint32_t* W, hipStream_t stream) {
-  hipLaunchKernelGGL(select_row_kernel, dim3((unsigned)M), dim3(kRowThreads), sizeof(RowSmem), stream, scores, ld,
-                     row_pos, nb_max, k, sel, n_sel, W);
-  return hipGetLastError();
-}
-
-
 hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_t* row_pos, int64_t nb_max,
                             int k, int32_t* sel, int32_t* n_sel, uint32_t* W, hipStream_t stream) {
   if (nb_max > k) {
@@ -714,11 +401,6 @@ hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_
                      row_pos, nb_max, k, sel, n_sel, W);
   return hipGetLastError();
 }
-
-// The one-launch row selection for many rows (a workgroup per row fills the
-// GPU: 143 vs 159 us for 2,048 prefill rows); the two-pass path otherwise
-// (also for short rows: 12.5 vs 10.7 us for one row of 8,192 blocks).
-bool row_select_fits(int M, int64_t /*nb_max*/) { return M >= 256; }
 
 }  // namespace
 
@@ -738,7 +420,6 @@ hipError_t launch_select_topk(const float* scores, int64_t ld, int M, const int6
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (row_select_fits(M, nb_max)) return select_rows(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel, W, stream);
   return collect_finalize(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel, W, stream);
 }
 
@@ -746,9 +427,8 @@ hipError_t launch_select_after_hist(const float* scores, int64_t ld, int M, cons
                                    int64_t nb_max, int k_blocks, int32_t* sel, int32_t* n_sel,
                                    void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  uint32_t* W = static_cast<uint32_t*>(ws);
-  if (row_select_fits(M, nb_max)) return select_rows(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel, W, stream);
-  return collect_finalize(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel, W, stream);
+  return collect_finalize(scores, ld, M, row_pos, nb_max, k_blocks, sel, n_sel, static_cast<uint32_t*>(ws),
+                          stream);
 }
 
 }  // namespace qsa

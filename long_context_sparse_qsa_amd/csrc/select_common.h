@@ -29,7 +29,6 @@ enum SelPath : uint32_t {
   kPathCandidates = 2,  // from the conservative candidates
   kPathExactChunks = 3, // exact whole-row select: more than kMaxChunks chunks
   kPathExactCount = 4,  // exact whole-row select: candidate count below k or above kCandMax
-  kPathExactTies = 5,   // exact whole-row select: more keys equal to the cut than the tie list holds
 };
 __host__ __device__ constexpr int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 __host__ __device__ constexpr int64_t n_chunks(int64_t nb_max) { return (nb_max + kChunk - 1) / kChunk; }

@@ -183,14 +183,13 @@ def test_thirteen_rows_two_row_groups(Q):
     _assert_candidate_path(res, layer)
 
 
-def test_row_selection_many_rows_all_paths(Q):
-    """288 bf16 rows of one 32K-context sequence: enough rows for the
-    one-launch row selection.  Rows 0..95 sit in the first 2,048 tokens (at
-    most k blocks: all kept), rows 96..191 have zero index queries (every score
-    0: every block ties at the cut, more than the on-chip lists hold, and the
-    exact whole-row select keeps the lowest ids), rows 192..287 are ordinary.  Every row's selection
-    is the exact top-k of the GPU scores and its path word says how it went."""
-    say("288 rows, row selection paths")
+def test_many_rows_selection_paths(Q):
+    """288 bf16 rows of one 32K-context sequence.  Rows 0..95 sit in the first
+    2,048 tokens (at most k blocks: all kept), rows 96..191 have zero index
+    queries (every score 0: every block is a candidate and ties at the cut; the
+    lowest ids are kept), rows 192..287 are ordinary.  Every row's selection is
+    the exact top-k of the GPU scores and its path word says how it went."""
+    say("288 rows, selection paths")
     d = dict(datagen.gen_layer("decode_32k"))
     n = d["idx"].shape[0]
     rng = np.random.default_rng(288)
@@ -207,12 +206,12 @@ def test_row_selection_many_rows_all_paths(Q):
     k = d["workload"].k_blocks
     nb = (rows + 1) // 4
     want = np.where(nb <= k, 1, 2)
-    # all-equal rows: more than the 4,096-entry candidate list holds -> exact
-    # by count (4); else every candidate ties at the cut and the ties exceed
-    # the 512-entry tie list -> exact by ties (5)
+    # all-equal rows: more candidates than the 4,096 the finalize pass holds
+    # -> exact by count (4); else the candidates' levels end on one cut bin of
+    # equal keys, ranked by block id (2)
     zb = nb[96:192]
-    want[96:192] = np.where(zb <= k, 1, np.where(zb > 4096, 4, 5))
-    assert {4, 5} <= set(want[96:192].tolist())
+    want[96:192] = np.where(zb <= k, 1, np.where(zb > 4096, 4, 2))
+    assert {2, 4} <= set(want[96:192].tolist())
     assert np.array_equal(res["paths"], want), (res["paths"][:8], res["paths"][96:104])
     sel = res["sel"].cpu().numpy()
     for i in range(96, 192):
