@@ -345,6 +345,16 @@ size_t qsa_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k_block
  * section 03: scratch reserved at load never grows under a captured graph). */
 size_t qsa_attn_workspace_bytes(int32_t max_M, int32_t hq, int32_t head_dim, int32_t k_blocks);
 
+/* The split plan qsa_gathered_attn uses for M rows (host-only query, no
+ * device work; the plan depends only on these arguments, so results are
+ * reproducible bit for bit).  Page: hipfire "QSA sparse attention ...",
+ * section 03 (one workgroup per KV group; gathered prefill tiles).
+ *  plan  int32 [4] (host memory, written): waves per workgroup, tokens per
+ *        tile, tiles walked by one workgroup, split-K parts per (row, KV head)
+ * Errors: QSA_ERR_ARG for M < 1, hkv < 1, k_blocks outside
+ * [1, QSA_MAX_K_BLOCKS], an unknown dtype or a NULL plan. */
+int qsa_attn_plan(int32_t M, int32_t hkv, int32_t k_blocks, int32_t dtype, int32_t* plan);
+
 /* Checks that the current HIP device is gfx950 and that the kernels load.
  * QSA_OK, or QSA_ERR_DEVICE with a reason. */
 int qsa_device_check(void);

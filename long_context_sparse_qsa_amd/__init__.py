@@ -36,7 +36,7 @@ MAX_SEGMENTS = 16
 EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
     "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
-    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes",
+    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes", "qsa_attn_plan",
     "qsa_device_check", "qsa_last_error", "qsa_version",
 )
 
@@ -77,11 +77,12 @@ _lib.qsa_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
 _lib.qsa_select_workspace_bytes.restype = _SZ
 _lib.qsa_attn_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
 _lib.qsa_attn_workspace_bytes.restype = _SZ
+_lib.qsa_attn_plan.argtypes = [_I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]
 _lib.qsa_device_check.argtypes = []
 _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-           "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_device_check"):
+           "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_attn_plan", "qsa_device_check"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -142,6 +143,14 @@ def qsa_select_workspace_bytes(max_m: int, nb_max: int, k_blocks: int) -> int:
 
 def qsa_attn_workspace_bytes(max_m: int, hq: int, head_dim: int, k_blocks: int) -> int:
     return int(_lib.qsa_attn_workspace_bytes(max_m, hq, head_dim, k_blocks))
+
+
+def qsa_attn_plan(m: int, hkv: int, k_blocks: int, dtype=torch.bfloat16) -> dict:
+    """The split plan ``qsa_gathered_attn`` uses for ``m`` rows (host only)."""
+    out = (_I32 * 4)()
+    code = QSA_BF16 if dtype == torch.bfloat16 else QSA_F32
+    _check(_lib.qsa_attn_plan(int(m), int(hkv), int(k_blocks), code, out))
+    return {"waves": out[0], "tile_tokens": out[1], "tiles_per_split": out[2], "splits": out[3]}
 
 
 def qsa_append_pool(new_idx: torch.Tensor, pos: torch.Tensor, idx_cache: torch.Tensor,

@@ -456,7 +456,10 @@ attn_decode_kernel(const typename E::T* __restrict__ q, int M, int hq, float sca
       float* o = ws_o + (head * splits + split) * D + dg * DPT;
 #pragma unroll
       for (int d = 0; d < DPT; ++d) o[d] = acc[h6][d] * inv;
-      if (dg == 0) ws_lse[head * splits + split] = lse;
+      if (dg == 0) {  // no rounding here: the two lse values of a partial agree
+        ws_lse[2 * (head * splits + split)] = lse;
+        ws_lse[2 * (head * splits + split) + 1] = lse;
+      }
     }
   }
 }
@@ -596,10 +599,12 @@ struct MfmaLds {
   static constexpr int acc(int w) { return w * kGroup * D; }
   static constexpr int m(int W, int w) { return W * kGroup * D + w * kGroup; }
   static constexpr int l(int W, int w) { return W * kGroup * D + W * kGroup + w * kGroup; }
-  static constexpr int wt(int W, int h) { return W * kGroup * D + 2 * W * kGroup + h * kMaxWaves; }
-  static constexpr int lse(int W) { return W * kGroup * D + 2 * W * kGroup + kGroup * kMaxWaves; }
+  static constexpr int l32(int W, int w) { return W * kGroup * D + 2 * W * kGroup + w * kGroup; }
+  static constexpr int wt(int W, int h) { return W * kGroup * D + 3 * W * kGroup + h * kMaxWaves; }
+  // per head: lse of the rounded normaliser (merge weights), lse of the float32 one (reported)
+  static constexpr int lse(int W) { return W * kGroup * D + 3 * W * kGroup + kGroup * kMaxWaves; }
   static constexpr size_t bytes(int W) {
-    return 4 * (size_t)(qop(W) + kQWords > lse(W) + kGroup ? qop(W) + kQWords : lse(W) + kGroup);
+    return 4 * (size_t)(qop(W) + kQWords > lse(W) + 2 * kGroup ? qop(W) + kQWords : lse(W) + 2 * kGroup);
   }
 };
 
@@ -728,12 +733,16 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 
   // running maxima of heads 4 g4 + v (identical over the 16 lanes of a row)
   // and this lane's share of their normalisers (its tokens' probabilities;
-  // summed over the row after the loop)
-  float m_run[4], l_part[4];
+  // summed over the row after the loop): l_part sums the bf16-rounded
+  // probabilities that P.V consumes (the output is normalised by it, so its
+  // weights sum to one), l_full the float32 probabilities (the reported lse
+  // comes from it, free of the bf16 rounding)
+  float m_run[4], l_part[4], l_full[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     m_run[v] = -INFINITY;
     l_part[v] = 0.f;
+    l_full[v] = 0.f;
   }
   // PV accumulators: pacc[n][r] = O[head 4 g4 + r][dim 16 n + n16] (heads
   // 12..15 of lane group 3 are padding)
@@ -874,6 +883,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       // values; fp8: V's scale joins the PV weight (the high half)
       const uint32_t both = bf16x2_bits(pv, F8 ? pv * v_sc : pv);
       l_part[v] = l_part[v] * alpha[v] + __uint_as_float(both << 16);
+      l_full[v] = l_full[v] * alpha[v] + pv;
       m_run[v] = m_new;
       const uint32_t pbv = both >> 16;
       pw[v] = pbv | ((uint32_t)dpp_row<kDppXor1>((int)pbv) << 16);
@@ -945,9 +955,12 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     __builtin_amdgcn_wave_barrier();
   }
 
-  float l_run[4];
+  float l_run[4], l_f32[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) l_run[v] = row16_sum(l_part[v]);
+  for (int v = 0; v < 4; ++v) {
+    l_run[v] = row16_sum(l_part[v]);
+    l_f32[v] = row16_sum(l_full[v]);
+  }
   // ---- merge the wave partials (log2 domain)
   __syncthreads();  // every wave is done with its V / P region
   float* fl = reinterpret_cast<float*>(lds);
@@ -962,6 +975,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     for (int v = 0; v < 4; ++v) {
       fl[Lds::m(nw, wave) + 4 * g4 + v] = m_run[v];
       fl[Lds::l(nw, wave) + 4 * g4 + v] = l_run[v];
+      fl[Lds::l32(nw, wave) + 4 * g4 + v] = l_f32[v];
     }
   }
   __syncthreads();
@@ -970,18 +984,20 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < nw; ++w) mx = fmaxf(mx, fl[Lds::m(nw, w) + h]);
-    float L = 0.f;
+    float L = 0.f, L32 = 0.f;
 #pragma unroll
     for (int w = 0; w < nw; ++w) {
       const float mw = fl[Lds::m(nw, w) + h];
       const float f = (mx == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - mx);
       fl[Lds::wt(nw, h) + w] = f;
       L += fl[Lds::l(nw, w) + h] * f;
+      L32 += fl[Lds::l32(nw, w) + h] * f;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int w = 0; w < nw; ++w) fl[Lds::wt(nw, h) + w] *= inv;
-    fl[Lds::lse(nw) + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    fl[Lds::lse(nw) + 2 * h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    fl[Lds::lse(nw) + 2 * h + 1] = L32 > 0.f ? (mx + log2f(L32)) * kLn2 : -INFINITY;
   }
   __syncthreads();
   // 4 consecutive dims of one head per thread and step: 16-byte LDS reads
@@ -1003,19 +1019,25 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       *reinterpret_cast<uint2*>(out + head * D + d) =
           make_uint2((uint32_t)f32_to_bf16_bits(O[0]) | ((uint32_t)f32_to_bf16_bits(O[1]) << 16),
                      (uint32_t)f32_to_bf16_bits(O[2]) | ((uint32_t)f32_to_bf16_bits(O[3]) << 16));
-      if (d == 0) lse_out[head] = fl[Lds::lse(nw) + h];
+      if (d == 0) lse_out[head] = fl[Lds::lse(nw) + 2 * h + 1];
     } else {
       *reinterpret_cast<f32x4_t*>(ws_o + (head * splits + split) * D + d) = O;
-      if (d == 0) ws_lse[head * splits + split] = fl[Lds::lse(nw) + h];
+      if (d == 0) *reinterpret_cast<f32x2_t*>(ws_lse + 2 * (head * splits + split)) =
+          f32x2_t{fl[Lds::lse(nw) + 2 * h], fl[Lds::lse(nw) + 2 * h + 1]};
     }
   }
 }
 
 // Merge split partials by log-sum-exp.  One workgroup per (row, head), one
 // thread per output dimension.  Each thread's partial outputs (up to
-// kRegSplits) and its own split's lse are loaded at once; thread i computes
-// split i's weight once and the weights are shared through LDS, so the merge
-// takes one memory round trip.
+// kRegSplits) and its own split's lse pair are loaded at once; thread i
+// computes split i's weight once and the weights are shared through LDS, so
+// the merge takes one memory round trip.  A partial carries two lse values:
+// that of the normaliser its output was divided by (the sum of the
+// bf16-rounded probabilities P.V consumed), which weighs the outputs so that
+// the merge equals one normalisation over all tokens, and that of the
+// float32 probabilities, which gives the reported lse.  (They coincide for
+// float32 K/V.)
 constexpr int kRegSplits = 72;
 
 // NS: the splits one thread holds in registers (the launch picks the
@@ -1027,33 +1049,35 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
                     typename E::T* __restrict__ out, float* __restrict__ lse_out) {
   static_assert(D >= NS && NS <= kRegSplits, "one thread per register-held split");
   __shared__ float w_sh[NS];
-  __shared__ float red[D / kWave];
+  __shared__ float red[D / kWave], red32[D / kWave];
   const int64_t head = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const float* __restrict__ L = ws_lse + head * splits;
+  const float* __restrict__ L = ws_lse + 2 * head * splits;  // (weighting, reported) per split
   const float* __restrict__ O = ws_o + head * splits * D + tid;
   if (splits > NS) {  // long budgets: plain loops
-    float mx = -INFINITY, tot = 0.f, o = 0.f;
-    for (int i = 0; i < splits; ++i) mx = fmaxf(mx, L[i]);
+    float mx = -INFINITY, tot = 0.f, tot32 = 0.f, o = 0.f;
+    for (int i = 0; i < splits; ++i) mx = fmaxf(mx, L[2 * i]);
     if (mx != -INFINITY) {
       for (int i = 0; i < splits; ++i) {
-        const float li = L[i];
+        const float li = L[2 * i], l32 = L[2 * i + 1];
         const float w = li == -INFINITY ? 0.f : expf(li - mx);
         tot += w;
+        tot32 += l32 == -INFINITY ? 0.f : expf(l32 - mx);
         o = fmaf(w, O[(int64_t)i * D], o);
       }
     }
     const bool empty = (mx == -INFINITY) || tot == 0.f;
     out[head * D + tid] = E::from_f(empty ? 0.f : o / tot);
-    if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot);
+    if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot32);
     return;
   }
   float ov[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) ov[i] = O[(int64_t)(i < splits ? i : splits - 1) * D];  // masked by w = 0
-  const float l_own = tid < splits ? L[tid] : -INFINITY;
+  const f32x2_t l_pair = tid < splits ? *reinterpret_cast<const f32x2_t*>(L + 2 * tid) : f32x2_t{-INFINITY, -INFINITY};
+  const float l_own = l_pair.x;
   float mx = wave_max(l_own);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
@@ -1061,20 +1085,29 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   for (int w = 0; w < D / kWave; ++w) mx = fmaxf(mx, red[w]);
   const bool empty = (mx == -INFINITY);
   const float w_own = (empty || l_own == -INFINITY) ? 0.f : expf(l_own - mx);
+  const float w32 = (empty || l_pair.y == -INFINITY) ? 0.f : expf(l_pair.y - mx);
   if (tid < NS) w_sh[tid] = w_own;
   float tot = wave_sum(w_own);
+  float tot32 = wave_sum(w32);
   __syncthreads();
-  if (lane == 0) red[wave] = tot;
+  if (lane == 0) {
+    red[wave] = tot;
+    red32[wave] = tot32;
+  }
   __syncthreads();
   tot = 0.f;
+  tot32 = 0.f;
 #pragma unroll
-  for (int w = 0; w < D / kWave; ++w) tot += red[w];
+  for (int w = 0; w < D / kWave; ++w) {
+    tot += red[w];
+    tot32 += red32[w];
+  }
   float o = 0.f;
 #pragma unroll
   for (int i = 0; i < NS; ++i) o = fmaf(w_sh[i], ov[i], o);  // every partial is finite
   const bool none = empty || tot == 0.f;
   out[head * D + tid] = E::from_f(none ? 0.f : o / tot);
-  if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot);
+  if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot32);
 }
 
 template <class E, int D, bool F8 = false>
@@ -1085,7 +1118,7 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
   constexpr bool kMfma = (E::kBytes == 2);
   const AttnPlan plan = kMfma ? attn_plan(M, hkv, k_blocks) : attn_plan_valu(M, hkv, k_blocks);
   float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o ? ws_o + (size_t)M * hq * plan.splits * D : nullptr;
+  float* ws_lse = ws_o ? ws_o + (size_t)M * hq * plan.splits * D : nullptr;  // 2 per partial
   dim3 grid(plan.splits, hkv, M), block(kWave * plan.waves);
   if constexpr (kMfma) {
     grid = dim3(hkv, M, plan.splits);
@@ -1183,7 +1216,7 @@ size_t attn_workspace_bytes(int max_M, int hq, int head_dim, int k_blocks) {
     const AttnPlan pl[2] = {attn_plan(m, hkv, k_blocks), attn_plan_valu(m, hkv, k_blocks)};
     for (const AttnPlan& p : pl) {
       if (p.splits == 1) continue;
-      const size_t need = (size_t)m * hq * p.splits * (head_dim + 1) * sizeof(float);
+      const size_t need = (size_t)m * hq * p.splits * (head_dim + 2) * sizeof(float);
       best = need > best ? need : best;
     }
   }

@@ -102,7 +102,7 @@ int qsa_append_score(const void* new_idx, int32_t n_new, const int64_t* new_pos,
   if (ld % 4 != 0 || ((uintptr_t)scores & 15u) != 0)
     return fail(QSA_ERR_ARG, "qsa_append_score: scores must be 16-byte aligned with ld a multiple of 4 (ld %lld)",
                 (long long)ld);
-  if (dtype == QSA_BF16 && M >= qsa::kPrefillMinRows && nullptr == nullptr && !qsa::prefill_views_fit(nb_max, ld))
+  if (dtype == QSA_BF16 && M >= qsa::kPrefillMinRows && !qsa::prefill_views_fit(nb_max, ld))
     return fail(QSA_ERR_UNSUPPORTED,
                 "qsa_append_score: %d bf16 rows with ld %lld, nb_max %lld: the many-row kernel needs 64 * ld and 64 * "
                 "(selection-workspace words per row) under 2 GiB",
@@ -155,6 +155,20 @@ int qsa_select_topk(const float* scores, int64_t ld, int32_t M, const int64_t* r
 size_t qsa_attn_workspace_bytes(int32_t max_M, int32_t hq, int32_t head_dim, int32_t k_blocks) {
   if (max_M <= 0 || hq <= 0 || head_dim <= 0 || k_blocks <= 0 || k_blocks > QSA_MAX_K_BLOCKS) return 0;
   return qsa::attn_workspace_bytes(max_M, hq, head_dim, k_blocks);
+}
+
+int qsa_attn_plan(int32_t M, int32_t hkv, int32_t k_blocks, int32_t dtype, int32_t* plan) {
+  if (M < 1 || hkv < 1) return fail(QSA_ERR_ARG, "qsa_attn_plan: M %d and hkv %d must be >= 1", M, hkv);
+  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
+    return fail(QSA_ERR_ARG, "qsa_attn_plan: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_attn_plan: dtype %d is not QSA_F32 or QSA_BF16", dtype);
+  if (!plan) return fail(QSA_ERR_ARG, "qsa_attn_plan: plan is NULL");
+  const qsa::AttnPlan p = dtype == QSA_BF16 ? qsa::attn_plan(M, hkv, k_blocks) : qsa::attn_plan_valu(M, hkv, k_blocks);
+  plan[0] = p.waves;
+  plan[1] = p.tile_tokens;
+  plan[2] = p.tiles_per_split;
+  plan[3] = p.splits;
+  return ok();
 }
 
 int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,

@@ -95,7 +95,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Three bf16 planes of two float32 values, packed in pairs: hi = bf16(x),
 // mid = bf16(x - hi), lo = bf16(x - hi - mid).  Each difference is exact in
 // float32 (it keeps at most 16, then 8, significant bits), so hi + mid + lo
-// = x for every finite x.
+// = x whenever 2^-110 <= |x| <= the largest finite bf16 (about 3.39e38).
+// Below 2^-110 the lo plane would need bits finer than bf16's subnormal
+// spacing (2^-133) and the last bits of x are lost; above the bf16 range hi
+// overflows.  Pooled keys (averages of unit-scale values) sit far inside.
 __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   hi = pack_bf16x2(a, b);
   const float ra = a - __uint_as_float(hi << 16);

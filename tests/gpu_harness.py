@@ -2,7 +2,9 @@
 the selection acceptance rule and the oracle comparisons (test code only)."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 
 import numpy as np
 import torch
@@ -160,9 +162,10 @@ def check_attention_fp8(out_gpu: np.ndarray, lse_gpu: np.ndarray, layer, row_i: 
     err = float(np.max(np.abs(out_gpu - ref)))
     lerr = float(np.max(np.abs(lse_gpu - ref_lse)))
     # as for bf16 K/V (probabilities rounded to bf16), plus one more bf16
-    # rounding of each weight times its V scale
+    # rounding of each weight times its V scale; the lse comes from the
+    # float32 probabilities, before any rounding
     assert err <= 2e-2, f"attention max-abs {err} > 2e-2"
-    assert lerr <= 2.5e-3, f"lse max-abs {lerr} > 2.5e-3"
+    assert lerr <= 1e-3, f"lse max-abs {lerr} > 1e-3"
     return err, lerr
 
 
@@ -174,15 +177,33 @@ def check_attention(out_gpu: np.ndarray, lse_gpu: np.ndarray, d: dict, row_i: in
     tok = O.attended_tokens(sel, p + 1)
     ref, ref_lse = O.attend(d["q"][row_i], d["k"], d["v"], tok, 1.0 / math.sqrt(wl.head_dim))
     tol = 2e-2 if dtype == "bf16" else 1e-4
-    # bf16 K/V: the kernel rounds each probability to bf16 (relative error at
-    # most 2^-9) and normalises by the sum of the rounded values, so lse may
-    # differ by up to log(1 + 2^-9) ~ 1.95e-3 when a few tokens dominate
-    ltol = 2.5e-3 if dtype == "bf16" else 1e-5
+    # the output is normalised by the sum of the bf16-rounded probabilities
+    # P.V consumes; the lse comes from the float32 probabilities
+    ltol = 1e-3 if dtype == "bf16" else 1e-5
     err = float(np.max(np.abs(out_gpu - ref)))
     lerr = float(np.max(np.abs(lse_gpu - ref_lse)))
     assert err <= tol, f"attention max-abs {err} > {tol}"
     assert lerr <= ltol, f"lse max-abs {lerr} > {ltol}"
     return err, lerr
+
+
+def host_map(fn, items):
+    """fn over items, in host threads when there are many (numpy's matrix
+    products and sorts release the interpreter lock); BLAS kept to one thread
+    per worker meanwhile."""
+    items = list(items)
+    if len(items) <= 4:
+        return [fn(x) for x in items]
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    workers = max(1, min(16, os.cpu_count() or 1))
+    if threadpool_limits is None:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))
+    with threadpool_limits(1), cf.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
 
 
 def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
@@ -199,25 +220,26 @@ def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
     pooled_gpu = layer.pooled[0, : n // 4].cpu().numpy()
     pooled_ref = O.pool_index_keys(d["idx"])
     assert np.array_equal(pooled_gpu.view(np.uint32), pooled_ref.view(np.uint32))
+    pooled64 = pooled_ref.astype(np.float64)  # exact; converted once for every row
     sc = res["scores"].cpu().numpy()
     sel = res["sel"].cpu().numpy()
     n_sel = res["n_sel"].cpu().numpy()
     out = to_host_f32(res["out"])
     lse = res["lse"].cpu().numpy()
     rows = range(len(d["rows"])) if rows is None else rows
-    attn_rows = rows if attn_rows is None else attn_rows
-    stats = []
-    for i in rows:
+    attn_rows = set(rows if attn_rows is None else attn_rows)
+
+    def one(i):
         p = int(d["rows"][i])
-        s64 = O.score_blocks(d["idx_q"][i], pooled_ref, p + 1)
+        s64 = O.score_blocks(d["idx_q"][i], pooled64, p + 1)
         nb = len(s64)
         g32 = sc[i, :nb].astype(np.float64)
         # entries past the row's block count are left untouched (the fill value)
-        assert np.all(sc[i, nb:] == -7.0), "scores written past the row's block count"
+        assert np.all(sc[i, nb:] == -7.0), f"row {i}: scores written past the row's block count"
         # scores: float32 accumulation against fp64
-        assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), float(np.max(np.abs(g32 - s64)))
+        assert np.all(np.abs(g32 - s64) <= 1e-5 * np.abs(s64) + 1e-6), (i, float(np.max(np.abs(g32 - s64))))
         # the select kernel is exact on its own input
-        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), "select != exact top-k of GPU scores"
+        assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), f"row {i}: select != exact top-k of GPU scores"
         st = check_selection(sel[i], int(n_sel[i]), s64, k)
         if i in attn_rows and layer.kv_mode == "fp8":
             err, lerr = check_attention_fp8(out[i], lse[i], layer, i, sel[i, : n_sel[i]])
@@ -225,8 +247,9 @@ def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
         elif i in attn_rows:
             err, lerr = check_attention(out[i], lse[i], d, i, sel[i, : n_sel[i]], wl.dtype)
             st.update(err=err, lse_err=lerr)
-        stats.append(st)
-    return stats
+        return st
+
+    return host_map(one, rows)
 
 
 def assert_candidate_path(res, layer, k=None):

@@ -171,12 +171,14 @@ def test_attn_null_kv():
 
 def test_workspace_sizes():
     # one row, 2 KV heads, budget 512 blocks = 2,051 tokens at most: 33
-    # splits of 64 tokens in both plans, one partial of 257 floats per head
-    assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 33 * 257 * 4
+    # splits of 64 tokens in both plans; a partial per head holds 256 floats
+    # of output and two lse values (that of the normaliser it was divided by,
+    # and that of the float32 probabilities)
+    assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 33 * 258 * 4
     # up to four rows: the bf16 plan needs at most 4 x 26 partials per head
     # (four rows in 5-wave workgroups); the float32 plan keeps 33 splits of
     # 64 tokens at four rows, which is the largest need
-    assert Q.qsa_attn_workspace_bytes(4, 24, 256, 512) == 4 * 24 * 33 * 257 * 4
+    assert Q.qsa_attn_workspace_bytes(4, 24, 256, 512) == 4 * 24 * 33 * 258 * 4
     # sizing is monotone in max_M (a call with fewer rows always fits)
     prev = 0
     for m in (1, 2, 3, 4, 8, 16, 64, 256, 2048):
@@ -184,6 +186,19 @@ def test_workspace_sizes():
         assert cur >= prev
         prev = cur
     assert Q.qsa_attn_workspace_bytes(0, 24, 256, 512) == 0
+
+
+def test_attn_plan_query():
+    """The plan query answers on the host and refuses bad arguments."""
+    p1 = Q.qsa_attn_plan(1, 2, 512)
+    assert p1 == {"waves": 4, "tile_tokens": 64, "tiles_per_split": 1, "splits": 33}
+    pf = Q.qsa_attn_plan(2048, 2, 512)
+    assert pf["waves"] == 8 and pf["tiles_per_split"] * pf["tile_tokens"] * pf["splits"] >= 2051
+    out = (ctypes.c_int32 * 4)()
+    assert L.qsa_attn_plan(0, 2, 512, 1, out) == ERR_ARG and "M" in _err()
+    assert L.qsa_attn_plan(1, 2, 0, 1, out) == ERR_ARG and "k_blocks" in _err()
+    assert L.qsa_attn_plan(1, 2, 512, 9, out) == ERR_ARG and "dtype" in _err()
+    assert L.qsa_attn_plan(1, 2, 512, 1, None) == ERR_ARG and "NULL" in _err()
     # select: one fixed-size record per row (histogram, candidate list)
     per_row = Q.qsa_select_workspace_bytes(1, 65280, 512)
     assert per_row > 0 and Q.qsa_select_workspace_bytes(4, 65280, 512) == 4 * per_row

@@ -158,3 +158,43 @@ def test_fp8_decode_32k_head_dim_128_tail_rows(Q):
     layer = Layer(d, prefix_split=32768, kv="fp8")
     res = layer.run()
     say(check_layer(d, res, layer))
+
+
+def test_fp8_prefill_full_size_multi_tile(Q):
+    """The 2,048-row prefill chunk over fp8 K/V: the attention plan walks 17
+    tiles of 128 tokens per (row, KV head) in one workgroup, so the next
+    slice's codes and scales are loaded while the current one is used.  256
+    rows (8 per 64-row tile) are checked against fp64 attention over the
+    oracle's dequantized K/V."""
+    say("fp8 K/V prefill 2048 rows at 200000 (full size, multi-tile plan)")
+    plan = Q.qsa_attn_plan(2048, 2, 512)
+    assert plan["tiles_per_split"] == 17 and plan["waves"] == 8, plan
+    d = datagen.gen_layer("prefill")
+    layer = Layer(d, prefix_split=200000, kv="fp8")
+    res = layer.run()
+    offs = (0, 7, 15, 21, 31, 42, 55, 63)
+    rows = [t + o for t in range(0, 2048, 64) for o in offs]
+    st = check_layer(d, res, layer, rows=rows)
+    assert_candidate_path(res, layer)
+    say(f"{len(st)} rows; max-abs {max(x['err'] for x in st):.3g}, lse {max(x['lse_err'] for x in st):.3g}")
+
+
+def test_fp8_many_rows_split_and_multi_tile(Q):
+    """131 scattered rows of a 32K context over fp8 K/V: 6 tiles per workgroup
+    and 3 split partials per (row, KV head) merged by the combine."""
+    say("fp8 K/V, 131 scattered rows of a 32K context")
+    plan = Q.qsa_attn_plan(131, 2, 512)
+    assert plan["tiles_per_split"] > 1 and plan["splits"] > 1, plan
+    base = datagen.gen_layer("decode_32k")
+    d = dict(base)
+    rng = np.random.default_rng(131)
+    fixed = [0, 3, 4, 2047, 2050, 2051, 4097, 32767]
+    rest = rng.choice(np.arange(5, 32767), 123, replace=False)
+    rows = np.sort(np.unique(np.concatenate([fixed, rest]))).astype(np.int64)[:131]
+    d["rows"] = rows
+    d["idx_q"] = datagen.round_bf16(rng.standard_normal((len(rows), 4, 128)).astype(np.float32))
+    d["q"] = datagen.round_bf16(rng.standard_normal((len(rows), 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=32768, kv="fp8")
+    res = layer.run()
+    st = check_layer(d, res, layer)
+    say(plan, f"max-abs {max(x['err'] for x in st):.3g}, lse {max(x['lse_err'] for x in st):.3g}")

@@ -114,15 +114,32 @@ def test_clustered_relevance_full_size(Q):
     say(st, in_chunk)
 
 
-def test_prefill_full_size_sampled(Q):
-    say("prefill 2048 rows at 200000 bf16 (full size, sampled rows)")
+def prefill_attention_rows(m: int = 2048, tile: int = 64) -> list:
+    """8 rows of every 64-row tile (first, last and six inside): 256 rows at
+    the 2,048-row chunk, spread over every tile of the many-row scorer and
+    every workgroup position of the attention launch."""
+    offs = (0, 7, 15, 21, 31, 42, 55, 63)
+    return [t + o for t in range(0, m, tile) for o in offs if t + o < m]
+
+
+def test_prefill_full_size_all_rows(Q):
+    """The 2,048-row prefill chunk at 200,000..202,047: scores and selection
+    of every row against the oracle, attention of 256 rows (8 per 64-row
+    tile) over the GPU's selection.  The attention plan walks 17 tiles of 128
+    tokens per (row, KV head) in one split."""
+    say("prefill 2048 rows at 200000 bf16 (full size, every row)")
+    plan = Q.qsa_attn_plan(2048, 2, 512)
+    assert plan["tiles_per_split"] == 17 and plan["splits"] == 1, plan
     d = datagen.gen_layer("prefill")
     layer = Layer(d, prefix_split=200000)
     res = layer.run()
-    rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 2, 3, 15, 16, 1023, 2046, 2047] + rng.choice(2048, 16, replace=False).tolist()))
-    say(_check_layer(d, res, layer, rows=rows))
+    st = _check_layer(d, res, layer, attn_rows=prefill_attention_rows())
     _assert_candidate_path(res, layer)
+    errs = [x["err"] for x in st if "err" in x]
+    lerrs = [x["lse_err"] for x in st if "lse_err" in x]
+    assert len(errs) == 256
+    say(f"{len(st)} rows; attention max-abs {max(errs):.3g}, lse {max(lerrs):.3g}; "
+        f"band sizes up to {max(x['band'] for x in st)}")
 
 
 def test_many_rows_ragged(Q):
@@ -306,11 +323,17 @@ def test_deterministic_bitwise(Q):
     assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
 
 
-def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
+def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512, head_dim=256, fp8=False):
     """Sequences with K/V in several segments (some empty, some cutting a
-    4-token block), one row per sequence, scored and attended in one call."""
+    4-token block), one row per sequence, scored and attended in one call.
+    With fp8 every segment holds E4M3 codes and f16 scales quantized on the
+    device from the bf16 rows (checked bit for bit against the oracle), and
+    attention is compared with the oracle's dequantized K/V."""
+    import dataclasses
+
     rng = np.random.default_rng(seed)
-    wl = datagen.WORKLOADS["decode_32k"]
+    wl = dataclasses.replace(datagen.WORKLOADS["decode_32k"], head_dim=head_dim)
+    D = head_dim
     n_seq = len(n_ctx_list)
     cap_max = max(-(-(n + 4) // 256) * 256 for n in n_ctx_list)
     idx_cache = torch.zeros((n_seq, cap_max, 128), dtype=torch.bfloat16, device=DEV)
@@ -319,20 +342,34 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     for s, (n, nseg) in enumerate(zip(n_ctx_list, nseg_list)):
         idx = datagen.round_bf16(rng.standard_normal((n, 128)).astype(np.float32))
         iq = datagen.round_bf16(rng.standard_normal((1, 4, 128)).astype(np.float32))
-        q = datagen.round_bf16(rng.standard_normal((1, 24, 256)).astype(np.float32))
-        k_ = datagen.round_bf16(rng.standard_normal((2, n, 256)).astype(np.float32))
-        v_ = datagen.round_bf16(rng.standard_normal((2, n, 256)).astype(np.float32))
+        q = datagen.round_bf16(rng.standard_normal((1, 24, D)).astype(np.float32))
+        k_ = datagen.round_bf16(rng.standard_normal((2, n, D)).astype(np.float32))
+        v_ = datagen.round_bf16(rng.standard_normal((2, n, D)).astype(np.float32))
         cuts = sorted(rng.choice(np.arange(0, n + 1), size=nseg - 1, replace=True).tolist()) if nseg > 1 else []
         bounds = [0] + cuts + [n]
         segs = []
         for lo, hi in zip(bounds[:-1], bounds[1:]):
             cap = max(hi - lo, 1) + int(rng.integers(0, 9))
-            kt = torch.zeros((2, cap, 256), dtype=torch.bfloat16, device=DEV)
+            kt = torch.zeros((2, cap, D), dtype=torch.bfloat16, device=DEV)
             vt = torch.zeros_like(kt)
             if hi > lo:
                 kt[:, : hi - lo] = to_dev(np.ascontiguousarray(k_[:, lo:hi]), "bf16")
                 vt[:, : hi - lo] = to_dev(np.ascontiguousarray(v_[:, lo:hi]), "bf16")
-            segs.append((lo, hi - lo, kt, vt))
+            if fp8:
+                k8 = torch.full((2, cap, D), 0x55, dtype=torch.uint8, device=DEV)
+                v8 = torch.full_like(k8, 0x55)
+                ks = torch.zeros((2, cap), dtype=torch.float16, device=DEV)
+                vs = torch.zeros_like(ks)
+                if hi > lo:
+                    Q.qsa_quantize_kv_fp8(kt[:, : hi - lo].contiguous(), k8, ks)
+                    Q.qsa_quantize_kv_fp8(vt[:, : hi - lo].contiguous(), v8, vs)
+                    for src, c8, sc8 in ((k_, k8, ks), (v_, v8, vs)):
+                        c_ref, s_ref = O.quantize_kv_fp8(src[:, lo:hi])
+                        assert np.array_equal(c8[:, : hi - lo].cpu().numpy(), c_ref), "fp8 codes differ"
+                        assert np.array_equal(sc8[:, : hi - lo].cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+                segs.append((lo, hi - lo, k8, v8, ks, vs))
+            else:
+                segs.append((lo, hi - lo, kt, vt))
         segs_dev.append(segs)
         Q.qsa_append_pool(to_dev(idx, "bf16"), torch.arange(n, dtype=torch.int64, device=DEV),
                           idx_cache[s : s + 1], pooled[s : s + 1])
@@ -344,6 +381,7 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     idx_q = to_dev(np.concatenate([h["idx_q"] for h in host]), "bf16")
     q = to_dev(np.concatenate([h["q"] for h in host]), "bf16")
     nb_max = max(h["n"] for h in host) // 4
+    plan = Q.qsa_attn_plan(m, 2, k)
     scores = torch.zeros((m, -(-(nb_max + 4) // 4) * 4), dtype=torch.float32, device=DEV)
     Q.qsa_score_blocks(idx_q, rows, pooled, scores, nb_max, row_seq=row_seq)
     sel = torch.empty((m, k), dtype=torch.int32, device=DEV)
@@ -352,7 +390,7 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     Q.qsa_select_topk(scores, rows, nb_max, k, sel, n_sel, ws_sel)
     out = torch.empty_like(q)
     lse = torch.empty((m, 24), dtype=torch.float32, device=DEV)
-    ws = torch.empty(Q.qsa_attn_workspace_bytes(m, 24, 256, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(Q.qsa_attn_workspace_bytes(m, 24, D, k), dtype=torch.uint8, device=DEV)
     Q.qsa_gathered_attn(q, rows, kv, sel, n_sel, out, lse, 2, row_seq=row_seq, workspace=ws)
     torch.cuda.synchronize()
     out = to_host_f32(out)
@@ -360,6 +398,7 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
     sc = scores.cpu().numpy()
     sel = sel.cpu().numpy()
     n_sel = n_sel.cpu().numpy()
+    errs = []
     for i, h in enumerate(host):
         pr = O.pool_index_keys(h["idx"])
         assert np.array_equal(pooled[i, : h["n"] // 4].cpu().numpy().view(np.uint32), pr.view(np.uint32))
@@ -367,8 +406,17 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512):
         g32 = sc[i, : len(s64)].astype(np.float64)
         assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k))
         check_selection(sel[i], int(n_sel[i]), s64, k)
-        dd = {"workload": wl, "rows": np.asarray([h["n"] - 1]), "q": h["q"], "k": h["k"], "v": h["v"]}
-        check_attention(out[i], lse[i], dd, 0, sel[i, : n_sel[i]], "bf16")
+        if fp8:
+            tok = O.attended_tokens(sel[i, : n_sel[i]], h["n"])
+            deq = [O.dequantize_kv_fp8(*O.quantize_kv_fp8(src[:, tok])) for src in (h["k"], h["v"])]
+            ref, ref_lse = O.attend(h["q"][0], deq[0], deq[1], np.arange(len(tok)), 1.0 / math.sqrt(D))
+            err, lerr = float(np.max(np.abs(out[i] - ref))), float(np.max(np.abs(lse[i] - ref_lse)))
+            assert err <= 2e-2 and lerr <= 1e-3, (i, err, lerr)
+        else:
+            dd = {"workload": wl, "rows": np.asarray([h["n"] - 1]), "q": h["q"], "k": h["k"], "v": h["v"]}
+            err, lerr = check_attention(out[i], lse[i], dd, 0, sel[i, : n_sel[i]], "bf16")
+        errs.append((err, lerr))
+    return plan, errs
 
 
 @pytest.mark.parametrize("seed,nseg", [(1, [1, 2, 3]), (2, [13, 5, 1]), (3, [4, 12, 7, 9]), (4, [16])])
@@ -377,6 +425,29 @@ def test_segments_small(Q, seed, nseg):
     rng = np.random.default_rng(seed)
     ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
     _segmented_case(Q, ctx, nseg, seed)
+
+
+@pytest.mark.parametrize("seed,nseg", [(5, [1, 3, 2]), (6, [12, 1, 5, 16])])
+def test_segments_head_dim_128(Q, seed, nseg):
+    """The batched segmented decode at head_dim 128 (MTPLX PR #610, "Tests":
+    segments at head_dims 128 and 256)."""
+    say("segments, head_dim 128", seed, nseg)
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
+    _segmented_case(Q, ctx, nseg, seed, head_dim=128)
+
+
+@pytest.mark.parametrize("seed,nseg,head_dim", [(7, [1, 4, 2], 256), (8, [16, 3, 5, 1, 9], 256),
+                                                (9, [2, 13, 1], 128)])
+def test_segments_fp8(Q, seed, nseg, head_dim):
+    """fp8 K/V (E4M3 codes + f16 scales) across several segments, some empty
+    or cutting a block, rows of different sequences in one call (row_seq)."""
+    say("segments, fp8 K/V", seed, nseg, head_dim)
+    rng = np.random.default_rng(seed)
+    ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
+    plan, errs = _segmented_case(Q, ctx, nseg, seed, head_dim=head_dim, fp8=True)
+    assert plan["splits"] > 1, plan  # split partials merged by the combine
+    say(plan, max(e for e, _ in errs), max(l for _, l in errs))
 
 
 def test_batched_segmented_full_size(Q):
