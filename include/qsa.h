@@ -262,6 +262,30 @@ int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32
                       void* workspace, size_t workspace_bytes, qsa_stream_t stream);
 
 /*
+ * qsa_gathered_attn_noalloc -- qsa_gathered_attn without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, results and errors are those of qsa_gathered_attn (same kernels,
+ * same split plan, bit-identical outputs).  The split-K partials live in a
+ * static device array of 16 MiB that the library holds on each device it runs
+ * on until the process ends; its address is looked up on the first call on a
+ * device.  Calls whose partials would need more (qsa_attn_workspace_bytes(M,
+ * hq, head_dim, k_blocks) > 16 MiB) return QSA_ERR_UNSUPPORTED and launch
+ * nothing; every shape this build serves needs at most 12.1 MiB (the split
+ * plans keep at most 1,024 partial workgroups of 12 heads).  Nothing is
+ * allocated or freed.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (different streams, or host
+ * threads) race and must be serialised by the caller.
+ */
+int qsa_gathered_attn_noalloc(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
+                              int32_t head_dim, float scale,
+                              const int64_t* row_pos, const int32_t* row_seq,
+                              const qsa_kv_segments* kv,
+                              const int32_t* sel, const int32_t* n_sel, int32_t k_blocks,
+                              void* out, float* lse, qsa_stream_t stream);
+
+/*
  * qsa_score_select -- scores and top-k selection of many rows of one
  * sequence without a score matrix (memory-flat prefill).
  *

@@ -36,7 +36,7 @@ MAX_SEGMENTS = 16
 EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
     "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
-    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes", "qsa_attn_plan",
+    "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes", "qsa_attn_plan", "qsa_gathered_attn_noalloc",
     "qsa_device_check", "qsa_last_error", "qsa_version",
 )
 
@@ -68,6 +68,8 @@ _lib.qsa_score_blocks.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I64, _I64, 
 _lib.qsa_select_topk.argtypes = [_P, _I64, _I32, _P, _I64, _I32, _P, _P, _P, _SZ, _I32, _P]
 _lib.qsa_gathered_attn.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                    ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P, _SZ, _P]
+_lib.qsa_gathered_attn_noalloc.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
+                                           ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P]
 _lib.qsa_append_score.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]
 _lib.qsa_quantize_kv_fp8.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
 _lib.qsa_score_select.argtypes = [_P, _I32, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
@@ -82,7 +84,8 @@ _lib.qsa_device_check.argtypes = []
 _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
-           "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_attn_plan", "qsa_device_check"):
+           "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_attn_plan", "qsa_device_check",
+           "qsa_gathered_attn_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -337,3 +340,23 @@ def qsa_gathered_attn(q: torch.Tensor, row_pos: torch.Tensor, kv: KvSegments, se
                                   _ptr(row_seq), ctypes.byref(kv.struct), _ptr(sel), _ptr(n_sel),
                                   sel.shape[1], _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static scratch of qsa_gathered_attn_noalloc, per device
+
+
+def qsa_gathered_attn_noalloc(q: torch.Tensor, row_pos: torch.Tensor, kv: KvSegments, sel: torch.Tensor,
+                              n_sel: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, hkv: int,
+                              scale: float | None = None, row_seq: torch.Tensor | None = None,
+                              stream=None) -> None:
+    """``qsa_gathered_attn`` with its split partials in the library's static
+    device scratch: no workspace argument, nothing allocated.  Calls that
+    overlap in time on one device race."""
+    m, hq, d = q.shape
+    _need(q.is_contiguous() and out.is_contiguous() and lse.is_contiguous(), "tensors must be contiguous")
+    _need(out.dtype == q.dtype and out.shape == q.shape and lse.dtype == torch.float32, "out/lse")
+    _need(sel.shape[0] >= m and n_sel.numel() >= m, "sel/n_sel rows")
+    scale = 1.0 / (d ** 0.5) if scale is None else float(scale)
+    _check(_lib.qsa_gathered_attn_noalloc(_ptr(q), _dtype_code(q), m, hq, int(hkv), d, scale, _ptr(row_pos),
+                                          _ptr(row_seq), ctypes.byref(kv.struct), _ptr(sel), _ptr(n_sel),
+                                          sel.shape[1], _ptr(out), _ptr(lse), _stream(stream)))

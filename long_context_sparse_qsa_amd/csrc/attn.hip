@@ -24,6 +24,8 @@
 //      of V and of P, float32 accumulation.
 // Split partials (normalised output + lse) go to the workspace and a second
 // kernel merges them; with a single split the output is written directly.
+#include <mutex>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -1252,6 +1254,38 @@ hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv
   }
   // float32 K/V is served at head_dim 128 (validated by the caller)
   return launch_typed<F32, 128>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the split-K partials live in a file-scope device
+// array instead of a caller workspace.  Its host-side name is only a stand-in:
+// each device's copy has its own address, taken once per device with
+// hipGetSymbolAddress (with that device current) and kept here; kernels get
+// that address, never the symbol.  Nothing in the array needs a starting
+// value (every partial is written before it is read), and every call on one
+// device shares that device's copy.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace qsa

@@ -171,52 +171,95 @@ int qsa_attn_plan(int32_t M, int32_t hkv, int32_t k_blocks, int32_t dtype, int32
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by qsa_gathered_attn and its allocation-free variant; the
+// workspace is checked by each caller.
+int check_attn_args(const char* fn, const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
+                    int32_t head_dim, float scale, const int64_t* row_pos, const qsa_kv_segments* kv,
+                    const int32_t* sel, const int32_t* n_sel, int32_t k_blocks, void* out, float* lse) {
+  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "%s: dtype %d is not QSA_F32 or QSA_BF16", fn, dtype);
+  if (M < 0) return fail(QSA_ERR_ARG, "%s: M = %d < 0", fn, M);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(QSA_ERR_ARG, "%s: hq %d must be a positive multiple of hkv %d", fn, hq, hkv);
+  if (hq / hkv != 12)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: %d query heads per KV head; this build serves 12", fn, hq / hkv);
+  if (head_dim != 128 && head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: head_dim %d; this build serves 128 and 256", fn, head_dim);
+  if (dtype == QSA_F32 && head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: float32 K/V is served at head_dim 128 only", fn);
+  if (!(scale == scale) || isinf(scale)) return fail(QSA_ERR_ARG, "%s: scale is not finite", fn);
+  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
+    return fail(QSA_ERR_ARG, "%s: k_blocks %d outside [1, %d]", fn, k_blocks, QSA_MAX_K_BLOCKS);
+  if (!kv) return fail(QSA_ERR_ARG, "%s: kv is NULL", fn);
+  if (kv->n_seq < 1 || kv->n_seg_total < kv->n_seq)
+    return fail(QSA_ERR_ARG, "%s: kv n_seq %d / n_seg_total %d invalid", fn, kv->n_seq, kv->n_seg_total);
+  if (kv->max_seg_per_seq < 1 || kv->max_seg_per_seq > QSA_MAX_SEGMENTS)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: max_seg_per_seq %d outside [1, %d]", fn, kv->max_seg_per_seq,
+                QSA_MAX_SEGMENTS);
+  if (!kv->seq_seg_begin || !kv->seg_start || !kv->seg_len || !kv->seg_cap || !kv->k_seg || !kv->v_seg)
+    return fail(QSA_ERR_ARG, "%s: null pointer in the kv segment table", fn);
+  if (kv->kv_format != QSA_KV_SAME && kv->kv_format != QSA_KV_FP8_E4M3)
+    return fail(QSA_ERR_ARG, "%s: kv_format %d is not QSA_KV_SAME or QSA_KV_FP8_E4M3", fn, kv->kv_format);
+  if (kv->kv_format == QSA_KV_FP8_E4M3) {
+    if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: fp8 K/V is served with bf16 queries only", fn);
+    if (!kv->k_scale_seg || !kv->v_scale_seg)
+      return fail(QSA_ERR_ARG, "%s: fp8 K/V needs k_scale_seg and v_scale_seg", fn);
+  }
+  if (M > 0 && (!q || !row_pos || !sel || !n_sel || !out || !lse))
+    return fail(QSA_ERR_ARG, "%s: null pointer (q, row_pos, sel, n_sel, out or lse)", fn);
+  if (M > 0 && ((uintptr_t)out & 15u))
+    return fail(QSA_ERR_ARG, "%s: out must be 16-byte aligned", fn);
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
                       int32_t head_dim, float scale, const int64_t* row_pos,
                       const int32_t* row_seq, const qsa_kv_segments* kv, const int32_t* sel,
                       const int32_t* n_sel, int32_t k_blocks, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
-  if (!dtype_ok(dtype)) return fail(QSA_ERR_ARG, "qsa_gathered_attn: dtype %d is not QSA_F32 or QSA_BF16", dtype);
-  if (M < 0) return fail(QSA_ERR_ARG, "qsa_gathered_attn: M = %d < 0", M);
-  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: hq %d must be a positive multiple of hkv %d", hq, hkv);
-  if (hq / hkv != 12)
-    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: %d query heads per KV head; this build serves 12", hq / hkv);
-  if (head_dim != 128 && head_dim != 256)
-    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: head_dim %d; this build serves 128 and 256", head_dim);
-  if (dtype == QSA_F32 && head_dim != 128)
-    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: float32 K/V is served at head_dim 128 only");
-  if (!(scale == scale) || isinf(scale)) return fail(QSA_ERR_ARG, "qsa_gathered_attn: scale is not finite");
-  if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
-  if (!kv) return fail(QSA_ERR_ARG, "qsa_gathered_attn: kv is NULL");
-  if (kv->n_seq < 1 || kv->n_seg_total < kv->n_seq)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: kv n_seq %d / n_seg_total %d invalid", kv->n_seq, kv->n_seg_total);
-  if (kv->max_seg_per_seq < 1 || kv->max_seg_per_seq > QSA_MAX_SEGMENTS)
-    return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: max_seg_per_seq %d outside [1, %d]",
-                kv->max_seg_per_seq, QSA_MAX_SEGMENTS);
-  if (!kv->seq_seg_begin || !kv->seg_start || !kv->seg_len || !kv->seg_cap || !kv->k_seg || !kv->v_seg)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: null pointer in the kv segment table");
-  if (kv->kv_format != QSA_KV_SAME && kv->kv_format != QSA_KV_FP8_E4M3)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: kv_format %d is not QSA_KV_SAME or QSA_KV_FP8_E4M3", kv->kv_format);
-  if (kv->kv_format == QSA_KV_FP8_E4M3) {
-    if (dtype != QSA_BF16)
-      return fail(QSA_ERR_UNSUPPORTED, "qsa_gathered_attn: fp8 K/V is served with bf16 queries only");
-    if (!kv->k_scale_seg || !kv->v_scale_seg)
-      return fail(QSA_ERR_ARG, "qsa_gathered_attn: fp8 K/V needs k_scale_seg and v_scale_seg");
-  }
+  const char* fn = "qsa_gathered_attn";
+  int r = check_attn_args(fn, q, dtype, M, hq, hkv, head_dim, scale, row_pos, kv, sel, n_sel, k_blocks, out, lse);
+  if (r != QSA_OK) return r;
   const size_t need = qsa::attn_workspace_bytes(M, hq, head_dim, k_blocks);
   if (M > 0 && (workspace_bytes < need || (need && !workspace)))
-    return fail(QSA_ERR_WORKSPACE, "qsa_gathered_attn: workspace %zu B < %zu B needed", workspace_bytes, need);
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace %zu B < %zu B needed", fn, workspace_bytes, need);
   if (M == 0) return ok();
-  if (!q || !row_pos || !sel || !n_sel || !out || !lse)
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: null pointer (q, row_pos, sel, n_sel, out or lse)");
-  if (((uintptr_t)out & 15u) || ((uintptr_t)workspace & 15u))
-    return fail(QSA_ERR_ARG, "qsa_gathered_attn: out and workspace must be 16-byte aligned");
-  return launch_status(qsa::launch_gathered_attn(q, dtype, M, hq, hkv, head_dim, scale, row_pos,
-                                                 row_seq, kv, sel, n_sel, k_blocks, out, lse,
-                                                 workspace, workspace_bytes, (hipStream_t)stream),
-                       "qsa_gathered_attn");
+  if ((uintptr_t)workspace & 15u) return fail(QSA_ERR_ARG, "%s: out and workspace must be 16-byte aligned", fn);
+  return launch_status(qsa::launch_gathered_attn(q, dtype, M, hq, hkv, head_dim, scale, row_pos, row_seq, kv, sel,
+                                                 n_sel, k_blocks, out, lse, workspace, workspace_bytes,
+                                                 (hipStream_t)stream),
+                       fn);
+}
+
+int qsa_gathered_attn_noalloc(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
+                              int32_t head_dim, float scale, const int64_t* row_pos, const int32_t* row_seq,
+                              const qsa_kv_segments* kv, const int32_t* sel, const int32_t* n_sel,
+                              int32_t k_blocks, void* out, float* lse, qsa_stream_t stream) {
+  const char* fn = "qsa_gathered_attn_noalloc";
+  int r = check_attn_args(fn, q, dtype, M, hq, hkv, head_dim, scale, row_pos, kv, sel, n_sel, k_blocks, out, lse);
+  if (r != QSA_OK) return r;
+  if (M == 0) return ok();
+  const size_t need = qsa::attn_workspace_bytes(M, hq, head_dim, k_blocks);
+  if (need > qsa::kNoAllocScratchBytes)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "%s: %d rows x %d heads at head_dim %d, budget %d blocks need %zu B of split partials, above the "
+                "%zu B static scratch",
+                fn, M, hq, head_dim, k_blocks, need, qsa::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = qsa::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(QSA_ERR_LAUNCH, "%s: static scratch address: %s", fn, hipGetErrorString(e));
+  }
+  return launch_status(qsa::launch_gathered_attn(q, dtype, M, hq, hkv, head_dim, scale, row_pos, row_seq, kv, sel,
+                                                 n_sel, k_blocks, out, lse, ws, need, (hipStream_t)stream),
+                       fn);
 }
 
 int qsa_score_select(const void* idx_q, int32_t M, const int64_t* row_pos, const float* pooled,

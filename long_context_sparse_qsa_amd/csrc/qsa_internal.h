@@ -79,6 +79,13 @@ hipError_t launch_quantize_kv_fp8(const void* src, int n_head, int n_tok, int he
                                   uint8_t* dst, uint16_t* dst_scale, int64_t dst_head_stride,
                                   hipStream_t stream);
 
+// The allocation-free attention entry point keeps its split-K partials in a
+// file-scope device array of this many bytes (attn.hip); noalloc_scratch
+// returns the current device's copy of it (its address is looked up once per
+// device).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv, int head_dim,
                                 float scale, const int64_t* row_pos, const int32_t* row_seq,
                                 const qsa_kv_segments* kv, const int32_t* sel,
