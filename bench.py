@@ -7,9 +7,17 @@ gathered attention with the split-K LSE merge -- over all 12 QSA layers of
 one synthetic batch, captured once as a HIP graph and replayed.  Inputs are
 resident in HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload verify_262k]
+  python bench.py [--steps K] [--warmup W] [--workload verify_262k] [--legs all]
 
-The metric is query-rows/s per layer (rows x layers x steps / time).
+The metric is query-rows/s per layer (rows x layers x steps / time) of the
+main workload (default: the 4-row verify at 261,122 context).  Every other
+workload of the benchmark set is timed as a leg of the same run and reported
+beside it: M = 1 at 262K, fp8 K/V, decode M = 1 at 32K, batched segmented
+decode, and the 2,048-row prefill chunk (with its matrix-core utilisation).
+
+Each timed sweep rotates over R replicas of the 12 layers' state, R chosen so
+that one sweep touches at least 1 GiB, so that the 256 MB last-level cache
+cannot hold what a step reads from one step to the next.
 """
 from __future__ import annotations
 
@@ -25,14 +33,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+ROTATE_BYTES = 1 << 30  # bytes one sweep over the layer states touches at least
 CSRC = os.path.join(ROOT, "long_context_sparse_qsa_amd", "csrc")
 # sources of the scoring kernel (the dominant kernel): PMC figures taken on
 # another build of them are not reported
 SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h", "append_common.h")
 PMC_FILE = os.path.join(ROOT, "profiles", "score_fewrow_kernel.verify_262k.pmc.txt")
 COPY_BYTES = 256 << 20  # plain copy of known size used to scale the PMC byte counters
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PREFILL_MIN_ROWS = 64  # rows at which scoring takes the many-row matrix-core kernel
+LEGS = ("m1", "fp8", "decode_32k", "batched", "prefill")
 
 
 def parse():
@@ -43,14 +53,33 @@ def parse():
     ap.add_argument("--workload", default="verify_262k",
                     choices=["verify_262k", "decode_262k", "decode_32k", "prefill", "batched"])
     ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--legs", default="all",
+                    help="comma list of " + ",".join(LEGS) + ", or all / none (legs of the verify_262k run)")
+    ap.add_argument("--replicas", type=int, default=0, help="layer-state replicas per sweep (0: the 1 GiB rule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-m1", action="store_true", help="skip the M=1 companion measurement")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 K/V companion measurement")
-    ap.add_argument("--no-flat", action="store_true", help="skip the memory-flat selection measurement (many rows)")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--no-flat", action="store_true", help="skip the memory-flat selection measurement (prefill)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 K/V measurements")
+    ap.add_argument("--no-m1", action="store_true", help="skip the M=1 leg")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (scales FETCH_SIZE / WRITE_SIZE)")
-    return ap.parse_args()
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the CPU oracle on every workload (1 thread and all threads) and exit")
+    a = ap.parse_args()
+    if a.legs == "all":
+        a.legs = set(LEGS)
+    elif a.legs == "none":
+        a.legs = set()
+    else:
+        a.legs = set(x for x in a.legs.split(",") if x)
+        bad = a.legs - set(LEGS)
+        if bad:
+            ap.error(f"unknown legs {sorted(bad)}")
+    if a.no_m1:
+        a.legs.discard("m1")
+    if a.no_fp8:
+        a.legs.discard("fp8")
+    return a
 
 
 def score_source_hash() -> str:
@@ -88,6 +117,11 @@ def stored_traffic() -> int | None:
         return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
         return None
+
+
+def kept_tokens(rows, k_blocks: int) -> int:
+    """Tokens the rows attend: min(k, nb) blocks of 4 plus each row's tail."""
+    return sum(min((p + 1) // 4, k_blocks) * 4 + (p + 1) % 4 for p in rows)
 
 
 # ----------------------------------------------------------------- set-up
@@ -168,20 +202,6 @@ class BatchedLayer:
         self.new_pos = self.rows.clone()
 
 
-def build_batched(Q, layers, dev):
-    import datagen
-
-    specs = datagen.batched_specs()
-    wl = datagen.Workload("batched", 3, max(sp.n_ctx for sp in specs), tuple(sp.row for sp in specs), "bf16", 256)
-    L = [BatchedLayer(Q, specs, i, dev) for i in range(layers)]
-    return wl, L, shared_buffers(Q, wl, dev), (max(wl.rows) + 1) // 4, [sp.n_ctx // 4 for sp in specs]
-
-
-def build_single(Q, wl, layers, dev):
-    L = [SeqLayer(Q, wl, i, dev) for i in range(layers)]
-    return L, shared_buffers(Q, wl, dev), (max(wl.rows) + 1) // 4
-
-
 def shared_buffers(Q, wl, dev):
     import torch
 
@@ -203,9 +223,16 @@ def shared_buffers(Q, wl, dev):
     return shared
 
 
+def replicas(per_layer_bytes: int, layers: int, forced: int = 0) -> int:
+    """Replicas of the layers' state so that one sweep touches >= 1 GiB."""
+    if forced > 0:
+        return forced
+    return max(1, -(-ROTATE_BYTES // max(1, per_layer_bytes * layers)))
+
+
 def step_fn(Q, L, sh, nb_max, wl, only=None, flat=False):
-    """Enqueue one step (all layers).  ``only`` restricts to one kernel family;
-    ``flat`` scores and selects through the memory-flat entry point."""
+    """Enqueue one step (the layers ``L``).  ``only`` restricts to one kernel
+    family; ``flat`` scores and selects through the memory-flat entry point."""
     def run():
         for ly in L:
             # one sequence: the append rides in the scoring launch
@@ -232,28 +259,68 @@ def step_fn(Q, L, sh, nb_max, wl, only=None, flat=False):
     return run
 
 
-def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
+def spin():
+    """Queue a long device-side spin first, so that everything enqueued after
+    it is queued before the device reaches it (no host gaps in an interval)."""
+    import torch
+
+    try:
+        torch.cuda._sleep(int(2e8))
+    except Exception:  # pragma: no cover - spin kernel unavailable: host gaps may inflate a figure
+        pass
+
+
+def timed_sweeps(Q, groups, sh, nb_max, wl, steps, warmup, eager=False, flat=False) -> float:
+    """Milliseconds per step: step i runs replica i % R of the layers (one
+    HIP graph per replica), ``steps`` steps between two HIP events on the
+    launch stream after ``warmup`` untimed ones."""
+    import torch
+
+    runs = [step_fn(Q, grp, sh, nb_max, wl, flat=flat) for grp in groups]
+    for r in runs:
+        r()
+    torch.cuda.synchronize()
+    if eager:
+        replays = runs
+    else:
+        replays = []
+        for r in runs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                r()
+            replays.append(g)
+        replays = [g.replay for g in replays]
+    for i in range(warmup):
+        replays[i % len(replays)]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        replays[i % len(replays)]()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4, flat=False):
     """Average device time of one launch of ``kind``, from HIP events on the
-    launch stream around ``reps`` x layers launches queued back to back.  A
-    spin kernel runs first so that the whole sequence is queued before the
-    device reaches it (no host gaps inside the interval).  The prepared
-    selection consumes what the scoring pass left in the workspace, so
-    "select" is timed as score+select pairs minus the scoring time."""
+    launch stream around ``reps`` x layers launches queued back to back over
+    every layer state.  The prepared selection consumes what the scoring pass
+    left in the workspace, so "select" is timed as score+select pairs minus
+    the scoring time."""
     import torch
 
     def timed(kinds):
         torch.cuda.synchronize()
-        try:
-            torch.cuda._sleep(int(2e8))
-        except Exception:  # pragma: no cover - spin kernel unavailable: host gaps may inflate the figure
-            pass
+        spin()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
             for ly in L:
                 for k_ in kinds:
-                    step_fn(Q, [ly], sh, nb_max, wl, only=k_)()
+                    step_fn(Q, [ly], sh, nb_max, wl, only=k_, flat=flat)()
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (reps * len(L))
@@ -263,101 +330,166 @@ def per_launch_us(Q, L, sh, nb_max, wl, kind, reps=4):
     return timed((kind,))
 
 
+def path_bytes(wl, rows, pooled_blocks: int) -> int:
+    """Algorithmic bytes of one layer step: pooled keys read once (per
+    sequence), gathered K/V, queries, outputs and index queries."""
+    tok = kept_tokens(rows, wl.k_blocks)
+    return (pooled_blocks * 512 + tok * wl.hkv * 2 * wl.head_dim * 2
+            + len(rows) * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2))
+
+
+def leg_record(name, m, layers, R, ms, pbytes, kt) -> dict:
+    layer_us = ms * 1e3 / layers
+    return {"workload": name, "value": m * layers / (ms / 1e3), "unit": "query-rows/s per layer",
+            "ms_per_step": ms, "layer_us": layer_us, "layers": layers, "replicas": R,
+            "path": {"bytes_per_layer_step": pbytes, "achieved_GBs": pbytes / (layer_us * 1e-6) / 1e9,
+                     "frac": pbytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}}
+
+
+def groups_of(L, layers):
+    return [L[i:i + layers] for i in range(0, len(L), layers)]
+
+
+def free():
+    import gc
+
+    import torch
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl_name: str, budget_s: float = 12.0) -> dict:
-    """The oracle, as it stands, on the host: same per-layer work for the
-    same rows (pool the blocks the new tokens complete, score, select, attend)."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(wl_name: str = "verify_262k", budget_s: float = 10.0, table: bool = False) -> dict:
+    """The CPU oracle, as it stands, on the host (the only part of this script
+    that runs it).  By default: rows/s per layer on rows of one ``wl_name``
+    layer, once with BLAS limited to one thread and once with every thread
+    BLAS starts with.  With ``table``: every workload of the benchmark set,
+    both thread counts, and where the time goes (pool / score / select /
+    attend)."""
     import datagen
     import oracle as O
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    d = datagen.gen_layer(wl_name)
-    wl = d["workload"]
-    pooled = O.pool_index_keys(d["idx"])
-    scale = 1.0 / math.sqrt(wl.head_dim)
-    rows = [int(r) for r in d["rows"]]
-    t0 = time.perf_counter()
-    done = 0
-    while True:
-        for i, p in enumerate(rows):
-            lo = (p // 4) * 4
-            if p % 4 == 3:
-                pooled[p // 4] = O.pool_index_keys(d["idx"][lo:lo + 4])[0]
-            s = O.score_blocks(d["idx_q"][i], pooled, p + 1)
-            sel = O.select_blocks(s, wl.k_blocks)
-            tok = O.attended_tokens(sel, p + 1)
-            O.attend(d["q"][i], d["k"], d["v"], tok, scale)
-            done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": done / el, "unit": "query-rows/s per layer", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} rows of one {wl_name} layer (n_ctx {wl.n_ctx}) in {el:.1f} s, numpy fp64"}
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    def limited(n):
+        if threadpool_limits is None or n is None:
+            import contextlib
+            return contextlib.nullcontext()
+        return threadpool_limits(limits=n)
+
+    def oracle_rows(d, budget, bd, rows_idx=None):
+        """Rows of one layer (pool the block a row's own token completes,
+        score, select, attend), repeated until ``budget`` seconds have
+        passed; returns (rows done, seconds)."""
+        wl = d["workload"]
+        pooled = O.pool_index_keys(d["idx"])
+        scale = 1.0 / math.sqrt(wl.head_dim)
+        rows = list(range(len(d["rows"]))) if rows_idx is None else list(rows_idx)
+        for key in ("pool", "score", "select", "attend"):
+            bd.setdefault(key, 0.0)
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            for i in rows:
+                p = int(d["rows"][i])
+                ta = time.perf_counter()
+                if p % 4 == 3:
+                    lo = (p // 4) * 4
+                    pooled[p // 4] = O.pool_index_keys(d["idx"][lo:lo + 4])[0]
+                tb = time.perf_counter()
+                s = O.score_blocks(d["idx_q"][i], pooled, p + 1)
+                tc = time.perf_counter()
+                sel = O.select_blocks(s, wl.k_blocks)
+                td = time.perf_counter()
+                O.attend(d["q"][i], d["k"], d["v"], O.attended_tokens(sel, p + 1), scale)
+                te = time.perf_counter()
+                bd["pool"] += tb - ta
+                bd["score"] += tc - tb
+                bd["select"] += td - tc
+                bd["attend"] += te - td
+                done += 1
+                if time.perf_counter() - t0 >= budget:
+                    return done, time.perf_counter() - t0
+
+    if not table:
+        d = datagen.gen_layer(wl_name)
+        wl = d["workload"]
+        with limited(1):
+            n1, t1 = oracle_rows(d, budget_s, {})
+        cores = blas_threads()
+        n, t = oracle_rows(d, budget_s, {})
+        sample = f"rows of one {wl_name} layer (n_ctx {wl.n_ctx}), numpy fp64"
+        return {"value": n / t, "unit": "query-rows/s per layer", "cores": int(cores), "kind": "oracle",
+                "sample": f"{n} {sample} in {t:.1f} s", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+                "single_thread": {"value": n1 / t1, "cores": 1,
+                                  "sample": f"{n1} {sample} in {t1:.1f} s, BLAS limited to one thread"}}
+
+    out = {"cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "all_threads": blas_threads(), "rows": {}}
+    cases = [("tiny", None), ("decode_32k", None), ("decode_262k", None), ("verify_262k", None),
+             ("prefill", list(range(0, 2048, 8)))]
+    for name, rows_idx in cases:
+        d = datagen.gen_layer(name)
+        rec = {}
+        for label, lim in (("1", 1), ("all", None)):
+            bd = {}
+            with limited(lim):
+                n, t = oracle_rows(d, budget_s, bd, rows_idx)
+            rec[label] = {"rows_per_s": n / t, "rows": n, "seconds": t, "share": {k_: v / t for k_, v in bd.items()}}
+        out["rows"][name] = rec
+        print(json.dumps({name: rec}), file=sys.stderr, flush=True)
+        del d
+    # batched decode: one row per sequence, each against its own context
+    specs = datagen.batched_specs()
+    data = datagen.gen_batched_layer(specs)
+    rec = {}
+    for label, lim in (("1", 1), ("all", None)):
+        done, tt, bd = 0, 0.0, {}
+        with limited(lim):
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < budget_s:
+                for h in data:
+                    dd = dict(h)
+                    dd["workload"] = datagen.WORKLOADS["decode_32k"]
+                    n, t = oracle_rows(dd, 0.0, bd)
+                    done += n
+                    tt += t
+        rec[label] = {"rows_per_s": done / tt, "rows": done, "seconds": tt,
+                      "share": {k_: v / tt for k_, v in bd.items()}}
+    out["rows"]["batched"] = rec
+    return out
 
 
-# ------------------------------------------------------------------ main
+# ------------------------------------------------------------------ legs
 
-def flat_leg(Q, L, sh, nb_max, wl, args, kt):
-    """Many rows scored and selected without the score matrix
-    (qsa_score_select): the whole step through a graph, the launch beside the
-    materialized score + select, and the memory each needs."""
-    import torch
-
-    sh = dict(sh)
-    wsb = Q.qsa_score_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
-    sh["ws_flat"] = torch.empty(wsb, dtype=torch.uint8, device=L[0].pooled.device)
-    run = step_fn(Q, L, sh, nb_max, wl, flat=True)
-    run()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run()
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-
-    def one(only):
-        torch.cuda.synchronize()
-        try:
-            torch.cuda._sleep(int(2e8))
-        except Exception:  # pragma: no cover
-            pass
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        step_fn(Q, L, sh, nb_max, wl, only=only, flat=True)()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / len(L)
-
-    flat_us = one("flat")
-    ld = -(-nb_max // 4) * 4
-    return {"workload": wl.name + " memory-flat select", "value": wl.m * len(L) * args.steps / (ms / 1e3),
-            "unit": "query-rows/s per layer", "ms_per_step": ms / args.steps,
-            "layer_us": ms * 1e3 / args.steps / len(L),
-            "score_select_us": round(flat_us, 1), "score_plus_select_us": round(kt["score"] + kt["select"], 1),
-            "workspace_bytes": wsb, "score_matrix_bytes": wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)}
-
-
-def fp8_leg(Q, L, sh, nb_max, wl, args, attn_bf16_us):
+def fp8_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us):
     """The same layers with K/V in the fp8 state (E4M3 codes + f16 scale per
     head and token), quantized on the device from the bf16 K/V: the whole
-    step through a graph, the attention launch beside the bf16 one, and the
+    step through graphs, the attention launch beside the bf16 one, and the
     quantize launch that writes one step's new K (or V) rows."""
     import torch
 
@@ -371,31 +503,12 @@ def fp8_leg(Q, L, sh, nb_max, wl, args, attn_bf16_us):
         ly.kv_bf16, ly.kv = ly.kv, Q.KvSegments.single(ly.k8, ly.v8, wl.n_ctx, ly.ks, ly.vs)
         ly.new_k = ly.k[:, ly.rows[0]:ly.rows[0] + min(wl.m, 4)].contiguous()  # new K rows [hkv, T, D]
     torch.cuda.synchronize()
-    run = step_fn(Q, L, sh, nb_max, wl)
-    run()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run()
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+    ms = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager)
     attn_us = per_launch_us(Q, L, sh, nb_max, wl, "attn")
     # one step's K write: M rows x hkv heads quantized into the cache
     t0 = int(wl.rows[0])
     torch.cuda.synchronize()
-    try:  # queue every launch before the device reaches them (no host gaps in the interval)
-        torch.cuda._sleep(int(2e8))
-    except Exception:  # pragma: no cover
-        pass
+    spin()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
@@ -405,20 +518,131 @@ def fp8_leg(Q, L, sh, nb_max, wl, args, attn_bf16_us):
     b.record()
     torch.cuda.synchronize()
     quant_us = a.elapsed_time(b) * 1e3 / (4 * len(L))
-    tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
+    tok = kept_tokens(wl.rows, wl.k_blocks)
     gather_fp8 = tok * wl.hkv * 2 * (wl.head_dim + 2)
     gather_bf16 = tok * wl.hkv * 2 * wl.head_dim * 2
     for ly in L:  # back to the bf16 state for whatever runs next
         ly.kv = ly.kv_bf16
         del ly.k8, ly.v8, ly.ks, ly.vs, ly.new_k
-    torch.cuda.synchronize()
-    return {"workload": wl.name + " fp8 K/V", "value": wl.m * len(L) * args.steps / (ms / 1e3),
-            "unit": "query-rows/s per layer", "ms_per_step": ms / args.steps,
-            "layer_us": ms * 1e3 / args.steps / len(L),
+    free()
+    layers = len(groups[0])
+    return {"workload": wl.name + " fp8 K/V", "value": wl.m * layers / (ms / 1e3),
+            "unit": "query-rows/s per layer", "ms_per_step": ms, "layer_us": ms * 1e3 / layers,
             "attn_us": round(attn_us, 2), "attn_us_bf16": round(attn_bf16_us, 2),
             "gather_bytes": gather_fp8, "gather_bytes_bf16": gather_bf16,
             "quantize_us_per_kv_write": round(quant_us, 2)}
 
+
+def single_leg(Q, name, args, dev, kinds=("append_score", "select", "attn")):
+    """A one-sequence workload over rotating replicas of its layer states."""
+    import datagen
+
+    wl = datagen.WORKLOADS[name]
+    nb_max = (max(wl.rows) + 1) // 4
+    pb = path_bytes(wl, wl.rows, nb_max)
+    R = replicas(pb, args.layers, args.replicas)
+    L = [SeqLayer(Q, wl, i, dev) for i in range(args.layers * R)]
+    sh = shared_buffers(Q, wl, dev)
+    groups = groups_of(L, args.layers)
+    ms = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager)
+    kt = {k_: per_launch_us(Q, L, sh, nb_max, wl, k_) for k_ in kinds}
+    rec = leg_record(name, wl.m, args.layers, R, ms, pb, kt)
+    del L, sh, groups
+    free()
+    return rec
+
+
+def batched_leg(Q, args, dev):
+    import datagen
+
+    specs = datagen.batched_specs()
+    wl = datagen.Workload("batched", 3, max(sp.n_ctx for sp in specs), tuple(sp.row for sp in specs), "bf16", 256)
+    nb_max = (max(wl.rows) + 1) // 4
+    pb = path_bytes(wl, wl.rows, sum(sp.n_ctx // 4 for sp in specs))
+    R = replicas(pb, args.layers, args.replicas)
+    L = [BatchedLayer(Q, specs, i, dev) for i in range(args.layers * R)]
+    sh = shared_buffers(Q, wl, dev)
+    groups = groups_of(L, args.layers)
+    ms = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager)
+    kt = {k_: per_launch_us(Q, L, sh, nb_max, wl, k_) for k_ in ("append", "score", "select", "attn")}
+    rec = leg_record("batched", wl.m, args.layers, R, ms, pb, kt)
+    rec["sequences"] = len(specs)
+    rec["contexts"] = [sp.n_ctx for sp in specs]
+    rec["segments"] = [len(sp.seg_len) for sp in specs]
+    del L, sh, groups
+    free()
+    return rec
+
+
+def prefill_leg(Q, args, dev):
+    """The 2,048-row prefill chunk at 200,000..202,047: rows/s per layer and
+    the matrix-core utilisation of its scoring pass, its attention and the
+    whole path, on algorithmic flops (and, for the scoring pass, on the bf16
+    flops its three-plane pooled keys issue)."""
+    import torch
+
+    import datagen
+
+    wl = datagen.WORKLOADS["prefill"]
+    nb_max = (max(wl.rows) + 1) // 4
+    steps = max(3, args.steps // 20)
+    warm = max(1, min(args.warmup, 3))
+    L = [SeqLayer(Q, wl, i, dev) for i in range(args.layers)]
+    sh = shared_buffers(Q, wl, dev)
+    groups = [L]
+    ms = timed_sweeps(Q, groups, sh, nb_max, wl, steps, warm, args.eager)
+    kt = {k_: per_launch_us(Q, L, sh, nb_max, wl, k_, reps=1) for k_ in ("append", "score", "select", "attn")}
+    pairs = sum(min((p + 1) // 4, nb_max) for p in wl.rows)
+    score_flops = pairs * 4 * 128 * 2                        # float32-equivalent products of the scores
+    tok = kept_tokens(wl.rows, wl.k_blocks)
+    attn_flops = tok * wl.hq * wl.head_dim * 2 * 2            # QK and PV over the kept tokens
+    layer_us = ms * 1e3 / args.layers
+    tf = lambda f, us: f / (us * 1e-6) / 1e12  # noqa: E731
+    rec = leg_record("prefill", wl.m, args.layers, 1, ms, path_bytes(wl, wl.rows, nb_max), kt)
+    # the gathered K/V above is counted per row (8.6 GB); rows share blocks, so
+    # the unique K/V is far less (at most the layer's 202,048 tokens)
+    rec["path"]["unique_kv_bytes"] = wl.n_ctx * wl.hkv * 2 * wl.head_dim * 2
+    rec["path"]["note"] = "gathered K/V counted per row: most of it is served from the caches, not HBM"
+    rec["mfma"] = {
+        "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+        "scoring": {"kernel": "score_prefill_pipe_kernel", "launch_us": kt["score"],
+                    "alg_flops": score_flops, "alg_tflops": tf(score_flops, kt["score"]),
+                    "alg_frac": tf(score_flops, kt["score"]) / MFMA_BF16_PEAK_TFLOPS,
+                    "issued_bf16_flops": 3 * score_flops,
+                    "issued_frac": tf(3 * score_flops, kt["score"]) / MFMA_BF16_PEAK_TFLOPS},
+        "attention": {"kernel": "attn_mfma_kernel", "launch_us": kt["attn"], "alg_flops": attn_flops,
+                      "alg_tflops": tf(attn_flops, kt["attn"]),
+                      "alg_frac": tf(attn_flops, kt["attn"]) / MFMA_BF16_PEAK_TFLOPS,
+                      "gathered_bytes": tok * wl.hkv * 2 * wl.head_dim * 2,
+                      "gathered_TBs": tok * wl.hkv * 2 * wl.head_dim * 2 / (kt["attn"] * 1e-6) / 1e12},
+        "path": {"alg_flops": score_flops + attn_flops, "alg_tflops": tf(score_flops + attn_flops, layer_us),
+                 "alg_frac": tf(score_flops + attn_flops, layer_us) / MFMA_BF16_PEAK_TFLOPS},
+    }
+    if not args.no_flat:
+        sh2 = dict(sh)
+        wsb = Q.qsa_score_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
+        sh2["ws_flat"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        msf = timed_sweeps(Q, groups, sh2, nb_max, wl, steps, warm, args.eager, flat=True)
+        flat_us = per_launch_us(Q, L, sh2, nb_max, wl, "flat", reps=1, flat=True)
+        ld = -(-nb_max // 4) * 4
+        rec["flat"] = {"workload": "prefill memory-flat select", "value": wl.m * args.layers / (msf / 1e3),
+                       "ms_per_step": msf, "layer_us": msf * 1e3 / args.layers,
+                       "score_select_us": round(flat_us, 1),
+                       "score_plus_select_us": round(kt["score"] + kt["select"], 1),
+                       "workspace_bytes": wsb,
+                       "score_matrix_bytes": wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)}
+        del sh2
+        free()
+    if "fp8" in args.legs:
+        f8 = fp8_leg(Q, L, groups, sh, nb_max, wl, argparse.Namespace(**{**vars(args), "steps": steps,
+                                                                          "warmup": warm}), kt["attn"])
+        rec["fp8"] = f8
+    del L, sh, groups
+    free()
+    return rec
+
+
+# ------------------------------------------------------------------ main
 
 def main():
     args = parse()
@@ -426,6 +650,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.cpu_table:
+        print(json.dumps(cpu_baseline(budget_s=8.0, table=True)), flush=True)
+        return
     import torch
 
     import datagen
@@ -434,18 +661,6 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     Q.qsa_device_check()
-    layers = args.layers
-    t_setup = time.time()
-    if args.workload == "batched":
-        wl, L, sh, nb_max, seq_nb = build_batched(Q, layers, dev)
-    else:
-        wl = datagen.WORKLOADS[args.workload]
-        L, sh, nb_max = build_single(Q, wl, layers, dev)
-        seq_nb = None  # one sequence: its pooled keys are read once for all rows
-    torch.cuda.synchronize()
-    print(f"[bench] set-up {wl.name}: {layers} layers, n_ctx {wl.n_ctx}, M {wl.m} in "
-          f"{time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
-
     if args.pmc_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -453,70 +668,43 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    run = step_fn(Q, L, sh, nb_max, wl)
-    run()
+    if args.workload in ("decode_32k", "prefill", "batched"):
+        # one workload on its own (profiling runs)
+        t0 = time.time()
+        rec = (prefill_leg(Q, args, dev) if args.workload == "prefill" else
+               batched_leg(Q, args, dev) if args.workload == "batched" else single_leg(Q, "decode_32k", args, dev))
+        print(f"[bench] {args.workload} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+        print(json.dumps(rec), flush=True)
+        return
+
+    # ---- main leg: the verify (or M = 1) workload at 261,122 context
+    wl = datagen.WORKLOADS[args.workload]
+    layers = args.layers
+    nb_max = (max(wl.rows) + 1) // 4
+    pbytes = path_bytes(wl, wl.rows, nb_max)
+    R = replicas(pbytes, layers, args.replicas)
+    t_setup = time.time()
+    L = [SeqLayer(Q, wl, i, dev) for i in range(layers * R)]
+    sh = shared_buffers(Q, wl, dev)
+    groups = groups_of(L, layers)
     torch.cuda.synchronize()
-    if args.eager:
-        replay = run
-    else:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            run()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            run()
-        replay = g.replay
-    for _ in range(args.warmup):
-        replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    ms_step = ms / args.steps
-    rows_per_s = wl.m * layers * args.steps / (ms / 1e3)
+    print(f"[bench] set-up {wl.name}: {layers} layers x {R} replicas, n_ctx {wl.n_ctx}, M {wl.m} in "
+          f"{time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    ms_step = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager)
+    rows_per_s = wl.m * layers / (ms_step / 1e3)
 
     # per-kernel device time (dominant kernel: scoring, HBM-bound)
     kt = {kind: per_launch_us(Q, L, sh, nb_max, wl, kind) for kind in ("score", "select", "attn", "append")}
-    if L[0].row_seq is None:
-        kt["append_score"] = per_launch_us(Q, L, sh, nb_max, wl, "append_score")
-    pooled_bytes = nb_max * 512 if seq_nb is None else sum(seq_nb) * 512
-    score_bytes = pooled_bytes + wl.m * 4 * 128 * 2 + (wl.m * nb_max if seq_nb is None else sum(seq_nb)) * 4
-    # the step scores through the launch that also appends (one sequence,
-    # few rows): its bytes include the append's
-    folded = L[0].row_seq is None and wl.m < PREFILL_MIN_ROWS
-    score_us = kt["append_score"] if folded else kt["score"]
-    if folded:
-        score_bytes += append_alg_bytes(L[0].new_pos.cpu().tolist(), 2)
+    kt["append_score"] = per_launch_us(Q, L, sh, nb_max, wl, "append_score")
+    score_bytes = nb_max * 512 + wl.m * 4 * 128 * 2 + wl.m * nb_max * 4
+    # the step scores through the launch that also appends: its bytes include the append's
+    score_us = kt["append_score"]
+    score_bytes += append_alg_bytes(L[0].new_pos.cpu().tolist(), 2)
     achieved = score_bytes / (score_us * 1e-6) / 1e9
-    if wl.m >= PREFILL_MIN_ROWS:
-        # many-row scoring runs on the bf16 matrix cores with three-plane
-        # pooled keys: report issued bf16 flops against the bf16 peak, and the
-        # float32-equivalent (algorithmic) rate beside it
-        alg_flops = sum(min((p + 1) // 4, nb_max) for p in wl.rows) * 4 * 128 * 2
-        roofline = {"bound": "mfma", "kernel": "score_prefill_pipe_kernel",
-                    "achieved": 3 * alg_flops / (score_us * 1e-6) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": 3 * alg_flops / (score_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                    "traffic": None, "algorithmic_tflops": alg_flops / (score_us * 1e-6) / 1e12,
-                    "flops_per_launch_bf16": 3 * alg_flops, "launch_us": score_us}
-    else:
-        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                    "kernel": ("score_fewrow_kernel (append folded in)" if folded else
-                               "score_fewrow_kernel" if seq_nb is None else
-                               "score_fewrow_kernel (one row per sequence)"),
-                    "traffic": stored_traffic() if wl.name == "verify_262k" else None,
-                    "bytes_per_launch": score_bytes, "launch_us": score_us}
-    # whole-path algorithmic bytes per layer step: pooled once + gathered K/V + q/out/index queries
-    tok = sum(min((p + 1) // 4, wl.k_blocks) * 4 + (p + 1) % 4 for p in wl.rows)
-    path_bytes = pooled_bytes + tok * wl.hkv * 2 * wl.head_dim * 2 + wl.m * (2 * wl.hq * wl.head_dim * 2 + 4 * 128 * 2)
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "kernel": "score_fewrow_kernel (append folded in)",
+                "traffic": stored_traffic() if wl.name == "verify_262k" else None,
+                "bytes_per_launch": score_bytes, "launch_us": score_us}
     layer_us = ms_step * 1e3 / layers
     res = {
         "metric": "QSA query-rows/s per layer at 262K ctx (M=1,4) + achieved HBM GB/s / MFMA %",
@@ -532,19 +720,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "n_ctx": wl.n_ctx, "rows": wl.m, "row_pos": [wl.rows[0], wl.rows[-1]],
-                   "layers": layers, "budget_tokens": wl.k_blocks * 4, "hq": wl.hq, "hkv": wl.hkv,
+                   "layers": layers, "replicas": R, "budget_tokens": wl.k_blocks * 4, "hq": wl.hq, "hkv": wl.hkv,
                    "head_dim": wl.head_dim, "graph": not args.eager},
         "roofline": roofline,
-        "path": {"layer_us": layer_us, "bytes_per_layer_step": path_bytes,
-                 "achieved_GBs": path_bytes / (layer_us * 1e-6) / 1e9,
-                 "frac": path_bytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "path": {"layer_us": layer_us, "bytes_per_layer_step": pbytes,
+                 "achieved_GBs": pbytes / (layer_us * 1e-6) / 1e9,
+                 "frac": pbytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                  "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}},
     }
-    if not args.no_flat and wl.m >= PREFILL_MIN_ROWS:
-        res["flat"] = flat_leg(Q, L, sh, nb_max, wl, args, kt)
-    if not args.no_fp8 and wl.name in ("verify_262k", "decode_262k", "decode_32k", "prefill"):
-        res["fp8"] = fp8_leg(Q, L, sh, nb_max, wl, args, kt["attn"])
-    if not args.no_m1 and wl.name == "verify_262k":
+    if "fp8" in args.legs and wl.name == "verify_262k":
+        res["fp8"] = fp8_leg(Q, L, groups, sh, nb_max, wl, args, kt["attn"])
+    if "m1" in args.legs and wl.name == "verify_262k":
         wl1 = datagen.WORKLOADS["decode_262k"]
         for ly in L:
             ly.rows = ly.rows[-1:].contiguous()
@@ -555,25 +741,21 @@ def main():
         sh1 = dict(sh)
         sh1["out"] = sh["out"][-1:].contiguous()
         sh1["lse"] = sh["lse"][-1:].contiguous()
-        run1 = step_fn(Q, L, sh1, nb_max, wl1)
-        run1()
-        torch.cuda.synchronize()
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g1):
-            run1()
-        for _ in range(args.warmup):
-            g1.replay()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            g1.replay()
-        end.record()
-        torch.cuda.synchronize()
-        ms1 = start.elapsed_time(end)
-        res["m1"] = {"workload": "decode_262k", "value": layers * args.steps / (ms1 / 1e3),
-                     "ms_per_step": ms1 / args.steps, "layer_us": ms1 * 1e3 / args.steps / layers}
+        ms1 = timed_sweeps(Q, groups, sh1, nb_max, wl1, args.steps, args.warmup, args.eager)
+        kt1 = {k_: per_launch_us(Q, L, sh1, nb_max, wl1, k_) for k_ in ("append_score", "select", "attn")}
+        res["m1"] = leg_record("decode_262k", 1, layers, R, ms1, path_bytes(wl1, wl1.rows, nb_max), kt1)
+        del sh1
+    del L, sh, groups
+    free()
+    if wl.name == "verify_262k":
+        for leg in ("decode_32k", "batched", "prefill"):
+            if leg in args.legs:
+                t0 = time.time()
+                res[leg] = (prefill_leg(Q, args, dev) if leg == "prefill" else
+                            batched_leg(Q, args, dev) if leg == "batched" else single_leg(Q, leg, args, dev))
+                print(f"[bench] leg {leg} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.workload)
+        res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)
 
 
