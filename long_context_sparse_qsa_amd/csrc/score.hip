@@ -276,6 +276,9 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   const int wave = threadIdx.x / kWave;
   const int m0 = blockIdx.y * RPG;
   const int rows = min(RPG, M - m0);
+  // the selection that consumes the sample counts its chunks in from zero
+  if (HIST && bx == 0 && (int)threadIdx.x < rows)
+    ws[(size_t)(m0 + threadIdx.x) * sel::row_words(nb_max) + sel::kArriveWord] = 0u;
 
   // Everything is loaded up front.  The row positions (wave-uniform) and the
   // index-query operand are small and cached; issued before the pooled

@@ -315,6 +315,9 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
   const int64_t t_end = n_tiles * (chunk + 1) / n_chunks;
   if (t_begin >= t_end) return;
   const int r0 = rt * kPfRows;
+  // the selection that consumes the sample counts its chunks in from zero
+  if (HIST && chunk == 0 && tid < kPfRows && r0 + tid < M)
+    ws[(size_t)(r0 + tid) * sel::row_words(nb_max) + sel::kArriveWord] = 0u;
 
   uint4 aq[kPfCg][kPfKs];
 #pragma unroll
