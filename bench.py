@@ -12,8 +12,9 @@ resident in HBM before the timed region.  Prints one JSON line.
 The metric is query-rows/s per layer (rows x layers x steps / time) of the
 main workload (default: the 4-row verify at 261,122 context).  Every other
 workload of the benchmark set is timed as a leg of the same run and reported
-beside it: M = 1 at 262K, fp8 K/V, decode M = 1 at 32K, batched segmented
-decode, and the 2,048-row prefill chunk (with its matrix-core utilisation).
+beside it: M = 1 at 262K, fp8 and Q8_0 K/V, decode M = 1 at 32K, batched
+segmented decode, and the 2,048-row prefill chunk (with its matrix-core
+utilisation).
 
 Each timed sweep rotates over R replicas of the 12 layers' state, R chosen so
 that one sweep touches at least 1 GiB, so that the 256 MB last-level cache
@@ -42,7 +43,7 @@ SCORE_SOURCES = ("score.hip", "select_common.h", "qsa_device.h", "append_common.
 PMC_FILE = os.path.join(ROOT, "profiles", "score_fewrow_kernel.verify_262k.pmc.txt")
 COPY_BYTES = 256 << 20  # plain copy of known size used to scale the PMC byte counters
 PREFILL_MIN_ROWS = 64  # rows at which scoring takes the many-row matrix-core kernel
-LEGS = ("m1", "fp8", "decode_32k", "batched", "prefill")
+LEGS = ("m1", "fp8", "q8", "decode_32k", "batched", "prefill")
 
 
 def parse():
@@ -486,20 +487,25 @@ def cpu_baseline(wl_name: str = "verify_262k", budget_s: float = 10.0, table: bo
 
 # ------------------------------------------------------------------ legs
 
-def fp8_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us):
-    """The same layers with K/V in the fp8 state (E4M3 codes + f16 scale per
-    head and token), quantized on the device from the bf16 K/V: the whole
-    step through graphs, the attention launch beside the bf16 one, and the
+def quant_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us, fmt="fp8"):
+    """The same layers with K/V in a quantized state -- fp8 (E4M3 codes + f16
+    scale per head and token) or q8 (Q8_0: int8 codes + f16 scale per 32
+    values) -- quantized on the device from the bf16 K/V: the whole step
+    through graphs, the attention launch beside the bf16 one, and the
     quantize launch that writes one step's new K (or V) rows."""
     import torch
 
+    q8 = fmt == "q8"
+    quantize = Q.qsa_quantize_kv_q8_0 if q8 else Q.qsa_quantize_kv_fp8
     for ly in L:
-        ly.k8 = torch.empty((wl.hkv, ly.cap, wl.head_dim), dtype=torch.uint8, device=ly.k.device)
+        ly.k8 = torch.empty((wl.hkv, ly.cap, wl.head_dim), dtype=torch.int8 if q8 else torch.uint8,
+                            device=ly.k.device)
         ly.v8 = torch.empty_like(ly.k8)
-        ly.ks = torch.empty((wl.hkv, ly.cap), dtype=torch.float16, device=ly.k.device)
+        ly.ks = torch.empty((wl.hkv, ly.cap, wl.head_dim // 32) if q8 else (wl.hkv, ly.cap), dtype=torch.float16,
+                            device=ly.k.device)
         ly.vs = torch.empty_like(ly.ks)
-        Q.qsa_quantize_kv_fp8(ly.k, ly.k8, ly.ks)
-        Q.qsa_quantize_kv_fp8(ly.v, ly.v8, ly.vs)
+        quantize(ly.k, ly.k8, ly.ks)
+        quantize(ly.v, ly.v8, ly.vs)
         ly.kv_bf16, ly.kv = ly.kv, Q.KvSegments.single(ly.k8, ly.v8, wl.n_ctx, ly.ks, ly.vs)
         ly.new_k = ly.k[:, ly.rows[0]:ly.rows[0] + min(wl.m, 4)].contiguous()  # new K rows [hkv, T, D]
     torch.cuda.synchronize()
@@ -514,22 +520,22 @@ def fp8_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us):
     a.record()
     for _ in range(4):
         for ly in L:
-            Q.qsa_quantize_kv_fp8(ly.new_k, ly.k8, ly.ks, t0=t0)
+            quantize(ly.new_k, ly.k8, ly.ks, t0=t0)
     b.record()
     torch.cuda.synchronize()
     quant_us = a.elapsed_time(b) * 1e3 / (4 * len(L))
     tok = kept_tokens(wl.rows, wl.k_blocks)
-    gather_fp8 = tok * wl.hkv * 2 * (wl.head_dim + 2)
+    gather_q = tok * wl.hkv * 2 * (wl.head_dim + (wl.head_dim // 16 if q8 else 2))
     gather_bf16 = tok * wl.hkv * 2 * wl.head_dim * 2
     for ly in L:  # back to the bf16 state for whatever runs next
         ly.kv = ly.kv_bf16
         del ly.k8, ly.v8, ly.ks, ly.vs, ly.new_k
     free()
     layers = len(groups[0])
-    return {"workload": wl.name + " fp8 K/V", "value": wl.m * layers / (ms / 1e3),
+    return {"workload": wl.name + (" Q8_0 K/V" if q8 else " fp8 K/V"), "value": wl.m * layers / (ms / 1e3),
             "unit": "query-rows/s per layer", "ms_per_step": ms, "layer_us": ms * 1e3 / layers,
             "attn_us": round(attn_us, 2), "attn_us_bf16": round(attn_bf16_us, 2),
-            "gather_bytes": gather_fp8, "gather_bytes_bf16": gather_bf16,
+            "gather_bytes": gather_q, "gather_bytes_bf16": gather_bf16,
             "quantize_us_per_kv_write": round(quant_us, 2)}
 
 
@@ -633,10 +639,10 @@ def prefill_leg(Q, args, dev):
                        "score_matrix_bytes": wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)}
         del sh2
         free()
-    if "fp8" in args.legs:
-        f8 = fp8_leg(Q, L, groups, sh, nb_max, wl, argparse.Namespace(**{**vars(args), "steps": steps,
-                                                                          "warmup": warm}), kt["attn"])
-        rec["fp8"] = f8
+    for fmt in ("fp8", "q8"):
+        if fmt in args.legs:
+            rec[fmt] = quant_leg(Q, L, groups, sh, nb_max, wl,
+                                 argparse.Namespace(**{**vars(args), "steps": steps, "warmup": warm}), kt["attn"], fmt)
     del L, sh, groups
     free()
     return rec
@@ -728,8 +734,9 @@ def main():
                  "frac": pbytes / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                  "kernel_us": {k_: round(v, 2) for k_, v in kt.items()}},
     }
-    if "fp8" in args.legs and wl.name == "verify_262k":
-        res["fp8"] = fp8_leg(Q, L, groups, sh, nb_max, wl, args, kt["attn"])
+    for fmt in ("fp8", "q8"):
+        if fmt in args.legs and wl.name == "verify_262k":
+            res[fmt] = quant_leg(Q, L, groups, sh, nb_max, wl, args, kt["attn"], fmt)
     if "m1" in args.legs and wl.name == "verify_262k":
         wl1 = datagen.WORKLOADS["decode_262k"]
         for ly in L:

@@ -62,9 +62,13 @@ typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
 /* K/V storage formats (qsa_kv_segments.kv_format).  QSA_KV_FP8_E4M3 is the
  * fp8 state of the hipfire page, section 03 ("State formats"): E4M3 K and V
  * (OCP E4M3FN: bias 7, largest finite 448, no infinities) with one f16 scale
- * per KV head and token; a row's values are code * scale. */
+ * per KV head and token; a row's values are code * scale.  QSA_KV_Q8_0 is
+ * the q8 state of the same table: Q8_0 K and V, int8 codes with one f16
+ * scale per 32 consecutive values of a row (34 bytes per 32 values); value
+ * = code * the scale of its block. */
 #define QSA_KV_SAME 0      /* K/V in the query dtype */
 #define QSA_KV_FP8_E4M3 1  /* E4M3 codes + f16 scales; queries bf16 */
+#define QSA_KV_Q8_0 2      /* Q8_0: int8 codes + one f16 scale per 32 values; queries bf16 */
 
 /*
  * qsa_append_pool -- write index keys in place and pool completed blocks.
@@ -216,7 +220,9 @@ typedef struct qsa_kv_segments {
                                    (QSA_KV_FP8_E4M3: uint8 codes) */
   const void* const* v_seg;     /* [n_seg_total] -> V, same layout */
   const uint16_t* const* k_scale_seg; /* QSA_KV_FP8_E4M3: [n_seg_total] -> f16 bits
-                                   [hkv][seg_cap], the scale of each K row; else NULL */
+                                   [hkv][seg_cap], the scale of each K row;
+                                   QSA_KV_Q8_0: -> f16 bits [hkv][seg_cap][head_dim/32],
+                                   the scale of each 32-value block; else NULL */
   const uint16_t* const* v_scale_seg; /* the same for V */
 } qsa_kv_segments;
 
@@ -251,7 +257,10 @@ typedef struct qsa_kv_segments {
  * E4M3 codes with f16 row scales (see qsa_quantize_kv_fp8): a logit is
  * scale_k(t) * (q . code_k(t)) * scale, and token t's softmax weight is
  * multiplied by scale_v(t) before it meets V's codes (rounded to bf16 as the
- * weights of the bf16 path are).
+ * weights of the bf16 path are).  With QSA_KV_Q8_0 (dtype QSA_BF16 only) K
+ * and V are Q8_0 (see qsa_quantize_kv_q8_0): a logit is the sum over the
+ * row's 32-value blocks j of scale_k(t, j) * (q_j . code_k(t)_j), times
+ * scale; V values are code * scale_v(t, j) rounded to bf16 before P.V.
  */
 int qsa_gathered_attn(const void* q, int32_t dtype, int32_t M, int32_t hq, int32_t hkv,
                       int32_t head_dim, float scale,
@@ -353,6 +362,37 @@ size_t qsa_score_select_workspace_bytes(int32_t max_M, int64_t nb_max, int32_t k
 int qsa_quantize_kv_fp8(const void* src, int32_t n_head, int32_t n_tok, int32_t head_dim,
                         int64_t src_head_stride, void* dst, uint16_t* dst_scale,
                         int64_t dst_head_stride, qsa_stream_t stream);
+
+/*
+ * qsa_quantize_kv_q8_0 -- write K or V rows into a Q8_0 cache (int8 codes,
+ * one f16 scale per 32 consecutive values of a row).
+ *
+ * Page: hipfire "QSA sparse attention ...", section 03, "State formats" (the
+ * opt-in q8 state: Q8_0 K/V with bf16 index keys, 1,408 bytes per token and
+ * layer).  The page names the format only; the rule here, per 32-value
+ * block of a row:
+ *   scale = f16(amax / 127), amax the block's largest magnitude, the quotient
+ *   in float32 and rounded to nearest even (an f16 overflow clamps to
+ *   65504); code = the integer nearest to the float32 quotient x / scale,
+ *   ties to even, clamped to [-127, 127]; a block whose scale rounds to zero
+ *   gets zero codes.
+ *
+ *  src       bf16 rows: row (h, t) at src + (h * src_head_stride + t) * head_dim
+ *  n_head, n_tok >= 0   rows written: n_head * n_tok
+ *  head_dim  128 or 256
+ *  dst       int8 codes: row (h, t) at dst + (h * dst_head_stride + t) * head_dim
+ *  dst_scale f16 bits: block j of row (h, t) at
+ *            dst_scale[(h * dst_head_stride + t) * (head_dim / 32) + j]
+ *  src_head_stride >= n_tok, dst_head_stride >= n_tok (in rows)
+ * src and dst 16-byte aligned, dst_scale 2-byte aligned; the caller owns
+ * every buffer.  In place, nothing allocated.  NaN or infinite inputs give
+ * undefined codes.  The attention reads a Q8_0 segment's scale rows with
+ * 16-byte (head_dim 256) or 8-byte (head_dim 128) loads: a segment's scale
+ * buffer must start 16-byte aligned.
+ */
+int qsa_quantize_kv_q8_0(const void* src, int32_t n_head, int32_t n_tok, int32_t head_dim,
+                         int64_t src_head_stride, void* dst, uint16_t* dst_scale,
+                         int64_t dst_head_stride, qsa_stream_t stream);
 
 /* Workspace bytes qsa_select_topk needs for up to max_M rows of up to
  * nb_max blocks (0 means no workspace is needed).  The workspace is one

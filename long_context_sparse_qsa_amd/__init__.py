@@ -27,6 +27,7 @@ QSA_F32 = 0
 QSA_BF16 = 1
 QSA_KV_SAME = 0
 QSA_KV_FP8_E4M3 = 1
+QSA_KV_Q8_0 = 2
 INDEX_DIM = 128
 INDEX_HEADS = 4
 BLOCK_TOKENS = 4
@@ -37,6 +38,7 @@ EXPORTED = (
     "qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
     "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_score_select_workspace_bytes",
     "qsa_select_workspace_bytes", "qsa_attn_workspace_bytes", "qsa_attn_plan", "qsa_gathered_attn_noalloc",
+    "qsa_quantize_kv_q8_0",
     "qsa_device_check", "qsa_last_error", "qsa_version",
 )
 
@@ -72,6 +74,7 @@ _lib.qsa_gathered_attn_noalloc.argtypes = [_P, _I32, _I32, _I32, _I32, _I32, cty
                                            ctypes.POINTER(QsaKvSegments), _P, _P, _I32, _P, _P, _P]
 _lib.qsa_append_score.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _SZ, _P]
 _lib.qsa_quantize_kv_fp8.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
+_lib.qsa_quantize_kv_q8_0.argtypes = [_P, _I32, _I32, _I32, _I64, _P, _P, _I64, _P]
 _lib.qsa_score_select.argtypes = [_P, _I32, _P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]
 _lib.qsa_score_select_workspace_bytes.argtypes = [_I32, _I64, _I32]
 _lib.qsa_score_select_workspace_bytes.restype = _SZ
@@ -85,7 +88,7 @@ _lib.qsa_last_error.restype = ctypes.c_char_p
 _lib.qsa_version.restype = ctypes.c_char_p
 for _f in ("qsa_append_pool", "qsa_score_blocks", "qsa_select_topk", "qsa_gathered_attn",
            "qsa_append_score", "qsa_quantize_kv_fp8", "qsa_score_select", "qsa_attn_plan", "qsa_device_check",
-           "qsa_gathered_attn_noalloc"):
+           "qsa_gathered_attn_noalloc", "qsa_quantize_kv_q8_0"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -210,20 +213,24 @@ class KvSegments:
 
     ``segments[s]`` is a list of (start, length, K, V) for sequence s, with
     K/V tensors [hkv, cap, head_dim] (cap >= length) in the query dtype, or
-    (start, length, K, V, K_scale, V_scale) for fp8 K/V: uint8 E4M3 codes
-    [hkv, cap, head_dim] and float16 scales [hkv, cap] (see
-    ``qsa_quantize_kv_fp8``).  The tensors must stay alive (and in place)
-    while the table is used; the table keeps references.
+    (start, length, K, V, K_scale, V_scale) for quantized K/V: fp8 as uint8
+    E4M3 codes [hkv, cap, head_dim] with float16 scales [hkv, cap] (see
+    ``qsa_quantize_kv_fp8``), Q8_0 as int8 codes [hkv, cap, head_dim] with
+    float16 scales [hkv, cap, head_dim / 32] (see ``qsa_quantize_kv_q8_0``).
+    The tensors must stay alive (and in place) while the table is used; the
+    table keeps references.
     """
 
     def __init__(self, segments: list, device=None):
         dev = device or segments[0][0][2].device
         self._keep = []
         begin, starts, lens, caps, kp, vp, ksp, vsp = [0], [], [], [], [], [], [], []
-        fp8 = len(segments[0][0]) == 6
+        quant = len(segments[0][0]) == 6
+        q8 = quant and segments[0][0][2].dtype == torch.int8
+        fp8 = quant and not q8
         for segs in segments:
             for seg in segs:
-                _need(len(seg) == (6 if fp8 else 4), "all segments fp8 or none")
+                _need(len(seg) == (6 if quant else 4), "all segments quantized or none")
                 st, ln, k, v = seg[:4]
                 assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
                 starts.append(int(st))
@@ -232,17 +239,20 @@ class KvSegments:
                 kp.append(k.data_ptr())
                 vp.append(v.data_ptr())
                 self._keep += [k, v]
-                if fp8:
+                if quant:
                     ks, vs = seg[4], seg[5]
-                    _need(k.dtype == torch.uint8 and ks.dtype == torch.float16 and vs.dtype == torch.float16,
-                          "fp8 segments: uint8 codes, float16 scales")
-                    _need(ks.is_contiguous() and vs.is_contiguous() and ks.shape == k.shape[:2] == vs.shape,
-                          "scale shape [hkv, cap]")
+                    want = torch.int8 if q8 else torch.uint8
+                    _need(k.dtype == want and ks.dtype == torch.float16 and vs.dtype == torch.float16,
+                          "quantized segments: uint8 (fp8) or int8 (Q8_0) codes, float16 scales")
+                    sshape = (k.shape[0], k.shape[1], k.shape[2] // 32) if q8 else k.shape[:2]
+                    _need(ks.is_contiguous() and vs.is_contiguous() and ks.shape == sshape == vs.shape,
+                          "scale shape [hkv, cap] (fp8) or [hkv, cap, head_dim / 32] (Q8_0)")
                     ksp.append(ks.data_ptr())
                     vsp.append(vs.data_ptr())
                     self._keep += [ks, vs]
             begin.append(len(starts))
         self.fp8 = fp8
+        self.q8 = q8
         self.max_seg = max(len(s) for s in segments)
         self.seq_seg_begin = torch.tensor(begin, dtype=torch.int32, device=dev)
         self.seg_start = torch.tensor(starts, dtype=torch.int64, device=dev)
@@ -250,18 +260,19 @@ class KvSegments:
         self.seg_cap = torch.tensor(caps, dtype=torch.int64, device=dev)
         self.k_ptrs = torch.tensor(kp, dtype=torch.int64, device=dev)
         self.v_ptrs = torch.tensor(vp, dtype=torch.int64, device=dev)
-        self.ks_ptrs = torch.tensor(ksp, dtype=torch.int64, device=dev) if fp8 else None
-        self.vs_ptrs = torch.tensor(vsp, dtype=torch.int64, device=dev) if fp8 else None
+        self.ks_ptrs = torch.tensor(ksp, dtype=torch.int64, device=dev) if quant else None
+        self.vs_ptrs = torch.tensor(vsp, dtype=torch.int64, device=dev) if quant else None
+        fmt = QSA_KV_Q8_0 if q8 else QSA_KV_FP8_E4M3 if fp8 else QSA_KV_SAME
         self.struct = QsaKvSegments(
-            len(segments), len(starts), self.max_seg, QSA_KV_FP8_E4M3 if fp8 else QSA_KV_SAME,
+            len(segments), len(starts), self.max_seg, fmt,
             self.seq_seg_begin.data_ptr(), self.seg_start.data_ptr(), self.seg_len.data_ptr(),
             self.seg_cap.data_ptr(), self.k_ptrs.data_ptr(), self.v_ptrs.data_ptr(),
-            self.ks_ptrs.data_ptr() if fp8 else None, self.vs_ptrs.data_ptr() if fp8 else None)
+            self.ks_ptrs.data_ptr() if quant else None, self.vs_ptrs.data_ptr() if quant else None)
 
     @classmethod
     def single(cls, k: torch.Tensor, v: torch.Tensor, length: int | None = None,
                k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None):
-        """One sequence held in one [hkv, cap, D] buffer (fp8: with its scales)."""
+        """One sequence held in one [hkv, cap, D] buffer (fp8 / Q8_0: with its scales)."""
         n = k.shape[1] if length is None else length
         if k_scale is not None:
             return cls([[(0, n, k, v, k_scale, v_scale)]])
@@ -322,6 +333,23 @@ def qsa_quantize_kv_fp8(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.T
     _need(0 <= t0 and t0 + t <= cap, "rows t0..t0+T-1 must lie inside the cache")
     _check(_lib.qsa_quantize_kv_fp8(_ptr(src), h, t, d, t, dst.data_ptr() + t0 * d,
                                     dst_scale.data_ptr() + 2 * t0, cap, _stream(stream)))
+
+
+def qsa_quantize_kv_q8_0(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.Tensor, t0: int = 0,
+                         stream=None) -> None:
+    """Q8_0 int8 codes and f16 scales (one per 32 values) of ``src`` [n_head,
+    T, D] bf16 written to rows t0 .. t0+T-1 of ``dst`` int8 [n_head, cap, D]
+    and ``dst_scale`` float16 [n_head, cap, D / 32]."""
+    _need(src.dtype == torch.bfloat16 and dst.dtype == torch.int8 and dst_scale.dtype == torch.float16,
+          "src bf16, dst int8, dst_scale float16")
+    _need(src.is_contiguous() and dst.is_contiguous() and dst_scale.is_contiguous(), "tensors must be contiguous")
+    h, t, d = src.shape
+    _need(dst.dim() == 3 and dst.shape[0] == h and dst.shape[2] == d and
+          dst_scale.shape == (h, dst.shape[1], d // 32), "dst [n_head, cap, D], dst_scale [n_head, cap, D / 32]")
+    cap = dst.shape[1]
+    _need(0 <= t0 and t0 + t <= cap, "rows t0..t0+T-1 must lie inside the cache")
+    _check(_lib.qsa_quantize_kv_q8_0(_ptr(src), h, t, d, t, dst.data_ptr() + t0 * d,
+                                     dst_scale.data_ptr() + 2 * t0 * (d // 32), cap, _stream(stream)))
 
 
 def qsa_gathered_attn(q: torch.Tensor, row_pos: torch.Tensor, kv: KvSegments, sel: torch.Tensor,

@@ -58,6 +58,14 @@ __device__ __forceinline__ uint4 ldg16(const unsigned char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 8-byte load through a global pointer (see ldg16).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ldg8(const unsigned char* p) {
+  typedef __attribute__((address_space(1))) const u32x2_t GU2;
+  const u32x2_t v = *(GU2*)(p);
+  return make_uint2(v.x, v.y);
+}
+
 struct KvArgs {
   const int32_t* seq_seg_begin;
   const int64_t* seg_start;
@@ -65,7 +73,7 @@ struct KvArgs {
   const int64_t* seg_cap;
   const void* const* k_seg;
   const void* const* v_seg;
-  const uint16_t* const* k_scale;  // fp8 K/V: f16 row scales per segment
+  const uint16_t* const* k_scale;  // fp8 / Q8_0 K/V: f16 scales per segment
   const uint16_t* const* v_scale;
   int n_seq;
   int n_seg_total;
@@ -610,7 +618,31 @@ struct MfmaLds {
   }
 };
 
-template <int D, int NW, bool F8>
+// K/V formats of the matrix-core kernel: bf16, fp8 E4M3 codes with one f16
+// scale per row, Q8_0 int8 codes with one f16 scale per 32 values.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvQ8 = 2;
+
+// Four signed bytes (one word) -> four bf16 values, exactly (|c| <= 128 fits
+// bf16's 8-bit significand): the unsigned-byte conversions of c + 128 (one
+// instruction each), minus 128, then the high halves of the float32 results.
+__device__ __forceinline__ float ubyte_f(uint32_t u, int i) { return (float)((u >> (8 * i)) & 0xffu); }
+__device__ __forceinline__ uint2 s8x4_to_bf16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const float a = ubyte_f(u, 0) - 128.f, b = ubyte_f(u, 1) - 128.f;
+  const float c = ubyte_f(u, 2) - 128.f, d = ubyte_f(u, 3) - 128.f;
+  return make_uint2(__builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u),
+                    __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07060302u));
+}
+// Four signed bytes times a scale -> four bf16 values (rounded to nearest
+// even by the packed hardware conversion).
+__device__ __forceinline__ uint2 s8x4_scaled_bf16x4(uint32_t w, float sc) {
+  const uint32_t u = w ^ 0x80808080u;
+  const float a = (ubyte_f(u, 0) - 128.f) * sc, b = (ubyte_f(u, 1) - 128.f) * sc;
+  const float c = (ubyte_f(u, 2) - 128.f) * sc, d = (ubyte_f(u, 3) - 128.f) * sc;
+  return make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
+}
+
+template <int D, int NW, int KVF>
 __global__ void __launch_bounds__(kWave * NW, NW < 8 ? 8 / NW : 1)  // at least 8 waves per CU: registers for 2 per SIMD
 attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2,
                  const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
@@ -620,11 +652,15 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
                  float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int KS = D / 32;               // QK k-steps
   constexpr int NT = D / 16;               // PV output tiles of 16 dims
-  constexpr int kRowBytes = F8 ? D : D * 2;
+  constexpr bool F8 = KVF == kKvFp8;
+  constexpr bool Q8 = KVF == kKvQ8;
+  constexpr bool B8 = F8 || Q8;            // one byte per K/V value
+  constexpr int kRowBytes = B8 ? D : D * 2;
+  constexpr int QB = D / 32;               // Q8_0 scale blocks per row (= QK k-steps)
   constexpr int VCH = kRowBytes / 16;      // 16-byte chunks per V row
   constexpr int VITEMS = 4 * VCH;          // (token quad, chunk) V staging items
   constexpr int VIT = (VITEMS + kWave - 1) / kWave;  // per lane
-  constexpr int KL = F8 ? KS / 2 : KS;     // 16-byte K loads per lane
+  constexpr int KL = B8 ? KS / 2 : KS;     // 16-byte K registers per lane (Q8: two 8-byte loads each)
   static_assert(kRowBytes <= (int)sizeof(kZeroRow), "zero row shorter than a K/V row");
   using Lds = MfmaLds<D>;
   extern __shared__ __align__(16) uint32_t lds[];
@@ -690,7 +726,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     mine.cap = kv.seg_cap[si];
     mine.k = static_cast<const unsigned char*>(kv.k_seg[si]);
     mine.v = static_cast<const unsigned char*>(kv.v_seg[si]);
-    if constexpr (F8) {
+    if constexpr (B8) {
       mine.ks = kv.k_scale[si];
       mine.vs = kv.v_scale[si];
     }
@@ -788,6 +824,9 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       if constexpr (F8) {
         a.ksp = hit ? sd.ks + row : a.ksp;
         a.vsp = hit ? sd.vs + row : a.vsp;
+      } else if constexpr (Q8) {
+        a.ksp = hit ? sd.ks + row * QB : a.ksp;
+        a.vsp = hit ? sd.vs + row * QB : a.vsp;
       }
       a.ok |= hit ? 1 : 0;
     };
@@ -807,9 +846,25 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   };
   uint4 kb[KL];  // K operand rows: all k-steps
   uint32_t ks_bits = 0, vs_bits = 0;
+  uint4 ksq = make_uint4(0, 0, 0, 0);  // Q8: the lane's token's K scales, one f16 per k-step
   auto load_k = [&](const SliceAddr& a) {
+    if constexpr (Q8) {  // k-step s = dims 32 s + 8 g4 .. + 7 = scale block s
 #pragma unroll
-    for (int s = 0; s < KL; ++s) kb[s] = ldg16(a.kr + (F8 ? 64 * s + 16 * g4 : (32 * s + 8 * g4) * 2));
+      for (int s = 0; s < KL; ++s) {
+        const uint2 lo = ldg8(a.kr + 64 * s + 8 * g4);
+        const uint2 hi = ldg8(a.kr + 64 * s + 32 + 8 * g4);
+        kb[s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      if constexpr (QB == 8) {
+        ksq = ldg16(reinterpret_cast<const unsigned char*>(a.ksp));
+      } else {
+        const uint2 q2 = ldg8(reinterpret_cast<const unsigned char*>(a.ksp));
+        ksq = make_uint4(q2.x, q2.y, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KL; ++s) kb[s] = ldg16(a.kr + (F8 ? 64 * s + 16 * g4 : (32 * s + 8 * g4) * 2));
+    }
     if constexpr (F8) {
       ks_bits = *a.ksp;
       vs_bits = *a.vsp;
@@ -818,6 +873,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   // V items: (token quad vq, chunk c) of the slice; lanes past the item
   // count (fp8 at head_dim 128) load a valid chunk and write nothing
   uint4 vt[VIT][4];
+  uint32_t vsc[VIT][4];  // Q8: each staged chunk's V scale (f16 bits)
   auto load_v = [&](const SliceAddr& a) {
 #pragma unroll
     for (int u = 0; u < VIT; ++u) {
@@ -826,6 +882,12 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
       const int c = item % VCH;
 #pragma unroll
       for (int e = 0; e < 4; ++e) vt[u][e] = ldg16(shfl_ptr(a.vr, 4 * vq + e) + c * 16);
+      if constexpr (Q8) {  // chunk c = dims 16 c .. 16 c + 15: scale block c / 2
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vsc[u][e] = *reinterpret_cast<const uint16_t*>(
+              shfl_ptr(reinterpret_cast<const unsigned char*>(a.vsp), 4 * vq + e) + (c >> 1) * 2);
+      }
     }
   };
   SliceAddr cur = resolve_slice(0, bid, true);
@@ -842,7 +904,22 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     // 2. QK: sacc[v] = q[head 4 g4 + v] . K[token n16] (a masked token's
     // logit is replaced below: its K needs no mask)
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (F8) {
+    if constexpr (Q8) {
+      // per k-step partial products, each scaled by the token's block scale
+      const uint32_t ksw[4] = {ksq.x, ksq.y, ksq.z, ksq.w};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint32_t w0 = (s & 1) ? kb[s >> 1].z : kb[s >> 1].x;
+        const uint32_t w1 = (s & 1) ? kb[s >> 1].w : kb[s >> 1].y;
+        const uint2 b0 = s8x4_to_bf16x4(w0), b1 = s8x4_to_bf16x4(w1);
+        const uint4 bq = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa(s), __builtin_bit_cast(bf16x8_t, bq),
+                                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float sc = f16_bits_to_f32((ksw[s >> 1] >> (16 * (s & 1))) & 0xffffu);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sacc[v] = fmaf(sc, part[v], sacc[v]);
+      }
+    } else if constexpr (F8) {
 #pragma unroll
       for (int s = 0; s < KL; ++s) {
         const uint4 lo = fp8x8_to_bf16x8(kb[s].x, kb[s].y);
@@ -915,7 +992,19 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
         for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(quad + vslot(u8, k)) = piece[k];
       };
       uint32_t* quad = vl + vq * Lds::kQuadWords;
-      if constexpr (F8) {  // 16 codes per token: dims 16 c .. 16 c + 15
+      if constexpr (Q8) {  // 16 codes per token: dims 16 c .. 16 c + 15, times the token's block scale
+        uint4 lo8[4], hi8[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = f16_bits_to_f32(vsc[u][e]);
+          const uint2 a0 = s8x4_scaled_bf16x4(t[e].x, sc), a1 = s8x4_scaled_bf16x4(t[e].y, sc);
+          const uint2 a2 = s8x4_scaled_bf16x4(t[e].z, sc), a3 = s8x4_scaled_bf16x4(t[e].w, sc);
+          lo8[e] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+          hi8[e] = make_uint4(a2.x, a2.y, a3.x, a3.y);
+        }
+        put8(lo8[0], lo8[1], lo8[2], lo8[3], quad, 2 * c);
+        put8(hi8[0], hi8[1], hi8[2], hi8[3], quad, 2 * c + 1);
+      } else if constexpr (F8) {  // 16 codes per token: dims 16 c .. 16 c + 15
         put8(fp8x8_to_bf16x8(t[0].x, t[0].y), fp8x8_to_bf16x8(t[1].x, t[1].y), fp8x8_to_bf16x8(t[2].x, t[2].y),
              fp8x8_to_bf16x8(t[3].x, t[3].y), quad, 2 * c);
         put8(fp8x8_to_bf16x8(t[0].z, t[0].w), fp8x8_to_bf16x8(t[1].z, t[1].w), fp8x8_to_bf16x8(t[2].z, t[2].w),
@@ -1112,7 +1201,7 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot32);
 }
 
-template <class E, int D, bool F8 = false>
+template <class E, int D, int KVF = kKvBf16>
 hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
                         const int64_t* row_pos, const int32_t* row_seq, const KvArgs& kv,
                         const int32_t* sel, const int32_t* n_sel, int k_blocks, void* out,
@@ -1127,7 +1216,7 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
     const size_t lds = MfmaLds<D>::bytes(plan.waves);
 #define QSA_MFMA_LAUNCH(W)                                                                              \
   case W:                                                                                             \
-    hipLaunchKernelGGL((attn_mfma_kernel<D, W, F8>), grid, block, lds, stream,                        \
+    hipLaunchKernelGGL((attn_mfma_kernel<D, W, KVF>), grid, block, lds, stream,                       \
                        static_cast<const uint16_t*>(q), M, hq, scale * kLog2e, row_pos, row_seq, kv,  \
                        sel, n_sel, k_blocks, plan.tiles_per_split, plan.splits,                       \
                        static_cast<uint16_t*>(out), lse, ws_o, ws_lse);                               \
@@ -1244,8 +1333,13 @@ hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv
   a.n_seg_total = kv->n_seg_total;
   if (kv->kv_format == QSA_KV_FP8_E4M3) {  // bf16 queries (validated by the caller)
     if (head_dim == 256)
-      return launch_typed<BF16, 256, true>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
-    return launch_typed<BF16, 128, true>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+      return launch_typed<BF16, 256, kKvFp8>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+    return launch_typed<BF16, 128, kKvFp8>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+  }
+  if (kv->kv_format == QSA_KV_Q8_0) {  // bf16 queries (validated by the caller)
+    if (head_dim == 256)
+      return launch_typed<BF16, 256, kKvQ8>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
+    return launch_typed<BF16, 128, kKvQ8>(q, M, hq, hkv, scale, row_pos, row_seq, a, sel, n_sel, k_blocks, out, lse, ws, stream);
   }
   if (dtype == QSA_BF16) {
     if (head_dim == 256)

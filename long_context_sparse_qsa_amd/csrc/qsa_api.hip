@@ -201,12 +201,14 @@ int check_attn_args(const char* fn, const void* q, int32_t dtype, int32_t M, int
                 QSA_MAX_SEGMENTS);
   if (!kv->seq_seg_begin || !kv->seg_start || !kv->seg_len || !kv->seg_cap || !kv->k_seg || !kv->v_seg)
     return fail(QSA_ERR_ARG, "%s: null pointer in the kv segment table", fn);
-  if (kv->kv_format != QSA_KV_SAME && kv->kv_format != QSA_KV_FP8_E4M3)
-    return fail(QSA_ERR_ARG, "%s: kv_format %d is not QSA_KV_SAME or QSA_KV_FP8_E4M3", fn, kv->kv_format);
-  if (kv->kv_format == QSA_KV_FP8_E4M3) {
-    if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: fp8 K/V is served with bf16 queries only", fn);
+  if (kv->kv_format != QSA_KV_SAME && kv->kv_format != QSA_KV_FP8_E4M3 && kv->kv_format != QSA_KV_Q8_0)
+    return fail(QSA_ERR_ARG, "%s: kv_format %d is not QSA_KV_SAME, QSA_KV_FP8_E4M3 or QSA_KV_Q8_0", fn,
+                kv->kv_format);
+  if (kv->kv_format != QSA_KV_SAME) {
+    const char* what = kv->kv_format == QSA_KV_FP8_E4M3 ? "fp8" : "Q8_0";
+    if (dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: %s K/V is served with bf16 queries only", fn, what);
     if (!kv->k_scale_seg || !kv->v_scale_seg)
-      return fail(QSA_ERR_ARG, "%s: fp8 K/V needs k_scale_seg and v_scale_seg", fn);
+      return fail(QSA_ERR_ARG, "%s: %s K/V needs k_scale_seg and v_scale_seg", fn, what);
   }
   if (M > 0 && (!q || !row_pos || !sel || !n_sel || !out || !lse))
     return fail(QSA_ERR_ARG, "%s: null pointer (q, row_pos, sel, n_sel, out or lse)", fn);
@@ -304,6 +306,26 @@ int qsa_quantize_kv_fp8(const void* src, int32_t n_head, int32_t n_tok, int32_t 
                                                    static_cast<uint8_t*>(dst), dst_scale, dst_head_stride,
                                                    (hipStream_t)stream),
                        "qsa_quantize_kv_fp8");
+}
+
+int qsa_quantize_kv_q8_0(const void* src, int32_t n_head, int32_t n_tok, int32_t head_dim,
+                         int64_t src_head_stride, void* dst, uint16_t* dst_scale,
+                         int64_t dst_head_stride, qsa_stream_t stream) {
+  if (n_head < 0 || n_tok < 0)
+    return fail(QSA_ERR_ARG, "qsa_quantize_kv_q8_0: n_head %d / n_tok %d < 0", n_head, n_tok);
+  if (head_dim != 128 && head_dim != 256)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_quantize_kv_q8_0: head_dim %d; this build serves 128 and 256", head_dim);
+  if (src_head_stride < n_tok || dst_head_stride < n_tok)
+    return fail(QSA_ERR_ARG, "qsa_quantize_kv_q8_0: head strides %lld / %lld below n_tok %d",
+                (long long)src_head_stride, (long long)dst_head_stride, n_tok);
+  if ((int64_t)n_head * n_tok == 0) return ok();
+  if (!src || !dst || !dst_scale) return fail(QSA_ERR_ARG, "qsa_quantize_kv_q8_0: null pointer (src, dst or dst_scale)");
+  if (((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u) || ((uintptr_t)dst_scale & 1u))
+    return fail(QSA_ERR_ARG, "qsa_quantize_kv_q8_0: src and dst must be 16-byte aligned, dst_scale 2-byte aligned");
+  return launch_status(qsa::launch_quantize_kv_q8(src, n_head, n_tok, head_dim, src_head_stride,
+                                                  static_cast<int8_t*>(dst), dst_scale, dst_head_stride,
+                                                  (hipStream_t)stream),
+                       "qsa_quantize_kv_q8_0");
 }
 
 int qsa_device_check(void) {

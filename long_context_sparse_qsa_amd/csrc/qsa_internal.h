@@ -86,6 +86,10 @@ hipError_t launch_quantize_kv_fp8(const void* src, int n_head, int n_tok, int he
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
+// Q8_0 K/V cache writes (kv_q8.hip).
+hipError_t launch_quantize_kv_q8(const void* src, int n_head, int n_tok, int head_dim, int64_t src_head_stride,
+                                 int8_t* dst, uint16_t* dst_scale, int64_t dst_head_stride, hipStream_t stream);
+
 hipError_t launch_gathered_attn(const void* q, int dtype, int M, int hq, int hkv, int head_dim,
                                 float scale, const int64_t* row_pos, const int32_t* row_seq,
                                 const qsa_kv_segments* kv, const int32_t* sel,

@@ -12,12 +12,14 @@ from .qsa_oracle import (  # noqa: F401
     attend_partitioned,
     attended_tokens,
     dequantize_kv_fp8,
+    dequantize_kv_q8_0,
     e4m3_decode,
     e4m3_encode,
     merge_partials,
     n_blocks,
     pool_index_keys,
     quantize_kv_fp8,
+    quantize_kv_q8_0,
     qsa_row,
     score_blocks,
     select_blocks,

@@ -26,7 +26,8 @@ than itself: dense causal attention through torch SDPA, brute-force sorting,
 closed forms and hand-derived golden values.  No function here is
 "parity unpinned".  The fp8 K/V functions at the end follow the same page,
 section 03 ("State formats"), and are pinned to torch's own float8_e4m3fn
-conversions.
+conversions; the Q8_0 functions after them (same section) are pinned to a
+brute-force nearest-integer search, closed forms and the page's byte count.
 """
 from __future__ import annotations
 
@@ -251,3 +252,44 @@ def dequantize_kv_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """float64 K or V rows from E4M3 codes [..., D] and f16 scales [...]."""
     return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
 
+
+
+# ----------------------------------------------------------- Q8_0 K/V state
+# hipfire page, section 03, "State formats": the opt-in q8 state keeps K and
+# V as Q8_0 with bf16 index keys, 1,408 bytes per token and layer -- at 2 KV
+# heads x 256 dims that is 34 bytes per 32 values of K and V (1,088 bytes)
+# plus the index key and its pooled share.  Q8_0 is a block of 32 signed
+# 8-bit integers with one f16 scale.  The page names the format only.
+# Readings: a block's scale is its largest magnitude divided by 127 in
+# float32, rounded to f16 (nearest even; an f16 overflow clamps to 65504);
+# each code is the integer nearest to the float32 quotient x / scale (the
+# stored f16 scale), ties to the even integer, clamped to [-127, 127]; a
+# block whose scale rounds to zero stores zero codes.
+
+Q8_BLOCK = 32
+Q8_MAX = 127.0
+
+
+def quantize_kv_q8_0(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Q8_0 codes (int8, same shape as ``x`` [..., D]) and f16 scales
+    [..., D / 32] of float32 (or bf16-exact float32) rows."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    xb = x.reshape(x.shape[:-1] + (d // Q8_BLOCK, Q8_BLOCK))
+    amax = np.max(np.abs(xb), axis=-1)
+    with np.errstate(over="ignore"):  # an f16 overflow is clamped just below
+        scale = (amax / np.float32(Q8_MAX)).astype(np.float16)
+    scale = np.where(np.isinf(scale), np.float16(F16_MAX), scale)
+    sf = scale.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(sf > 0, xb / np.where(sf > 0, sf, np.float32(1.0)), np.float32(0.0))
+    codes = np.clip(np.rint(y), -Q8_MAX, Q8_MAX).astype(np.int8)  # rint: nearest, ties to even
+    return codes.reshape(x.shape), scale
+
+
+def dequantize_kv_q8_0(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """float64 K or V rows from Q8_0 codes [..., D] and f16 scales [..., D / 32]."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.float64)
+    d = c.shape[-1]
+    cb = c.reshape(c.shape[:-1] + (d // Q8_BLOCK, Q8_BLOCK))
+    return (cb * np.asarray(scale, dtype=np.float64)[..., None]).reshape(c.shape)

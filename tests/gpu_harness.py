@@ -62,6 +62,14 @@ class Layer:
         self.v[:, :n] = to_dev(d["v"], wl.dtype)
         self.kv = Q.KvSegments.single(self.k, self.v, n)
         self.kv_mode = kv
+        if kv == "q8":  # Q8_0 int8 codes + one f16 scale per 32 values, quantized on the device
+            self.k8 = torch.zeros((wl.hkv, self.cap, wl.head_dim), dtype=torch.int8, device=DEV)
+            self.v8 = torch.zeros_like(self.k8)
+            self.ks = torch.zeros((wl.hkv, self.cap, wl.head_dim // 32), dtype=torch.float16, device=DEV)
+            self.vs = torch.zeros_like(self.ks)
+            Q.qsa_quantize_kv_q8_0(to_dev(d["k"], "bf16"), self.k8, self.ks)
+            Q.qsa_quantize_kv_q8_0(to_dev(d["v"], "bf16"), self.v8, self.vs)
+            self.kv = Q.KvSegments.single(self.k8, self.v8, n, self.ks, self.vs)
         if kv == "fp8":  # E4M3 codes + f16 scales, quantized on the device
             self.k8 = torch.zeros((wl.hkv, self.cap, wl.head_dim), dtype=torch.uint8, device=DEV)
             self.v8 = torch.zeros_like(self.k8)
@@ -144,20 +152,23 @@ def check_selection(sel_gpu: np.ndarray, n_sel_gpu: int, scores64: np.ndarray, k
 
 
 def check_attention_fp8(out_gpu: np.ndarray, lse_gpu: np.ndarray, layer, row_i: int, sel: np.ndarray):
-    """fp8 K/V: the device cache holds the oracle's codes and scales for every
-    attended token (bit for bit), and attention matches fp64 attention over
-    the oracle's dequantized rows within the bf16 tolerances."""
+    """fp8 or Q8_0 K/V: the device cache holds the oracle's codes and scales
+    for every attended token (bit for bit), and attention matches fp64
+    attention over the oracle's dequantized rows within the bf16 tolerances."""
     d = layer.d
     wl = d["workload"]
     p = int(d["rows"][row_i])
     tok = O.attended_tokens(sel, p + 1)
     ti = torch.from_numpy(tok).to(DEV)
+    quant, dequant = ((O.quantize_kv_q8_0, O.dequantize_kv_q8_0) if layer.kv_mode == "q8" else
+                      (O.quantize_kv_fp8, O.dequantize_kv_fp8))
     deq = []
     for src, codes, sc in ((d["k"], layer.k8, layer.ks), (d["v"], layer.v8, layer.vs)):
-        c_ref, s_ref = O.quantize_kv_fp8(src[:, tok])
-        assert np.array_equal(codes[:, ti].cpu().numpy(), c_ref), "fp8 codes differ from the oracle"
-        assert np.array_equal(sc[:, ti].cpu().numpy().view(np.uint16), s_ref.view(np.uint16)), "fp8 scales differ"
-        deq.append(O.dequantize_kv_fp8(c_ref, s_ref))
+        c_ref, s_ref = quant(src[:, tok])
+        assert np.array_equal(codes[:, ti].cpu().numpy(), c_ref), f"{layer.kv_mode} codes differ from the oracle"
+        assert np.array_equal(sc[:, ti].cpu().numpy().view(np.uint16), s_ref.view(np.uint16)), \
+            f"{layer.kv_mode} scales differ"
+        deq.append(dequant(c_ref, s_ref))
     ref, ref_lse = O.attend(d["q"][row_i], deq[0], deq[1], np.arange(len(tok)), 1.0 / math.sqrt(wl.head_dim))
     err = float(np.max(np.abs(out_gpu - ref)))
     lerr = float(np.max(np.abs(lse_gpu - ref_lse)))
@@ -241,7 +252,7 @@ def check_layer(d, res, layer, k=None, rows=None, attn_rows=None):
         # the select kernel is exact on its own input
         assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k)), f"row {i}: select != exact top-k of GPU scores"
         st = check_selection(sel[i], int(n_sel[i]), s64, k)
-        if i in attn_rows and layer.kv_mode == "fp8":
+        if i in attn_rows and layer.kv_mode in ("fp8", "q8"):
             err, lerr = check_attention_fp8(out[i], lse[i], layer, i, sel[i, : n_sel[i]])
             st.update(err=err, lse_err=lerr)
         elif i in attn_rows:

@@ -137,8 +137,11 @@ def test_attn_validation(kw, code, word):
     (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3)), ERR_ARG, "scale"),
     (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3, scales=True), dtype=0, d=128), Q.QSA_ERR_UNSUPPORTED, "bf16"),
     (dict(kv=_kv(fmt=Q.QSA_KV_FP8_E4M3, scales=True), wsb=0), Q.QSA_ERR_WORKSPACE, "workspace"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_Q8_0)), ERR_ARG, "Q8_0 K/V needs"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_Q8_0, scales=True), dtype=0, d=128), Q.QSA_ERR_UNSUPPORTED, "bf16"),
+    (dict(kv=_kv(fmt=Q.QSA_KV_Q8_0, scales=True), wsb=0), Q.QSA_ERR_WORKSPACE, "workspace"),
 ])
-def test_attn_fp8_validation(kw, code, word):
+def test_attn_quantized_validation(kw, code, word):
     assert _attn(**kw) == code
     assert word in _err()
 
@@ -160,6 +163,30 @@ def _quant(src=FAKE, nh=2, nt=4, d=256, shs=4, dst=FAKE, dsc=FAKE, dhs=16):
 ])
 def test_quantize_kv_fp8_validation(kw, code, word):
     assert _quant(**kw) == code
+    assert word in _err()
+
+
+def _quant_q8(src=FAKE, nh=2, nt=4, d=256, shs=4, dst=FAKE, dsc=FAKE, dhs=16):
+    return L.qsa_quantize_kv_q8_0(src, nh, nt, d, shs, dst, dsc, dhs, None)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(nh=-1), ERR_ARG, "n_head"),
+    (dict(nt=-3), ERR_ARG, "n_tok"),
+    (dict(d=64), Q.QSA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(d=192), Q.QSA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(shs=3), ERR_ARG, "stride"),
+    (dict(dhs=2), ERR_ARG, "stride"),
+    (dict(dst=None), ERR_ARG, "null"),
+    (dict(dsc=None), ERR_ARG, "null"),
+    (dict(src=FAKE + 2), ERR_ARG, "aligned"),
+    (dict(dst=FAKE + 8), ERR_ARG, "aligned"),
+    (dict(dsc=FAKE + 1), ERR_ARG, "aligned"),
+    (dict(nh=0, src=None, dst=None, dsc=None), Q.QSA_OK, ""),
+])
+def test_quantize_kv_q8_0_validation(kw, code, word):
+    assert _quant_q8(**kw) == code
+    assert "qsa_quantize_kv_q8_0" in _err() or code == Q.QSA_OK
     assert word in _err()
 
 

@@ -323,12 +323,13 @@ def test_deterministic_bitwise(Q):
     assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
 
 
-def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512, head_dim=256, fp8=False):
+def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512, head_dim=256, quant=None):
     """Sequences with K/V in several segments (some empty, some cutting a
     4-token block), one row per sequence, scored and attended in one call.
-    With fp8 every segment holds E4M3 codes and f16 scales quantized on the
-    device from the bf16 rows (checked bit for bit against the oracle), and
-    attention is compared with the oracle's dequantized K/V."""
+    With quant ("fp8" or "q8") every segment holds codes and f16 scales
+    quantized on the device from the bf16 rows (checked bit for bit against
+    the oracle), and attention is compared with the oracle's dequantized
+    K/V."""
     import dataclasses
 
     rng = np.random.default_rng(seed)
@@ -355,16 +356,19 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512, head_dim=256, fp8=Fal
             if hi > lo:
                 kt[:, : hi - lo] = to_dev(np.ascontiguousarray(k_[:, lo:hi]), "bf16")
                 vt[:, : hi - lo] = to_dev(np.ascontiguousarray(v_[:, lo:hi]), "bf16")
-            if fp8:
-                k8 = torch.full((2, cap, D), 0x55, dtype=torch.uint8, device=DEV)
+            if quant:
+                q8 = quant == "q8"
+                k8 = torch.full((2, cap, D), 0x55, dtype=torch.int8 if q8 else torch.uint8, device=DEV)
                 v8 = torch.full_like(k8, 0x55)
-                ks = torch.zeros((2, cap), dtype=torch.float16, device=DEV)
+                ks = torch.zeros((2, cap, D // 32) if q8 else (2, cap), dtype=torch.float16, device=DEV)
                 vs = torch.zeros_like(ks)
+                qfn = Q.qsa_quantize_kv_q8_0 if q8 else Q.qsa_quantize_kv_fp8
+                ofn = O.quantize_kv_q8_0 if q8 else O.quantize_kv_fp8
                 if hi > lo:
-                    Q.qsa_quantize_kv_fp8(kt[:, : hi - lo].contiguous(), k8, ks)
-                    Q.qsa_quantize_kv_fp8(vt[:, : hi - lo].contiguous(), v8, vs)
+                    qfn(kt[:, : hi - lo].contiguous(), k8, ks)
+                    qfn(vt[:, : hi - lo].contiguous(), v8, vs)
                     for src, c8, sc8 in ((k_, k8, ks), (v_, v8, vs)):
-                        c_ref, s_ref = O.quantize_kv_fp8(src[:, lo:hi])
+                        c_ref, s_ref = ofn(src[:, lo:hi])
                         assert np.array_equal(c8[:, : hi - lo].cpu().numpy(), c_ref), "fp8 codes differ"
                         assert np.array_equal(sc8[:, : hi - lo].cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
                 segs.append((lo, hi - lo, k8, v8, ks, vs))
@@ -406,9 +410,11 @@ def _segmented_case(Q, n_ctx_list, nseg_list, seed, k=512, head_dim=256, fp8=Fal
         g32 = sc[i, : len(s64)].astype(np.float64)
         assert np.array_equal(sel[i, : n_sel[i]], O.select_blocks(g32, k))
         check_selection(sel[i], int(n_sel[i]), s64, k)
-        if fp8:
+        if quant:
             tok = O.attended_tokens(sel[i, : n_sel[i]], h["n"])
-            deq = [O.dequantize_kv_fp8(*O.quantize_kv_fp8(src[:, tok])) for src in (h["k"], h["v"])]
+            qo, dq = ((O.quantize_kv_q8_0, O.dequantize_kv_q8_0) if quant == "q8" else
+                      (O.quantize_kv_fp8, O.dequantize_kv_fp8))
+            deq = [dq(*qo(src[:, tok])) for src in (h["k"], h["v"])]
             ref, ref_lse = O.attend(h["q"][0], deq[0], deq[1], np.arange(len(tok)), 1.0 / math.sqrt(D))
             err, lerr = float(np.max(np.abs(out[i] - ref))), float(np.max(np.abs(lse[i] - ref_lse)))
             assert err <= 2e-2 and lerr <= 1e-3, (i, err, lerr)
@@ -437,15 +443,17 @@ def test_segments_head_dim_128(Q, seed, nseg):
     _segmented_case(Q, ctx, nseg, seed, head_dim=128)
 
 
-@pytest.mark.parametrize("seed,nseg,head_dim", [(7, [1, 4, 2], 256), (8, [16, 3, 5, 1, 9], 256),
-                                                (9, [2, 13, 1], 128)])
-def test_segments_fp8(Q, seed, nseg, head_dim):
-    """fp8 K/V (E4M3 codes + f16 scales) across several segments, some empty
-    or cutting a block, rows of different sequences in one call (row_seq)."""
-    say("segments, fp8 K/V", seed, nseg, head_dim)
+@pytest.mark.parametrize("quant,seed,nseg,head_dim", [("fp8", 7, [1, 4, 2], 256), ("fp8", 8, [16, 3, 5, 1, 9], 256),
+                                                      ("fp8", 9, [2, 13, 1], 128), ("q8", 10, [1, 5, 2], 256),
+                                                      ("q8", 11, [12, 3, 1, 7], 256), ("q8", 12, [3, 1, 16], 128)])
+def test_segments_quantized(Q, quant, seed, nseg, head_dim):
+    """fp8 (E4M3 + f16 row scales) or Q8_0 (int8 + f16 scale per 32 values)
+    K/V across several segments, some empty or cutting a block, rows of
+    different sequences in one call (row_seq)."""
+    say("segments,", quant, "K/V", seed, nseg, head_dim)
     rng = np.random.default_rng(seed)
     ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
-    plan, errs = _segmented_case(Q, ctx, nseg, seed, head_dim=head_dim, fp8=True)
+    plan, errs = _segmented_case(Q, ctx, nseg, seed, head_dim=head_dim, quant=quant)
     assert plan["splits"] > 1, plan  # split partials merged by the combine
     say(plan, max(e for e, _ in errs), max(l for _, l in errs))
 

@@ -411,3 +411,82 @@ def test_quantize_kv_fp8_closed_forms():
     big = np.full((1, 16), 3.0e7, np.float32)
     cb, sb = O.quantize_kv_fp8(big)
     assert sb[0] == np.float16(65504.0) and np.all(cb == 0x7E)
+
+
+# ------------------------------------------------------- Q8_0 K/V (the q8 state)
+
+def _q8_brute(x: np.ndarray):
+    """Nearest integer code by exhaustive search over [-127, 127] (ties to the
+    even integer), against float32 quotients by the f16 scale -- no rint."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1, 32)
+    codes = np.zeros(x.shape, dtype=np.int64)
+    scales = np.zeros(x.shape[0], dtype=np.float16)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for b in range(x.shape[0]):
+        amax = float(np.max(np.abs(x[b])))
+        q = np.float32(amax) / np.float32(127.0)
+        s16 = np.float16(q) if np.isfinite(np.float16(q)) else np.float16(65504.0)
+        scales[b] = s16
+        if float(s16) == 0.0:
+            continue
+        for j in range(32):
+            y = float(np.float32(x[b, j]) / np.float32(s16))
+            dist = np.abs(cand - y)
+            best = cand[dist == dist.min()]
+            codes[b, j] = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+    return codes, scales
+
+
+def test_q8_0_matches_brute_force():
+    """Codes are the nearest integers (ties to even, clamped to 127) of the
+    float32 quotients by the stored f16 scale, one scale per 32 values."""
+    rng = np.random.default_rng(21)
+    x = datagen.round_bf16(rng.standard_normal((24, 256)).astype(np.float32) * 2.0)
+    x[1] *= 1e-4      # scale in the f16 subnormal range
+    x[2, :32] = 0.0   # a zero block
+    x[3] *= 1e-9      # scales that round to zero
+    c, s = O.quantize_kv_q8_0(x)
+    assert c.dtype == np.int8 and c.shape == x.shape and s.shape == (24, 8)
+    bc, bs = _q8_brute(x)
+    assert np.array_equal(s.reshape(-1).view(np.uint16), bs.view(np.uint16))
+    assert np.array_equal(c.reshape(-1, 32).astype(np.int64), bc)
+    assert np.all(s[2, 0] == 0) and np.all(c[2, :32] == 0) and np.all(c[3] == 0)
+
+
+def test_q8_0_ties_go_to_even():
+    """A block scaled exactly by 2^-4 (largest value 127 / 16): values at
+    n + 1/2 steps round to the even neighbour, integer steps are exact."""
+    n = np.arange(-31, 32, dtype=np.float32)
+    blk = np.zeros((2, 32), np.float32)
+    blk[0] = np.resize(n[:32], 32) / 16.0
+    blk[0, 0] = 127.0 / 16.0
+    blk[1, :16] = (np.arange(16, dtype=np.float32) + 0.5) / 16.0
+    blk[1, 16] = 127.0 / 16.0
+    c, s = O.quantize_kv_q8_0(blk.reshape(1, 64))
+    assert s[0, 0] == np.float16(0.0625) and s[0, 1] == np.float16(0.0625)
+    assert np.array_equal(c[0, :32].astype(np.float32), blk[0] * 16.0)
+    half = c[0, 32:48].astype(np.int64)
+    want = np.array([int(2 * round((k + 0.5) / 2)) for k in range(16)])  # even neighbour of k + 1/2
+    assert np.array_equal(half, want)
+
+
+def test_q8_0_round_trip_and_bytes():
+    """Round trip within half a step of each block; sign symmetry; an f16
+    overflow clamps to 65504; 34 bytes per 32 values, so the page's 1,408
+    bytes per token and layer at 2 KV heads x 256 dims = K + V (1,088) + a
+    bf16 index key (256) + 64 bytes of pooled share."""
+    rng = np.random.default_rng(22)
+    x = datagen.round_bf16(rng.standard_normal((16, 128)).astype(np.float32) * 5.0)
+    c, s = O.quantize_kv_q8_0(x)
+    cn, sn = O.quantize_kv_q8_0(-x)
+    assert np.array_equal(s, sn) and np.array_equal(cn, -c)
+    r = O.dequantize_kv_q8_0(c, s)
+    step = np.repeat(s.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(r - x) <= 0.5 * step * (1 + 1e-3) + 1e-12)
+    assert np.all(np.abs(c).max(axis=1) >= 126)
+    big = np.full((1, 32), 3.0e7, np.float32)
+    cb, sb = O.quantize_kv_q8_0(big)
+    assert sb[0, 0] == np.float16(65504.0) and np.all(cb == 127)
+    per_block = 32 * 1 + 2
+    assert per_block == 34
+    assert 2 * 2 * 256 // 32 * per_block + 128 * 2 + 64 == 1408
