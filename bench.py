@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graphs")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (scales FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--probes", action="store_true",
+                    help="time the memory-pattern probes (libqsa_probe.so) and exit")
     ap.add_argument("--cpu-table", action="store_true",
                     help="time the CPU oracle on every workload (1 thread and all threads) and exit")
     a = ap.parse_args()
@@ -650,6 +652,89 @@ def prefill_leg(Q, args, dev):
 
 # ------------------------------------------------------------------ main
 
+def probes(dev) -> dict:
+    """What the memory system delivers for the path's access patterns, with
+    no arithmetic (libqsa_probe.so): a one-launch contiguous read of one
+    layer's pooled keys at 262K (the scoring pass's bytes and workgroup
+    shape), random 2 KiB gathers (4-token K or V rows at head_dim 256) over
+    working sets from L2-sized to the prefill chunk's K/V and beyond, and the
+    cost of one more launch in a graph of dependent launches."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_sparse_qsa_amd", "libqsa_probe.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.qsa_probe_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.qsa_probe_gather.argtypes = [vp, i64, vp, i64, vp, vp]
+    lib.qsa_probe_empty.argtypes = [i32, vp]
+    lib.qsa_probe_last_error.restype = ctypes.c_char_p
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
+    def ok(r):
+        if r != 0:
+            raise RuntimeError(lib.qsa_probe_last_error().decode())
+
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        fn(0)
+        torch.cuda.synchronize()
+        spin()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    out = {"peak_GBs": HBM_PEAK_GBS}
+    # one launch reading the pooled keys of one 262K layer (65,280 blocks x 512 B)
+    pooled = 65280 * 512
+    nbuf = -(-ROTATE_BYTES // pooled)
+    big = torch.empty(nbuf * pooled // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    rd = {}
+    for wgb in (16384, 32768, 65536):
+        us = timed(lambda i: ok(lib.qsa_probe_read(vp(big.data_ptr() + (i % nbuf) * pooled), pooled, wgb,
+                                                   vp(sink.data_ptr()), stream)), 4 * nbuf)
+        rd[f"{wgb // 1024}KiB_per_wg"] = {"workgroups": pooled // wgb, "us": round(us, 2),
+                                          "GBs": round(pooled / us / 1e3, 1),
+                                          "frac": round(pooled / us / 1e3 / HBM_PEAK_GBS, 3)}
+    out["read_33MB_one_launch"] = rd
+    del big
+    # random 2 KiB gathers: the prefill chunk's count (2,048 rows x 2 KV heads
+    # x 512 blocks x K and V) over several working sets
+    n = 2048 * 2 * 512 * 2
+    buf = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    rng = np.random.default_rng(0)
+    ga = {}
+    for name, ws in (("4MiB", 4 << 20), ("64MiB", 64 << 20), ("prefill_kv_413.8MB", 413794304),
+                     ("1GiB", 1 << 30)):
+        ids = torch.from_numpy(rng.integers(0, ws // 2048, size=n, dtype=np.int64).astype(np.int32)).to(dev)
+        us = timed(lambda i: ok(lib.qsa_probe_gather(vp(buf.data_ptr()), ws, vp(ids.data_ptr()), n,
+                                                     vp(sink.data_ptr()), stream)), 5)
+        ga[name] = {"working_set_bytes": ws, "us": round(us, 1), "GBs": round(n * 2048 / us / 1e3, 1),
+                    "frac": round(n * 2048 / us / 1e3 / HBM_PEAK_GBS, 3)}
+        del ids
+    out["gather_2KiB_8.6GB"] = ga
+    del buf
+    # one more launch in a graph: 48 dependent empty launches (12 layers x 4)
+    em = {}
+    for wgs in (1, 256):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(48):
+                ok(lib.qsa_probe_empty(wgs, vp(torch.cuda.current_stream().cuda_stream)))
+        us = timed(lambda i: g.replay(), 50)
+        em[f"{wgs}_workgroups"] = {"us_per_launch": round(us / 48, 2)}
+    out["empty_launch_in_graph"] = em
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -667,6 +752,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     Q.qsa_device_check()
+    if args.probes:
+        print(json.dumps({"probes": probes(dev)}), flush=True)
+        return
     if args.pmc_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

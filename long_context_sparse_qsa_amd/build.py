@@ -1,7 +1,9 @@
 """Build libqsa.so (HIP, gfx950) in-tree with hipcc.
 
 Every source under csrc/ is compiled to an object in parallel, then linked
-into ``long_context_sparse_qsa_amd/libqsa.so``.  Flags:
+into ``long_context_sparse_qsa_amd/libqsa.so``; the measurement kernels
+under probe/ become ``libqsa_probe.so`` (loaded by the benchmark only).
+Flags:
   --offload-arch=gfx950      CDNA4 only
   -O3, no fast-math          pooling must keep IEEE adds in a fixed order
   -packed-fp32-ops disabled  packed float32 VALU ops stay out of the code
@@ -17,9 +19,11 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -37,13 +41,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the QSA library needs ROCm's hipcc to build")
 
 
-def sources() -> list:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d: str = CSRC) -> list:
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{os.path.dirname(src)}", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,20 +61,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libqsa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link of libqsa.so failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libqsa.so and libqsa_probe.so;
+    returns the path of libqsa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, psrcs = sources(CSRC), sources(PROBE)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + psrcs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 
