@@ -610,7 +610,9 @@ def prefill_leg(Q, args, dev):
     # the gathered K/V above is counted per row (8.6 GB); rows share blocks, so
     # the unique K/V is far less (at most the layer's 202,048 tokens)
     rec["path"]["unique_kv_bytes"] = wl.n_ctx * wl.hkv * 2 * wl.head_dim * 2
-    rec["path"]["note"] = "gathered K/V counted per row: most of it is served from the caches, not HBM"
+    rec["path"]["note"] = ("gathered K/V counted per row: the rows' selections are nearly independent, so each "
+                           "row's gather is its own traffic (bench.py --probes: random 2 KiB gathers over the "
+                           "same 413.8 MB run at ~7.7 TB/s)")
     rec["mfma"] = {
         "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
         "scoring": {"kernel": "score_prefill_pipe_kernel", "launch_us": kt["score"],
