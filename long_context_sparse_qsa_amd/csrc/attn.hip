@@ -1015,7 +1015,8 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
     }
     load_v(nxt);  // the V registers are free again
     cur = nxt;
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
+    // (on a wave's first slice the accumulators are still zero: nothing to rescale)
+    if (t > 0 && __ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
