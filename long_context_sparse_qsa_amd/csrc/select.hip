@@ -67,6 +67,8 @@ constexpr int kLowBins = 1024;                     // 10-bit digits below the 12
 // costs more than the kernel boundary once the collect spans many waves of
 // workgroups (measured: 2,048 rows, 0.49 ms fused against 0.21 ms).
 constexpr int64_t kFusedMaxWorkgroups = 1024;
+// Rows of at most this many blocks take the one-workgroup form.
+constexpr int64_t kRowMaxBlocks = 32 * kFinThreads;
 using sel::kWinBase;
 using sel::kWinBins;
 using sel::win_bin;
@@ -160,6 +162,98 @@ __device__ uint32_t row_threshold(const float* __restrict__ smp, int64_t n_grp, 
   find_digit_desc<kWinBins>(h, sel::sample_target((uint32_t)k), out3);
   // window bin 0 (or a target never reached): every block is a candidate
   return (out3[2] || out3[0] == 0u) ? 0u : kWinBase + out3[0];
+}
+
+// Exact selection among the candidates: sm.ck / sm.ci hold the candidate list
+// (ascending block order, n_cand entries), sm.hist16 the count of each 12-bit
+// digit, sm.h2 / sm.h3 are zero, and each thread holds candidates in kk (those
+// flagged in vm) -- the caller has synchronised.  Writes the kept ids to out,
+// ascending.
+__device__ void select_from_candidates(FinSmem& sm, const uint32_t (&kk)[kFinPer], uint32_t vm, uint32_t n_cand,
+                                       int k, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  // The k-th largest candidate key, 12 + 10 + 10 bits at a time; each level
+  // histograms only the candidates that share the bits found so far, and the
+  // search stops as soon as the cut bin is kept whole.  Then a key is kept if
+  // (key >> shift) > prefix, or == prefix and (whole, or among the first
+  // `need` such keys in block order).
+  find_digit_desc<kDigits>(sm.hist16, (uint32_t)k, sm.out3);
+  uint32_t prefix = sm.out3[0];
+  uint32_t need = sm.out3[1];
+  int shift = kDigitShift;
+  bool whole = sm.hist16[prefix] == need;
+  if (!whole) {
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      if (((vm >> e) & 1u) && (kk[e] >> kDigitShift) == prefix) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_desc<kLowBins>(sm.h2, need, sm.out3);
+    const uint32_t d2 = sm.out3[0];
+    prefix = (prefix << 10) | d2;
+    need = sm.out3[1];
+    shift = 10;
+    whole = sm.h2[d2] == need;
+  }
+  if (!whole) {
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      if (((vm >> e) & 1u) && (kk[e] >> 10) == prefix) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_desc<kLowBins>(sm.h3, need, sm.out3);
+    const uint32_t d3 = sm.out3[0];
+    prefix = (prefix << 10) | d3;
+    need = sm.out3[1];
+    shift = 0;
+    whole = sm.h3[d3] == need;
+  }
+
+  // keep flags over contiguous ranges of the (ascending) candidate list
+  const uint32_t r0 = (uint32_t)tid * kFinPer;
+  static_assert(kFinPer == 8, "two 16-byte LDS reads per thread");
+  uint32_t key[kFinPer], cid[kFinPer];
+  {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(&sm.ck[r0]);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(&sm.ck[r0 + 4]);
+    const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.ci[r0]);
+    const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.ci[r0 + 4]);
+    key[0] = a0.x; key[1] = a0.y; key[2] = a0.z; key[3] = a0.w;
+    key[4] = a1.x; key[5] = a1.y; key[6] = a1.z; key[7] = a1.w;
+    cid[0] = b0.x; cid[1] = b0.y; cid[2] = b0.z; cid[3] = b0.w;
+    cid[4] = b1.x; cid[5] = b1.y; cid[6] = b1.z; cid[7] = b1.w;
+  }
+  uint32_t keep = 0u, n_keep = 0u, tot;
+  if (whole) {
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      const bool kp = r0 + e < n_cand && (key[e] >> shift) >= prefix;
+      keep |= kp ? (1u << e) : 0u;
+      n_keep += kp ? 1u : 0u;
+    }
+  } else {
+    // equal keys straddle the cut: the first `need` of them in block order
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) n_eq += (r0 + e < n_cand && key[e] == prefix) ? 1u : 0u;
+    uint32_t eq_rank = block_excl_scan<kFinThreads>(n_eq, sm.scan_sh, tot);
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      bool kp = r0 + e < n_cand && key[e] > prefix;
+      if (r0 + e < n_cand && key[e] == prefix) kp = eq_rank++ < need;
+      keep |= kp ? (1u << e) : 0u;
+      n_keep += kp ? 1u : 0u;
+    }
+  }
+  // kept candidates are already in ascending block order: compact them
+  uint32_t pos = block_excl_scan<kFinThreads>(n_keep, sm.scan_sh, tot);
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    if ((keep >> e) & 1u) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)cid[e];
+      ++pos;
+    }
+  }
 }
 
 // Final selection of row m from its chunks' candidates (or, on the exact
@@ -276,88 +370,7 @@ __device__ void finalize_row(const float* __restrict__ s, int64_t nb, int64_t nb
     }
   }
   __syncthreads();
-  // The k-th largest candidate key, 12 + 10 + 10 bits at a time; each level
-  // histograms only the candidates that share the bits found so far, and the
-  // search stops as soon as the cut bin is kept whole.  Then a key is kept if
-  // (key >> shift) > prefix, or == prefix and (whole, or among the first
-  // `need` such keys in block order).
-  find_digit_desc<kDigits>(sm.hist16, (uint32_t)k, sm.out3);
-  uint32_t prefix = sm.out3[0];
-  uint32_t need = sm.out3[1];
-  int shift = kDigitShift;
-  bool whole = sm.hist16[prefix] == need;
-  if (!whole) {
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) {
-      if (((vm >> e) & 1u) && (kk[e] >> kDigitShift) == prefix) atomicAdd(&sm.h2[(kk[e] >> 10) & (kLowBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_digit_desc<kLowBins>(sm.h2, need, sm.out3);
-    const uint32_t d2 = sm.out3[0];
-    prefix = (prefix << 10) | d2;
-    need = sm.out3[1];
-    shift = 10;
-    whole = sm.h2[d2] == need;
-  }
-  if (!whole) {
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) {
-      if (((vm >> e) & 1u) && (kk[e] >> 10) == prefix) atomicAdd(&sm.h3[kk[e] & (kLowBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_digit_desc<kLowBins>(sm.h3, need, sm.out3);
-    const uint32_t d3 = sm.out3[0];
-    prefix = (prefix << 10) | d3;
-    need = sm.out3[1];
-    shift = 0;
-    whole = sm.h3[d3] == need;
-  }
-
-  // keep flags over contiguous ranges of the (ascending) candidate list
-  const uint32_t r0 = (uint32_t)tid * kFinPer;
-  static_assert(kFinPer == 8, "two 16-byte LDS reads per thread");
-  uint32_t key[kFinPer], cid[kFinPer];
-  {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(&sm.ck[r0]);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(&sm.ck[r0 + 4]);
-    const uint4 b0 = *reinterpret_cast<const uint4*>(&sm.ci[r0]);
-    const uint4 b1 = *reinterpret_cast<const uint4*>(&sm.ci[r0 + 4]);
-    key[0] = a0.x; key[1] = a0.y; key[2] = a0.z; key[3] = a0.w;
-    key[4] = a1.x; key[5] = a1.y; key[6] = a1.z; key[7] = a1.w;
-    cid[0] = b0.x; cid[1] = b0.y; cid[2] = b0.z; cid[3] = b0.w;
-    cid[4] = b1.x; cid[5] = b1.y; cid[6] = b1.z; cid[7] = b1.w;
-  }
-  uint32_t keep = 0u, n_keep = 0u, tot;
-  if (whole) {
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) {
-      const bool kp = r0 + e < n_cand && (key[e] >> shift) >= prefix;
-      keep |= kp ? (1u << e) : 0u;
-      n_keep += kp ? 1u : 0u;
-    }
-  } else {
-    // equal keys straddle the cut: the first `need` of them in block order
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) n_eq += (r0 + e < n_cand && key[e] == prefix) ? 1u : 0u;
-    uint32_t eq_rank = block_excl_scan<kFinThreads>(n_eq, sm.scan_sh, tot);
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) {
-      bool kp = r0 + e < n_cand && key[e] > prefix;
-      if (r0 + e < n_cand && key[e] == prefix) kp = eq_rank++ < need;
-      keep |= kp ? (1u << e) : 0u;
-      n_keep += kp ? 1u : 0u;
-    }
-  }
-  // kept candidates are already in ascending block order: compact them
-  uint32_t pos = block_excl_scan<kFinThreads>(n_keep, sm.scan_sh, tot);
-#pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
-    if ((keep >> e) & 1u) {
-      if (pos < (uint32_t)k) out[pos] = (int32_t)cid[e];
-      ++pos;
-    }
-  }
+  select_from_candidates(sm, kk, vm, n_cand, k, out);
 }
 
 // Collect of one 4,096-block chunk of a row; with FUSED the last chunk of the
@@ -451,6 +464,103 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   }
 }
 
+// Rows of at most kRowMaxBlocks blocks (decode at 32K context): one
+// workgroup per row does the whole selection.  Its PER scores per lane and the
+// row's sample arrive in one round trip, the threshold comes from the sample
+// as in the collect pass, and the candidates go straight into LDS in
+// ascending block order (a block scan), so none of them leaves the compute
+// unit and no other workgroup is waited for.  Same paths and result as the
+// collect + finalize form.
+template <int PER>
+__global__ void __launch_bounds__(kFinThreads)
+select_row_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
+                  int64_t nb_max, int k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                  uint32_t* __restrict__ ws) {
+  static_assert(PER % 4 == 0 && PER <= 32, "float4 score loads, one flag bit per score");
+  __shared__ FinSmem sm;
+  __shared__ uint32_t h[kWinBins];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* __restrict__ s = scores + (int64_t)m * ld;
+  uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
+  const float* __restrict__ smp = reinterpret_cast<const float*>(W + sel::sample_off(nb_max));
+  const int64_t n_grp = sel::sample_groups(nb_max);
+  int32_t* __restrict__ out = sel + (int64_t)m * k;
+
+  // every load this pass needs, issued together
+  const int64_t i0 = (int64_t)tid * PER;  // this lane's consecutive blocks
+  float4 sv[PER / 4];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const int64_t j = i0 + 4 * q;  // rows are padded to a multiple of 4 floats
+    sv[q] = j < nb_max ? *reinterpret_cast<const float4*>(s + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  constexpr int kSampPer = kChunk / kChunkThreads;  // row_threshold's register-held sample
+  float smpv[kSampPer];
+#pragma unroll
+  for (int e = 0; e < kSampPer; ++e) {
+    const int64_t gi = (int64_t)e * kChunkThreads + tid;
+    smpv[e] = gi < n_grp ? smp[gi] : 0.f;
+  }
+  const int64_t nb = clamp_nb(row_pos[m], nb_max);
+  if (nb <= k) {
+    for (int i = tid; i < k; i += kFinThreads) out[i] = i < nb ? i : -1;
+    if (tid == 0) {
+      n_sel[m] = (int32_t)nb;
+      W[sel::kPathWord] = sel::kPathAll;
+    }
+    return;
+  }
+  if (tid == 0) n_sel[m] = k;
+  for (int i = tid; i < kWinBins; i += kFinThreads) h[i] = 0u;
+  for (int i = tid; i < kDigits; i += kFinThreads) sm.hist16[i] = 0u;
+  for (int i = tid; i < kLowBins; i += kFinThreads) {
+    sm.h2[i] = 0u;
+    sm.h3[i] = 0u;
+  }
+  __syncthreads();
+  const uint32_t B = row_threshold(smp, n_grp, nb, k, h, sm.out3, smpv);
+  uint32_t key[PER];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    key[4 * q + 0] = order_key(sv[q].x);
+    key[4 * q + 1] = order_key(sv[q].y);
+    key[4 * q + 2] = order_key(sv[q].z);
+    key[4 * q + 3] = order_key(sv[q].w);
+  }
+  uint32_t flags = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (i0 + e < nb && (key[e] >> kDigitShift) >= B) flags |= 1u << e;
+  uint32_t total;
+  uint32_t pos = block_excl_scan<kFinThreads>((uint32_t)__popc(flags), sm.scan_sh, total);
+  if (total < (uint32_t)k || total > (uint32_t)kCandMax) {  // uniform
+    if (tid == 0) W[sel::kPathWord] = sel::kPathExactCount;
+    exact_row_select(s, nb, k, out, sm);
+    return;
+  }
+  if (tid == 0) W[sel::kPathWord] = sel::kPathCandidates;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if ((flags >> e) & 1u) {  // pos < total <= kCandMax
+      sm.ck[pos] = key[e];
+      sm.ci[pos] = (uint32_t)(i0 + e);
+      atomicAdd(&sm.hist16[key[e] >> kDigitShift], 1u);
+      ++pos;
+    }
+  }
+  __syncthreads();
+  uint32_t kk[kFinPer];
+  uint32_t vm = 0u;
+#pragma unroll
+  for (int e = 0; e < kFinPer; ++e) {
+    const uint32_t i = (uint32_t)(e * kFinThreads + tid);  // < kCandMax
+    kk[e] = sm.ck[i];
+    vm |= i < total ? (1u << e) : 0u;
+  }
+  select_from_candidates(sm, kk, vm, total, k, out);
+}
+
 // Finalize pass of the two-launch form (one workgroup per row).
 __global__ void __launch_bounds__(kFinThreads)
 select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
@@ -465,7 +575,14 @@ select_finalize_kernel(const float* __restrict__ scores, int64_t ld, const int64
 hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_t* row_pos, int64_t nb_max,
                             int k, int32_t* sel, int32_t* n_sel, uint32_t* W, hipStream_t stream) {
   const int64_t chunks = (nb_max + kChunk - 1) / kChunk;
-  if (nb_max > k && M * chunks <= kFusedMaxWorkgroups) {  // collect, and the last chunk of each row finalizes it
+  if (nb_max > k && nb_max <= kRowMaxBlocks) {  // short rows: one workgroup per row
+    if (nb_max <= 16 * kFinThreads)
+      hipLaunchKernelGGL(select_row_kernel<16>, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld, row_pos,
+                         nb_max, k, sel, n_sel, W);
+    else
+      hipLaunchKernelGGL(select_row_kernel<32>, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld, row_pos,
+                         nb_max, k, sel, n_sel, W);
+  } else if (nb_max > k && M * chunks <= kFusedMaxWorkgroups) {  // collect, and the last chunk of each row finalizes it
     hipLaunchKernelGGL(select_collect_kernel<true>, dim3((unsigned)chunks, (unsigned)M), dim3(kChunkThreads), 0,
                        stream, scores, ld, row_pos, nb_max, k, sel, n_sel, W);
   } else if (nb_max > k) {  // many rows: collect, then one finalize workgroup per row
