@@ -67,8 +67,12 @@ constexpr int kLowBins = 1024;                     // 10-bit digits below the 12
 // costs more than the kernel boundary once the collect spans many waves of
 // workgroups (measured: 2,048 rows, 0.49 ms fused against 0.21 ms).
 constexpr int64_t kFusedMaxWorkgroups = 1024;
-// Rows of at most this many blocks take the one-workgroup form.
-constexpr int64_t kRowMaxBlocks = 32 * kFinThreads;
+// Rows of at most this many blocks take the one-workgroup form (measured,
+// sample + selection of one row: 9.3 against 11.1 us at 8,192 blocks; from
+// 12,288 blocks on the chunked form is faster: one compute unit then streams
+// the row too slowly).
+constexpr int kRowPer = 16;
+constexpr int64_t kRowMaxBlocks = kRowPer * kFinThreads;
 using sel::kWinBase;
 using sel::kWinBins;
 using sel::win_bin;
@@ -576,12 +580,8 @@ hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_
                             int k, int32_t* sel, int32_t* n_sel, uint32_t* W, hipStream_t stream) {
   const int64_t chunks = (nb_max + kChunk - 1) / kChunk;
   if (nb_max > k && nb_max <= kRowMaxBlocks) {  // short rows: one workgroup per row
-    if (nb_max <= 16 * kFinThreads)
-      hipLaunchKernelGGL(select_row_kernel<16>, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld, row_pos,
-                         nb_max, k, sel, n_sel, W);
-    else
-      hipLaunchKernelGGL(select_row_kernel<32>, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld, row_pos,
-                         nb_max, k, sel, n_sel, W);
+    hipLaunchKernelGGL(select_row_kernel<kRowPer>, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld,
+                       row_pos, nb_max, k, sel, n_sel, W);
   } else if (nb_max > k && M * chunks <= kFusedMaxWorkgroups) {  // collect, and the last chunk of each row finalizes it
     hipLaunchKernelGGL(select_collect_kernel<true>, dim3((unsigned)chunks, (unsigned)M), dim3(kChunkThreads), 0,
                        stream, scores, ld, row_pos, nb_max, k, sel, n_sel, W);
