@@ -377,9 +377,36 @@ __device__ void finalize_row(const float* __restrict__ s, int64_t nb, int64_t nb
   select_from_candidates(sm, kk, vm, n_cand, k, out);
 }
 
+// The candidate threshold of each row, once (many rows): one workgroup per
+// row histograms the row's sample and stores the digit in the row's record,
+// so that the row's chunk workgroups load one word instead of the sample.
+__global__ void __launch_bounds__(kChunkThreads)
+select_threshold_kernel(const int64_t* __restrict__ row_pos, int64_t nb_max, int k, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t h[kWinBins];
+  __shared__ uint32_t out3[3];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  uint32_t* W = ws + (size_t)m * sel::row_words(nb_max);
+  const float* __restrict__ smp = reinterpret_cast<const float*>(W + sel::sample_off(nb_max));
+  const int64_t n_grp = sel::sample_groups(nb_max);
+  constexpr int kSampPer = kChunk / kChunkThreads;
+  float smpv[kSampPer];
+#pragma unroll
+  for (int e = 0; e < kSampPer; ++e) {
+    const int64_t gi = (int64_t)e * kChunkThreads + tid;
+    smpv[e] = gi < n_grp ? smp[gi] : 0.f;
+  }
+  const int64_t nb = clamp_nb(row_pos[m], nb_max);
+  for (int i = tid; i < kWinBins; i += kChunkThreads) h[i] = 0u;
+  if (nb <= k) return;  // uniform: the collect pass skips the row
+  __syncthreads();
+  const uint32_t B = row_threshold(smp, n_grp, nb, k, h, out3, smpv);
+  if (tid == 0) W[sel::kThrWord] = B;
+}
+
 // Collect of one 4,096-block chunk of a row; with FUSED the last chunk of the
 // row to finish also finalizes the row.
-template <bool FUSED>
+template <bool FUSED, bool PRE_THR = false>
 __global__ void __launch_bounds__(kChunkThreads)
 select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ row_pos,
                       int64_t nb_max, int k, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
@@ -407,18 +434,27 @@ select_collect_kernel(const float* __restrict__ scores, int64_t ld, const int64_
   }
   constexpr int kSampPer = kChunk / kChunkThreads;  // samples per lane per round
   float smpv[kSampPer];
+  uint32_t thr = 0u;
+  if constexpr (PRE_THR) {
+    thr = W[sel::kThrWord];  // written by select_threshold_kernel
+  } else {
 #pragma unroll
-  for (int e = 0; e < kSampPer; ++e) {
-    const int64_t gi = (int64_t)e * kChunkThreads + tid;
-    smpv[e] = gi < n_grp ? smp[gi] : 0.f;
+    for (int e = 0; e < kSampPer; ++e) {
+      const int64_t gi = (int64_t)e * kChunkThreads + tid;
+      smpv[e] = gi < n_grp ? smp[gi] : 0.f;
+    }
   }
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
-  for (int i = tid; i < kWinBins; i += kChunkThreads) h[i] = 0u;
+  if constexpr (!PRE_THR)
+    for (int i = tid; i < kWinBins; i += kChunkThreads) h[i] = 0u;
   // every block kept, or a chunk the finalize pass does not read: nothing to collect
   const bool collect = !(nb <= k || base >= nb);
   if (collect) {
-    __syncthreads();
-    const uint32_t B = row_threshold(smp, n_grp, nb, k, h, out3, smpv);
+    uint32_t B = thr;
+    if constexpr (!PRE_THR) {
+      __syncthreads();
+      B = row_threshold(smp, n_grp, nb, k, h, out3, smpv);
+    }
     uint32_t key[kChunkPer];
     uint32_t flags = 0u;
 #pragma unroll
@@ -585,9 +621,11 @@ hipError_t collect_finalize(const float* scores, int64_t ld, int M, const int64_
   } else if (nb_max > k && M * chunks <= kFusedMaxWorkgroups) {  // collect, and the last chunk of each row finalizes it
     hipLaunchKernelGGL(select_collect_kernel<true>, dim3((unsigned)chunks, (unsigned)M), dim3(kChunkThreads), 0,
                        stream, scores, ld, row_pos, nb_max, k, sel, n_sel, W);
-  } else if (nb_max > k) {  // many rows: collect, then one finalize workgroup per row
-    hipLaunchKernelGGL(select_collect_kernel<false>, dim3((unsigned)chunks, (unsigned)M), dim3(kChunkThreads), 0,
-                       stream, scores, ld, row_pos, nb_max, k, sel, n_sel, W);
+  } else if (nb_max > k) {  // many rows: thresholds, collect, then one finalize workgroup per row
+    hipLaunchKernelGGL(select_threshold_kernel, dim3((unsigned)M), dim3(kChunkThreads), 0, stream, row_pos, nb_max, k,
+                       W);
+    hipLaunchKernelGGL((select_collect_kernel<false, true>), dim3((unsigned)chunks, (unsigned)M), dim3(kChunkThreads),
+                       0, stream, scores, ld, row_pos, nb_max, k, sel, n_sel, W);
     hipLaunchKernelGGL(select_finalize_kernel, dim3((unsigned)M), dim3(kFinThreads), 0, stream, scores, ld,
                        row_pos, nb_max, k, sel, n_sel, W);
   } else {  // every row keeps all its blocks

@@ -17,7 +17,8 @@ constexpr int kCandMax = 4096;                 // candidates the finalize pass h
 // Per-row workspace record (32-bit words, every part 256-byte aligned);
 // nothing in it needs to start at any particular value:
 //   [0, kCtlWords)       word kPathWord: how the last selection of the row went;
-//                        word kArriveWord: chunk arrivals of the selection launch
+//                        word kArriveWord: chunk arrivals of the selection launch;
+//                        word kThrWord: the row's candidate threshold digit
 //   cnt_off + c          candidate count of 4,096-block chunk c
 //   key_off + c*kChunk   candidate keys of chunk c, ascending block order
 //   id_off  + c*kChunk   their block ids
@@ -27,6 +28,10 @@ constexpr int kPathWord = 0;
 // Arrival counter of the row's chunk workgroups in the selection launch:
 // cleared by the pass that writes the row's sample, and by the last arrival.
 constexpr int kArriveWord = 1;
+// The row's candidate threshold digit, when a launch of its own computes it
+// (many rows: the collect workgroups then read one word instead of the
+// row's whole sample).
+constexpr int kThrWord = 2;
 // Selection paths (a diagnostic: every path gives the same exact result).
 enum SelPath : uint32_t {
   kPathAll = 1,         // at most k blocks: all kept
