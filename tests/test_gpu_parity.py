@@ -66,6 +66,25 @@ def test_decode_32k(Q):
     _assert_candidate_path(res, layer)
 
 
+@pytest.mark.parametrize("name,k", [("verify_262k", 1024), ("verify_262k", 1), ("decode_32k", 1024),
+                                    ("decode_32k", 1)])
+def test_budget_extremes(Q, name, k):
+    """The largest budget the library serves (QSA_MAX_K_BLOCKS = 1,024 blocks,
+    4,096 tokens: the attention plans walk twice the slices, the selections
+    keep twice the candidates) and the smallest (one block plus the tail),
+    at full size through the chunked selection (262K) and the one-workgroup
+    selection (32K)."""
+    say("budget extremes", name, "k =", k)
+    d = datagen.gen_layer(name)
+    layer = Layer(d)
+    res = layer.run(k_blocks=k)
+    st = _check_layer(d, res, layer, k=k)
+    nb = (layer.rows.cpu().numpy() + 1) // 4
+    assert np.array_equal(res["n_sel"].cpu().numpy(), np.minimum(nb, k))
+    _assert_candidate_path(res, layer, k=k)
+    say(f"{len(st)} rows; band sizes up to {max(x['band'] for x in st)}")
+
+
 def test_decode_32k_layers_differ(Q):
     say("decode 32k, layer 5")
     d = datagen.gen_layer("decode_32k", layer=5)
