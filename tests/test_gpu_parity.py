@@ -219,15 +219,30 @@ def test_thirteen_rows_two_row_groups(Q):
     _assert_candidate_path(res, layer)
 
 
-def test_many_rows_selection_paths(Q):
-    """288 bf16 rows of one 32K-context sequence.  Rows 0..95 sit in the first
-    2,048 tokens (at most k blocks: all kept), rows 96..191 have zero index
-    queries (every score 0: every block is a candidate and ties at the cut; the
-    lowest ids are kept), rows 192..287 are ordinary.  Every row's selection is
-    the exact top-k of the GPU scores and its path word says how it went."""
-    say("288 rows, selection paths")
-    d = dict(datagen.gen_layer("decode_32k"))
+def _context_prefix(name, n):
+    """The first n tokens of a workload's layer (index keys, K, V)."""
+    d = dict(datagen.gen_layer(name))
+    d["idx"] = np.ascontiguousarray(d["idx"][:n])
+    d["k"] = np.ascontiguousarray(d["k"][:, :n])
+    d["v"] = np.ascontiguousarray(d["v"][:, :n])
+    return d
+
+
+@pytest.mark.parametrize("n_ctx", [32768, 40000, 65536])
+def test_many_rows_selection_paths(Q, n_ctx):
+    """288 bf16 rows of one sequence.  Rows 0..95 sit in the first 2,048
+    tokens (at most k blocks: all kept), rows 96..191 have zero index queries
+    (every score 0: every block is a candidate and ties at the cut; the lowest
+    ids are kept), rows 192..287 are ordinary.  Every row's selection is the
+    exact top-k of the GPU scores and its path word says how it went.  The
+    context picks the selection's form: 8,192 blocks one workgroup per row,
+    10,000 blocks the one-launch collect + finalize (3 chunks x 288 rows),
+    16,384 blocks the separate threshold, collect and finalize launches
+    (4 chunks x 288 rows is more than the one-launch form takes)."""
+    say("288 rows, selection paths, context", n_ctx)
+    d = dict(datagen.gen_layer("decode_32k")) if n_ctx == 32768 else _context_prefix("verify_262k", n_ctx)
     n = d["idx"].shape[0]
+    assert n == n_ctx
     rng = np.random.default_rng(288)
     rows = np.concatenate([rng.integers(0, 2048, 96), rng.integers(8192, n, 96), rng.integers(8192, n, 96)])
     d["rows"] = rows.astype(np.int64)
@@ -236,6 +251,9 @@ def test_many_rows_selection_paths(Q):
     d["idx_q"] = idx_q
     d["q"] = datagen.round_bf16(rng.standard_normal((288, 24, 256)).astype(np.float32))
     layer = Layer(d, prefix_split=n - 4)
+    # the form this context is meant to exercise (4,096-block chunks)
+    chunks = -(-layer.nb_max // 4096)
+    assert {32768: layer.nb_max <= 8192, 40000: chunks == 3, 65536: chunks == 4}[n_ctx], layer.nb_max
     res = layer.run()
     st = _check_layer(d, res, layer, rows=list(range(0, 288, 7)), attn_rows=[0, 100, 200, 287])
     say(st[:3])
