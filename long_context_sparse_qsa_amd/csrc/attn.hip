@@ -1261,9 +1261,10 @@ constexpr long kCUs = 256;
 // has a compute unit of its own; otherwise the fewest waves, up to 8, that
 // fit: a second workgroup on a unit slows both more than a fifth wave does,
 // and fewer waves than four only add split partials to merge.  When even 8
-// waves cannot fit, several tiles per workgroup: as many as keep the grid to
-// one workgroup per unit up to 4 tiles' worth of one-tile workgroups per unit,
-// then as many as keep it to 4 workgroups per unit (prefill).
+// waves cannot fit, several tiles per workgroup: up to 4 units' worth of
+// one-tile workgroups, 4 waves walking as many tiles as keep the grid to one
+// workgroup per unit; beyond that (prefill) 8 waves walking as many tiles as
+// keep it to 4 workgroups per unit.
 AttnPlan attn_plan(int M, int hkv, int k_blocks) {
   const int max_tokens = k_blocks * kBlockTokens + (kBlockTokens - 1);
   const int slices = (max_tokens + 15) / 16;
@@ -1280,14 +1281,21 @@ AttnPlan attn_plan(int M, int hkv, int k_blocks) {
     if (want < 1) want = 1;
     p.tiles_per_split = (int)((tiles + want - 1) / want);
   } else if (rows * tiles > kCUs) {
-    // more one-tile workgroups than compute units (8 waves: one workgroup per
-    // compute unit at a time): walk several tiles per split so that the grid
-    // is one round of workgroups, not two or three rounds of short ones
-    // (measured, 16 rows of batched decode: 24.6 us against 35.2 us; 2, 4 and
-    // 5 tiles per split 28.7, 28.4, 30.3 us)
+    // more one-tile workgroups than compute units: walk several tiles per
+    // split so that the grid is one round of workgroups, not two or three
+    // rounds of short ones, with 4 waves (one per SIMD: a walk's slices are
+    // latency-bound, a SIMD of its own shortens each).  Measured, 16 rows of
+    // batched decode: 23.1 us against 35.2 us for one-tile splits; 8 waves
+    // with 3 tiles per split 24.4 us, 4 waves with 3, 4, 5 or 9 tiles 26.0,
+    // 23.1, 23.2, 30.4 us.
+    p.waves = 4;
+    p.tile_tokens = 64;
+    const int tiles4 = (slices + 3) / 4;
     long want = kCUs / rows;
     if (want < 1) want = 1;
-    p.tiles_per_split = (int)((tiles + want - 1) / want);
+    p.tiles_per_split = (int)((tiles4 + want - 1) / want);
+    p.splits = (tiles4 + p.tiles_per_split - 1) / p.tiles_per_split;
+    return p;
   }
   p.splits = (tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
