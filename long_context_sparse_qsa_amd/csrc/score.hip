@@ -51,9 +51,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroupBlocks = 16;   // blocks per MFMA row group
 constexpr int kChunks = kIndexDim / 16;  // 8 chunks of 16 dims
 constexpr int kGroupsPerWave = 2;
-constexpr int kWavesPerWG = 4;
+// Waves per workgroup (the kernels' WPG): 4 for long rows of one
+// sequence, 2 for rows of at most 16,384 blocks or rows of different
+// sequences (measured: decode at 32K context 4.9 against 6.0 us, batched
+// decode 32.8 against 34.2 us; the 262K verify equal either way).
+constexpr int kWavesLong = 4;
+constexpr int kWavesShort = 2;
+constexpr int64_t kShortRowBlocks = 16384;
 constexpr int kBlocksPerWave = kGroupBlocks * kGroupsPerWave;
-constexpr int kBlocksPerWG = kBlocksPerWave * kWavesPerWG;
 constexpr float kScoreScale = 0.08838834764831845f;  // 1/sqrt(128)
 
 // Index-query elements as loaded (4 per lane per chunk) and as MFMA operands.
@@ -152,7 +157,7 @@ __device__ __forceinline__ void group_scores(const float4 (&a)[kChunks], const f
 // block's pooled key is built in every A row and goes through the scoring
 // waves' MFMA sequence (an output element depends only on its own A row and
 // B column), so the score equals theirs on the stored pooled key.
-template <class EQ, int NSET, int RPG, bool HIST>
+template <class EQ, int NSET, int RPG, bool HIST, int WPG>
 __device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int M,
                                    const int64_t* __restrict__ row_pos, int64_t nb_max, float* __restrict__ scores,
                                    int64_t ld, uint32_t* __restrict__ ws, const AppendArgs& ap) {
@@ -187,9 +192,9 @@ __device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int
   const T* ca = static_cast<const T*>(ap.cache);
   const int64_t rw = sel::row_words(nb_max);
   const int64_t smp_off = sel::sample_off(nb_max);
-  for (; i < ap.n_new; i += kWavesPerWG) {
+  for (; i < ap.n_new; i += WPG) {
     const int64_t cur = pl;
-    pl = load_pos4(i + kWavesPerWG);  // the wave's next token, in flight meanwhile
+    pl = load_pos4(i + WPG);  // the wave's next token, in flight meanwhile
     int64_t pw[kBlockTokens];  // wave-uniform copies
 #pragma unroll
     for (int j = 0; j < kBlockTokens; ++j) {
@@ -244,8 +249,8 @@ __device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int
   }
 }
 
-template <class EQ, int NSET, int RPG, bool HIST, bool APPEND>
-__global__ void __launch_bounds__(kWave * kWavesPerWG)
+template <class EQ, int NSET, int RPG, bool HIST, bool APPEND, int WPG>
+__global__ void __launch_bounds__(kWave * WPG)
 score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
                     const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                     const float* __restrict__ pooled, int n_seq, int64_t capacity,
@@ -261,9 +266,9 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     // (every row group's)
     if (bx < 2) {
       if (bx == 1) {
-        score_fresh_blocks<EQ, NSET, RPG, HIST>(idx_q, M, row_pos, nb_max, scores, ld, ws, ap);
+        score_fresh_blocks<EQ, NSET, RPG, HIST, WPG>(idx_q, M, row_pos, nb_max, scores, ld, ws, ap);
       } else if (blockIdx.y == 0) {
-        for (int e = threadIdx.x; e < ap.n_new * kIndexDim; e += kWave * kWavesPerWG)
+        for (int e = threadIdx.x; e < ap.n_new * kIndexDim; e += kWave * WPG)
           append_token_dim<EQ>(static_cast<const typename EQ::T*>(ap.new_idx), ap.pos, nullptr,
                                static_cast<typename EQ::T*>(ap.cache), ap.pooled, 1, ap.capacity, e / kIndexDim,
                                e % kIndexDim);
@@ -286,7 +291,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   // depend only on nb_max (the host bound), not on the row positions.
   // (a wave past nb_max issues its clamped loads and leaves below: no
   // early branch holds the argument loads back)
-  const int64_t wave_b0 = (int64_t)bx * kBlocksPerWG + wave * kBlocksPerWave;
+  const int64_t wave_b0 = (int64_t)bx * (WPG * kBlocksPerWave) + wave * kBlocksPerWave;
   const int i16 = lane & 15;   // A row (block in group) / B column
   const int kq = lane >> 4;    // k slot 0..3
   int64_t pos_r[RPG];
@@ -384,22 +389,34 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   }
 }
 
-template <class EQ, int NSET, int RPG, bool HIST>
-hipError_t launch_fewrow(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
-                         const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
-                         float* scores, int64_t ld, uint32_t* ws, const AppendArgs* ap, hipStream_t stream) {
+template <class EQ, int NSET, int RPG, bool HIST, int WPG>
+hipError_t launch_fewrow_wpg(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
+                             const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
+                             float* scores, int64_t ld, uint32_t* ws, const AppendArgs* ap, hipStream_t stream) {
+  constexpr int kBlocksPerWG = WPG * kBlocksPerWave;
   const int64_t wgs = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
   if (wgs == 0) return hipSuccess;
   dim3 grid((unsigned)wgs, (unsigned)((M + RPG - 1) / RPG));
   if (ap)
-    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true>), dim3(grid.x + 2, grid.y),
-                       dim3(kWave * kWavesPerWG), 0, stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
+    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true, WPG>), dim3(grid.x + 2, grid.y),
+                       dim3(kWave * WPG), 0, stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
                        capacity, nb_max, scores, ld, ws, *ap);
   else
-    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, false>), grid, dim3(kWave * kWavesPerWG), 0,
+    hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, false, WPG>), grid, dim3(kWave * WPG), 0,
                        stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
                        capacity, nb_max, scores, ld, ws, AppendArgs{});
   return hipGetLastError();
+}
+
+template <class EQ, int NSET, int RPG, bool HIST>
+hipError_t launch_fewrow(const void* idx_q, int M, const int64_t* row_pos, const int32_t* row_seq,
+                         const float* pooled, int n_seq, int64_t capacity, int64_t nb_max,
+                         float* scores, int64_t ld, uint32_t* ws, const AppendArgs* ap, hipStream_t stream) {
+  if (RPG == 1 || nb_max <= kShortRowBlocks)
+    return launch_fewrow_wpg<EQ, NSET, RPG, HIST, kWavesShort>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity,
+                                                               nb_max, scores, ld, ws, ap, stream);
+  return launch_fewrow_wpg<EQ, NSET, RPG, HIST, kWavesLong>(idx_q, M, row_pos, row_seq, pooled, n_seq, capacity,
+                                                            nb_max, scores, ld, ws, ap, stream);
 }
 
 template <class EQ, bool HIST>
