@@ -5,25 +5,31 @@
 // merge of split partials (MTPLX PR #610, "What changes": float32 partials,
 // merged by log-sum-exp, rounded once; rows with no visible key give zeros).
 //
-// Decode / verify kernel: one workgroup (4 waves) per (row, KV head, split).
-// A split walks 64-token tiles of the row's token list (kept blocks in
-// ascending order, then the tail).  Memory round trips are what bound this
-// kernel at decode sizes, so every independent load (row position, kept
-// count, the kept block ids of this split, the segment table) is issued at
-// once, and each lane resolves its own staging rows.  Per tile:
-//   1. each lane resolves 8 of the tile's tokens to K/V rows through the
-//      segment table (segments may cut a 4-token block anywhere) and stages
-//      one 16-byte chunk of each into LDS, once for all 12 query heads: K
-//      row-major with padded rows, V (bf16) interleaved by token pairs;
-//   2. QK: wave w handles heads 3w..3w+2, lane = token; the query row is
-//      wave-uniform (scalar registers) and bf16 pairs go through the packed
-//      dot2 instruction with float32 accumulation;
-//   3. online softmax with base-2 exponentials of logits pre-scaled by log2 e;
-//      bf16 probabilities are packed in token pairs;
-//   4. PV: lane = (dims, 6 heads); for bf16 one dot2 consumes a token pair
-//      of V and of P, float32 accumulation.
-// Split partials (normalised output + lse) go to the workspace and a second
-// kernel merges them; with a single split the output is written directly.
+// Two kernels compute the attention, one grid of (row, KV head, split)
+// workgroups each; split partials (output normalised by its own sum, and its
+// lse) go to the workspace and attn_combine_kernel merges them (a single split
+// writes the output directly).
+//
+// attn_mfma_kernel (bf16, fp8 E4M3 or Q8_0 K/V with bf16 queries): W waves
+// per workgroup, each owning one 16-token slice of every tile of 16 W tokens,
+// with its own online softmax (no workgroup barrier in the slice loop).  QK
+// and P.V run on the matrix cores with the group's 12 query heads as one
+// operand; K rows are loaded straight into the other operand's layout, V is
+// staged through LDS as 4-token quads per dim, and the next slice's loads are
+// in flight during the current slice's softmax and P.V.  The W wave partials
+// are merged by log-sum-exp in LDS.  The plan (attn_plan) picks W, the tiles a
+// split walks and the split count.
+//
+// attn_decode_kernel (float32 K/V): 4 waves over 64-token tiles on the vector
+// ALU.  Each lane resolves 8 of the tile's tokens to K/V rows through the
+// segment table and stages them in LDS once for all 12 query heads; QK with
+// wave w on heads 3w..3w+2 (lane = token, the query row in scalar
+// registers), an online softmax with base-2 exponentials, and P.V with lane =
+// (dims, 6 heads), all in float32.
+//
+// Every independent load (row position, kept count, the kept block ids of
+// the split, the segment table, the queries) is issued at once: memory round
+// trips bound both kernels at decode sizes.
 #include <mutex>
 
 #include "qsa_device.h"
