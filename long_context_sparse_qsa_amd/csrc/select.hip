@@ -30,10 +30,15 @@
 //           than the on-chip list (massive ties) or a row of more than 64
 //           chunks takes an exact radix select over the whole row in the same
 //           workgroup, so the result is exact in every case.
-// Collect and finalize are one launch (up to 1,024 collect workgroups): the
-// finalize of a row starts as soon as its chunks are collected, with no
-// kernel boundary in between.  Measured at the 262K verify: 11.7 us for the
-// selection against 13.4 us as two launches.
+// Three forms, by size:
+//  - rows of at most 8,192 blocks: one workgroup per row does it all
+//    (select_row_kernel): the candidates never leave its LDS;
+//  - up to 1,024 collect workgroups: collect and finalize are one launch, the
+//    finalize of a row starting as soon as its chunks are collected, with no
+//    kernel boundary in between (measured at the 262K verify: 11.7 us against
+//    13.4 us as two launches);
+//  - more (prefill): each row's threshold once (select_threshold_kernel),
+//    then the collect pass reading it, then one finalize workgroup per row.
 //
 // The workspace holds one record per row (sel::row_words); no part of it
 // needs initialising (the pass that writes the sample clears the arrival
