@@ -482,22 +482,30 @@ def test_segments_head_dim_128(Q, seed, nseg):
 
 @pytest.mark.parametrize("quant,seed,nseg,head_dim", [("fp8", 7, [1, 4, 2], 256), ("fp8", 8, [16, 3, 5, 1, 9], 256),
                                                       ("fp8", 9, [2, 13, 1], 128), ("q8", 10, [1, 5, 2], 256),
-                                                      ("q8", 11, [12, 3, 1, 7], 256), ("q8", 12, [3, 1, 16], 128)])
+                                                      ("q8", 11, [12, 3, 1, 7], 256), ("q8", 12, [3, 1, 16], 128),
+                                                      ("fp8", 13, [2, 1, 3, 1, 2, 4, 1, 1, 2, 3, 1, 5, 1, 2, 1, 3], 256),
+                                                      ("q8", 14, [1, 2, 1, 3, 5, 1, 2, 1, 1, 4, 2, 1, 3, 1, 2, 1], 256)])
 def test_segments_quantized(Q, quant, seed, nseg, head_dim):
     """fp8 (E4M3 + f16 row scales) or Q8_0 (int8 + f16 scale per 32 values)
     K/V across several segments, some empty or cutting a block, rows of
-    different sequences in one call (row_seq)."""
+    different sequences in one call (row_seq).  With 16 sequences the
+    attention plan is the 4-wave walk of several tiles per split."""
     say("segments,", quant, "K/V", seed, nseg, head_dim)
     rng = np.random.default_rng(seed)
     ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
     plan, errs = _segmented_case(Q, ctx, nseg, seed, head_dim=head_dim, quant=quant)
     assert plan["splits"] > 1, plan  # split partials merged by the combine
+    if len(nseg) == 16:
+        assert plan["waves"] == 4 and plan["tiles_per_split"] > 1, plan
     say(plan, max(e for e, _ in errs), max(l for _, l in errs))
 
 
 def test_batched_segmented_full_size(Q):
-    """16 sequences, contexts 4,096..131,072, 1..5 segments each (seeded)."""
+    """16 sequences, contexts 4,096..131,072, 1..5 segments each (seeded).
+    The attention plan is the 4-wave walk: 5 tiles of 64 tokens per split."""
     say("batched segmented decode, 16 sequences (full size)")
+    plan = Q.qsa_attn_plan(16, 2, 512)
+    assert plan["waves"] == 4 and plan["tiles_per_split"] == 5 and plan["splits"] == 7, plan
     specs = datagen.batched_specs()
     data = datagen.gen_batched_layer(specs)
     n_seq = len(specs)
