@@ -641,10 +641,13 @@ __device__ __forceinline__ uint2 s8x4_to_bf16x4(uint32_t w) {
 }
 // Four signed bytes times a scale -> four bf16 values (rounded to nearest
 // even by the packed hardware conversion).
+// (c + 128) sc - 128 sc in one fused multiply-add: the same single rounding
+// of the exact product (c + 128 - 128) sc as a subtraction then a multiply.
 __device__ __forceinline__ uint2 s8x4_scaled_bf16x4(uint32_t w, float sc) {
   const uint32_t u = w ^ 0x80808080u;
-  const float a = (ubyte_f(u, 0) - 128.f) * sc, b = (ubyte_f(u, 1) - 128.f) * sc;
-  const float c = (ubyte_f(u, 2) - 128.f) * sc, d = (ubyte_f(u, 3) - 128.f) * sc;
+  const float off = -128.f * sc;  // exact: a power-of-two multiple
+  const float a = fmaf(ubyte_f(u, 0), sc, off), b = fmaf(ubyte_f(u, 1), sc, off);
+  const float c = fmaf(ubyte_f(u, 2), sc, off), d = fmaf(ubyte_f(u, 3), sc, off);
   return make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
 }
 
