@@ -470,7 +470,8 @@ def test_segments_small(Q, seed, nseg):
     _segmented_case(Q, ctx, nseg, seed)
 
 
-@pytest.mark.parametrize("seed,nseg", [(5, [1, 3, 2]), (6, [12, 1, 5, 16])])
+@pytest.mark.parametrize("seed,nseg", [(5, [1, 3, 2]), (6, [12, 1, 5, 16]),
+                                       (15, [1, 2, 3, 1, 2, 1, 4, 1, 2, 1, 1, 3, 2, 1, 5, 1])])
 def test_segments_head_dim_128(Q, seed, nseg):
     """The batched segmented decode at head_dim 128 (MTPLX PR #610, "Tests":
     segments at head_dims 128 and 256)."""
@@ -478,6 +479,20 @@ def test_segments_head_dim_128(Q, seed, nseg):
     rng = np.random.default_rng(seed)
     ctx = [int(x) for x in rng.integers(1500, 9000, size=len(nseg))]
     _segmented_case(Q, ctx, nseg, seed, head_dim=128)
+
+
+@pytest.mark.parametrize("head_dim", [256, 128])
+def test_segments_many_rows_walk(Q, head_dim):
+    """131 sequences, one row each, 1..3 K/V segments: the attention plan is 8
+    waves walking several 128-token tiles per split (the multi-tile walk of
+    the prefill plan, here over segments and rows of different sequences)."""
+    say("segments, 131 sequences, head_dim", head_dim)
+    rng = np.random.default_rng(131 + head_dim)
+    ctx = [int(x) for x in rng.integers(1500, 9000, size=131)]
+    nseg = [int(x) for x in rng.integers(1, 4, size=131)]
+    plan, errs = _segmented_case(Q, ctx, nseg, 131 + head_dim, head_dim=head_dim)
+    assert plan["waves"] == 8 and plan["tiles_per_split"] > 1 and plan["splits"] > 1, plan
+    say(plan, max(e for e, _ in errs), max(l for _, l in errs))
 
 
 @pytest.mark.parametrize("quant,seed,nseg,head_dim", [("fp8", 7, [1, 4, 2], 256), ("fp8", 8, [16, 3, 5, 1, 9], 256),
