@@ -47,6 +47,7 @@ typedef struct ihipStream_t* qsa_stream_t;
 #define QSA_BLOCK_TOKENS 4      /* tokens per pooled block */
 #define QSA_MAX_K_BLOCKS 1024   /* largest supported budget, in blocks */
 #define QSA_MAX_SEGMENTS 16     /* K/V segments per sequence */
+#define QSA_SCORE_SELECT_MAX_BLOCKS ((int64_t)1 << 30) /* largest nb_max of qsa_score_select */
 
 typedef enum {
   QSA_OK = 0,
@@ -310,7 +311,9 @@ int qsa_gathered_attn_noalloc(const void* q, int32_t dtype, int32_t M, int32_t h
  *  idx_q     bf16 [M][4][128]            index queries (one sequence)
  *  M >= 0; row_pos int64 [M]; pooled float32 [nb_max][128] (the sequence's
  *  pooled keys, e.g. the first sequence of qsa_append_pool's buffer)
- *  nb_max    >= max blocks of any row (a host bound)
+ *  nb_max    >= max blocks of any row (a host bound), at most
+ *            QSA_SCORE_SELECT_MAX_BLOCKS (2^30 blocks: block ids are held in
+ *            32-bit signed lanes)
  *  k_blocks  1..QSA_MAX_K_BLOCKS
  *  sel       int32 [M][k_blocks], ascending block ids, -1 padded (written)
  *  n_sel     int32 [M] = min(k_blocks, nb) (written)

@@ -268,7 +268,9 @@ int qsa_score_select(const void* idx_q, int32_t M, const int64_t* row_pos, const
                      int64_t nb_max, int32_t k_blocks, int32_t* sel, int32_t* n_sel,
                      void* workspace, size_t workspace_bytes, qsa_stream_t stream) {
   if (M < 0) return fail(QSA_ERR_ARG, "qsa_score_select: M = %d < 0", M);
-  if (nb_max < 0) return fail(QSA_ERR_ARG, "qsa_score_select: nb_max %lld < 0", (long long)nb_max);
+  if (nb_max < 0 || nb_max > QSA_SCORE_SELECT_MAX_BLOCKS)
+    return fail(QSA_ERR_ARG, "qsa_score_select: nb_max %lld outside [0, %lld]", (long long)nb_max,
+                (long long)QSA_SCORE_SELECT_MAX_BLOCKS);
   if (k_blocks < 1 || k_blocks > QSA_MAX_K_BLOCKS)
     return fail(QSA_ERR_ARG, "qsa_score_select: k_blocks %d outside [1, %d]", k_blocks, QSA_MAX_K_BLOCKS);
   const size_t need = qsa::score_select_workspace_bytes(M, nb_max, k_blocks);

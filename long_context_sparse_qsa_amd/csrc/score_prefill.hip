@@ -43,6 +43,12 @@
 //    work later) and appends the (key, block) pairs to the row's candidate
 //    slots in no particular order; slots past the capacity are dropped (the
 //    count still records them, which sends the row to the exact selection).
+//    The epilogue takes no branch (ballots of the comparisons, a lane write
+//    for the counts, buffer atomics and stores whose masked lanes fall
+//    outside the view), so the whole tile stays one block of straight-line
+//    code and the compiler interleaves the epilogue with the matrix work; a
+//    branch per output row, as a conditional store makes, cuts the loop into
+//    small blocks that the scheduler cannot overlap.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "select_common.h"
@@ -53,6 +59,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 enum PfMode { kPfScores = 0, kPfScoresSample = 1, kPfSampleOnly = 2, kPfEmit = 3 };
 
@@ -61,8 +69,7 @@ struct FlatArgs {
   const uint32_t* thr;
   uint32_t* cnt;
   float* samples;
-  uint32_t* keys;
-  uint32_t* ids;
+  uint32_t* pairs;
   int64_t n_grp;
   int k;
 };
@@ -216,20 +223,39 @@ __device__ __forceinline__ void group_sample(const f32x16_t (&acc)[kPfCg], int64
 }
 
 // Emit mode's record of one 32-block group: the keys of the lane's 8
-// outputs (row group cg, row pair q), which of them are candidates, and
-// (lane L < 16) the candidate count of row L of the wave.
+// outputs (row group cg, row pair q) and (lane L < 16) the candidate count
+// of row L of the wave.  Whether an output is a candidate is recomputed from
+// its key where it is needed.
 struct EmitRec {
-  uint32_t key[kPfCg * 4];
-  uint32_t flags;
+  u32x8_t key;  // a vector value, not an array, so the record stays in registers
   uint32_t run;
 };
 
-// Emit mode's epilogue of one 32-block group: keys, candidate flags (score
-// digit at or above the row's threshold) and per-row counts by ballot.
-__device__ __forceinline__ void group_emit(const f32x16_t (&acc)[kPfCg], int64_t b, bool valid, int h, int lane,
-                                           const int (&nbq)[kPfCg][4], const uint32_t* thr_w, int k, EmitRec& rec) {
-  rec.flags = 0u;
-  rec.run = 0u;
+// Order key of a score of this kernel: the scores are sums of ReLU'd terms
+// (never negative, never -0), where the order key (select_common.h) is the
+// bit pattern with the sign bit set.
+__device__ __forceinline__ uint32_t nonneg_key(float x) { return __float_as_uint(x) | 0x80000000u; }
+
+// Emit mode's candidate test: block b is visible to the row (b < nbe,
+// unsigned; nbe is 0 for rows that keep all their blocks and b is -1, above
+// every nbe, for a group that holds no blocks of this workgroup) and its
+// key's digit reaches the row's threshold digit (key >= thk, the digit
+// shifted into place).  The ballot is taken of each comparison on its own
+// (each is the comparison's own result).
+__device__ __forceinline__ uint64_t cand_ballot(bool vis, bool reach) {
+  return __builtin_amdgcn_ballot_w64(vis) & __builtin_amdgcn_ballot_w64(reach);
+}
+
+// v_writelane (the compiler's intrinsic, which has no builtin here): lane
+// `lane` of the result is the wave-uniform x, the other lanes are v's.
+extern "C" __device__ int qsa_writelane_i32(int x, int lane, int v) __asm("llvm.amdgcn.writelane.i32");
+
+// Emit mode's epilogue of one 32-block group: keys, and each row's
+// candidate count by ballot.  Branch-free, so the compiler can interleave it
+// with the matrix instructions.
+__device__ __forceinline__ void group_emit(const f32x16_t (&acc)[kPfCg], int b, const int (&nbe)[kPfCg][4],
+                                           const uint32_t (&thk)[kPfCg][4], EmitRec& rec) {
+  int run = 0;
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg) {
 #pragma unroll
@@ -237,39 +263,43 @@ __device__ __forceinline__ void group_emit(const f32x16_t (&acc)[kPfCg], int64_t
       float x = relu(acc[cg][4 * q]) + relu(acc[cg][4 * q + 1]);
       x += relu(acc[cg][4 * q + 2]) + relu(acc[cg][4 * q + 3]);
       x *= kScoreScale;
-      const uint32_t key = sel::order_key(x);
-      const int nbr = nbq[cg][q];
-      const bool c = valid && b < nbr && nbr > k && (key >> sel::kDigitShift) >= thr_w[8 * cg + 2 * q + h];
+      const uint32_t key = nonneg_key(x);
       rec.key[cg * 4 + q] = key;
-      rec.flags |= c ? 1u << (cg * 4 + q) : 0u;
-      const uint64_t m = __ballot(c);
-      const uint32_t n0 = (uint32_t)__popcll(m & 0x00000000FFFFFFFFull);  // row 8 cg + 2q
-      const uint32_t n1 = (uint32_t)__popcll(m & 0xFFFFFFFF00000000ull);  // row 8 cg + 2q + 1
-      rec.run += lane == 8 * cg + 2 * q ? n0 : (lane == 8 * cg + 2 * q + 1 ? n1 : 0u);
+      const uint64_t m = cand_ballot((uint32_t)b < (uint32_t)nbe[cg][q], key >= thk[cg][q]);
+      run = qsa_writelane_i32(__popc((uint32_t)m), 8 * cg + 2 * q, run);              // row 8 cg + 2q
+      run = qsa_writelane_i32(__popc((uint32_t)(m >> 32)), 8 * cg + 2 * q + 1, run);  // row 8 cg + 2q + 1
     }
   }
+  rec.run = (uint32_t)run;
 }
 
 // Emit mode: appends a finished group's candidates (lane block b) to their
-// rows' slots from the bases its reservation returned.
-__device__ __forceinline__ void scatter_emit(const EmitRec& rec, uint32_t base, int64_t b, int h, int lane,
-                                             int wrow0_rel, int r0, const FlatArgs& fa) {
-  const uint64_t half = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;  // the lane's row in a ballot
-  const uint64_t lane_lt = (1ull << lane) - 1ull;
+// rows' slots from the bases its reservation returned (lane L < 16: row L's
+// base).  prs views the wave's 16 rows of (key, id) slots; a candidate's
+// slot is its row's base plus the number of candidates of the same row in
+// lower lanes.  Stores of non-candidates and of slots past kFlatCap go to
+// an offset outside the view and are dropped, so no branch is taken.
+__device__ __forceinline__ void scatter_emit(const EmitRec& rec, uint32_t base, int b, int h,
+                                             const int (&nbe)[kPfCg][4], const uint32_t (&thk)[kPfCg][4],
+                                             __amdgpu_buffer_rsrc_t prs) {
+  const uint32_t lower = h ? 0u : ~0u;  // the lower half's ballot bits count for lanes below 32 only
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rw8 = 8 * cg + 2 * q + h;
-      const int64_t r = r0 + wrow0_rel + rw8;
-      const uint32_t pos = (uint32_t)__shfl((int)base, rw8, kWave);
-      const bool c = (rec.flags >> (cg * 4 + q)) & 1u;
-      const uint64_t mk = __ballot(c) & half;
-      const uint32_t p = pos + (uint32_t)__popcll(mk & lane_lt);
-      if (c && p < (uint32_t)sel::kFlatCap) {
-        fa.keys[r * sel::kFlatCap + p] = rec.key[cg * 4 + q];
-        fa.ids[r * sel::kFlatCap + p] = (uint32_t)b;
-      }
+      const uint32_t key = rec.key[cg * 4 + q];
+      const bool vis = (uint32_t)b < (uint32_t)nbe[cg][q], reach = key >= thk[cg][q];
+      const uint64_t m = cand_ballot(vis, reach);
+      // rank among the lane's half (row) of the ballot: the upper lanes
+      // count no lower-half bits (lanes below 32 see no upper-half bits)
+      const uint32_t rank =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m & lower, 0u));
+      const uint32_t p = (uint32_t)__builtin_amdgcn_ds_bpermute(rw8 * 4, (int)base) + rank;
+      const bool keep = vis & reach & (p < (uint32_t)sel::kFlatCap);
+      const u32x2_t v = {key, (uint32_t)b};
+      __builtin_amdgcn_raw_buffer_store_b64(v, prs, keep ? (int)((rw8 * sel::kFlatCap + (int)p) * 8) : kBufferDrop,
+                                            0, 0);
     }
   }
 }
@@ -351,12 +381,20 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
   stage_tile(pk, tid, planes0);
   load_tile<MODE>(pooled, nb_max, t_begin + 1 < t_end ? t_begin + 1 : t_end - 1, tid, pk);
   __syncthreads();
+  // each (row group, row pair)'s visible block count; in emit mode 0 for
+  // rows that keep all their blocks (they have no candidates), and the
+  // row's threshold digit shifted into key position
   int nbq[kPfCg][4];
+  uint32_t thk[kPfCg][4];
 #pragma unroll
   for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) nbq[cg][q] = nb_sh[wave * kPfRowsPerWave + 8 * cg + 2 * q + h];
-  const uint32_t* thr_w = thr_sh + wave * kPfRowsPerWave;  // emit mode: the wave's row thresholds (LDS)
+    for (int q = 0; q < 4; ++q) {
+      const int rr = wave * kPfRowsPerWave + 8 * cg + 2 * q + h;
+      const int nb = nb_sh[rr];
+      nbq[cg][q] = EMIT && nb <= fa.k ? 0 : nb;
+      thk[cg][q] = EMIT ? thr_sh[rr] << sel::kDigitShift : 0u;
+    }
 
   f32x16_t accA[kPfCg], accB[kPfCg];
 #pragma unroll
@@ -368,12 +406,19 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
   // group, recB: its second)
   EmitRec recA{}, recB{};
   uint32_t baseA = 0u;
-  // reserve a finished record's slots: one atomic per row (lane L < 16: row L)
+  // the wave's rows' candidate counters and (key, id) slots; rows past M
+  // are outside both views
+  const int64_t wrows = EMIT ? (M - wrow0 < 0 ? 0 : M - wrow0 < kPfRowsPerWave ? M - wrow0 : kPfRowsPerWave) : 0;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(EMIT ? fa.cnt + wrow0 : nullptr, 0,
+                                                                       (int)(wrows * 4), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      EMIT ? fa.pairs + wrow0 * sel::kFlatCap * 2 : nullptr, 0, (int)(wrows * sel::kFlatCap * 8), kBufferWord3);
+  // reserve a finished record's slots: one atomic per row (lane L < 16: row
+  // L; the other lanes' atomics are dropped and return zero)
   auto reserve = [&](const EmitRec& rec) -> uint32_t {
-    const int64_t r = wrow0 + lane;
-    uint32_t base = 0u;
-    if (lane < kPfRowsPerWave && r < M && rec.run > 0u) base = atomicAdd(fa.cnt + r, rec.run);
-    return base;
+    const bool act = lane < kPfRowsPerWave && rec.run > 0u;
+    return (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)rec.run, crs, act ? lane * 4 : kBufferDrop,
+                                                                   0, 0);
   };
   // one tile: matrix reads from cur_planes, staging (of tile t+1) into nxt
   auto tile = [&](int64_t t, const uint32_t (*cur_planes)[kPfBlocks * kPfRowWords],
@@ -381,10 +426,14 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
     const int64_t b0 = t * kPfBlocks;
     group_mfma(cur_planes, 0, j32, h, aq, accA);
     uint32_t baseB = 0u;
+    // emit mode: the lane's blocks of the previous tile's groups, or none
+    // (-1) on the run's first tile (nb_max <= 2^30: the entry point)
+    const int bpA = t > t_begin ? (int)b0 - kPfBlocks + j32 : -1;
+    const int bpB = t > t_begin ? (int)b0 - 32 + j32 : -1;
     if constexpr (EMIT) {
-      group_emit(accB, b0 - 32 + j32, t > t_begin, h, lane, nbq, thr_w, fa.k, recB);  // previous tile, group 1
+      group_emit(accB, bpB, nbq, thk, recB);  // previous tile, group 1
       baseB = reserve(recB);
-      if (t > t_begin) scatter_emit(recA, baseA, b0 - kPfBlocks + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+      scatter_emit(recA, baseA, bpA, h, nbq, thk, prs);
     } else if constexpr (SAMPLE) {
       group_sample(accB, b0 - 32 + j32, t > t_begin, h, nbq, srs, fa.n_grp);
     } else {
@@ -392,9 +441,9 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
     }
     group_mfma(cur_planes, 1, j32, h, aq, accB);
     if constexpr (EMIT) {
-      group_emit(accA, b0 + j32, true, h, lane, nbq, thr_w, fa.k, recA);
+      group_emit(accA, (int)b0 + j32, nbq, thk, recA);
       baseA = reserve(recA);
-      if (t > t_begin) scatter_emit(recB, baseB, b0 - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+      scatter_emit(recB, baseB, bpB, h, nbq, thk, prs);
     } else if constexpr (SAMPLE) {
       group_sample(accA, b0 + j32, true, h, nbq, srs, fa.n_grp);
     } else {
@@ -415,10 +464,11 @@ score_prefill_pipe_kernel(const uint16_t* __restrict__ idx_q, int M, const int64
   }
   // last tile, group 1
   if constexpr (EMIT) {
-    scatter_emit(recA, baseA, t * kPfBlocks - kPfBlocks + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
-    group_emit(accB, t * kPfBlocks - 32 + j32, true, h, lane, nbq, thr_w, fa.k, recB);
+    const int bl = (int)(t * kPfBlocks) - kPfBlocks + j32;
+    scatter_emit(recA, baseA, bl, h, nbq, thk, prs);
+    group_emit(accB, bl + 32, nbq, thk, recB);
     const uint32_t base = reserve(recB);
-    scatter_emit(recB, base, t * kPfBlocks - 32 + j32, h, lane, wave_u * kPfRowsPerWave, r0, fa);
+    scatter_emit(recB, base, bl + 32, h, nbq, thk, prs);
   } else if constexpr (SAMPLE) {
     group_sample(accB, t * kPfBlocks - 32 + j32, true, h, nbq, srs, fa.n_grp);
   } else {
@@ -478,8 +528,7 @@ hipError_t launch_score_prefill_flat(const void* idx_q, int M, const int64_t* ro
   fa.thr = ws + L.thr;
   fa.cnt = ws + L.cnt;
   fa.samples = reinterpret_cast<float*>(ws + L.samples);
-  fa.keys = ws + L.keys;
-  fa.ids = ws + L.ids;
+  fa.pairs = ws + L.pairs;
   fa.n_grp = sel::sample_groups(nb_max);
   fa.k = k_blocks;
   if (emit) {

@@ -53,11 +53,11 @@ __host__ __device__ constexpr int64_t row_words(int64_t nb_max) {
 // Memory-flat score -> top-k (many rows, no score matrix): per-call
 // workspace, in 32-bit words.  Per row: its threshold digit, its candidate
 // count (an atomic append counter), the path its selection took, its score
-// sample (one per 16-block group) and kFlatCap candidate (key, id) slots in
-// no particular order.
+// sample (one per 16-block group) and kFlatCap candidate slots in no
+// particular order, each slot a (key, block id) pair of two words.
 constexpr int kFlatCap = 4096;
 struct FlatLayout {
-  int64_t thr, cnt, path, samples, keys, ids, total;
+  int64_t thr, cnt, path, samples, pairs, total;
 };
 __host__ __device__ inline FlatLayout flat_layout(int64_t M, int64_t nb_max) {
   FlatLayout L;
@@ -70,10 +70,8 @@ __host__ __device__ inline FlatLayout flat_layout(int64_t M, int64_t nb_max) {
   o += round64(M);
   L.samples = o;
   o += round64(M * sample_groups(nb_max));
-  L.keys = o;
-  o += M * kFlatCap;
-  L.ids = o;
-  o += M * kFlatCap;
+  L.pairs = o;
+  o += M * kFlatCap * 2;
   L.total = o;
   return L;
 }

@@ -145,13 +145,13 @@ flat_finalize_kernel(const uint16_t* __restrict__ idx_q, const int64_t* __restri
   int32_t* __restrict__ out = sel + (int64_t)m * k;
   const uint16_t* q_row = idx_q + (int64_t)m * kIndexHeads * kIndexDim;
   // every slot and the count are loaded at once; the count decides which are live
-  const uint32_t* K = ws + L.keys + (int64_t)m * kFlatCap;
-  const uint32_t* I = ws + L.ids + (int64_t)m * kFlatCap;
+  const uint2* P = reinterpret_cast<const uint2*>(ws + L.pairs) + (int64_t)m * kFlatCap;
   uint32_t kk[kFinPer], ii[kFinPer];
 #pragma unroll
   for (int e = 0; e < kFinPer; ++e) {
-    kk[e] = K[e * kFinThreads + tid];
-    ii[e] = I[e * kFinThreads + tid];
+    const uint2 kv = P[e * kFinThreads + tid];
+    kk[e] = kv.x;
+    ii[e] = kv.y;
   }
   const uint32_t n_cand = ws[L.cnt + m];
   const int64_t nb = clamp_nb(row_pos[m], nb_max);

@@ -238,6 +238,7 @@ def _ssel(M=2, nb=100, k=16, ws=FAKE, wsb=1 << 30, idx=FAKE):
 @pytest.mark.parametrize("kw,code,word", [
     (dict(M=-1), ERR_ARG, "M ="),
     (dict(nb=-1), ERR_ARG, "nb_max"),
+    (dict(nb=(1 << 30) + 1), ERR_ARG, "nb_max"),
     (dict(k=0), ERR_ARG, "k_blocks"),
     (dict(k=5000), ERR_ARG, "k_blocks"),
     (dict(wsb=100), ERR_WS, "workspace"),
@@ -253,7 +254,7 @@ def test_score_select_validation(kw, code, word):
 
 def test_score_select_workspace_bytes():
     # per row: threshold, count, path (rounded to 64 rows), the sample (one
-    # word per 16 blocks, rounded to 64 words), 4,096 key and id slots
+    # word per 16 blocks, rounded to 64 words), 4,096 (key, id) slots
     m, nb = 2048, 50512
     n_grp = -(-nb // 16)
     words = 3 * 2048 + (-(-(m * n_grp) // 64) * 64) + 2 * m * 4096
