@@ -489,12 +489,13 @@ def cpu_baseline(wl_name: str = "verify_262k", budget_s: float = 10.0, table: bo
 
 # ------------------------------------------------------------------ legs
 
-def quant_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us, fmt="fp8"):
+def quant_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us, fmt="fp8", flat=False):
     """The same layers with K/V in a quantized state -- fp8 (E4M3 codes + f16
     scale per head and token) or q8 (Q8_0: int8 codes + f16 scale per 32
     values) -- quantized on the device from the bf16 K/V: the whole step
     through graphs, the attention launch beside the bf16 one, and the
-    quantize launch that writes one step's new K (or V) rows."""
+    quantize launch that writes one step's new K (or V) rows.  ``flat``: the
+    step selects through the memory-flat entry point (sh["ws_flat"])."""
     import torch
 
     q8 = fmt == "q8"
@@ -511,7 +512,7 @@ def quant_leg(Q, L, groups, sh, nb_max, wl, args, attn_bf16_us, fmt="fp8"):
         ly.kv_bf16, ly.kv = ly.kv, Q.KvSegments.single(ly.k8, ly.v8, wl.n_ctx, ly.ks, ly.vs)
         ly.new_k = ly.k[:, ly.rows[0]:ly.rows[0] + min(wl.m, 4)].contiguous()  # new K rows [hkv, T, D]
     torch.cuda.synchronize()
-    ms = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager)
+    ms = timed_sweeps(Q, groups, sh, nb_max, wl, args.steps, args.warmup, args.eager, flat=flat)
     attn_us = per_launch_us(Q, L, sh, nb_max, wl, "attn")
     # one step's K write: M rows x hkv heads quantized into the cache
     t0 = int(wl.rows[0])
@@ -586,7 +587,11 @@ def prefill_leg(Q, args, dev):
     """The 2,048-row prefill chunk at 200,000..202,047: rows/s per layer and
     the matrix-core utilisation of its scoring pass, its attention and the
     whole path, on algorithmic flops (and, for the scoring pass, on the bf16
-    flops its three-plane pooled keys issue)."""
+    flops its three-plane pooled keys issue).  The step selects through the
+    memory-flat entry point (qsa_score_select: no score matrix, and the faster
+    of the two); the materialized path (qsa_score_blocks + qsa_select_topk) is
+    timed beside it, and its score-only kernel gives the scoring pass's
+    matrix-core figures."""
     import torch
 
     import datagen
@@ -604,9 +609,31 @@ def prefill_leg(Q, args, dev):
     score_flops = pairs * 4 * 128 * 2                        # float32-equivalent products of the scores
     tok = kept_tokens(wl.rows, wl.k_blocks)
     attn_flops = tok * wl.hq * wl.head_dim * 2 * 2            # QK and PV over the kept tokens
-    layer_us = ms * 1e3 / args.layers
     tf = lambda f, us: f / (us * 1e-6) / 1e12  # noqa: E731
-    rec = leg_record("prefill", wl.m, args.layers, 1, ms, path_bytes(wl, wl.rows, nb_max), kt)
+    pbytes = path_bytes(wl, wl.rows, nb_max)
+    ld = -(-nb_max // 4) * 4
+    matrix_bytes = wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
+    rec = leg_record("prefill", wl.m, args.layers, 1, ms, pbytes, kt)
+    rec["selection"] = "materialized (qsa_score_blocks + qsa_select_topk)"
+    flat = None
+    if not args.no_flat:
+        sh2 = dict(sh)
+        wsb = Q.qsa_score_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
+        sh2["ws_flat"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        msf = timed_sweeps(Q, groups, sh2, nb_max, wl, steps, warm, args.eager, flat=True)
+        flat_us = per_launch_us(Q, L, sh2, nb_max, wl, "flat", reps=1, flat=True)
+        flat = {"ms_per_step": msf, "score_select_us": flat_us, "workspace_bytes": wsb}
+        if msf < ms:  # the step's figure is the faster path's
+            sh = sh2
+            mat = {"workload": "prefill, materialized scores", "value": rec["value"], "ms_per_step": ms,
+                   "layer_us": rec["layer_us"], "kernel_us": rec["kernel_us"],
+                   "score_plus_select_us": round(kt["score"] + kt["select"], 1),
+                   "score_matrix_bytes": matrix_bytes}
+            rec = leg_record("prefill", wl.m, args.layers, 1, msf, pbytes,
+                             {"append": kt["append"], "score_select": flat_us, "attn": kt["attn"]})
+            rec["selection"] = "memory-flat (qsa_score_select)"
+            rec["materialized"] = mat
+    layer_us = rec["layer_us"]
     # the gathered K/V above is counted per row (8.6 GB); rows share blocks, so
     # the unique K/V is far less (at most the layer's 202,048 tokens)
     rec["path"]["unique_kv_bytes"] = wl.n_ctx * wl.hkv * 2 * wl.head_dim * 2
@@ -615,7 +642,7 @@ def prefill_leg(Q, args, dev):
                            "same 413.8 MB run at ~7.7 TB/s)")
     rec["mfma"] = {
         "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-        "scoring": {"kernel": "score_prefill_pipe_kernel", "launch_us": kt["score"],
+        "scoring": {"kernel": "score_prefill_pipe_kernel (score-only mode)", "launch_us": kt["score"],
                     "alg_flops": score_flops, "alg_tflops": tf(score_flops, kt["score"]),
                     "alg_frac": tf(score_flops, kt["score"]) / MFMA_BF16_PEAK_TFLOPS,
                     "issued_bf16_flops": 3 * score_flops,
@@ -628,25 +655,19 @@ def prefill_leg(Q, args, dev):
         "path": {"alg_flops": score_flops + attn_flops, "alg_tflops": tf(score_flops + attn_flops, layer_us),
                  "alg_frac": tf(score_flops + attn_flops, layer_us) / MFMA_BF16_PEAK_TFLOPS},
     }
-    if not args.no_flat:
-        sh2 = dict(sh)
-        wsb = Q.qsa_score_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)
-        sh2["ws_flat"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        msf = timed_sweeps(Q, groups, sh2, nb_max, wl, steps, warm, args.eager, flat=True)
-        flat_us = per_launch_us(Q, L, sh2, nb_max, wl, "flat", reps=1, flat=True)
-        ld = -(-nb_max // 4) * 4
-        rec["flat"] = {"workload": "prefill memory-flat select", "value": wl.m * args.layers / (msf / 1e3),
-                       "ms_per_step": msf, "layer_us": msf * 1e3 / args.layers,
-                       "score_select_us": round(flat_us, 1),
+    if flat is not None:
+        fus = flat["score_select_us"]
+        rec["flat"] = {"workload": "prefill memory-flat select", "value": wl.m * args.layers / (flat["ms_per_step"] / 1e3),
+                       "ms_per_step": flat["ms_per_step"], "layer_us": flat["ms_per_step"] * 1e3 / args.layers,
+                       "score_select_us": round(fus, 1),
                        "score_plus_select_us": round(kt["score"] + kt["select"], 1),
-                       "workspace_bytes": wsb,
-                       "score_matrix_bytes": wl.m * ld * 4 + Q.qsa_select_workspace_bytes(wl.m, nb_max, wl.k_blocks)}
-        del sh2
-        free()
+                       "scoring_alg_frac": tf(score_flops, fus) / MFMA_BF16_PEAK_TFLOPS,
+                       "workspace_bytes": flat["workspace_bytes"], "score_matrix_bytes": matrix_bytes}
     for fmt in ("fp8", "q8"):
         if fmt in args.legs:
             rec[fmt] = quant_leg(Q, L, groups, sh, nb_max, wl,
-                                 argparse.Namespace(**{**vars(args), "steps": steps, "warmup": warm}), kt["attn"], fmt)
+                                 argparse.Namespace(**{**vars(args), "steps": steps, "warmup": warm}), kt["attn"], fmt,
+                                 flat="ws_flat" in sh)
     del L, sh, groups
     free()
     return rec
