@@ -160,17 +160,23 @@ __device__ __forceinline__ void group_mfma(const uint32_t (*planes)[kPfBlocks * 
   for (int cg = 0; cg < kPfCg; ++cg)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[cg][e] = 0.f;
+  // B operand of step i = (k-step s, plane pl): block bg*32 + j32, dims
+  // 16 s + 8 h .. + 7 of plane pl; step i + 1's is read before step i's
+  // matrix instructions issue, so the LDS latency overlaps them
+  const uint32_t* bsrc = &planes[0][(bg * 32 + j32) * kPfRowWords + 4 * h];
+  auto bload = [&](int i) {
+    const int s = i / 3, pl = i % 3;
+    return *reinterpret_cast<const uint4*>(bsrc + pl * (kPfBlocks * kPfRowWords) + 8 * s);
+  };
+  uint4 bv = bload(0);
 #pragma unroll
-  for (int s = 0; s < kPfKs; ++s) {
+  for (int i = 0; i < kPfKs * 3; ++i) {
+    const uint4 bn = i + 1 < kPfKs * 3 ? bload(i + 1) : bv;
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
-      // B operand: block bg*32 + j32, dims 16 s + 8 h .. + 7 of plane pl
-      const uint4 bv = *reinterpret_cast<const uint4*>(&planes[pl][(bg * 32 + j32) * kPfRowWords + (16 * s + 8 * h) / 2]);
-#pragma unroll
-      for (int cg = 0; cg < kPfCg; ++cg)
-        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][s]),
-                                                         __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
-    }
+    for (int cg = 0; cg < kPfCg; ++cg)
+      acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[cg][i / 3]),
+                                                       __builtin_bit_cast(bf16x8_t, bv), acc[cg], 0, 0, 0);
+    bv = bn;
   }
 }
 
