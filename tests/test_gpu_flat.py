@@ -155,3 +155,38 @@ def test_flat_small_budget_and_ties_at_the_cut(Q):
     s_ = sel.cpu().numpy()
     assert all(np.array_equal(s_[i], np.concatenate([[50], np.arange(100, 163)])) for i in range(3)), s_[:, :8]
     say(check_layer(d, res, layer, k=k, attn_rows=[]))
+
+
+def test_flat_every_block_a_candidate(Q):
+    """2,048 short rows at positions 2,100..4,147 (525..1,037 blocks): rows
+    whose sample is too small to set a threshold make every visible block a
+    candidate, so a row's candidate count must equal its block count.  Every
+    scoring workgroup's run (one or two 64-block tiles here: 17 tiles over 16
+    runs per 128-row tile) starts with an empty record for the group before
+    its first, which must add no candidate."""
+    say("flat select, 2048 short rows where every block is a candidate")
+    base = datagen.gen_layer("decode_32k")
+    d = dict(base)
+    rng = np.random.default_rng(31)
+    m = 2048
+    rows = np.arange(2100, 2100 + m, dtype=np.int64)
+    d["rows"] = rows
+    d["idx_q"] = datagen.round_bf16(rng.standard_normal((m, 4, 128)).astype(np.float32))
+    d["q"] = datagen.round_bf16(rng.standard_normal((m, 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=32768)
+    k = layer.wl.k_blocks
+    n_tiles = -(-layer.nb_max // 64)
+    runs = -(-256 // -(-m // 128))  # the scorer's runs per 128-row tile
+    assert n_tiles > runs, (n_tiles, runs)  # some runs hold two tiles
+    res = layer.run()
+    sel, n_sel, paths, ws = _flat(Q, layer, k)
+    assert np.array_equal(paths, _want_paths(layer, k)), np.unique(paths, return_counts=True)
+    r64 = -(-m // 64) * 64
+    words = ws.view(torch.int32).cpu().numpy().view(np.uint32)
+    thr, cnt = words[:m], words[r64:r64 + m]
+    nb = (rows + 1) // 4
+    every = (thr == 0) & (nb > k)
+    assert every.sum() > 100, int(every.sum())
+    assert np.array_equal(cnt[every], nb[every]), (cnt[every][:8], nb[every][:8])
+    assert torch.equal(n_sel, res["n_sel"]) and torch.equal(sel, res["sel"])
+    say(f"{int(every.sum())} rows with every block a candidate")
