@@ -10,7 +10,10 @@ are interleaved with eager steps and with eager writes over every output, and
 each replay is compared with the eager result bit for bit.  The step is the
 one the benchmark captures: the append folded into the scoring launch (the
 rows' own last tokens appended again, which rewrites the same bytes), the
-prepared selection, the gathered attention with its split merge.
+prepared selection, the gathered attention with its split merge; for the
+prefill chunk also the memory-flat step (the append launch, then the
+memory-flat score + select, whose workspace needs no initialisation either:
+its threshold launch clears each row's candidate counter).
 """
 import math
 import sys
@@ -40,11 +43,12 @@ def Q():
 
 
 class Step:
-    """Buffers and enqueue function of one layer step."""
+    """Buffers and enqueue function of one layer step; ``flat``: the append
+    launch, then the memory-flat score + select entry point."""
 
-    def __init__(self, Q, d, layer):
+    def __init__(self, Q, d, layer, flat=False):
         wl = d["workload"]
-        self.Q, self.layer, self.wl = Q, layer, wl
+        self.Q, self.layer, self.wl, self.flat = Q, layer, wl, flat
         n = d["idx"].shape[0]
         self.new = to_dev(d["idx"][n - 4:], wl.dtype).contiguous()
         self.pos = torch.arange(n - 4, n, dtype=torch.int64, device=DEV)
@@ -58,6 +62,8 @@ class Step:
         wsb = Q.qsa_select_workspace_bytes(m, layer.nb_max, k)
         # the selection workspace starts as garbage and is never cleared again
         self.ws_sel = torch.randint(0, 255, (max(wsb, 1),), dtype=torch.uint8, device=DEV)
+        wsf = Q.qsa_score_select_workspace_bytes(m, layer.nb_max, k) if flat else 1
+        self.ws_flat = torch.randint(0, 255, (max(wsf, 1),), dtype=torch.uint8, device=DEV)
         wsa = Q.qsa_attn_workspace_bytes(m, wl.hq, wl.head_dim, k)
         self.ws_attn = torch.empty(max(wsa, 1), dtype=torch.uint8, device=DEV)
 
@@ -71,9 +77,14 @@ class Step:
 
     def enqueue(self):
         Q, ly = self.Q, self.layer
-        Q.qsa_append_score(self.new, self.pos, ly.idx_cache, ly.pooled, ly.idx_q, ly.rows, self.scores, ly.nb_max,
-                           sel_workspace=self.ws_sel)
-        Q.qsa_select_topk(self.scores, ly.rows, ly.nb_max, self.k, self.sel, self.n_sel, self.ws_sel, prepared=True)
+        if self.flat:
+            Q.qsa_append_pool(self.new, self.pos, ly.idx_cache, ly.pooled)
+            Q.qsa_score_select(ly.idx_q, ly.rows, ly.pooled, ly.nb_max, self.k, self.sel, self.n_sel, self.ws_flat)
+        else:
+            Q.qsa_append_score(self.new, self.pos, ly.idx_cache, ly.pooled, ly.idx_q, ly.rows, self.scores,
+                               ly.nb_max, sel_workspace=self.ws_sel)
+            Q.qsa_select_topk(self.scores, ly.rows, ly.nb_max, self.k, self.sel, self.n_sel, self.ws_sel,
+                              prepared=True)
         Q.qsa_gathered_attn(ly.q, ly.rows, ly.kv, self.sel, self.n_sel, self.out, self.lse, self.wl.hkv,
                             scale=1.0 / math.sqrt(self.wl.head_dim), workspace=self.ws_attn)
 
@@ -88,13 +99,14 @@ def same(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
-@pytest.mark.parametrize("name", ["verify_262k", "decode_32k", "prefill"])
-def test_graph_replays_equal_eager(Q, name):
-    say("graph replay vs eager,", name)
+@pytest.mark.parametrize("name,flat", [("verify_262k", False), ("decode_32k", False), ("prefill", False),
+                                       ("prefill", True)])
+def test_graph_replays_equal_eager(Q, name, flat):
+    say("graph replay vs eager,", name, "memory-flat selection" if flat else "")
     d = datagen.gen_layer(name)
     n = d["idx"].shape[0]
     layer = Layer(d, prefix_split=n - 4)
-    st = Step(Q, d, layer)
+    st = Step(Q, d, layer, flat=flat)
     st.clobber()
     st.enqueue()
     ref = st.snapshot()
