@@ -526,16 +526,15 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
 }
 
 // E4M3 codes -> bf16.  Every E4M3 value (4 significant bits, exponents
-// 2^-9 .. 2^8) is exact in bf16, so the hardware conversion to float32
-// followed by dropping the low 16 bits loses nothing.
-__device__ __forceinline__ uint32_t bf16_pair_of(f32x2_t v) {
-  return __builtin_amdgcn_perm(__float_as_uint(v.y), __float_as_uint(v.x), 0x07060302u);
+// 2^-9 .. 2^8) is exact in bf16; gfx950 converts two codes to a bf16 pair
+// in one instruction (its scale operand 1: no scaling).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
 }
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  return make_uint4(bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false)),
-                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true)),
-                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false)),
-                    bf16_pair_of(__builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true)));
+  return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                    fp8x2_to_bf16x2<true>(w1));
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
