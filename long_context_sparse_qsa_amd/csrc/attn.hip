@@ -627,26 +627,22 @@ struct MfmaLds {
 // scale per row, Q8_0 int8 codes with one f16 scale per 32 values.
 constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvQ8 = 2;
 
+// Byte i of w as a signed integer, in float32: one conversion that reads the
+// byte with sign extension (the compiler's sub-dword operand select).
+__device__ __forceinline__ float sbyte_f(uint32_t w, int i) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * i)); }
 // Four signed bytes (one word) -> four bf16 values, exactly (|c| <= 128 fits
-// bf16's 8-bit significand): the unsigned-byte conversions of c + 128 (one
-// instruction each), minus 128, then the high halves of the float32 results.
-__device__ __forceinline__ float ubyte_f(uint32_t u, int i) { return (float)((u >> (8 * i)) & 0xffu); }
+// bf16's 8-bit significand): the high halves of the float32 conversions.
 __device__ __forceinline__ uint2 s8x4_to_bf16x4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  const float a = ubyte_f(u, 0) - 128.f, b = ubyte_f(u, 1) - 128.f;
-  const float c = ubyte_f(u, 2) - 128.f, d = ubyte_f(u, 3) - 128.f;
+  const float a = sbyte_f(w, 0), b = sbyte_f(w, 1), c = sbyte_f(w, 2), d = sbyte_f(w, 3);
   return make_uint2(__builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u),
                     __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x07060302u));
 }
-// Four signed bytes times a scale -> four bf16 values (rounded to nearest
-// even by the packed hardware conversion).
-// (c + 128) sc - 128 sc in one fused multiply-add: the same single rounding
-// of the exact product (c + 128 - 128) sc as a subtraction then a multiply.
+// Four signed bytes times a scale -> four bf16 values: the float32 product
+// (one rounding of the exact c sc), then the packed hardware conversion
+// (rounded to nearest even).
 __device__ __forceinline__ uint2 s8x4_scaled_bf16x4(uint32_t w, float sc) {
-  const uint32_t u = w ^ 0x80808080u;
-  const float off = -128.f * sc;  // exact: a power-of-two multiple
-  const float a = fmaf(ubyte_f(u, 0), sc, off), b = fmaf(ubyte_f(u, 1), sc, off);
-  const float c = fmaf(ubyte_f(u, 2), sc, off), d = fmaf(ubyte_f(u, 3), sc, off);
+  const float a = sbyte_f(w, 0) * sc, b = sbyte_f(w, 1) * sc;
+  const float c = sbyte_f(w, 2) * sc, d = sbyte_f(w, 3) * sc;
   return make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
 }
 
