@@ -116,7 +116,8 @@ int qsa_append_pool(const void* new_idx, int32_t dtype, int32_t n_new,
  * heads, sum of ReLU'd dot products, scaled by 1/sqrt(128)) and section 03
  * (a few-row variant for <= 8 rows and a 16-row variant for prefill).
  *
- *  idx_q    [M][4][128] dtype           index queries of the rows
+ *  idx_q    [M][4][128] dtype           index queries of the rows, 16-byte
+ *                                       aligned
  *  M        >= 0 rows (0: no-op)
  *  row_pos  int64 [M]                    absolute position of each row
  *  row_seq  int32 [M] or NULL            sequence of each row (NULL: all 0;

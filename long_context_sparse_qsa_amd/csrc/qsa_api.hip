@@ -80,6 +80,7 @@ int qsa_score_blocks(const void* idx_q, int32_t dtype, int32_t M, const int64_t*
   if (M == 0 || nb_max == 0) return ok();
   if (!idx_q || !row_pos || !pooled || !scores)
     return fail(QSA_ERR_ARG, "qsa_score_blocks: null pointer (idx_q, row_pos, pooled or scores)");
+  if ((uintptr_t)idx_q & 15u) return fail(QSA_ERR_ARG, "qsa_score_blocks: idx_q must be 16-byte aligned");
   return launch_status(qsa::launch_score_blocks(idx_q, dtype, M, row_pos, row_seq, pooled, n_seq,
                                                 capacity, nb_max, scores, ld,
                                                 static_cast<uint32_t*>(sel_workspace), (hipStream_t)stream),
@@ -114,6 +115,7 @@ int qsa_append_score(const void* new_idx, int32_t n_new, const int64_t* new_pos,
     return fail(QSA_ERR_ARG, "qsa_append_score: null pointer (new_idx, new_pos, idx_cache or pooled)");
   if (M > 0 && nb_max > 0 && (!idx_q || !row_pos || !pooled || !scores))
     return fail(QSA_ERR_ARG, "qsa_append_score: null pointer (idx_q, row_pos, pooled or scores)");
+  if ((uintptr_t)idx_q & 15u) return fail(QSA_ERR_ARG, "qsa_append_score: idx_q must be 16-byte aligned");
   return launch_status(qsa::launch_append_score(new_idx, n_new, new_pos, idx_cache, pooled, capacity, idx_q, dtype,
                                                 M, row_pos, nb_max, scores, ld,
                                                 static_cast<uint32_t*>(sel_workspace), (hipStream_t)stream),

@@ -125,6 +125,60 @@ __device__ __forceinline__ void q_operand(const typename QRaw<EQ>::T (&qraw)[NSE
   }
 }
 
+// The scoring waves' index-query operand, read as one contiguous span and
+// redistributed through a wave-private LDS copy.  A row group's queries are
+// contiguous in memory ([4 NSET rows][4 heads][128]), so a wave reads the
+// span 16 bytes per lane and instruction (4 instructions for 4 bf16 rows);
+// read directly in the operand layout, each of 8 instructions per lane would
+// touch 16 partial cache lines, and those requests, repeated by every wave
+// of the launch, delay the pooled stream queued behind them.  Rows of the
+// span past M re-read the group's first row (their columns are zeroed).
+template <class EQ, int NSET>
+struct QSpan {
+  static constexpr int kRowBytes = kIndexHeads * kIndexDim * (int)sizeof(typename EQ::T);
+  static constexpr int kU4 = NSET * 4 * kRowBytes / (kWave * 16);  // 16-byte loads per lane
+  static constexpr int kWords = NSET * 4 * kRowBytes / 4;          // LDS words per wave
+};
+template <class EQ, int NSET>
+__device__ __forceinline__ void load_q_span(const typename EQ::T* __restrict__ idx_q, int M, int m0, int lane,
+                                            uint4 (&qv)[QSpan<EQ, NSET>::kU4]) {
+  using S = QSpan<EQ, NSET>;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(idx_q) + (int64_t)m0 * S::kRowBytes;
+#pragma unroll
+  for (int u = 0; u < S::kU4; ++u) {
+    const int o = (u * kWave + lane) * 16;
+    const int r = o / S::kRowBytes;
+    qv[u] = *reinterpret_cast<const uint4*>(base + (m0 + r < M ? o : o % S::kRowBytes));
+  }
+}
+template <class EQ, int NSET>
+__device__ __forceinline__ void stage_q_span(const uint4 (&qv)[QSpan<EQ, NSET>::kU4], uint32_t* __restrict__ qst,
+                                             int lane) {
+#pragma unroll
+  for (int u = 0; u < QSpan<EQ, NSET>::kU4; ++u) *reinterpret_cast<uint4*>(qst + (u * kWave + lane) * 4) = qv[u];
+}
+template <class EQ, int NSET>
+__device__ __forceinline__ void q_operand_lds(const uint32_t* __restrict__ qst, int rows, int i16, int kq,
+                                              float4 (&bq)[NSET][kChunks]) {
+  __builtin_amdgcn_wave_barrier();
+  // every piece read before any is used: one LDS round trip
+  typename QRaw<EQ>::T raw[NSET][kChunks];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int r = st * 4 + (i16 >> 2);
+    const int e0 = (r * kIndexHeads + (i16 & 3)) * kIndexDim + 4 * kq;  // element index of dims 4 kq .. + 3
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      raw[st][c] = *reinterpret_cast<const typename QRaw<EQ>::T*>(qst + (e0 + 16 * c) * (int)sizeof(typename EQ::T) / 4);
+  }
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const bool live = st * 4 + (i16 >> 2) < rows;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(raw[st][c]) : zero4();
+  }
+}
+
 // Scores of one 16-block group against every column set: sv[st][v] is the
 // score of block 4 kq + v of the group for row 4 st + i16 / 4 (the 4 heads'
 // ReLU'd dot products summed by two lane shuffles, then scaled).
@@ -297,8 +351,10 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   int64_t pos_r[RPG];
 #pragma unroll
   for (int r = 0; r < RPG; ++r) pos_r[r] = row_pos[m0 + (r < rows ? r : 0)];
-  typename QRaw<EQ>::T qraw[NSET][kChunks];
-  load_q_operand<EQ, NSET>(idx_q, m0, rows, i16, kq, qraw);
+  __shared__ __align__(16) uint32_t qstage[WPG][QSpan<EQ, NSET>::kWords];
+  uint4 qv[QSpan<EQ, NSET>::kU4];
+  load_q_span<EQ, NSET>(idx_q, M, m0, lane, qv);
+  stage_q_span<EQ, NSET>(qv, qstage[wave], lane);
   // folded append: one new token's position per lane (lanes past the count
   // repeat the last; 1 <= n_new <= 64)
   int64_t new_p = -1;
@@ -333,7 +389,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   if (!active) return;
 
   float4 bq[NSET][kChunks];
-  q_operand<EQ, NSET>(qraw, rows, i16, bq);
+  q_operand_lds<EQ, NSET>(qstage[wave], rows, i16, kq, bq);
   int64_t nb_row[NSET];
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {

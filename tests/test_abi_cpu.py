@@ -66,6 +66,8 @@ def test_append_pool_validation(args, code, word):
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 18, None, 0, None), ERR_ARG, "aligned"),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE + 4, 16, None, 0, None), ERR_ARG, "aligned"),
     ((FAKE, 1, 1, FAKE, None, None, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "null"),
+    # the index queries are read 16 bytes at a time
+    ((FAKE + 8, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, None, 0, None), ERR_ARG, "idx_q must be 16-byte"),
     ((FAKE, 1, 1, FAKE, None, FAKE, 1, 64, 16, FAKE, 16, FAKE, 100, None), ERR_WS, "workspace"),
     # 64 bf16 rows take the many-row kernel, whose buffer views of 16 score
     # rows must stay under 2 GiB
@@ -280,6 +282,7 @@ def _apsc(dtype=1, n_new=4, M=1, cap=64, nb=16, ld=16, scores=FAKE, ws=None, wsb
     (dict(M=64, ld=1 << 25), ERR_UNS, "many-row"),
     (dict(new=None), ERR_ARG, "null"),
     (dict(idx_q=None), ERR_ARG, "null"),
+    (dict(idx_q=FAKE + 2), ERR_ARG, "idx_q must be 16-byte"),
     (dict(n_new=0, M=0, new=None, idx_q=None), Q.QSA_OK, ""),
 ])
 def test_append_score_validation(kw, code, word):
