@@ -81,7 +81,10 @@ __device__ __forceinline__ float4 q_to_f4<BF16>(uint2 x) {
                      __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
 }
 
-__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+// Raw query words ANDed with an all-ones or all-zeros mask: a dead row's
+// operand becomes +0 in either format without a branch.
+__device__ __forceinline__ uint4 mask_raw(uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); }
+__device__ __forceinline__ uint2 mask_raw(uint2 x, uint32_t m) { return make_uint2(x.x & m, x.y & m); }
 
 // The append folded into the launch (one sequence).
 struct AppendArgs {
@@ -119,9 +122,9 @@ __device__ __forceinline__ void q_operand(const typename QRaw<EQ>::T (&qraw)[NSE
                                           float4 (&bq)[NSET][kChunks]) {
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {
-    const bool live = st * 4 + (i16 >> 2) < rows;
+    const uint32_t live = st * 4 + (i16 >> 2) < rows ? ~0u : 0u;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(qraw[st][c]) : zero4();
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = q_to_f4<EQ>(mask_raw(qraw[st][c], live));
   }
 }
 
@@ -173,9 +176,9 @@ __device__ __forceinline__ void q_operand_lds(const uint32_t* __restrict__ qst, 
   }
 #pragma unroll
   for (int st = 0; st < NSET; ++st) {
-    const bool live = st * 4 + (i16 >> 2) < rows;
+    const uint32_t live = st * 4 + (i16 >> 2) < rows ? ~0u : 0u;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) bq[st][c] = live ? q_to_f4<EQ>(raw[st][c]) : zero4();
+    for (int c = 0; c < kChunks; ++c) bq[st][c] = q_to_f4<EQ>(mask_raw(raw[st][c], live));
   }
 }
 
