@@ -60,6 +60,9 @@ constexpr int kWavesShort = 2;
 constexpr int64_t kShortRowBlocks = 16384;
 constexpr int kBlocksPerWave = kGroupBlocks * kGroupsPerWave;
 constexpr float kScoreScale = 0.08838834764831845f;  // 1/sqrt(128)
+constexpr int kBufferWord3 = 0x00020000;            // raw buffer view (gfx9 family)
+constexpr int kBufferDrop = (int)0x80000000u;       // an offset past any view: the store is dropped
+constexpr int64_t kMaxView = (int64_t)1 << 31;      // bytes of a buffer view
 
 // Index-query elements as loaded (4 per lane per chunk) and as MFMA operands.
 template <class EQ> struct QRaw;
@@ -79,6 +82,14 @@ template <>
 __device__ __forceinline__ float4 q_to_f4<BF16>(uint2 x) {
   return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
                      __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+}
+
+// A wave-uniform pointer, held in scalar registers.
+__device__ __forceinline__ float* scalar_ptr(float* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return reinterpret_cast<float*>(((uint64_t)hi << 32) | lo);
 }
 
 // Raw query words ANDed with an all-ones or all-zeros mask: a dead row's
@@ -414,6 +425,28 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     for (int off = kWave / 2; off > 0; off >>= 1) fresh |= (uint32_t)__shfl_xor((int)fresh, off, kWave);
   }
 
+  // Stores through buffer views of each column set's 4 rows (scores and,
+  // with HIST, the rows' workspace records), a masked lane's offset past the
+  // view: no branch, so the epilogue is one straight-line block.  Lane
+  // (kq, i16) stores block 4 kq + i16 % 4 of the group for row i16 / 4 of the
+  // set (the head sum left every head lane of a row with all four scores).
+  // Views over 2^31 bytes (rows of more than 2^27 blocks) take the branching
+  // form below.
+  // (readfirstlane: the compiler then keeps the test and the views scalar)
+  const bool views = __builtin_amdgcn_readfirstlane(4 * ld * 4 < kMaxView && (!HIST || 4 * rw * 4 < kMaxView)) != 0;
+  __amdgpu_buffer_rsrc_t srs[NSET], wrs[NSET];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const int rs = rows - 4 * st < 0 ? 0 : (rows - 4 * st < 4 ? rows - 4 * st : 4);  // live rows of the set
+    srs[st] = __builtin_amdgcn_make_buffer_rsrc(scalar_ptr(scores + (int64_t)(m0 + 4 * st) * ld), 0,
+                                                __builtin_amdgcn_readfirstlane(views ? (int)(rs * ld * 4) : 0),
+                                                kBufferWord3);
+    wrs[st] = __builtin_amdgcn_make_buffer_rsrc(
+        scalar_ptr(HIST ? reinterpret_cast<float*>(ws) + (int64_t)(m0 + 4 * st) * rw : nullptr), 0,
+        __builtin_amdgcn_readfirstlane(HIST && views ? (int)(rs * rw * 4) : 0), kBufferWord3);
+  }
+  const int hd = i16 & 3;
+
   // group by group, so that the first group's matrix work and stores
   // proceed while the second group's pooled loads are still arriving
 #pragma unroll
@@ -421,6 +454,29 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     float sv[NSET][4];
     group_scores<NSET>(a[g], bq, sv);
     const int64_t bb = wave_b0 + g * kGroupBlocks + 4 * kq;
+    if (views) {
+      const int64_t b = bb + hd;
+      const bool fr = (fresh >> (g * kGroupBlocks + 4 * kq + hd)) & 1u;
+      const bool smp = sel::sampled((uint32_t)b);
+#pragma unroll
+      for (int st = 0; st < NSET; ++st) {
+        const int rr = i16 >> 2;  // row of the set
+        // score hd of the four, picked with bit masks (a select chain here
+        // compiles to branches)
+        const uint32_t m1 = 0u - (uint32_t)(hd & 1), m2 = 0u - (uint32_t)(hd >> 1);
+        const uint32_t x01 = (__float_as_uint(sv[st][0]) & ~m1) | (__float_as_uint(sv[st][1]) & m1);
+        const uint32_t x23 = (__float_as_uint(sv[st][2]) & ~m1) | (__float_as_uint(sv[st][3]) & m1);
+        const uint32_t x = (x01 & ~m2) | (x23 & m2);
+        const bool keep = st * 4 + rr < rows && b < nb_row[st] && !fr;
+        __builtin_amdgcn_raw_buffer_store_b32(x, srs[st], keep ? (int)((rr * ld + b) * 4) : kBufferDrop, 0, 0);
+        if constexpr (HIST)
+          __builtin_amdgcn_raw_buffer_store_b32(x, wrs[st],
+                                                keep && smp ? (int)((rr * rw + smp_off + (b >> 4)) * 4) : kBufferDrop,
+                                                0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      continue;
+    }
 #pragma unroll
     for (int st = 0; st < NSET; ++st) {
       const int r = st * 4 + (i16 >> 2);
