@@ -228,7 +228,8 @@ __device__ __forceinline__ void group_scores(const float4 (&a)[kChunks], const f
 template <class EQ, int NSET, int RPG, bool HIST, int WPG>
 __device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int M,
                                    const int64_t* __restrict__ row_pos, int64_t nb_max, float* __restrict__ scores,
-                                   int64_t ld, uint32_t* __restrict__ ws, const AppendArgs& ap) {
+                                   int64_t ld, uint32_t* __restrict__ ws, int64_t rw, int64_t smp_off,
+                                   const AppendArgs& ap) {
   using T = typename EQ::T;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -258,8 +259,6 @@ __device__ void score_fresh_blocks(const typename EQ::T* __restrict__ idx_q, int
   q_operand<EQ, NSET>(qraw, rows, i16, bq);
   const T* nw = static_cast<const T*>(ap.new_idx);
   const T* ca = static_cast<const T*>(ap.cache);
-  const int64_t rw = sel::row_words(nb_max);
-  const int64_t smp_off = sel::sample_off(nb_max);
   for (; i < ap.n_new; i += WPG) {
     const int64_t cur = pl;
     pl = load_pos4(i + WPG);  // the wave's next token, in flight meanwhile
@@ -323,7 +322,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
                     const int64_t* __restrict__ row_pos, const int32_t* __restrict__ row_seq,
                     const float* __restrict__ pooled, int n_seq, int64_t capacity,
                     int64_t nb_max, float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ ws,
-                    AppendArgs ap) {
+                    int64_t rw, int64_t smp_off, AppendArgs ap) {
   static_assert(RPG <= 4 * NSET, "rows per group exceed the column sets");
   int bx = blockIdx.x;
   if constexpr (APPEND) {
@@ -334,7 +333,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     // (every row group's)
     if (bx < 2) {
       if (bx == 1) {
-        score_fresh_blocks<EQ, NSET, RPG, HIST, WPG>(idx_q, M, row_pos, nb_max, scores, ld, ws, ap);
+        score_fresh_blocks<EQ, NSET, RPG, HIST, WPG>(idx_q, M, row_pos, nb_max, scores, ld, ws, rw, smp_off, ap);
       } else if (blockIdx.y == 0) {
         for (int e = threadIdx.x; e < ap.n_new * kIndexDim; e += kWave * WPG)
           append_token_dim<EQ>(static_cast<const typename EQ::T*>(ap.new_idx), ap.pos, nullptr,
@@ -351,7 +350,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   const int rows = min(RPG, M - m0);
   // the selection that consumes the sample counts its chunks in from zero
   if (HIST && bx == 0 && (int)threadIdx.x < rows)
-    ws[(size_t)(m0 + threadIdx.x) * sel::row_words(nb_max) + sel::kArriveWord] = 0u;
+    ws[(size_t)(m0 + threadIdx.x) * rw + sel::kArriveWord] = 0u;
 
   // Everything is loaded up front.  The row positions (wave-uniform) and the
   // index-query operand are small and cached; issued before the pooled
@@ -377,8 +376,6 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
   // rows is one sequence's, so only the one-row kernel looks its sequence up
   const int s = (RPG == 1 && row_seq) ? row_seq[m0] : 0;
   const bool seq_ok = s >= 0 && s < n_seq;
-  const int64_t rw = sel::row_words(nb_max);
-  const int64_t smp_off = sel::sample_off(nb_max);
   const float* __restrict__ P = pooled + (int64_t)(seq_ok ? s : 0) * (capacity / kBlockTokens) * kIndexDim;
 
   // Pooled loads: all groups, all chunks, unconditional (blocks past nb_max
@@ -515,11 +512,12 @@ hipError_t launch_fewrow_wpg(const void* idx_q, int M, const int64_t* row_pos, c
   if (ap)
     hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, true, WPG>), dim3(grid.x + 2, grid.y),
                        dim3(kWave * WPG), 0, stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
-                       capacity, nb_max, scores, ld, ws, *ap);
+                       capacity, nb_max, scores, ld, ws, sel::row_words(nb_max), sel::sample_off(nb_max), *ap);
   else
     hipLaunchKernelGGL((score_fewrow_kernel<EQ, NSET, RPG, HIST, false, WPG>), grid, dim3(kWave * WPG), 0,
                        stream, static_cast<const typename EQ::T*>(idx_q), M, row_pos, row_seq, pooled, n_seq,
-                       capacity, nb_max, scores, ld, ws, AppendArgs{});
+                       capacity, nb_max, scores, ld, ws, sel::row_words(nb_max), sel::sample_off(nb_max),
+                       AppendArgs{});
   return hipGetLastError();
 }
 
