@@ -71,6 +71,32 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/) {
   return dpp_add_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
 }
 
+// Bitwise OR over the 64 lanes of a wave, through DPP moves: two quad
+// permutations and the half-row and row mirrors give every lane its 16-lane
+// row's OR, row_bcast 15 and 31 carry rows 0-2 into row 3, whose last lane is
+// read (the result is wave-uniform).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_or_step(uint32_t v) {
+  return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v = dpp_or_step<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_or_step<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_or_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_or_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_or_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_or_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// x plus the value of the lane whose index differs in bit 0 (XOR1) or bit 1,
+// within a quad of lanes: one DPP quad permutation, no LDS round trip.
+template <int XOR>
+__device__ __forceinline__ float quad_xor_add(float x) {
+  constexpr int kCtrl = XOR == 1 ? 0xB1 : 0x4E;  // quad_perm [1, 0, 3, 2] or [2, 3, 0, 1]
+  static_assert(XOR == 1 || XOR == 2, "quad lanes");
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
 // Make a value known to be wave-uniform visible as such to the compiler, so
 // that loads addressed by it become scalar loads.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

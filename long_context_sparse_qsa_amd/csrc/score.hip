@@ -21,7 +21,7 @@
 // the index-query operand is loaded with the same permutation, so the sum
 // is unchanged.  All of a wave's loads are issued before the first MFMA.
 // Output D[i][j] (i = block, j = row*4 + head) is ReLU'd and summed over the
-// 4 heads with two lane shuffles inside each group of 4 lanes.
+// 4 heads with two DPP quad permutations inside each group of 4 lanes.
 //
 // With HIST, the epilogue also feeds the top-k selection: the score of one
 // block per 16-block group (at a hashed offset) is stored in the row's sample
@@ -195,7 +195,7 @@ __device__ __forceinline__ void q_operand_lds(const uint32_t* __restrict__ qst, 
 
 // Scores of one 16-block group against every column set: sv[st][v] is the
 // score of block 4 kq + v of the group for row 4 st + i16 / 4 (the 4 heads'
-// ReLU'd dot products summed by two lane shuffles, then scaled).
+// ReLU'd dot products summed by two DPP quad permutations, then scaled).
 template <int NSET>
 __device__ __forceinline__ void group_scores(const float4 (&a)[kChunks], const float4 (&bq)[NSET][kChunks],
                                              float (&sv)[NSET][4]) {
@@ -212,9 +212,7 @@ __device__ __forceinline__ void group_scores(const float4 (&a)[kChunks], const f
     // acc[v] = D[4*kq + v][i16]: block 4kq + v of the group, column i16
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float x = fmaxf(acc[v], 0.f);
-      x += __shfl_xor(x, 1, kWave);
-      x += __shfl_xor(x, 2, kWave);
+      const float x = quad_xor_add<2>(quad_xor_add<1>(fmaxf(acc[v], 0.f)));
       sv[st][v] = x * kScoreScale;
     }
   }
@@ -418,8 +416,7 @@ score_fewrow_kernel(const typename EQ::T* __restrict__ idx_q, int M,
     const int64_t rel = (new_p >> 2) - wave_b0;
     fresh = completes_scored_block(new_p, ap.capacity, nb_max) && rel >= 0 && rel < kBlocksPerWave
                 ? 1u << rel : 0u;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) fresh |= (uint32_t)__shfl_xor((int)fresh, off, kWave);
+    fresh = wave_or(fresh);
   }
 
   // Stores through buffer views of each column set's 4 rows (scores and,
