@@ -48,8 +48,14 @@ quantize_kv_q8_kernel(const uint16_t* __restrict__ src, int n_head, int n_tok, i
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-  for (int off = 1; off < LANES; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));  // the block's lanes
+  // over the block's lanes through DPP moves: after the quad steps the
+  // half-row mirror joins the two quads of 8 lanes and the row mirror the two
+  // halves of 16 (a max needs no particular pairing)
+  static_assert(LANES == 8 || LANES == 16, "a 32-value block is 8 or 16 lanes");
+  amax = dpp_max_step<0xB1, 0xF>(amax);
+  amax = dpp_max_step<0x4E, 0xF>(amax);
+  amax = dpp_max_step<0x141, 0xF>(amax);
+  if constexpr (LANES == 16) amax = dpp_max_step<0x140, 0xF>(amax);
   const _Float16 s16 = (_Float16)(amax / kQ8Max);  // float32 quotient, round to nearest even
   uint16_t sbits = __builtin_bit_cast(uint16_t, s16);
   if ((sbits & 0x7fffu) == 0x7c00u) sbits = kF16MaxBits;  // f16 overflow clamps to 65504

@@ -37,21 +37,37 @@ struct BF16 {
   __device__ static __forceinline__ T from_f(float x) { return f32_to_bf16_bits(x); }
 };
 
-// Wave-wide reductions over 64 lanes (result in every lane).
+// Wave-wide reductions over 64 lanes through DPP moves (no LDS round
+// trips): two quad permutations and the half-row and row mirrors combine
+// each 16-lane row, row_bcast 15 and 31 carry rows 0-2 into row 3, and the
+// last lane's value is returned (wave-uniform).  Every lane of the wave must
+// be active.  Lanes a step does not update combine with the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROWS,
+                                                              0xF, false)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = dpp_sum_step<0xB1, 0xF>(v);
+  v = dpp_sum_step<0x4E, 0xF>(v);
+  v = dpp_sum_step<0x141, 0xF>(v);
+  v = dpp_sum_step<0x140, 0xF>(v);
+  v = dpp_sum_step<0x142, 0xA>(v);
+  v = dpp_sum_step<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 // Inclusive prefix sum over the 64 lanes of a wave, through DPP moves (no
 // LDS round trips): row_shr 1, 2, 4, 8 scan each 16-lane row (a lane whose

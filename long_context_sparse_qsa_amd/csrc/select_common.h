@@ -154,7 +154,7 @@ __device__ void find_digit_desc(const uint32_t* cnt, uint32_t want, uint32_t* ou
       }
     } else {
       const int L = __ffsll((unsigned long long)hit) - 1;
-      const uint32_t above = (uint32_t)__shfl((int)(incl - c), L, kWave);
+      const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - c), L);  // L is wave-uniform
       const int top = NBINS - L * R - 1;  // the run's top bin
       uint32_t v = 0u;
       if (l < R) {
