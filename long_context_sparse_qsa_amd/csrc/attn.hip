@@ -1126,9 +1126,11 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 
 // Merge split partials by log-sum-exp.  One workgroup per (row, head), one
 // thread per output dimension.  Each thread's partial outputs (up to
-// kRegSplits) and its own split's lse pair are loaded at once; thread i
-// computes split i's weight once and the weights are shared through LDS, so
-// the merge takes one memory round trip.  A partial carries two lse values:
+// kRegSplits) are loaded at once, and every wave loads all the splits' lse
+// pairs (lane i holds splits i and 64 + i): each wave finds the maximum,
+// the weights and their sums itself (DPP reductions) and reads the weights
+// out of its lanes, so the merge takes one memory round trip and no
+// workgroup barrier.  A partial carries two lse values:
 // that of the normaliser its output was divided by (the sum of the
 // bf16-rounded probabilities P.V consumed), which weighs the outputs so that
 // the merge equals one normalisation over all tokens, and that of the
@@ -1143,13 +1145,10 @@ template <class E, int D, int NS>
 __global__ void __launch_bounds__(D)
 attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int splits,
                     typename E::T* __restrict__ out, float* __restrict__ lse_out) {
-  static_assert(D >= NS && NS <= kRegSplits, "one thread per register-held split");
-  __shared__ float w_sh[NS];
-  __shared__ float red[D / kWave], red32[D / kWave];
+  static_assert(D >= NS && NS <= kRegSplits && kRegSplits <= 2 * kWave, "split lse pairs: two per lane");
   const int64_t head = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const float* __restrict__ L = ws_lse + 2 * head * splits;  // (weighting, reported) per split
   const float* __restrict__ O = ws_o + head * splits * D + tid;
   if (splits > NS) {  // long budgets: plain loops
@@ -1169,38 +1168,34 @@ attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     if (tid == 0) lse_out[head] = empty ? -INFINITY : mx + logf(tot32);
     return;
   }
+  constexpr int kHalves = NS > kWave ? 2 : 1;
   float ov[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) ov[i] = O[(int64_t)(i < splits ? i : splits - 1) * D];  // masked by w = 0
-  const f32x2_t l_pair = tid < splits ? *reinterpret_cast<const f32x2_t*>(L + 2 * tid) : f32x2_t{-INFINITY, -INFINITY};
-  const float l_own = l_pair.x;
-  float mx = wave_max(l_own);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
+  f32x2_t lp[kHalves];
 #pragma unroll
-  for (int w = 0; w < D / kWave; ++w) mx = fmaxf(mx, red[w]);
-  const bool empty = (mx == -INFINITY);
-  const float w_own = (empty || l_own == -INFINITY) ? 0.f : expf(l_own - mx);
-  const float w32 = (empty || l_pair.y == -INFINITY) ? 0.f : expf(l_pair.y - mx);
-  if (tid < NS) w_sh[tid] = w_own;
-  float tot = wave_sum(w_own);
-  float tot32 = wave_sum(w32);
-  __syncthreads();
-  if (lane == 0) {
-    red[wave] = tot;
-    red32[wave] = tot32;
+  for (int hv = 0; hv < kHalves; ++hv) {
+    const int i = lane + kWave * hv;
+    lp[hv] = i < splits ? *reinterpret_cast<const f32x2_t*>(L + 2 * i) : f32x2_t{-INFINITY, -INFINITY};
   }
-  __syncthreads();
-  tot = 0.f;
-  tot32 = 0.f;
+  float mx = lp[0].x;
 #pragma unroll
-  for (int w = 0; w < D / kWave; ++w) {
-    tot += red[w];
-    tot32 += red32[w];
+  for (int hv = 1; hv < kHalves; ++hv) mx = fmaxf(mx, lp[hv].x);
+  mx = wave_max(mx);
+  const bool empty = (mx == -INFINITY);
+  float w[kHalves];
+  float tot = 0.f, tot32 = 0.f;
+#pragma unroll
+  for (int hv = 0; hv < kHalves; ++hv) {
+    w[hv] = (empty || lp[hv].x == -INFINITY) ? 0.f : expf(lp[hv].x - mx);
+    const float w32 = (empty || lp[hv].y == -INFINITY) ? 0.f : expf(lp[hv].y - mx);
+    tot += wave_sum(w[hv]);
+    tot32 += wave_sum(w32);
   }
   float o = 0.f;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) o = fmaf(w_sh[i], ov[i], o);  // every partial is finite
+  for (int i = 0; i < NS; ++i)  // every partial is finite
+    o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[i / kWave]), i % kWave)), ov[i], o);
   const bool none = empty || tot == 0.f;
   out[head * D + tid] = E::from_f(none ? 0.f : o / tot);
   if (tid == 0) lse_out[head] = none ? -INFINITY : mx + logf(tot32);
