@@ -1077,21 +1077,28 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
   __syncthreads();
   if (tid < kGroup) {  // per-head merge weights, once
     const int h = tid;
+    // every wave's (m, l, l32) read in one batch, the weights written in one
+    float mw[nw], lw[nw], l32w[nw];
+#pragma unroll
+    for (int w = 0; w < nw; ++w) {
+      mw[w] = fl[Lds::m(nw, w) + h];
+      lw[w] = fl[Lds::l(nw, w) + h];
+      l32w[w] = fl[Lds::l32(nw, w) + h];
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, fl[Lds::m(nw, w) + h]);
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, mw[w]);
+    float f[nw];
     float L = 0.f, L32 = 0.f;
 #pragma unroll
     for (int w = 0; w < nw; ++w) {
-      const float mw = fl[Lds::m(nw, w) + h];
-      const float f = (mx == -INFINITY || mw == -INFINITY) ? 0.f : exp2f(mw - mx);
-      fl[Lds::wt(nw, h) + w] = f;
-      L += fl[Lds::l(nw, w) + h] * f;
-      L32 += fl[Lds::l32(nw, w) + h] * f;
+      f[w] = (mx == -INFINITY || mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - mx);
+      L += lw[w] * f[w];
+      L32 += l32w[w] * f[w];
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int w = 0; w < nw; ++w) fl[Lds::wt(nw, h) + w] *= inv;
+    for (int w = 0; w < nw; ++w) fl[Lds::wt(nw, h) + w] = f[w] * inv;
     fl[Lds::lse(nw) + 2 * h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
     fl[Lds::lse(nw) + 2 * h + 1] = L32 > 0.f ? (mx + log2f(L32)) * kLn2 : -INFINITY;
   }
