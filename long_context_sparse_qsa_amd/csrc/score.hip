@@ -52,11 +52,13 @@ constexpr int kGroupBlocks = 16;   // blocks per MFMA row group
 constexpr int kChunks = kIndexDim / 16;  // 8 chunks of 16 dims
 constexpr int kGroupsPerWave = 2;
 // Waves per workgroup (the kernels' WPG): 4 for long rows of one
-// sequence, 2 for rows of at most 16,384 blocks or rows of different
-// sequences (measured: decode at 32K context 4.9 against 6.0 us, batched
-// decode 32.8 against 34.2 us; the 262K verify equal either way).
+// sequence, 1 for rows of at most 16,384 blocks or rows of different
+// sequences, so that short rows spread over more compute units (measured:
+// decode at 32K context 4.3 us with 2 waves, 4.15 with 1, 6.0 with 4;
+// batched decode 28.0 against 27.4 us with 1; the 262K verify's launch is
+// 0.15 us faster with 2 but its step no faster).
 constexpr int kWavesLong = 4;
-constexpr int kWavesShort = 2;
+constexpr int kWavesShort = 1;
 constexpr int64_t kShortRowBlocks = 16384;
 constexpr int kBlocksPerWave = kGroupBlocks * kGroupsPerWave;
 constexpr float kScoreScale = 0.08838834764831845f;  // 1/sqrt(128)
