@@ -1229,6 +1229,7 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
                        static_cast<uint16_t*>(out), lse, ws_o, ws_lse);                               \
     break;
     switch (plan.waves) {
+      QSA_MFMA_LAUNCH(3)
       QSA_MFMA_LAUNCH(4)
       QSA_MFMA_LAUNCH(5)
       QSA_MFMA_LAUNCH(6)
@@ -1263,10 +1264,12 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
 constexpr long kCUs = 256;
 
 // Matrix-core kernel: a workgroup holds `waves` 16-token slices of a tile.
-// Four waves (one per SIMD) when every (row, KV head, split) workgroup then
-// has a compute unit of its own; otherwise the fewest waves, up to 8, that
-// fit: a second workgroup on a unit slows both more than a fifth wave does,
-// and fewer waves than four only add split partials to merge.  When even 8
+// The fewest waves, from 3 up to 8, with which every (row, KV head, split)
+// workgroup has a compute unit of its own: a second workgroup on a unit
+// slows both more than another wave does.  Three waves serve one or two rows
+// (measured, M = 1 at a 2,051-token budget: 10.2 us with 3 waves and 43
+// splits, 10.5 with 4 and 33, 17.3 with 2 and 65: past that the combine's
+// partials cost more than the shorter tiles save).  When even 8
 // waves cannot fit, several tiles per workgroup: up to 4 units' worth of
 // one-tile workgroups, 4 waves walking as many tiles as keep the grid to one
 // workgroup per unit; beyond that (prefill) 8 waves walking as many tiles as
@@ -1276,7 +1279,7 @@ AttnPlan attn_plan(int M, int hkv, int k_blocks) {
   const int slices = (max_tokens + 15) / 16;
   const long rows = (long)M * hkv;
   AttnPlan p;
-  int w = 4;
+  int w = 3;
   while (w < kMaxWaves && rows * ((slices + w - 1) / w) > kCUs) ++w;
   const int tiles = (slices + w - 1) / w;
   p.waves = w;

@@ -199,11 +199,12 @@ def test_attn_null_kv():
 
 
 def test_workspace_sizes():
-    # one row, 2 KV heads, budget 512 blocks = 2,051 tokens at most: 33
-    # splits of 64 tokens in both plans; a partial per head holds 256 floats
-    # of output and two lse values (that of the normaliser it was divided by,
-    # and that of the float32 probabilities)
-    assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 33 * 258 * 4
+    # one row, 2 KV heads, budget 512 blocks = 2,051 tokens at most: 43
+    # splits of 48 tokens in the bf16 plan (3 waves), 33 of 64 in the float32
+    # one; a partial per head holds 256 floats of output and two lse values
+    # (that of the normaliser it was divided by, and that of the float32
+    # probabilities)
+    assert Q.qsa_attn_workspace_bytes(1, 24, 256, 512) == 1 * 24 * 43 * 258 * 4
     # up to four rows: the bf16 plan needs at most 4 x 26 partials per head
     # (four rows in 5-wave workgroups); the float32 plan keeps 33 splits of
     # 64 tokens at four rows, which is the largest need
@@ -220,7 +221,8 @@ def test_workspace_sizes():
 def test_attn_plan_query():
     """The plan query answers on the host and refuses bad arguments."""
     p1 = Q.qsa_attn_plan(1, 2, 512)
-    assert p1 == {"waves": 4, "tile_tokens": 64, "tiles_per_split": 1, "splits": 33}
+    assert p1 == {"waves": 3, "tile_tokens": 48, "tiles_per_split": 1, "splits": 43}
+    assert Q.qsa_attn_plan(4, 2, 512) == {"waves": 5, "tile_tokens": 80, "tiles_per_split": 1, "splits": 26}
     pf = Q.qsa_attn_plan(2048, 2, 512)
     assert pf["waves"] == 8 and pf["tiles_per_split"] * pf["tile_tokens"] * pf["splits"] >= 2051
     out = (ctypes.c_int32 * 4)()

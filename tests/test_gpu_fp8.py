@@ -198,3 +198,22 @@ def test_fp8_many_rows_split_and_multi_tile(Q):
     res = layer.run()
     st = check_layer(d, res, layer)
     say(plan, f"max-abs {max(x['err'] for x in st):.3g}, lse {max(x['lse_err'] for x in st):.3g}")
+
+
+@pytest.mark.parametrize("rows", [[32767], [20001, 32766]])
+def test_fp8_one_and_two_rows_three_wave_plan(Q, rows):
+    """One or two rows at a 512-block budget take the 3-wave plan (48-token
+    tiles, 43 one-tile splits) with fp8 K/V."""
+    plan = Q.qsa_attn_plan(len(rows), 2, 512)
+    assert plan["waves"] == 3 and plan["tiles_per_split"] == 1 and plan["splits"] == 43, plan
+    say("fp8 K/V, rows", rows, plan)
+    base = datagen.gen_layer("decode_32k")
+    d = dict(base)
+    rng = np.random.default_rng(5 + len(rows))
+    m = len(rows)
+    d["rows"] = np.array(rows, dtype=np.int64)
+    d["idx_q"] = datagen.round_bf16(rng.standard_normal((m, 4, 128)).astype(np.float32))
+    d["q"] = datagen.round_bf16(rng.standard_normal((m, 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=32768, kv="fp8")
+    res = layer.run()
+    say(check_layer(d, res, layer))
