@@ -49,6 +49,7 @@ using sel::order_key;
 constexpr int kThrThreads = 256;
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kFlatCap / kFinThreads;  // 8 candidate slots per thread
+constexpr int kSpecPer = 3;                        // slots per thread loaded with the count (1,536)
 constexpr int kLowBins = 1024;
 constexpr int kMaxTies = 512;                      // keys equal to TK ranked on chip
 constexpr int64_t kBitmapBlocks = 262144;          // rows up to 1M tokens take the candidate path
@@ -144,16 +145,31 @@ flat_finalize_kernel(const uint16_t* __restrict__ idx_q, const int64_t* __restri
   const sel::FlatLayout L = sel::flat_layout(M, nb_max);
   int32_t* __restrict__ out = sel + (int64_t)m * k;
   const uint16_t* q_row = idx_q + (int64_t)m * kIndexHeads * kIndexDim;
-  // every slot and the count are loaded at once; the count decides which are live
+  // The first kSpecPer slots per thread and the count are loaded at once
+  // (a row usually holds about 1.25 k + 256 candidates, well within them);
+  // the other slots only when the count reaches past them.
   const uint2* P = reinterpret_cast<const uint2*>(ws + L.pairs) + (int64_t)m * kFlatCap;
   uint32_t kk[kFinPer], ii[kFinPer];
 #pragma unroll
-  for (int e = 0; e < kFinPer; ++e) {
+  for (int e = 0; e < kSpecPer; ++e) {
     const uint2 kv = P[e * kFinThreads + tid];
     kk[e] = kv.x;
     ii[e] = kv.y;
   }
   const uint32_t n_cand = ws[L.cnt + m];
+#pragma unroll
+  for (int e = kSpecPer; e < kFinPer; ++e) {
+    kk[e] = 0u;
+    ii[e] = 0u;
+  }
+  if (n_cand > (uint32_t)(kSpecPer * kFinThreads) && n_cand <= (uint32_t)kFlatCap) {  // uniform
+#pragma unroll
+    for (int e = kSpecPer; e < kFinPer; ++e) {
+      const uint2 kv = P[e * kFinThreads + tid];
+      kk[e] = kv.x;
+      ii[e] = kv.y;
+    }
+  }
   const int64_t nb = clamp_nb(row_pos[m], nb_max);
   uint32_t* path = ws + L.path + m;
   if (nb <= k) {

@@ -190,3 +190,49 @@ def test_flat_every_block_a_candidate(Q):
     assert np.array_equal(cnt[every], nb[every]), (cnt[every][:8], nb[every][:8])
     assert torch.equal(n_sel, res["n_sel"]) and torch.equal(sel, res["sel"])
     say(f"{int(every.sum())} rows with every block a candidate")
+
+
+def test_flat_candidates_past_the_first_slot_load(Q):
+    """Rows of 1,600..1,727 blocks whose scores all fall in one histogram
+    digit: every index key is 1 + j/128 (j = 0..7, drawn per token) on
+    dimension 0 and zero elsewhere, and each row's query is 1 on dimension 0
+    of one head, so its scores take 27 distinct values within 6 % and every
+    block is a candidate -- more than the 1,536 slots the finalize loads with
+    the count, so it loads the rest in a second round trip.  The cut's ties
+    (about 120) fit the on-chip tie list, so these rows take the candidate
+    path.  One row in eight has zero queries instead: every block ties at
+    score 0, more than the tie list holds, and the exact whole-row path keeps
+    the k lowest ids.  Every selection equals the materialized path's."""
+    say("flat select, rows with 1,600..1,727 candidates")
+    base = datagen.gen_layer("decode_32k")
+    d = dict(base)
+    rng = np.random.default_rng(37)
+    n_ctx = d["idx"].shape[0]
+    idx = np.zeros((n_ctx, 128), dtype=np.float32)
+    idx[:, 0] = 1.0 + rng.integers(0, 8, size=n_ctx) / 128.0  # exact in bf16
+    d["idx"] = idx
+    m = 256
+    rows = np.arange(6400, 6400 + 2 * m, 2, dtype=np.int64)
+    q = np.zeros((m, 4, 128), dtype=np.float32)
+    tie = np.arange(m) % 8 == 7
+    for i in np.flatnonzero(~tie):
+        q[i, i % 4, 0] = 1.0
+    d["rows"] = rows
+    d["idx_q"] = q
+    d["q"] = datagen.round_bf16(rng.standard_normal((m, 24, 256)).astype(np.float32))
+    layer = Layer(d, prefix_split=32768)
+    k = layer.wl.k_blocks
+    res = layer.run()
+    sel, n_sel, paths, ws = _flat(Q, layer, k)
+    assert np.array_equal(paths, np.where(tie, 5, 2)), np.unique(paths, return_counts=True)
+    r64 = -(-m // 64) * 64
+    cnt = ws.view(torch.int32).cpu().numpy().view(np.uint32)[r64:r64 + m]
+    nb = (rows + 1) // 4
+    assert np.array_equal(cnt, nb) and (cnt > 1536).all(), cnt[:8]
+    assert torch.equal(n_sel, res["n_sel"]) and torch.equal(sel, res["sel"])
+    s = sel.cpu().numpy()
+    assert (s[tie] == np.arange(k)).all()
+    pooled = O.pool_index_keys(d["idx"])
+    for i in list(np.flatnonzero(~tie)[:4]) + [int(np.flatnonzero(tie)[0])]:
+        s64 = O.score_blocks(d["idx_q"][i], pooled, int(rows[i]) + 1)
+        check_selection(s[i], int(n_sel[i]), s64, k)
