@@ -1146,7 +1146,7 @@ attn_mfma_kernel(const uint16_t* __restrict__ q, int M, int hq, float scale_log2
 constexpr int kRegSplits = 72;
 
 // NS: the splits one thread holds in registers (the launch picks the
-// smallest of 16, 32, 72 that covers the plan, so no load is spent on
+// smallest multiple of 8 up to 72 that covers the plan, so no load is spent on
 // padding); more splits than 72 take plain loops.
 template <class E, int D, int NS>
 __global__ void __launch_bounds__(D)
@@ -1248,13 +1248,26 @@ hipError_t launch_typed(const void* q, int M, int hq, int hkv, float scale,
   if (e != hipSuccess || plan.splits == 1) return e;
   const dim3 cgrid((unsigned)M * hq), cblock(D);
   typename E::T* o = static_cast<typename E::T*>(out);
-  if (plan.splits <= 16)
-    hipLaunchKernelGGL((attn_combine_kernel<E, D, 16>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits, o, lse);
-  else if (plan.splits <= 32)
-    hipLaunchKernelGGL((attn_combine_kernel<E, D, 32>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits, o, lse);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<E, D, kRegSplits>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits,
-                       o, lse);
+  // the smallest multiple of 8 register-held splits that covers the plan
+#define QSA_COMBINE(NS)                                                                                  \
+  case NS / 8:                                                                                          \
+    hipLaunchKernelGGL((attn_combine_kernel<E, D, NS>), cgrid, cblock, 0, stream, ws_o, ws_lse, plan.splits, o, \
+                       lse);                                                                            \
+    break;
+  switch (plan.splits <= kRegSplits ? (plan.splits + 7) / 8 : kRegSplits / 8) {
+    QSA_COMBINE(8)
+    QSA_COMBINE(16)
+    QSA_COMBINE(24)
+    QSA_COMBINE(32)
+    QSA_COMBINE(40)
+    QSA_COMBINE(48)
+    QSA_COMBINE(56)
+    QSA_COMBINE(64)
+    default:  // more than 64 splits (the kernel loops past kRegSplits)
+      hipLaunchKernelGGL((attn_combine_kernel<E, D, kRegSplits>), cgrid, cblock, 0, stream, ws_o, ws_lse,
+                         plan.splits, o, lse);
+  }
+#undef QSA_COMBINE
   return hipGetLastError();
 }
 
