@@ -309,7 +309,8 @@ int qsa_gathered_attn_noalloc(const void* q, int32_t dtype, int32_t M, int32_t h
  * scores: a sampled threshold per row, candidates above it appended during
  * scoring, an exact selection among them.
  *
- *  idx_q     bf16 [M][4][128]            index queries (one sequence)
+ *  idx_q     bf16 [M][4][128]            index queries (one sequence), 16-byte
+ *                                        aligned
  *  M >= 0; row_pos int64 [M]; pooled float32 [nb_max][128] (the sequence's
  *  pooled keys, e.g. the first sequence of qsa_append_pool's buffer)
  *  nb_max    >= max blocks of any row (a host bound), at most

@@ -282,6 +282,7 @@ int qsa_score_select(const void* idx_q, int32_t M, const int64_t* row_pos, const
   if (((uintptr_t)workspace & 15u) != 0) return fail(QSA_ERR_ARG, "qsa_score_select: workspace must be 16-byte aligned");
   if (!idx_q || !row_pos || !sel || !n_sel || (nb_max > 0 && !pooled))
     return fail(QSA_ERR_ARG, "qsa_score_select: null pointer (idx_q, row_pos, pooled, sel or n_sel)");
+  if ((uintptr_t)idx_q & 15u) return fail(QSA_ERR_ARG, "qsa_score_select: idx_q must be 16-byte aligned");
   return launch_status(qsa::launch_score_select_flat(idx_q, M, row_pos, pooled, nb_max, k_blocks, sel, n_sel,
                                                      workspace, (hipStream_t)stream),
                        "qsa_score_select");

@@ -249,6 +249,7 @@ def _ssel(M=2, nb=100, k=16, ws=FAKE, wsb=1 << 30, idx=FAKE):
     (dict(ws=None), ERR_WS, "workspace"),
     (dict(ws=FAKE + 4), ERR_ARG, "aligned"),
     (dict(idx=None), ERR_ARG, "null"),
+    (dict(idx=FAKE + 8), ERR_ARG, "idx_q must be 16-byte"),
     (dict(M=0, ws=None, wsb=0), Q.QSA_OK, ""),
 ])
 def test_score_select_validation(kw, code, word):
