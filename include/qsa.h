@@ -238,7 +238,7 @@ typedef struct qsa_kv_segments {
  * cores); MTPLX PR #610 ("What changes": partials merged by log-sum-exp in
  * float32, rounded once; rows with no visible key give zeros, not NaN).
  *
- *  q          [M][hq][head_dim] dtype   query rows
+ *  q          [M][hq][head_dim] dtype   query rows, 16-byte aligned
  *  M >= 0; hq, hkv with hq % hkv == 0 and hq/hkv == 12; head_dim 128 or 256
  *  scale      softmax scale (finite), usually 1/sqrt(head_dim)
  *  row_pos    int64 [M]; row_seq int32 [M] or NULL (all sequence 0)

@@ -216,6 +216,8 @@ int check_attn_args(const char* fn, const void* q, int32_t dtype, int32_t M, int
     return fail(QSA_ERR_ARG, "%s: null pointer (q, row_pos, sel, n_sel, out or lse)", fn);
   if (M > 0 && ((uintptr_t)out & 15u))
     return fail(QSA_ERR_ARG, "%s: out must be 16-byte aligned", fn);
+  if (M > 0 && ((uintptr_t)q & 15u))
+    return fail(QSA_ERR_ARG, "%s: q must be 16-byte aligned", fn);
   return QSA_OK;
 }
 

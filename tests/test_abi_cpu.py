@@ -103,9 +103,9 @@ def _kv(n_seq=1, n_seg=1, max_seg=1, null=False, fmt=0, scales=False):
 
 
 def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FAKE, wsb=1 << 30,
-          out=FAKE):
+          out=FAKE, q=FAKE):
     kv = kv or _kv()
-    return L.qsa_gathered_attn(FAKE, dtype, M, hq, hkv, d, scale, FAKE, None, ctypes.byref(kv), FAKE,
+    return L.qsa_gathered_attn(q, dtype, M, hq, hkv, d, scale, FAKE, None, ctypes.byref(kv), FAKE,
                                FAKE, k, out, FAKE, ws, wsb, None)
 
 
@@ -126,6 +126,7 @@ def _attn(dtype=1, M=1, hq=24, hkv=2, d=256, scale=0.0625, kv=None, k=512, ws=FA
     (dict(wsb=100), ERR_WS, "workspace"),
     (dict(out=None), ERR_ARG, "null"),
     (dict(out=FAKE + 8), ERR_ARG, "aligned"),
+    (dict(q=FAKE + 8), ERR_ARG, "q must be 16-byte"),
     (dict(ws=FAKE + 4), ERR_ARG, "aligned"),
     (dict(M=0, ws=None, wsb=0), Q.QSA_OK, ""),
 ])
